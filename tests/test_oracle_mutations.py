@@ -1,0 +1,191 @@
+"""Plants plausible mistakes in the CPU oracle and requires that at least one
+pin in ``oracle_pins`` fails for each: evidence that the pins would notice a
+dropped term, a wrong sign or index, or a transposed operand."""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle.olmo3_oracle as O
+from oracle_pins import ALL_CHECKS
+
+_orig = {name: getattr(O, name) for name in dir(O) if not name.startswith("__")}
+
+
+def _mask_le_window(T, window):
+    t = np.arange(T)[:, None]
+    s = np.arange(T)[None, :]
+    return (s <= t) & (t - s <= window)
+
+
+def _mask_at_le_window(q_pos, k_pos, kind, window):
+    t = np.asarray(q_pos)[:, None]
+    s = np.asarray(k_pos)[None, :]
+    ok = (s >= 0) & (s <= t)
+    if kind == O.SLIDING:
+        ok &= (t - s) <= window
+    return ok
+
+
+def _mask_at_noncausal(q_pos, k_pos, kind, window):
+    t = np.asarray(q_pos)[:, None]
+    s = np.asarray(k_pos)[None, :]
+    ok = s >= 0
+    if kind == O.SLIDING:
+        ok &= np.abs(t - s) < window
+    return ok
+
+
+def _layer_types_no_last(n):
+    return [O.FULL if layer % 4 == 3 else O.SLIDING for layer in range(n)]
+
+
+def _layer_types_mod4_eq0(n):
+    return [O.FULL if (layer % 4 == 0 or layer == n - 1) else O.SLIDING for layer in range(n)]
+
+
+def _rms_mean_abs(x, gain, eps):
+    x = np.asarray(x, dtype=np.float64)
+    return x / (np.mean(np.abs(x), axis=-1, keepdims=True) + eps) * gain
+
+
+def _rms_no_gain(x, gain, eps):
+    x = np.asarray(x, dtype=np.float64)
+    if np.asarray(gain).shape != x.shape[-1:]:
+        raise ValueError("gain")
+    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+
+
+def _rms_per_head(x, gain, eps, d=8):
+    x = np.asarray(x, dtype=np.float64)
+    n = x.shape[-1]
+    if n % d:
+        return _orig["rms_norm"](x, gain, eps)
+    y = x.reshape(*x.shape[:-1], n // d, d)
+    y = y / np.sqrt(np.mean(y * y, axis=-1, keepdims=True) + eps)
+    return y.reshape(x.shape) * gain
+
+
+def _gain_widths_per_head(H, G, d):
+    return d, d
+
+
+def _rope_sign(x, positions, inv_freq, mscale=1.0):
+    return _orig["rope_rotate"](x, -np.asarray(positions), inv_freq, mscale)
+
+
+def _rope_adjacent(x, positions, inv_freq, mscale=1.0):
+    x = np.asarray(x, dtype=np.float64)
+    ang = np.asarray(positions, dtype=np.float64)[:, None] * inv_freq[None, :]
+    cos, sin = np.cos(ang)[:, None, :], np.sin(ang)[:, None, :]
+    x1, x2 = x[..., 0::2], x[..., 1::2]
+    out = np.empty_like(x)
+    out[..., 0::2] = x1 * cos - x2 * sin
+    out[..., 1::2] = x2 * cos + x1 * sin
+    return out * mscale
+
+
+def _rope_no_mscale(x, positions, inv_freq, mscale=1.0):
+    return _orig["rope_rotate"](x, positions, inv_freq, 1.0)
+
+
+def _inv_freq_i_over_d(theta, d):
+    i = np.arange(d // 2, dtype=np.float64)
+    return np.float64(theta) ** (-1.0 * i / d)
+
+
+def _yarn_swapped(theta, d, factor, orig_ctx, beta_fast=32.0, beta_slow=1.0):
+    w = O.rope_inv_freq(theta, d)
+    if factor == 1.0:
+        return w
+    r = orig_ctx * w / (2 * math.pi)
+    gamma = np.clip((r - beta_slow) / (beta_fast - beta_slow), 0.0, 1.0)
+    return gamma * (w / factor) + (1.0 - gamma) * w
+
+
+def _yarn_mscale_log2(factor):
+    return 1.0 if factor <= 1.0 else 0.1 * math.log2(factor) + 1.0
+
+
+def _layer_rope_yarn_everywhere(rope, kind, d):
+    return _orig["layer_rope"](rope, O.FULL if rope.yarn else kind, d)
+
+
+def _attend_factory(scale_fn=None, group_fn=None, transpose_p=False):
+    def attend(q, q_pos, k, v, k_pos, kind, window, row_block=1024):
+        Tq, H, d = q.shape
+        N, G, _ = k.shape
+        group = H // G
+        scale = scale_fn(d) if scale_fn else 1.0 / math.sqrt(d)
+        out = np.zeros((Tq, H, d))
+        allowed = O.mask_at_positions(q_pos, k_pos, kind, window)
+        for h in range(H):
+            g = group_fn(h, G, group) if group_fn else h // group
+            s = (q[:, h, :] @ k[:, g, :].T) * scale
+            s = np.where(allowed, s, -np.inf)
+            s = s - s.max(axis=1, keepdims=True)
+            p = np.exp(s)
+            p = p / p.sum(axis=1, keepdims=True)
+            if transpose_p and p.shape[0] == p.shape[1]:
+                p = p.T
+            out[:, h, :] = p @ v[:, g, :]
+        return out
+    return attend
+
+
+class _RingOffByOne(O.KvCacheRef):
+    def slot(self, p):
+        return p % (self.window + 1) % self.capacity if self.kind == O.SLIDING else p
+
+
+class _RingKeepsFirst(O.KvCacheRef):
+    def append(self, k, v, positions):
+        for j, p in reversed(list(enumerate(np.asarray(positions)))):
+            s = self.slot(int(p))
+            self.k[:, :, s, :] = k[:, j]
+            self.v[:, :, s, :] = v[:, j]
+            self.pos[s] = p
+
+
+def _cache_entries_all(kind, window, context):
+    return context
+
+
+MUTANTS = {
+    "mask t-s <= window": dict(sliding_window_mask=_mask_le_window, mask_at_positions=_mask_at_le_window),
+    "mask not causal": dict(mask_at_positions=_mask_at_noncausal),
+    "last layer not full": dict(layer_types=_layer_types_no_last),
+    "full when l mod 4 == 0": dict(layer_types=_layer_types_mod4_eq0),
+    "rms uses mean |x|": dict(rms_norm=_rms_mean_abs),
+    "rms drops gain": dict(rms_norm=_rms_no_gain),
+    "rms per head": dict(rms_norm=_rms_per_head),
+    "gain widths per head": dict(qk_gain_widths=_gain_widths_per_head),
+    "rope sign flipped": dict(rope_rotate=_rope_sign),
+    "rope adjacent pairs": dict(rope_rotate=_rope_adjacent),
+    "rope drops mscale": dict(rope_rotate=_rope_no_mscale),
+    "rope exponent i/d": dict(rope_inv_freq=_inv_freq_i_over_d),
+    "yarn ramp swapped": dict(yarn_inv_freq=_yarn_swapped),
+    "yarn mscale log2": dict(yarn_mscale=_yarn_mscale_log2),
+    "yarn on sliding layers": dict(layer_rope=_layer_rope_yarn_everywhere),
+    "scale 1/d": dict(attend=_attend_factory(scale_fn=lambda d: 1.0 / d)),
+    "scale missing": dict(attend=_attend_factory(scale_fn=lambda d: 1.0)),
+    "gqa h mod G": dict(attend=_attend_factory(group_fn=lambda h, G, grp: h % G)),
+    "probabilities transposed": dict(attend=_attend_factory(transpose_p=True)),
+    "ring slot p mod (w+1)": dict(KvCacheRef=_RingOffByOne),
+    "ring keeps first writer": dict(KvCacheRef=_RingKeepsFirst),
+    "no window bound on cache": dict(cache_entries=_cache_entries_all),
+}
+
+
+@pytest.mark.parametrize("name", list(MUTANTS))
+def test_pins_catch_planted_mistake(name, monkeypatch):
+    for attr, fn in MUTANTS[name].items():
+        monkeypatch.setattr(O, attr, fn)
+    failed = []
+    for check in ALL_CHECKS:
+        try:
+            check()
+        except (AssertionError, ValueError, IndexError):
+            failed.append(check.__name__)
+    assert failed, f"no pin noticed the planted mistake '{name}'"
