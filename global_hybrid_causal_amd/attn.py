@@ -1,0 +1,238 @@
+"""ctypes binding of libolmo3attn (C ABI in include/olmo3_attn.h).
+
+Argument marshalling only: shapes are read off the tensors, device pointers
+and the current HIP stream are passed through, and a non-zero status is
+raised as ``Olmo3Error``.  Every step of the computation runs in the HIP
+library; there is no fallback, and a missing library is an error.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+from . import LAYER_FULL, LAYER_SLIDING  # noqa: F401  (re-exported)
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libolmo3attn.so")
+
+DTYPE_BF16, DTYPE_F32 = 0, 1
+MODE_PREFILL, MODE_DECODE = 0, 1
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_CAPACITY, ERR_HIP, ERR_WORKSPACE = range(6)
+
+# Every symbol include/olmo3_attn.h declares.
+EXPORTS = (
+    "olmo3_layer_type", "olmo3_workspace_bytes", "olmo3_kv_append", "olmo3_attn_prefill",
+    "olmo3_attn_decode", "olmo3_status_string", "olmo3_abi_version",
+    "olmo3_probe_prefill_visits", "olmo3_probe_decode_reads",
+)
+
+
+class RopeStruct(ctypes.Structure):
+    """Mirror of ``olmo3_rope``."""
+
+    _fields_ = [
+        ("theta", ctypes.c_double),
+        ("yarn", ctypes.c_int32),
+        ("factor", ctypes.c_double),
+        ("orig_ctx", ctypes.c_int64),
+        ("beta_fast", ctypes.c_double),
+        ("beta_slow", ctypes.c_double),
+        ("attn_factor", ctypes.c_double),
+    ]
+
+
+@dataclass(frozen=True)
+class Rope:
+    """RoPE / YaRN settings; YaRN (when on) applies to full layers only."""
+
+    theta: float = 500000.0
+    yarn: bool = False
+    factor: float = 8.0
+    orig_ctx: int = 8192
+    beta_fast: float = 32.0
+    beta_slow: float = 1.0
+    attn_factor: float = 0.0
+
+    def to_c(self) -> RopeStruct:
+        return RopeStruct(self.theta, int(bool(self.yarn)), self.factor, int(self.orig_ctx),
+                          self.beta_fast, self.beta_slow, self.attn_factor)
+
+
+class Olmo3Error(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} (status {status})")
+
+
+_lib = None
+_i, _i64, _f, _p, _sz = ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                               "(hipcc --offload-arch=gfx950)")
+        L = ctypes.CDLL(LIB_PATH)
+        L.olmo3_layer_type.argtypes = [_i, _i]
+        L.olmo3_layer_type.restype = _i
+        L.olmo3_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _i, _i, _i, _i64]
+        L.olmo3_workspace_bytes.restype = _sz
+        L.olmo3_kv_append.argtypes = [_i, _i, _i, _i, _i, _i, ctypes.POINTER(RopeStruct), _f, _i64,
+                                      _i, _p, _p, _p, _p, _p, _i64, _p]
+        L.olmo3_kv_append.restype = _i
+        L.olmo3_attn_prefill.argtypes = [_i, _i, _i, _i, _i, _i, _i, ctypes.POINTER(RopeStruct), _f,
+                                         _i64, _i, _p, _p, _p, _p, _p, _p, _p, _i64, _p, _p, _sz, _p]
+        L.olmo3_attn_prefill.restype = _i
+        L.olmo3_attn_decode.argtypes = [_i, _i, _i, _i, _i, _i, ctypes.POINTER(RopeStruct), _f, _i64,
+                                        _i, _p, _p, _p, _p, _p, _p, _p, _i64, _p, _p, _sz, _p]
+        L.olmo3_attn_decode.restype = _i
+        L.olmo3_status_string.argtypes = [_i]
+        L.olmo3_status_string.restype = ctypes.c_char_p
+        L.olmo3_abi_version.argtypes = []
+        L.olmo3_abi_version.restype = _i
+        L.olmo3_probe_prefill_visits.argtypes = [_i, _i, _i, _p, _p]
+        L.olmo3_probe_prefill_visits.restype = _i
+        L.olmo3_probe_decode_reads.argtypes = [_i, _i, _i, _i, _i, _i64, _i64, _p, _p]
+        L.olmo3_probe_decode_reads.restype = _i
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().olmo3_status_string(int(status)).decode()
+
+
+def _check(status: int, what: str) -> None:
+    if status != OK:
+        raise Olmo3Error(status, what)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return DTYPE_BF16
+    if t.dtype == torch.float32:
+        return DTYPE_F32
+    raise TypeError(f"unsupported dtype {t.dtype}: bf16 or fp32")
+
+
+def _ptr(t: torch.Tensor | None, name: str, dtype=None) -> int:
+    if t is None:
+        return 0
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    return t.data_ptr()
+
+
+def _stream(stream, device) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def olmo3_layer_type(layer: int, n_layers: int) -> int:
+    return lib().olmo3_layer_type(int(layer), int(n_layers))
+
+
+def olmo3_abi_version() -> int:
+    return lib().olmo3_abi_version()
+
+
+def olmo3_workspace_bytes(mode: int, B: int, T: int, H: int, G: int, d: int, layer_type: int,
+                          dtype: int, cache_capacity: int) -> int:
+    return lib().olmo3_workspace_bytes(mode, B, T, H, G, d, layer_type, dtype, cache_capacity)
+
+
+def _cache_dims(k_cache: torch.Tensor):
+    if k_cache.dim() != 4:
+        raise ValueError("caches are [B, G, capacity, d]")
+    B, G, cap, d = k_cache.shape
+    return B, G, cap, d
+
+
+def olmo3_kv_append(k_pre, v, k_gain, k_cache, v_cache, *, window: int, layer_type: int,
+                    rope: Rope, eps: float = 1e-6, pos_offset: int = 0, stream=None) -> None:
+    """Append k_pre/v [B, T, G*d] at positions pos_offset.. to the cache."""
+    B, G, cap, d = _cache_dims(k_cache)
+    T = k_pre.shape[1]
+    dt = k_pre.dtype
+    r = rope.to_c()
+    st = lib().olmo3_kv_append(B, T, G, d, window, layer_type, ctypes.byref(r), eps, pos_offset,
+                               _dtype_code(k_pre), _ptr(k_pre, "k_pre", dt), _ptr(v, "v", dt),
+                               _ptr(k_gain, "k_gain", dt), _ptr(k_cache, "k_cache", dt),
+                               _ptr(v_cache, "v_cache", dt), cap, _stream(stream, k_pre.device))
+    _check(st, "olmo3_kv_append")
+
+
+def olmo3_attn_prefill(q_pre, k_pre, v, q_gain, k_gain, k_cache, v_cache, out, workspace, *,
+                       window: int, layer_type: int, rope: Rope, eps: float = 1e-6,
+                       pos_offset: int = 0, stream=None) -> None:
+    """Prefill: q_pre [B, T, H*d], k_pre/v [B, T, G*d] -> out [B, T, H*d]."""
+    B, G, cap, d = _cache_dims(k_cache)
+    T = q_pre.shape[1]
+    H = q_pre.shape[2] // d
+    dt = q_pre.dtype
+    r = rope.to_c()
+    st = lib().olmo3_attn_prefill(
+        B, T, H, G, d, window, layer_type, ctypes.byref(r), eps, pos_offset, _dtype_code(q_pre),
+        _ptr(q_pre, "q_pre", dt), _ptr(k_pre, "k_pre", dt), _ptr(v, "v", dt),
+        _ptr(q_gain, "q_gain", dt), _ptr(k_gain, "k_gain", dt), _ptr(k_cache, "k_cache", dt),
+        _ptr(v_cache, "v_cache", dt), cap, _ptr(out, "out", dt), _ptr(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream(stream, q_pre.device))
+    _check(st, "olmo3_attn_prefill")
+
+
+def olmo3_attn_decode(q_pre, k_pre, v, q_gain, k_gain, k_cache, v_cache, out, workspace, *,
+                      window: int, layer_type: int, rope: Rope, pos: int, eps: float = 1e-6,
+                      stream=None) -> None:
+    """Decode one token per sequence at position ``pos``: q_pre [B, H*d],
+    k_pre/v [B, G*d] -> out [B, H*d]."""
+    B, G, cap, d = _cache_dims(k_cache)
+    H = q_pre.shape[-1] // d
+    dt = q_pre.dtype
+    r = rope.to_c()
+    st = lib().olmo3_attn_decode(
+        B, H, G, d, window, layer_type, ctypes.byref(r), eps, pos, _dtype_code(q_pre),
+        _ptr(q_pre, "q_pre", dt), _ptr(k_pre, "k_pre", dt), _ptr(v, "v", dt),
+        _ptr(q_gain, "q_gain", dt), _ptr(k_gain, "k_gain", dt), _ptr(k_cache, "k_cache", dt),
+        _ptr(v_cache, "v_cache", dt), cap, _ptr(out, "out", dt), _ptr(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream(stream, q_pre.device))
+    _check(st, "olmo3_attn_decode")
+
+
+def workspace(mode: int, B: int, T: int, H: int, G: int, d: int, layer_type: int,
+              dtype: torch.dtype, cache_capacity: int, device) -> torch.Tensor:
+    """Device byte buffer of the size ``olmo3_workspace_bytes`` asks for."""
+    n = olmo3_workspace_bytes(mode, B, T, H, G, d, layer_type,
+                              DTYPE_BF16 if dtype == torch.bfloat16 else DTYPE_F32, cache_capacity)
+    if n == 0:
+        raise Olmo3Error(ERR_INVALID_ARG, "olmo3_workspace_bytes")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def olmo3_probe_prefill_visits(T: int, window: int, layer_type: int, device="cuda") -> torch.Tensor:
+    """[T, T] uint8 table of the (query, key) pairs the prefill kernel accumulates."""
+    visit = torch.empty((T, T), dtype=torch.uint8, device=device)
+    st = lib().olmo3_probe_prefill_visits(T, window, layer_type, _ptr(visit, "visit"),
+                                          _stream(None, visit.device))
+    _check(st, "olmo3_probe_prefill_visits")
+    return visit
+
+
+def olmo3_probe_decode_reads(B: int, G: int, d: int, window: int, layer_type: int, pos: int,
+                             cache_capacity: int, device="cuda") -> torch.Tensor:
+    """[cache_capacity] int32 count of reads per slot by the decode kernel."""
+    count = torch.empty(cache_capacity, dtype=torch.int32, device=device)
+    st = lib().olmo3_probe_decode_reads(B, G, d, window, layer_type, pos, cache_capacity,
+                                        _ptr(count, "count"), _stream(None, count.device))
+    _check(st, "olmo3_probe_decode_reads")
+    return count

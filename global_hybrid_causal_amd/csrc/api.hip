@@ -1,0 +1,421 @@
+// C ABI of libolmo3attn: argument validation, RoPE / YaRN rate tables,
+// workspace layout and kernel dispatch.  Every check runs before the first
+// launch, so a call that fails has no effect.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "../../include/olmo3_attn.h"
+#include "kernels.h"
+#include "tiles.h"
+
+using namespace olmo3;
+
+namespace {
+
+constexpr double kLog2e = 1.4426950408889634;
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+size_t elem_size(int dtype) { return dtype == OLMO3_DTYPE_BF16 ? 2 : 4; }
+
+bool supported_d(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+
+struct Span {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+Span span(const void* p, size_t bytes) {
+  return Span{(uintptr_t)p, (uintptr_t)p + bytes};
+}
+bool overlap(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi; }
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+// Sizes shared by all entry points.
+int check_common(int B, int T, int H, int G, int d, int window, int layer_type, int dtype,
+                 const olmo3_rope* rope, float eps, int64_t pos_offset) {
+  if (B < 1 || T < 1 || H < 1 || G < 1 || d < 2 || window < 1) return OLMO3_ERR_INVALID_ARG;
+  if (H % G) return OLMO3_ERR_INVALID_ARG;
+  if (d % 2) return OLMO3_ERR_INVALID_ARG;
+  if (layer_type != OLMO3_LAYER_SLIDING && layer_type != OLMO3_LAYER_FULL) return OLMO3_ERR_INVALID_ARG;
+  if (dtype != OLMO3_DTYPE_BF16 && dtype != OLMO3_DTYPE_F32) return OLMO3_ERR_INVALID_ARG;
+  if (!rope || !(rope->theta > 0.0) || !isfinite(rope->theta)) return OLMO3_ERR_INVALID_ARG;
+  if (rope->yarn && (!(rope->factor >= 1.0) || rope->orig_ctx < 1 ||
+                     !(rope->beta_fast > rope->beta_slow)))
+    return OLMO3_ERR_INVALID_ARG;
+  if (!(eps >= 0.0f) || !isfinite(eps)) return OLMO3_ERR_INVALID_ARG;
+  if (pos_offset < 0) return OLMO3_ERR_INVALID_ARG;
+  if (!supported_d(d)) return OLMO3_ERR_UNSUPPORTED;
+  const int max_heads = prologue_max_heads(dtype, d);
+  if (H > max_heads || G > max_heads) return OLMO3_ERR_UNSUPPORTED;
+  if ((int64_t)B * T > INT32_MAX / 2 || (int64_t)B * H > 65535 * 64) return OLMO3_ERR_UNSUPPORTED;
+  if (pos_offset + T > ((int64_t)1 << 40)) return OLMO3_ERR_UNSUPPORTED;
+  return OLMO3_OK;
+}
+
+int check_capacity(int layer_type, int window, int64_t cap, int64_t last_pos) {
+  if (cap < 1) return OLMO3_ERR_CAPACITY;
+  if (layer_type == OLMO3_LAYER_SLIDING) return cap == window ? OLMO3_OK : OLMO3_ERR_CAPACITY;
+  return cap >= last_pos + 1 ? OLMO3_OK : OLMO3_ERR_CAPACITY;
+}
+
+// Rates of a layer: theta^(-2i/d), or the YaRN interpolation of them on full
+// layers (Peng et al., 2023: ramp over r = L / wavelength between beta_slow
+// and beta_fast rotations), and the multiplier of rotated q and k.
+void rope_table(const olmo3_rope* rope, int layer_type, int d, RopeTable* t) {
+  memset(t, 0, sizeof(*t));
+  const bool yarn = rope->yarn && layer_type == OLMO3_LAYER_FULL && rope->factor > 1.0;
+  for (int i = 0; i < d / 2; ++i) {
+    const double w = pow(rope->theta, -2.0 * i / d);
+    if (!yarn) {
+      t->inv_freq[i] = w;
+      continue;
+    }
+    const double r = (double)rope->orig_ctx * w / (2.0 * M_PI);
+    double gamma = (r - rope->beta_slow) / (rope->beta_fast - rope->beta_slow);
+    gamma = gamma < 0.0 ? 0.0 : (gamma > 1.0 ? 1.0 : gamma);
+    t->inv_freq[i] = (1.0 - gamma) * (w / rope->factor) + gamma * w;
+  }
+  double m = 1.0;
+  if (rope->yarn && layer_type == OLMO3_LAYER_FULL) {
+    if (rope->attn_factor > 0.0)
+      m = rope->attn_factor;
+    else if (rope->factor > 1.0)
+      m = 0.1 * log(rope->factor) + 1.0;
+  }
+  t->mscale = (float)m;
+}
+
+float scale_log2(int d) { return (float)(kLog2e / sqrt((double)d)); }
+
+bool use_mfma(int dtype, int d) { return dtype == OLMO3_DTYPE_BF16 && d == 128; }
+
+bool decode_uses_split(int dtype, int d, int H, int G) {
+  return use_mfma(dtype, d) && H / G <= 8;
+}
+
+size_t prefill_ws(int B, int T, int H, int G, int d, int layer_type, int dtype) {
+  const size_t es = elem_size(dtype);
+  size_t bytes = align_up((size_t)B * T * H * d * es);
+  if (layer_type == OLMO3_LAYER_SLIDING) bytes += align_up((size_t)B * G * T * d * es);
+  return bytes;
+}
+
+size_t decode_ws(int B, int H, int G, int d, int layer_type, int window, int dtype, int64_t cap) {
+  const size_t es = elem_size(dtype);
+  size_t bytes = align_up((size_t)B * H * d * es);
+  if (decode_uses_split(dtype, d, H, G)) {
+    const int64_t n_max = layer_type == OLMO3_LAYER_SLIDING ? window : cap;
+    const int splits = decode_splits(B, G, n_max);
+    bytes += align_up((size_t)B * H * splits * (d + 2) * sizeof(float));
+  }
+  return bytes;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? OLMO3_OK : OLMO3_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int olmo3_abi_version(void) { return OLMO3_ABI_VERSION; }
+
+const char* olmo3_status_string(int status) {
+  switch (status) {
+    case OLMO3_OK: return "ok";
+    case OLMO3_ERR_INVALID_ARG: return "invalid argument";
+    case OLMO3_ERR_UNSUPPORTED: return "unsupported configuration";
+    case OLMO3_ERR_CAPACITY: return "cache capacity does not fit the positions or the window";
+    case OLMO3_ERR_HIP: return "HIP launch failed";
+    case OLMO3_ERR_WORKSPACE: return "workspace missing or too small";
+    default: return "unknown status";
+  }
+}
+
+int olmo3_layer_type(int layer, int n_layers) {
+  if (n_layers < 1 || layer < 0 || layer >= n_layers) return -1;
+  return (layer % 4 == 3 || layer == n_layers - 1) ? OLMO3_LAYER_FULL : OLMO3_LAYER_SLIDING;
+}
+
+size_t olmo3_workspace_bytes(int mode, int B, int T, int H, int G, int d, int layer_type,
+                             int dtype, int64_t cache_capacity) {
+  olmo3_rope plain = {10000.0, 0, 1.0, 1, 32.0, 1.0, 0.0};
+  if (mode == OLMO3_MODE_DECODE) T = 1;
+  if (check_common(B, T, H, G, d, 1, layer_type, dtype, &plain, 0.f, 0) != OLMO3_OK) return 0;
+  if (mode == OLMO3_MODE_PREFILL) return prefill_ws(B, T, H, G, d, layer_type, dtype);
+  if (mode == OLMO3_MODE_DECODE) {
+    if (cache_capacity < 1) return 0;
+    // a sliding layer's ring holds cache_capacity == window slots
+    return decode_ws(B, H, G, d, layer_type, (int)std::min<int64_t>(cache_capacity, INT32_MAX),
+                     dtype, cache_capacity);
+  }
+  return 0;
+}
+
+int olmo3_kv_append(int B, int T, int G, int d, int window, int layer_type,
+                    const olmo3_rope* rope, float eps, int64_t pos_offset, int dtype,
+                    const void* k_pre, const void* v, const void* k_gain, void* k_cache,
+                    void* v_cache, int64_t cache_capacity, void* stream) {
+  int st = check_common(B, T, G, G, d, window, layer_type, dtype, rope, eps, pos_offset);
+  if (st) return st;
+  if (!k_pre || !v || !k_gain || !k_cache || !v_cache) return OLMO3_ERR_INVALID_ARG;
+  if (!aligned16(k_pre) || !aligned16(v) || !aligned16(k_gain) || !aligned16(k_cache) ||
+      !aligned16(v_cache))
+    return OLMO3_ERR_INVALID_ARG;
+  st = check_capacity(layer_type, window, cache_capacity, pos_offset + T - 1);
+  if (st) return st;
+  const size_t es = elem_size(dtype);
+  const Span kc = span(k_cache, (size_t)B * G * cache_capacity * d * es);
+  const Span vc = span(v_cache, (size_t)B * G * cache_capacity * d * es);
+  const Span in[] = {span(k_pre, (size_t)B * T * G * d * es), span(v, (size_t)B * T * G * d * es),
+                     span(k_gain, (size_t)G * d * es)};
+  if (overlap(kc, vc)) return OLMO3_ERR_INVALID_ARG;
+  for (const Span& s : in)
+    if (overlap(s, kc) || overlap(s, vc)) return OLMO3_ERR_INVALID_ARG;
+
+  RopeTable table;
+  rope_table(rope, layer_type, d, &table);
+  PrologueArgs a = {};
+  a.k_pre = k_pre;
+  a.v = v;
+  a.k_gain = k_gain;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.cap = cache_capacity;
+  a.pos_offset = pos_offset;
+  a.cache_first_t = layer_type == OLMO3_LAYER_SLIDING ? std::max<int64_t>(0, (int64_t)T - window) : 0;
+  a.B = B;
+  a.T = T;
+  a.H = G;
+  a.G = G;
+  a.window = window;
+  a.sliding = layer_type == OLMO3_LAYER_SLIDING;
+  a.eps = eps;
+  return hip_status(launch_prologue(a, table, dtype, d, (hipStream_t)stream));
+}
+
+static int validate_attn(int B, int T, int H, int G, int d, int window, int layer_type,
+                         const olmo3_rope* rope, float eps, int64_t pos_offset, int dtype,
+                         const void* q_pre, const void* k_pre, const void* v, const void* q_gain,
+                         const void* k_gain, void* k_cache, void* v_cache,
+                         int64_t cache_capacity, void* out, void* workspace,
+                         size_t workspace_bytes, size_t ws_needed) {
+  int st = check_common(B, T, H, G, d, window, layer_type, dtype, rope, eps, pos_offset);
+  if (st) return st;
+  const void* ptrs[] = {q_pre, k_pre, v, q_gain, k_gain, k_cache, v_cache, out};
+  for (const void* p : ptrs)
+    if (!p || !aligned16(p)) return OLMO3_ERR_INVALID_ARG;
+  st = check_capacity(layer_type, window, cache_capacity, pos_offset + T - 1);
+  if (st) return st;
+  if (!workspace || !aligned16(workspace) || workspace_bytes < ws_needed) return OLMO3_ERR_WORKSPACE;
+  const size_t es = elem_size(dtype);
+  const Span kc = span(k_cache, (size_t)B * G * cache_capacity * d * es);
+  const Span vc = span(v_cache, (size_t)B * G * cache_capacity * d * es);
+  const Span o = span(out, (size_t)B * T * H * d * es);
+  const Span ws = span(workspace, ws_needed);
+  const Span in[] = {span(q_pre, (size_t)B * T * H * d * es), span(k_pre, (size_t)B * T * G * d * es),
+                     span(v, (size_t)B * T * G * d * es), span(q_gain, (size_t)H * d * es),
+                     span(k_gain, (size_t)G * d * es)};
+  if (overlap(kc, vc) || overlap(o, kc) || overlap(o, vc) || overlap(ws, kc) || overlap(ws, vc) ||
+      overlap(ws, o))
+    return OLMO3_ERR_INVALID_ARG;
+  for (const Span& s : in)
+    if (overlap(s, kc) || overlap(s, vc) || overlap(s, o) || overlap(s, ws)) return OLMO3_ERR_INVALID_ARG;
+  return OLMO3_OK;
+}
+
+int olmo3_attn_prefill(int B, int T, int H, int G, int d, int window, int layer_type,
+                       const olmo3_rope* rope, float eps, int64_t pos_offset, int dtype,
+                       const void* q_pre, const void* k_pre, const void* v, const void* q_gain,
+                       const void* k_gain, void* k_cache, void* v_cache, int64_t cache_capacity,
+                       void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  const size_t need = (B > 0 && T > 0 && H > 0 && G > 0 && d > 0)
+                          ? prefill_ws(B, T, H, G, d, layer_type, dtype)
+                          : 0;
+  int st = validate_attn(B, T, H, G, d, window, layer_type, rope, eps, pos_offset, dtype, q_pre,
+                         k_pre, v, q_gain, k_gain, k_cache, v_cache, cache_capacity, out,
+                         workspace, workspace_bytes, need);
+  if (st) return st;
+  if (pos_offset != 0) return OLMO3_ERR_UNSUPPORTED;
+
+  const hipStream_t s = (hipStream_t)stream;
+  const bool sliding = layer_type == OLMO3_LAYER_SLIDING;
+  const size_t es = elem_size(dtype);
+  char* ws = (char*)workspace;
+  void* q_rot = ws;
+  void* k_rot = sliding ? ws + align_up((size_t)B * T * H * d * es) : nullptr;
+
+  RopeTable table;
+  rope_table(rope, layer_type, d, &table);
+  PrologueArgs p = {};
+  p.q_pre = q_pre;
+  p.k_pre = k_pre;
+  p.v = v;
+  p.q_gain = q_gain;
+  p.k_gain = k_gain;
+  p.q_out = q_rot;
+  p.k_out = k_rot;
+  p.k_sb = (int64_t)G * T * d;
+  p.k_sg = (int64_t)T * d;
+  p.k_st = d;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.cap = cache_capacity;
+  p.pos_offset = 0;
+  p.cache_first_t = sliding ? std::max<int64_t>(0, (int64_t)T - window) : 0;
+  p.B = B;
+  p.T = T;
+  p.H = H;
+  p.G = G;
+  p.window = window;
+  p.sliding = sliding;
+  p.eps = eps;
+  st = hip_status(launch_prologue(p, table, dtype, d, s));
+  if (st) return st;
+
+  AttnArgs a = {};
+  a.q = q_rot;
+  if (sliding) {
+    // rotated keys from the workspace [B][G][T][d], values from the input
+    a.k = k_rot;
+    a.k_sb = (int64_t)G * T * d;
+    a.k_sg = (int64_t)T * d;
+    a.k_sr = d;
+    a.v = v;
+    a.v_sb = (int64_t)T * G * d;
+    a.v_sg = d;
+    a.v_sr = (int64_t)G * d;
+  } else {
+    // the linear cache now holds positions 0 .. T-1 at slots 0 .. T-1
+    a.k = k_cache;
+    a.v = v_cache;
+    a.k_sb = a.v_sb = (int64_t)G * cache_capacity * d;
+    a.k_sg = a.v_sg = cache_capacity * d;
+    a.k_sr = a.v_sr = d;
+  }
+  a.out = out;
+  a.B = B;
+  a.Tq = T;
+  a.H = H;
+  a.G = G;
+  a.n_keys = T;
+  a.q_pos0 = 0;
+  a.window = window;
+  a.sliding = sliding;
+  a.all_visible = 0;
+  a.scale_log2 = scale_log2(d);
+  if (use_mfma(dtype, d)) return hip_status(launch_prefill_mfma(a, s));
+  return hip_status(launch_attn_generic(a, dtype, d, s));
+}
+
+int olmo3_attn_decode(int B, int H, int G, int d, int window, int layer_type,
+                      const olmo3_rope* rope, float eps, int64_t pos, int dtype,
+                      const void* q_pre, const void* k_pre, const void* v, const void* q_gain,
+                      const void* k_gain, void* k_cache, void* v_cache, int64_t cache_capacity,
+                      void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  const size_t need = (B > 0 && H > 0 && G > 0 && d > 0 && G <= H && cache_capacity > 0)
+                          ? decode_ws(B, H, G, d, layer_type, window, dtype, cache_capacity)
+                          : 0;
+  int st = validate_attn(B, 1, H, G, d, window, layer_type, rope, eps, pos, dtype, q_pre, k_pre,
+                         v, q_gain, k_gain, k_cache, v_cache, cache_capacity, out, workspace,
+                         workspace_bytes, need);
+  if (st) return st;
+
+  const hipStream_t s = (hipStream_t)stream;
+  const bool sliding = layer_type == OLMO3_LAYER_SLIDING;
+  const size_t es = elem_size(dtype);
+  char* ws = (char*)workspace;
+  void* q_rot = ws;
+
+  RopeTable table;
+  rope_table(rope, layer_type, d, &table);
+  PrologueArgs p = {};
+  p.q_pre = q_pre;
+  p.k_pre = k_pre;
+  p.v = v;
+  p.q_gain = q_gain;
+  p.k_gain = k_gain;
+  p.q_out = q_rot;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.cap = cache_capacity;
+  p.pos_offset = pos;
+  p.cache_first_t = 0;
+  p.B = B;
+  p.T = 1;
+  p.H = H;
+  p.G = G;
+  p.window = window;
+  p.sliding = sliding;
+  p.eps = eps;
+  st = hip_status(launch_prologue(p, table, dtype, d, s));
+  if (st) return st;
+
+  const int64_t n = sliding ? std::min<int64_t>(pos + 1, window) : pos + 1;
+  if (decode_uses_split(dtype, d, H, G)) {
+    DecodeArgs a = {};
+    a.q = q_rot;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.cap = cache_capacity;
+    a.n = n;
+    a.splits = decode_splits(B, G, n);
+    const int64_t per = (n + a.splits - 1) / a.splits;
+    a.rows_per_split = (per + dec::kRowsPerIter - 1) / dec::kRowsPerIter * dec::kRowsPerIter;
+    a.part = (float*)(ws + align_up((size_t)B * H * d * es));
+    a.out = out;
+    a.B = B;
+    a.H = H;
+    a.G = G;
+    a.scale_log2 = scale_log2(d);
+    return hip_status(launch_decode_mfma(a, s));
+  }
+  AttnArgs a = {};
+  a.q = q_rot;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.k_sb = a.v_sb = (int64_t)G * cache_capacity * d;
+  a.k_sg = a.v_sg = cache_capacity * d;
+  a.k_sr = a.v_sr = d;
+  a.out = out;
+  a.B = B;
+  a.Tq = 1;
+  a.H = H;
+  a.G = G;
+  a.n_keys = n;
+  a.q_pos0 = pos;
+  a.window = window;
+  a.sliding = sliding;
+  a.all_visible = 1;
+  a.scale_log2 = scale_log2(d);
+  return hip_status(launch_attn_generic(a, dtype, d, s));
+}
+
+int olmo3_probe_prefill_visits(int T, int window, int layer_type, uint8_t* visit, void* stream) {
+  if (T < 1 || T > 4096 || window < 1 || !visit) return OLMO3_ERR_INVALID_ARG;
+  if (layer_type != OLMO3_LAYER_SLIDING && layer_type != OLMO3_LAYER_FULL) return OLMO3_ERR_INVALID_ARG;
+  return hip_status(launch_probe_prefill(T, window, layer_type == OLMO3_LAYER_SLIDING, visit,
+                                         (hipStream_t)stream));
+}
+
+int olmo3_probe_decode_reads(int B, int G, int d, int window, int layer_type, int64_t pos,
+                             int64_t cache_capacity, int32_t* count, void* stream) {
+  if (B < 1 || G < 1 || d != 128 || window < 1 || pos < 0 || !count) return OLMO3_ERR_INVALID_ARG;
+  if (layer_type != OLMO3_LAYER_SLIDING && layer_type != OLMO3_LAYER_FULL) return OLMO3_ERR_INVALID_ARG;
+  int st = check_capacity(layer_type, window, cache_capacity, pos);
+  if (st) return st;
+  const bool sliding = layer_type == OLMO3_LAYER_SLIDING;
+  DecodeArgs a = {};
+  a.cap = cache_capacity;
+  a.n = sliding ? std::min<int64_t>(pos + 1, window) : pos + 1;
+  a.splits = decode_splits(B, G, a.n);
+  const int64_t per = (a.n + a.splits - 1) / a.splits;
+  a.rows_per_split = (per + dec::kRowsPerIter - 1) / dec::kRowsPerIter * dec::kRowsPerIter;
+  a.B = B;
+  a.G = G;
+  return hip_status(launch_probe_decode(a, count, (hipStream_t)stream));
+}
+
+}  // extern "C"

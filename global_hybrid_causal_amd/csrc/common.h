@@ -1,0 +1,77 @@
+// Device-side helpers shared by the OLMo 3 attention kernels (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace olmo3 {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr int kMaxHalfDim = 128;  // d <= 256
+
+// RoPE rates of one layer, fp64, passed by value in the kernel arguments.
+struct RopeTable {
+  double inv_freq[kMaxHalfDim];
+  float mscale;  // multiplier of rotated q and k (YaRN temperature, else 1)
+};
+
+__device__ __forceinline__ float bf16_to_f32(bf16 x) { return (float)x; }
+
+// Round-to-nearest-even fp32 -> bf16 (gfx950 converts with RNE in hardware).
+__device__ __forceinline__ bf16 f32_to_bf16(float x) { return (bf16)x; }
+
+template <typename T> struct Io;
+template <> struct Io<bf16> {
+  static constexpr int kVec = 8;  // elements per 16-byte access
+  typedef bf16x8 vec;
+  __device__ static inline void to_f32(const vec& v, float* f) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = (float)v[i];
+  }
+  __device__ static inline vec from_f32(const float* f) {
+    vec v;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = (bf16)f[i];
+    return v;
+  }
+};
+template <> struct Io<float> {
+  static constexpr int kVec = 4;
+  typedef f32x4 vec;
+  __device__ static inline void to_f32(const vec& v, float* f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f[i] = v[i];
+  }
+  __device__ static inline vec from_f32(const float* f) {
+    vec v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = f[i];
+    return v;
+  }
+};
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, kWave);
+  return x;
+}
+
+// Map the hardware workgroup id so that consecutive logical work items land
+// on the same XCD (workgroups are dealt round-robin over the 8 XCDs), which
+// keeps items that share K/V in one XCD's L2.  Identity when n % 8 != 0.
+__device__ __forceinline__ int xcd_remap(int bid, int n) {
+  constexpr int kXcd = 8;
+  if (n % kXcd) return bid;
+  return (bid % kXcd) * (n / kXcd) + bid / kXcd;
+}
+
+}  // namespace olmo3

@@ -1,0 +1,86 @@
+// Host-side launchers of the attention kernels and their argument blocks.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.h"
+
+namespace olmo3 {
+
+// QK-norm + RoPE + cache append over B*T token rows.
+struct PrologueArgs {
+  const void* q_pre;   // [B][T][H*d] or null (keys/values only)
+  const void* k_pre;   // [B][T][G*d]
+  const void* v;       // [B][T][G*d]
+  const void* q_gain;  // [H*d]
+  const void* k_gain;  // [G*d]
+  void* q_out;         // [B][T][H][d] rotated queries (when q_pre is set)
+  void* k_out;         // rotated keys at b*k_sb + g*k_sg + t*k_st, or null
+  int64_t k_sb, k_sg, k_st;
+  void* k_cache;       // [B][G][cap][d]
+  void* v_cache;
+  int64_t cap;
+  int64_t pos_offset;
+  int64_t cache_first_t;  // rows t >= this are stored in the cache
+  int B, T, H, G;
+  int window;
+  int sliding;
+  float eps;
+};
+
+hipError_t launch_prologue(const PrologueArgs& a, const RopeTable& rope, int dtype, int d,
+                           hipStream_t s);
+int prologue_max_heads(int dtype, int d);
+
+// Attention over keys held in a strided buffer.
+//   queries  q[(b*Tq + t)*H + h][d], absolute position q_pos0 + t
+//   keys     k + b*k_sb + g*k_sg + r*k_sr, r in [0, n_keys); same for v
+//   prefill: key row r is at position r and the mask decides;
+//   decode (all_visible): every row r < n_keys is visible.
+//   out[(b*Tq + t)*H*d + h*d + e]
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  int64_t k_sb, k_sg, k_sr;
+  int64_t v_sb, v_sg, v_sr;
+  void* out;
+  int B, Tq, H, G;
+  int64_t n_keys;
+  int64_t q_pos0;
+  int window;
+  int sliding;
+  int all_visible;
+  float scale_log2;  // log2(e) / sqrt(d)
+};
+
+// Flash-style prefill, d = 128, bf16, MFMA (requires q_pos0 == 0 and
+// n_keys == Tq, keys at positions 0..Tq-1).
+hipError_t launch_prefill_mfma(const AttnArgs& a, hipStream_t s);
+// Plain per-query kernel for the other head sizes and for fp32.
+hipError_t launch_attn_generic(const AttnArgs& a, int dtype, int d, hipStream_t s);
+
+// Split-KV decode, d = 128, bf16: one workgroup per (b, g, split) reads the
+// split's cache rows once for all H/G query heads and writes a partial
+// softmax state (m, l, o[d]) per head to part[((b*H + h)*splits + sp)*(d+2)].
+struct DecodeArgs {
+  const void* q;       // [B][H][d] rotated queries
+  const void* k_cache; // [B][G][cap][d]
+  const void* v_cache;
+  int64_t cap;
+  int64_t n;           // rows read: slots 0 .. n-1
+  int64_t rows_per_split;
+  float* part;
+  void* out;           // [B][H*d]
+  int B, H, G, splits;
+  float scale_log2;
+};
+int decode_splits(int B, int G, int64_t n);
+hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t s);
+
+// Probes: the prefill kernel's tile walk and the decode kernel's row walk.
+hipError_t launch_probe_prefill(int T, int window, int sliding, uint8_t* visit, hipStream_t s);
+hipError_t launch_probe_decode(const DecodeArgs& a, int32_t* count, hipStream_t s);
+
+}  // namespace olmo3

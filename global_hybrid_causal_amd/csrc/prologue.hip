@@ -1,0 +1,195 @@
+// Fused QK-norm + RoPE + KV-cache append (one wavefront per token).
+//
+// QK-norm: one RMS statistic over the token's whole query vector (H*d
+// features) and one over its whole key vector (G*d features), then a
+// per-feature gain ("Case Study: OLMo 3", architecture item 2; gains of width
+// H*d and G*d per "Count OLMo 3's Parameters").  RoPE: pair (i, i + d/2)
+// turns by pos * omega_i at absolute position pos = pos_offset + t ("Case
+// Study: OLMo 3", item 3; "Olmo-3 End-to-End Implementation", "Inference
+// Pipeline").  Append: rotated key and untouched value go to the cache slot
+// of the position, ring slot pos mod window on sliding layers ("Olmo 3 7B",
+// per-layer-type cache).
+//
+// Each lane owns "pair chunks": 16-byte pieces of the first half of a head
+// and the matching piece of the second half, so a rotation never crosses
+// lanes.  The lane's pair chunks all sit at the same offset inside their
+// heads, so its RoPE angles are computed once per token (fp64 product and
+// range reduction, fp32 sincos) and reused for every query and key head.
+#include "common.h"
+#include "kernels.h"
+
+namespace olmo3 {
+
+namespace {
+
+constexpr int kTokensPerBlock = 4;  // one wavefront per token
+constexpr int kMaxChunksPerLane = 8;
+
+template <typename T, int D>
+struct PairChunks {
+  static constexpr int kVec = Io<T>::kVec;
+  static constexpr int kPerHead = D / (2 * kVec);  // pair chunks per head
+  static_assert(kPerHead >= 1 && kWave % kPerHead == 0, "unsupported head size");
+};
+
+template <typename T, int D>
+__device__ __forceinline__ void rope_angles(int lane, int64_t pos, const RopeTable& rope,
+                                            float* cs, float* sn) {
+  constexpr int kVec = Io<T>::kVec;
+  const int j = lane % PairChunks<T, D>::kPerHead;
+  constexpr double kTwoPi = 6.283185307179586;
+  constexpr double kInvTwoPi = 0.15915494309189535;
+#pragma unroll
+  for (int e = 0; e < kVec; ++e) {
+    const double a = (double)pos * rope.inv_freq[j * kVec + e];
+    const double r = a - kTwoPi * rint(a * kInvTwoPi);  // |r| <= pi
+    sincosf((float)r, &sn[e], &cs[e]);
+  }
+}
+
+// Normalise, rotate and emit the `nheads` heads of one token row.
+// dst0(h) and dst1(h) return where head h goes (the start of its d
+// elements), or nullptr to skip that destination.
+template <typename T, int D, typename Dst0, typename Dst1>
+__device__ __forceinline__ void norm_rope_row(const T* __restrict__ src, const T* __restrict__ gain,
+                                              int nheads, float eps, int lane, const float* cs,
+                                              const float* sn, float mscale, Dst0 dst0, Dst1 dst1) {
+  typedef typename Io<T>::vec vec;
+  constexpr int kVec = Io<T>::kVec;
+  constexpr int kPerHead = PairChunks<T, D>::kPerHead;
+  const int n_chunks = nheads * kPerHead;
+  vec a0[kMaxChunksPerLane], a1[kMaxChunksPerLane];
+  float ss = 0.f;
+#pragma unroll
+  for (int k = 0; k < kMaxChunksPerLane; ++k) {
+    const int pc = lane + kWave * k;
+    if (pc < n_chunks) {
+      const int h = pc / kPerHead, j = pc % kPerHead;
+      const T* p = src + h * D + j * kVec;
+      a0[k] = *(const vec*)p;
+      a1[k] = *(const vec*)(p + D / 2);
+      float f0[kVec], f1[kVec];
+      Io<T>::to_f32(a0[k], f0);
+      Io<T>::to_f32(a1[k], f1);
+#pragma unroll
+      for (int e = 0; e < kVec; ++e) ss += f0[e] * f0[e] + f1[e] * f1[e];
+    }
+  }
+  ss = wave_sum(ss);
+  const float r = 1.0f / sqrtf(ss / (float)(nheads * D) + eps);
+#pragma unroll
+  for (int k = 0; k < kMaxChunksPerLane; ++k) {
+    const int pc = lane + kWave * k;
+    if (pc < n_chunks) {
+      const int h = pc / kPerHead, j = pc % kPerHead;
+      const T* gp = gain + h * D + j * kVec;
+      float g0[kVec], g1[kVec], x0[kVec], x1[kVec], y0[kVec], y1[kVec];
+      Io<T>::to_f32(*(const vec*)gp, g0);
+      Io<T>::to_f32(*(const vec*)(gp + D / 2), g1);
+      Io<T>::to_f32(a0[k], x0);
+      Io<T>::to_f32(a1[k], x1);
+#pragma unroll
+      for (int e = 0; e < kVec; ++e) {
+        const float u = x0[e] * r * g0[e];
+        const float w = x1[e] * r * g1[e];
+        y0[e] = (u * cs[e] - w * sn[e]) * mscale;
+        y1[e] = (w * cs[e] + u * sn[e]) * mscale;
+      }
+      const vec v0 = Io<T>::from_f32(y0), v1 = Io<T>::from_f32(y1);
+      if (T* d = dst0(h)) {
+        *(vec*)(d + j * kVec) = v0;
+        *(vec*)(d + D / 2 + j * kVec) = v1;
+      }
+      if (T* d = dst1(h)) {
+        *(vec*)(d + j * kVec) = v0;
+        *(vec*)(d + D / 2 + j * kVec) = v1;
+      }
+    }
+  }
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(kWave * kTokensPerBlock) void qknorm_rope_append_kernel(
+    PrologueArgs a, RopeTable rope) {
+  typedef typename Io<T>::vec vec;
+  constexpr int kVec = Io<T>::kVec;
+  const int lane = threadIdx.x % kWave;
+  const int64_t row = (int64_t)blockIdx.x * kTokensPerBlock + threadIdx.x / kWave;
+  if (row >= (int64_t)a.B * a.T) return;
+  const int b = (int)(row / a.T);
+  const int t = (int)(row % a.T);
+  const int64_t pos = a.pos_offset + t;
+
+  float cs[kVec], sn[kVec];
+  rope_angles<T, D>(lane, pos, rope, cs, sn);
+
+  // queries -> q_out [B][T][H][D]
+  if (a.q_pre) {
+    const T* src = (const T*)a.q_pre + row * a.H * D;
+    T* qo = (T*)a.q_out + row * a.H * D;
+    norm_rope_row<T, D>(src, (const T*)a.q_gain, a.H, a.eps, lane, cs, sn, rope.mscale,
+                        [&](int h) -> T* { return qo + h * D; },
+                        [&](int) -> T* { return nullptr; });
+  }
+
+  const bool to_cache = t >= a.cache_first_t;
+  const int64_t slot = a.sliding ? pos % a.window : pos;
+
+  // keys -> optional strided copy (prefill workspace) and the cache slot
+  {
+    const T* src = (const T*)a.k_pre + row * a.G * D;
+    T* ko = (T*)a.k_out;
+    T* kc = (T*)a.k_cache;
+    norm_rope_row<T, D>(
+        src, (const T*)a.k_gain, a.G, a.eps, lane, cs, sn, rope.mscale,
+        [&](int h) -> T* {
+          return ko ? ko + b * a.k_sb + h * a.k_sg + (int64_t)t * a.k_st : nullptr;
+        },
+        [&](int h) -> T* {
+          return to_cache ? kc + (((int64_t)b * a.G + h) * a.cap + slot) * D : nullptr;
+        });
+  }
+
+  // values -> cache slot, unchanged
+  if (to_cache) {
+    const T* src = (const T*)a.v + row * a.G * D;
+    T* vc = (T*)a.v_cache;
+    const int n_vec = a.G * D / kVec;
+    for (int c = lane; c < n_vec; c += kWave) {
+      const int h = c / (D / kVec), e = c % (D / kVec);
+      *(vec*)(vc + (((int64_t)b * a.G + h) * a.cap + slot) * D + e * kVec) =
+          *(const vec*)(src + c * kVec);
+    }
+  }
+}
+
+template <typename T, int D>
+hipError_t launch_prologue_t(const PrologueArgs& a, const RopeTable& rope, hipStream_t s) {
+  const int64_t rows = (int64_t)a.B * a.T;
+  const int blocks = (int)((rows + kTokensPerBlock - 1) / kTokensPerBlock);
+  qknorm_rope_append_kernel<T, D><<<blocks, kWave * kTokensPerBlock, 0, s>>>(a, rope);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int prologue_max_heads(int dtype, int d) {
+  const int vec = dtype == 0 ? 8 : 4;
+  const int per_head = d / (2 * vec);
+  return kMaxChunksPerLane * kWave / per_head;
+}
+
+hipError_t launch_prologue(const PrologueArgs& a, const RopeTable& rope, int dtype, int d,
+                           hipStream_t s) {
+#define OLMO3_PRO(T, DD) \
+  if (d == DD) return launch_prologue_t<T, DD>(a, rope, s);
+  if (dtype == 0) {
+    OLMO3_PRO(bf16, 16) OLMO3_PRO(bf16, 32) OLMO3_PRO(bf16, 64) OLMO3_PRO(bf16, 128)
+  } else {
+    OLMO3_PRO(float, 16) OLMO3_PRO(float, 32) OLMO3_PRO(float, 64) OLMO3_PRO(float, 128)
+  }
+#undef OLMO3_PRO
+  return hipErrorInvalidValue;
+}
+
+}  // namespace olmo3

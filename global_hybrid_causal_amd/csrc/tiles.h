@@ -1,0 +1,85 @@
+// Tile walk and lane mapping of the prefill and decode kernels.  The
+// probes include this same header, so what they record is what the kernels
+// visit.
+#pragma once
+
+#include "common.h"
+
+namespace olmo3 {
+namespace pf {
+
+constexpr int kD = 128;     // head size
+constexpr int kBQ = 128;    // queries per workgroup (4 wavefronts x 32)
+constexpr int kBK = 64;     // keys per tile
+constexpr int kWaves = 4;
+constexpr int kQW = 32;     // queries per wavefront
+
+// Key s is visible from query t ("OLMo 3's Sliding-Window Attention
+// Pattern", "The sliding-window mask"): s <= t, and t - s < window on
+// sliding layers.
+__host__ __device__ __forceinline__ bool visible(int t, int s, int window, int sliding) {
+  return s <= t && (!sliding || t - s < window);
+}
+
+// Key tiles [kt0, kt1) that hold any key visible from queries [q0, q1):
+// keys from q0 - window + 1 (sliding) or 0 (full) up to q1 - 1.
+__host__ __device__ __forceinline__ void key_tiles(int q0, int q1, int window, int sliding,
+                                                   int& kt0, int& kt1) {
+  const int first = sliding ? (q0 - window + 1 > 0 ? q0 - window + 1 : 0) : 0;
+  kt0 = first / kBK;
+  kt1 = (q1 + kBK - 1) / kBK;
+}
+
+// True when every pair of queries [q0, q1) and keys [k0, k0 + kBK) is
+// visible, so the tile needs no per-element mask.
+__host__ __device__ __forceinline__ bool tile_interior(int k0, int q0, int q1, int window,
+                                                       int sliding) {
+  return k0 + kBK - 1 <= q0 && (!sliding || (q1 - 1) - k0 < window);
+}
+
+struct Work {
+  int b, h, qb;
+};
+
+// Workgroup -> (batch, head, query block).  Query blocks of one head sit on
+// one XCD (shared K/V in its L2) and start with the longest causal rows.
+__device__ __forceinline__ Work work_of(int bid, int nblk, int n_qblk, int H) {
+  const int L = xcd_remap(bid, nblk);
+  const int qi = L % n_qblk;
+  const int bh = L / n_qblk;
+  return Work{bh / H, bh % H, n_qblk - 1 - qi};
+}
+
+// Query of a lane: wavefront w owns 32 consecutive queries; lanes l and
+// l + 32 share a query (MFMA 32x32 output column l % 32).
+__device__ __forceinline__ int lane_query(int q0, int wave, int lane) {
+  return q0 + wave * kQW + (lane & 31);
+}
+
+// Key held in accumulator register r of 32-key block kb of a tile at k0
+// (v_mfma_f32_32x32x16_bf16 output row: 8*(r/4) + 4*(lane/32) + r%4).
+__device__ __forceinline__ int lane_key(int k0, int kb, int r, int lane) {
+  return k0 + kb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+}
+
+}  // namespace pf
+
+namespace dec {
+
+constexpr int kD = 128;
+constexpr int kThreads = 256;
+constexpr int kLanesPerRow = 16;             // 16 lanes x 8 bf16 cover a row
+constexpr int kGroups = kThreads / kLanesPerRow;  // rows in flight per step
+constexpr int kUnroll = 4;                   // steps per loop iteration
+constexpr int kRowsPerIter = kGroups * kUnroll;
+constexpr int kMaxSplits = 64;
+constexpr int64_t kMinRowsPerSplit = 256;
+constexpr int64_t kTargetWorkgroups = 2048;
+
+// Rows of a split at iteration i, step u, for lane group grp.
+__host__ __device__ __forceinline__ int64_t row_of(int64_t r0, int64_t i, int u, int grp) {
+  return r0 + i * kRowsPerIter + u * kGroups + grp;
+}
+
+}  // namespace dec
+}  // namespace olmo3

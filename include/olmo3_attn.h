@@ -1,0 +1,188 @@
+/*
+ * olmo3_attn.h -- C ABI of the OLMo 3 per-layer hybrid attention library
+ * (libolmo3attn.so, HIP kernels for MI355X / gfx950).
+ *
+ * One call runs one attention layer of OLMo 3: QK-norm, RoPE at absolute
+ * positions (YaRN-scaled on full layers), KV-cache append, and causal
+ * attention that is either sliding-window or full.
+ *
+ * Sources of the operations (titles and sections of the pages they follow):
+ *   - layer kinds: "OLMo 3's Sliding-Window Attention Pattern", "Which layers
+ *     are full" (full iff layer mod 4 == 3, and always the last layer);
+ *   - mask: same page, "The sliding-window mask" (key s visible from query t
+ *     iff s <= t and, on sliding layers, t - s < window);
+ *   - QK-norm: "Case Study: OLMo 3", architecture item 2, with gains of width
+ *     H*d and G*d ("Count OLMo 3's Parameters", "What to count") and
+ *     eps = 1e-6 ("Olmo-3 End-to-End Implementation", "Technical Details");
+ *   - RoPE: "Case Study: OLMo 3", item 3 (rotate-half pairs i, i+d/2, base
+ *     theta), with position offsets ("Olmo-3 End-to-End Implementation",
+ *     "Inference Pipeline"); YaRN on full layers (item 7);
+ *   - cache: "Olmo-3 End-to-End Implementation", "KV Cache Implementation"
+ *     (per-layer [B, H_kv, T_total, D] tensors) and "Olmo 3 7B",
+ *     "SERVICEABILITY JOIN" (a per-layer-type cache: windowed layers keep a
+ *     bounded cache, and decode on them reads exactly `window` entries).
+ *
+ * Conventions common to every entry point
+ *   Memory.  Every tensor pointer is a DEVICE pointer owned by the caller;
+ *     `rope` is a HOST pointer.  The library never allocates or frees device
+ *     memory and keeps no state between calls; calls are thread-safe.
+ *   Layouts (row-major, contiguous, element type = `dtype`):
+ *     q_pre  [B][T][H*d]      projected queries before QK-norm
+ *     k_pre  [B][T][G*d]      projected keys before QK-norm
+ *     v      [B][T][G*d]      projected values
+ *     q_gain [H*d], k_gain [G*d]   QK-norm gains
+ *     k_cache, v_cache [B][G][cache_capacity][d]
+ *     out    [B][T][H*d]      attention output, heads concatenated in order
+ *   Query head h reads key/value head h / (H/G).
+ *   Cache slots.  Position p is stored at slot p on a full layer (linear
+ *     cache, cache_capacity >= last position + 1) and at slot p mod window on
+ *     a sliding layer (ring, cache_capacity == window).  When one call writes
+ *     more than `window` positions to a ring, only the last `window` of them
+ *     are stored.  Keys are stored after QK-norm and RoPE; values unchanged.
+ *   Arithmetic.  bf16 inputs and outputs with fp32 accumulation (dtype 0),
+ *     or fp32 throughout (dtype 1).  Softmax scale 1/sqrt(d).
+ *   Streams.  `stream` is a hipStream_t cast to void* (NULL = the default
+ *     stream).  Calls enqueue kernels and return without waiting.
+ *   Errors.  Every entry point returns an olmo3_status.  All arguments are
+ *     validated on the host before anything is enqueued, so a call that
+ *     returns an error has no effect.  OLMO3_ERR_HIP reports a failed launch;
+ *     faults inside a kernel surface at the caller's next synchronisation.
+ */
+#ifndef OLMO3_ATTN_H
+#define OLMO3_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define OLMO3_ABI_VERSION 1
+
+typedef enum olmo3_status {
+  OLMO3_OK = 0,
+  OLMO3_ERR_INVALID_ARG = 1, /* bad size, null or overlapping pointer, bad enum   */
+  OLMO3_ERR_UNSUPPORTED = 2, /* valid request this build does not implement       */
+  OLMO3_ERR_CAPACITY = 3,    /* cache too small, or ring size != window            */
+  OLMO3_ERR_HIP = 4,         /* a HIP call or kernel launch failed                 */
+  OLMO3_ERR_WORKSPACE = 5    /* workspace null or smaller than olmo3_workspace_bytes */
+} olmo3_status;
+
+enum { OLMO3_LAYER_SLIDING = 0, OLMO3_LAYER_FULL = 1 };
+enum { OLMO3_DTYPE_BF16 = 0, OLMO3_DTYPE_F32 = 1 };
+enum { OLMO3_MODE_PREFILL = 0, OLMO3_MODE_DECODE = 1 };
+
+/* RoPE / YaRN settings ("Case Study: OLMo 3", items 3 and 7).
+ *   theta        RoPE base; rate of pair i is theta^(-2i/d).
+ *   yarn         nonzero: full layers use YaRN rates and temperature;
+ *                sliding layers always use plain RoPE.
+ *   factor       YaRN scale s (>= 1), e.g. 8 for 8192 -> 65536 positions.
+ *   orig_ctx     original training context L, e.g. 8192.
+ *   beta_fast    ramp end in rotations over L (rates with more are kept), e.g. 32.
+ *   beta_slow    ramp start (rates with fewer are divided by s), e.g. 1.
+ *   attn_factor  multiplier applied to rotated q and k; <= 0 selects
+ *                0.1*ln(s) + 1 (Peng et al., 2023).  Logits scale by its square.
+ * YaRN rate of pair i: with r = L*omega_i/(2*pi) and
+ * gamma = clamp((r - beta_slow)/(beta_fast - beta_slow), 0, 1):
+ * omega'_i = (1 - gamma)*omega_i/s + gamma*omega_i. */
+typedef struct olmo3_rope {
+  double theta;
+  int32_t yarn;
+  double factor;
+  int64_t orig_ctx;
+  double beta_fast;
+  double beta_slow;
+  double attn_factor;
+} olmo3_rope;
+
+/* Kind of layer `layer` (0-based) in a model of `n_layers` layers
+ * ("OLMo 3's Sliding-Window Attention Pattern", "Which layers are full").
+ * Returns OLMO3_LAYER_FULL (1) or OLMO3_LAYER_SLIDING (0); -1 when
+ * n_layers < 1 or layer is outside [0, n_layers). */
+int olmo3_layer_type(int layer, int n_layers);
+
+/* Device workspace, in bytes, that olmo3_attn_prefill (mode 0, T tokens) or
+ * olmo3_attn_decode (mode 1, T ignored) needs for these sizes; the decode
+ * figure covers every position that fits `cache_capacity`.  Returns 0 for
+ * invalid sizes. */
+size_t olmo3_workspace_bytes(int mode, int B, int T, int H, int G, int d,
+                             int layer_type, int dtype, int64_t cache_capacity);
+
+/* Append T positions pos_offset .. pos_offset+T-1 of keys and values to one
+ * layer's cache without attending: keys get QK-norm (gain k_gain, eps) and
+ * RoPE at their absolute positions; values are copied unchanged.  k_pre, v:
+ * [B][T][G*d].  Errors: INVALID_ARG (sizes <= 0, odd d, pos_offset < 0, bad
+ * enum, null pointer, k_cache/v_cache overlapping each other or an input),
+ * CAPACITY (ring size != window, or a linear cache shorter than
+ * pos_offset + T), UNSUPPORTED (d not in {16, 32, 64, 128, 256}). */
+int olmo3_kv_append(int B, int T, int G, int d, int window, int layer_type,
+                    const olmo3_rope* rope, float eps, int64_t pos_offset,
+                    int dtype, const void* k_pre, const void* v,
+                    const void* k_gain, void* k_cache, void* v_cache,
+                    int64_t cache_capacity, void* stream);
+
+/* Prefill: attention of T new tokens at positions pos_offset .. +T-1, which
+ * are also appended to the cache.  Query t attends to the new keys s <= t
+ * (and t - s < window on sliding layers).  out is fully overwritten.
+ * workspace must hold olmo3_workspace_bytes(OLMO3_MODE_PREFILL, ...) bytes
+ * (device memory, contents on entry ignored).  Errors: as olmo3_kv_append,
+ * plus H % G != 0 (INVALID_ARG), out overlapping any other buffer
+ * (INVALID_ARG), a short or null workspace (WORKSPACE), and pos_offset > 0
+ * (UNSUPPORTED: attending to an earlier cached prefix is not implemented). */
+int olmo3_attn_prefill(int B, int T, int H, int G, int d, int window,
+                       int layer_type, const olmo3_rope* rope, float eps,
+                       int64_t pos_offset, int dtype, const void* q_pre,
+                       const void* k_pre, const void* v, const void* q_gain,
+                       const void* k_gain, void* k_cache, void* v_cache,
+                       int64_t cache_capacity, void* out, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+/* Decode: one new token per sequence at absolute position `pos` (the same
+ * for every sequence of the batch).  Its key and value are appended at
+ * slot(pos) first; the query then attends to the n = min(pos+1, window)
+ * filled ring slots (sliding) or to slots 0..pos (full), i.e. positions
+ * max(0, pos-window+1) .. pos or 0 .. pos, which the caller must have
+ * filled earlier.  q_pre [B][H*d], k_pre and v [B][G*d], out [B][H*d].
+ * The key range is split across workgroups and the partial softmax states
+ * are merged by log-sum-exp.  Errors: as olmo3_attn_prefill with T = 1
+ * (pos >= 0 required; CAPACITY if a linear cache has fewer than pos + 1
+ * slots). */
+int olmo3_attn_decode(int B, int H, int G, int d, int window, int layer_type,
+                      const olmo3_rope* rope, float eps, int64_t pos,
+                      int dtype, const void* q_pre, const void* k_pre,
+                      const void* v, const void* q_gain, const void* k_gain,
+                      void* k_cache, void* v_cache, int64_t cache_capacity,
+                      void* out, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+/* Static text for a status code; never NULL. */
+const char* olmo3_status_string(int status);
+
+/* OLMO3_ABI_VERSION of the built library. */
+int olmo3_abi_version(void);
+
+/* ---- Test probes (not part of the user API) ----------------------------
+ * They run the prefill kernel's own tile enumeration and mask predicate, or
+ * the decode kernel's own split / row enumeration, and record what those
+ * visit, so that indexing can be compared bit for bit with the oracle.  */
+
+/* visit [T][T] uint8 (device): set to 1 for every (query t, key s) pair the
+ * d = 128 bf16 prefill kernel would accumulate, 0 elsewhere (the probe
+ * clears it first).  T <= 4096.  Errors: INVALID_ARG, UNSUPPORTED. */
+int olmo3_probe_prefill_visits(int T, int window, int layer_type,
+                               uint8_t* visit, void* stream);
+
+/* count [cache_capacity] int32 (device): number of times the decode kernel
+ * at position `pos` reads each cache slot of one (sequence, KV head), for
+ * the split count it would choose for batch B and G key/value heads.
+ * Errors: INVALID_ARG, CAPACITY.  */
+int olmo3_probe_decode_reads(int B, int G, int d, int window, int layer_type,
+                             int64_t pos, int64_t cache_capacity,
+                             int32_t* count, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* OLMO3_ATTN_H */

@@ -54,7 +54,7 @@ __all__ = [
     "qk_gain_widths", "rope_inv_freq", "yarn_inv_freq", "yarn_mscale",
     "RopeParams", "layer_rope", "rope_rotate", "KvCacheRef", "cache_entries",
     "kv_bytes_per_token", "attend", "prefill_ref", "decode_ref",
-    "attention_rows_ref",
+    "attention_rows_ref", "decode_rows_ref", "ring_positions",
 ]
 
 SLIDING = "sliding"
@@ -466,3 +466,51 @@ def attention_rows_ref(q_pre_rows, q_rows_pos, k_pre_keys, v_keys, k_keys_pos,
     sub_v = np.asarray(v_keys, dtype=np.float64)[:, kv_heads, :]
     return attend(sub_q, np.asarray(q_rows_pos), sub_k, sub_v,
                   np.asarray(k_keys_pos), kind, window)
+
+
+def ring_positions(kind: str, window: int, capacity: int, pos: int) -> np.ndarray:
+    """Absolute position held by each slot of a cache into which positions
+    0 .. pos-1 have been appended (-1 = empty): slot s holds s on a linear
+    cache, and on a ring the latest p < pos with p mod window == s."""
+    slots = np.arange(capacity, dtype=np.int64)
+    if kind == FULL:
+        return np.where(slots < pos, slots, -1)
+    held = (pos - 1) - ((pos - 1 - slots) % window)
+    return np.where((slots < window) & (held >= 0), held, -1)
+
+
+def decode_rows_ref(q_pre_b, k_pre_b, v_b, q_gain, k_gain, cache_k, cache_v, cache_pos, *,
+                    H: int, G: int, d: int, kv_heads, kind: str, window: int,
+                    rope: RopeParams, eps: float = 1e-6, pos: int) -> np.ndarray:
+    """Decode of ONE sequence, evaluated for the query heads of ``kv_heads``
+    only, for checks where the whole cache is too large for the host.
+
+    q_pre_b [H*d], k_pre_b and v_b [G*d] are the token's full projected
+    vectors (QK-norm needs every feature); cache_k, cache_v
+    [len(kv_heads), capacity, d] are those heads' cache rows before the call
+    (rotated keys) and cache_pos [capacity] the position each slot holds.
+    Steps as ``decode_ref``: normalise and rotate the new query and key at
+    ``pos``, store key and value at the slot of ``pos``, attend over the
+    filled slots.  Returns [len(kv_heads) * H/G, d] in head order.
+    """
+    group = H // G
+    kv_heads = list(kv_heads)
+    w, m = layer_rope(rope, kind, d)
+    qh = rms_norm(np.asarray(q_pre_b, dtype=np.float64)[None], q_gain, eps).reshape(1, H, d)
+    kh = rms_norm(np.asarray(k_pre_b, dtype=np.float64)[None], k_gain, eps).reshape(1, G, d)
+    p = np.array([pos], dtype=np.int64)
+    q_rot = rope_rotate(qh, p, w, m)
+    k_rot = rope_rotate(kh, p, w, m)
+    slot = pos % window if kind == SLIDING else pos
+    ck = np.array(cache_k, dtype=np.float64)
+    cv = np.array(cache_v, dtype=np.float64)
+    cp = np.array(cache_pos, dtype=np.int64)
+    ck[:, slot] = k_rot[0, kv_heads]
+    cv[:, slot] = np.asarray(v_b, dtype=np.float64).reshape(G, d)[kv_heads]
+    cp[slot] = pos
+    filled = cp >= 0
+    heads = [g * group + j for g in kv_heads for j in range(group)]
+    keys = ck[:, filled].transpose(1, 0, 2)
+    vals = cv[:, filled].transpose(1, 0, 2)
+    return attend(q_rot[0][None, heads].reshape(1, len(heads), d), p, keys, vals,
+                  cp[filled], kind, window)[0]

@@ -1,0 +1,197 @@
+"""The C-ABI library on the CPU: it loads, exports every symbol its header
+declares, and rejects every invalid argument with its status code before
+anything reaches the device.  No compute call is made here: invalid calls
+use stand-in pointer values that are never dereferenced."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "olmo3_attn.h")
+
+A = pytest.importorskip("global_hybrid_causal_amd.attn")
+
+if not os.path.exists(A.LIB_PATH):
+    pytest.skip("libolmo3attn.so not built", allow_module_level=True)
+
+
+def header_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(olmo3_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    syms = header_symbols()
+    assert len(syms) >= 9
+    L = ctypes.CDLL(A.LIB_PATH)
+    for s in syms:
+        assert hasattr(L, s), f"{s} declared in the header but not exported"
+    assert sorted(A.EXPORTS) == syms
+
+
+def test_abi_version():
+    assert A.olmo3_abi_version() == 1
+
+
+def test_layer_type_matches_oracle_bit_exact():
+    for n in range(1, 80):
+        want = [O.layer_type_code(k) for k in O.layer_types(n)]
+        assert [A.olmo3_layer_type(i, n) for i in range(n)] == want
+    assert A.olmo3_layer_type(-1, 4) == -1
+    assert A.olmo3_layer_type(4, 4) == -1
+    assert A.olmo3_layer_type(0, 0) == -1
+
+
+def test_status_strings():
+    for s in range(6):
+        assert A.status_string(s)
+    assert A.status_string(99) == "unknown status"
+
+
+def test_workspace_bytes():
+    ws = A.olmo3_workspace_bytes
+    assert ws(A.MODE_PREFILL, 1, 8192, 32, 32, 128, 0, 0, 4096) >= 2 * 8192 * 4096 * 2
+    assert ws(A.MODE_PREFILL, 1, 8192, 32, 32, 128, 1, 0, 8192) >= 8192 * 4096 * 2
+    # sliding prefill also stages rotated keys
+    assert ws(A.MODE_PREFILL, 1, 100, 4, 2, 128, 0, 0, 64) > ws(A.MODE_PREFILL, 1, 100, 4, 2, 128, 1, 0, 100)
+    assert ws(A.MODE_DECODE, 32, 1, 32, 32, 128, 1, 0, 65536) > 32 * 32 * 128 * 2
+    assert ws(A.MODE_PREFILL, 0, 8, 2, 1, 16, 0, 1, 16) == 0
+    assert ws(A.MODE_PREFILL, 1, 8, 3, 2, 16, 0, 1, 16) == 0
+    assert ws(A.MODE_DECODE, 1, 1, 2, 1, 16, 0, 1, 0) == 0
+    assert ws(7, 1, 8, 2, 1, 16, 0, 1, 16) == 0
+
+
+# ---- invalid arguments -------------------------------------------------
+BASE = 1 << 44
+SPACING = 1 << 38  # stand-in buffers far apart, 256-byte aligned
+
+
+def fake(i):
+    return BASE + i * SPACING
+
+
+GOOD = dict(B=2, T=64, H=4, G=2, d=128, window=16, layer_type=0, eps=1e-6, pos_offset=0,
+            dtype=0, cap=16)
+
+
+def prefill_call(**kw):
+    a = dict(GOOD)
+    ptrs = {n: fake(i) for i, n in enumerate(
+        ["q_pre", "k_pre", "v", "q_gain", "k_gain", "k_cache", "v_cache", "out", "workspace"])}
+    ws_bytes = 1 << 34
+    rope = A.Rope(theta=500000.0)
+    for k in list(kw):
+        if k in ptrs:
+            ptrs[k] = kw.pop(k)
+    if "rope" in kw:
+        rope = kw.pop("rope")
+    ws_bytes = kw.pop("ws_bytes", ws_bytes)
+    a.update(kw)
+    r = ctypes.byref(rope.to_c()) if rope is not None else None
+    return A.lib().olmo3_attn_prefill(
+        a["B"], a["T"], a["H"], a["G"], a["d"], a["window"], a["layer_type"], r, a["eps"],
+        a["pos_offset"], a["dtype"], ptrs["q_pre"], ptrs["k_pre"], ptrs["v"], ptrs["q_gain"],
+        ptrs["k_gain"], ptrs["k_cache"], ptrs["v_cache"], a["cap"], ptrs["out"], ptrs["workspace"],
+        ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), A.ERR_INVALID_ARG),
+    (dict(T=0), A.ERR_INVALID_ARG),
+    (dict(H=3), A.ERR_INVALID_ARG),          # H % G != 0
+    (dict(G=0), A.ERR_INVALID_ARG),
+    (dict(d=127), A.ERR_INVALID_ARG),
+    (dict(d=48), A.ERR_UNSUPPORTED),
+    (dict(d=256), A.ERR_UNSUPPORTED),
+    (dict(window=0), A.ERR_INVALID_ARG),
+    (dict(layer_type=2), A.ERR_INVALID_ARG),
+    (dict(dtype=3), A.ERR_INVALID_ARG),
+    (dict(eps=-1.0), A.ERR_INVALID_ARG),
+    (dict(eps=float("nan")), A.ERR_INVALID_ARG),
+    (dict(pos_offset=-1), A.ERR_INVALID_ARG),
+    (dict(rope=None), A.ERR_INVALID_ARG),
+    (dict(rope=A.Rope(theta=0.0)), A.ERR_INVALID_ARG),
+    (dict(rope=A.Rope(theta=1e4, yarn=True, factor=0.5)), A.ERR_INVALID_ARG),
+    (dict(rope=A.Rope(theta=1e4, yarn=True, beta_fast=1.0, beta_slow=32.0)), A.ERR_INVALID_ARG),
+    (dict(q_pre=0), A.ERR_INVALID_ARG),
+    (dict(out=0), A.ERR_INVALID_ARG),
+    (dict(q_pre=fake(0) + 8), A.ERR_INVALID_ARG),   # misaligned
+    (dict(out=fake(0) + 4096), A.ERR_INVALID_ARG),  # out overlaps q_pre
+    (dict(v_cache=fake(5) + 256), A.ERR_INVALID_ARG),  # caches overlap
+    (dict(workspace=fake(7)), A.ERR_INVALID_ARG),   # workspace overlaps out
+    (dict(cap=17), A.ERR_CAPACITY),           # ring must equal window
+    (dict(layer_type=1, cap=63), A.ERR_CAPACITY),   # linear cache shorter than T
+    (dict(workspace=0), A.ERR_WORKSPACE),
+    (dict(ws_bytes=100), A.ERR_WORKSPACE),
+    (dict(layer_type=1, cap=200, pos_offset=5), A.ERR_UNSUPPORTED),  # chunked prefill
+    (dict(H=40 * 8, G=8), A.ERR_UNSUPPORTED),  # too many heads for one wavefront's norm
+])
+def test_prefill_rejects(kw, status):
+    assert prefill_call(**kw) == status
+
+
+def decode_call(**kw):
+    a = dict(GOOD, pos=100)
+    a.pop("T")
+    a.update(kw)
+    ptrs = [fake(i) for i in range(9)]
+    r = ctypes.byref(A.Rope(theta=500000.0).to_c())
+    return A.lib().olmo3_attn_decode(
+        a["B"], a["H"], a["G"], a["d"], a["window"], a["layer_type"], r, a["eps"], a["pos"],
+        a["dtype"], *ptrs[:7], a["cap"], ptrs[7], ptrs[8], a.get("ws_bytes", 1 << 34), None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(pos=-1), A.ERR_INVALID_ARG),
+    (dict(cap=15), A.ERR_CAPACITY),
+    (dict(layer_type=1, cap=100), A.ERR_CAPACITY),  # needs pos + 1 slots
+    (dict(ws_bytes=16), A.ERR_WORKSPACE),
+    (dict(H=5, G=2), A.ERR_INVALID_ARG),
+])
+def test_decode_rejects(kw, status):
+    assert decode_call(**kw) == status
+
+
+def append_call(**kw):
+    a = dict(B=2, T=8, G=2, d=64, window=16, layer_type=1, eps=1e-6, pos=0, dtype=0, cap=8)
+    a.update(kw)
+    p = [fake(i) for i in range(5)]
+    if "k_cache" in kw:
+        p[3] = kw["k_cache"]
+    r = ctypes.byref(A.Rope(theta=1e4).to_c())
+    return A.lib().olmo3_kv_append(a["B"], a["T"], a["G"], a["d"], a["window"], a["layer_type"],
+                                   r, a["eps"], a["pos"], a["dtype"], *p, a["cap"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(cap=7), A.ERR_CAPACITY),
+    (dict(pos=1), A.ERR_CAPACITY),
+    (dict(layer_type=0, cap=8), A.ERR_CAPACITY),
+    (dict(k_cache=fake(0)), A.ERR_INVALID_ARG),  # cache overlaps an input
+    (dict(d=24), A.ERR_UNSUPPORTED),
+])
+def test_append_rejects(kw, status):
+    assert append_call(**kw) == status
+
+
+def test_probe_rejects():
+    L = A.lib()
+    assert L.olmo3_probe_prefill_visits(0, 4, 0, fake(0), None) == A.ERR_INVALID_ARG
+    assert L.olmo3_probe_prefill_visits(5000, 4, 0, fake(0), None) == A.ERR_INVALID_ARG
+    assert L.olmo3_probe_decode_reads(1, 1, 64, 4, 0, 3, 4, fake(0), None) == A.ERR_INVALID_ARG
+    assert L.olmo3_probe_decode_reads(1, 1, 128, 4, 0, 3, 5, fake(0), None) == A.ERR_CAPACITY
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    x = torch.zeros(1, 4, 32, dtype=torch.bfloat16)
+    c = torch.zeros(1, 1, 4, 32, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        A.olmo3_kv_append(x, x, torch.zeros(32, dtype=torch.bfloat16), c, c.clone(), window=4,
+                          layer_type=0, rope=A.Rope())
