@@ -1,0 +1,307 @@
+#!/usr/bin/env python3
+"""Throughput of the OLMo 3 per-layer attention path on one MI355X.
+
+One step runs the whole path once per layer kind:
+  prefill of T new tokens (QK-norm + RoPE + cache append, then attention), on
+  a sliding layer and on a full (YaRN) layer, and
+  decode of one token per sequence against a pre-filled cache (append, then
+  split-KV attention and merge), on a sliding (ring) and a full layer.
+Workloads (synthetic, seeded, shaped like the OLMo 3 configurations):
+  7b   (default) prefill B=1, T=8192, H=G=32, d=128, window 4096;
+       decode B=32 at cache length 65,536 (new token at position 65,535)
+  32b  prefill B=1, T=8192, H=40, G=8; decode B=64 at cache length 32,768
+  long 32-layer attention-only stack (24 sliding, 8 full YaRN), B=1,
+       T=65,536, 7B head shapes, prefill only
+
+Printed: one JSON line.  `value` is prefill TFLOP/s (algorithmic FLOPs of the
+allowed query/key pairs over the whole prefill call time); decode KV GB/s is
+in "decode".  Each kernel is bracketed by HIP events on the stream it is
+launched on (the stage-by-stage entry points), giving the per-kernel
+rooflines.  The CPU oracle is timed on a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "prefill TFLOP/s (% MFMA peak) + decode KV GB/s (% HBM peak), 7B & 32B shapes"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+WINDOW = 4096
+THETA = 500000.0
+
+
+def prefill_pairs(T: int, window: int, sliding: bool) -> int:
+    """Allowed (query, key) pairs: sum over t of min(t+1, window), or T(T+1)/2."""
+    if not sliding or window >= T:
+        return T * (T + 1) // 2
+    return window * (window + 1) // 2 + (T - window) * window
+
+
+def prefill_flops(T, H, d, window, sliding, B=1) -> int:
+    return 4 * d * H * prefill_pairs(T, window, sliding) * B
+
+
+def decode_rows(pos, window, sliding) -> int:
+    return min(pos + 1, window) if sliding else pos + 1
+
+
+def decode_kv_bytes(B, G, d, n, elem=2) -> int:
+    return B * G * n * d * 2 * elem
+
+
+WORKLOADS = {
+    "7b": dict(name="olmo3-7b-layer", prefill=dict(B=1, T=8192, H=32, G=32),
+               decode=dict(B=32, H=32, G=32, L=65536)),
+    "32b": dict(name="olmo3-32b-layer", prefill=dict(B=1, T=8192, H=40, G=8),
+                decode=dict(B=64, H=40, G=8, L=32768)),
+    "long": dict(name="olmo3-7b-long-context-stack", prefill=dict(B=1, T=65536, H=32, G=32, layers=32),
+                 decode=None),
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", choices=sorted(WORKLOADS), default="7b")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="CPU time budget of the oracle baseline (0 disables it)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from global_hybrid_causal_amd import attn as A
+    from global_hybrid_causal_amd import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    A.lib()  # fail loudly if the HIP library is missing
+    wl = WORKLOADS[args.workload]
+    d = 128
+    bf16 = torch.bfloat16
+    rope = A.Rope(theta=THETA, yarn=True, factor=8.0, orig_ctx=8192)
+    segments = []  # (name, kind, callable(phases), phase list, work, work unit)
+
+    # ---- prefill layers
+    pf = wl["prefill"]
+    B, T, H, G = pf["B"], pf["T"], pf["H"], pf["G"]
+    n_layers = pf.get("layers", 0)
+    layer_list = ([(ell, A.olmo3_layer_type(ell, n_layers)) for ell in range(n_layers)]
+                  if n_layers else [(0, 0), (3, 1)])
+    print(f"[bench] workload {wl['name']}: preparing {len(layer_list)} prefill layer(s)", file=sys.stderr,
+          flush=True)
+    seed_base = 5 if n_layers else (2 if args.workload == "7b" else 4)
+    for ell, lt in layer_list:
+        sliding = lt == 0
+        x = synth.layer_inputs(seed_base + (ell if n_layers else 0), ell, B, T, H, G, d,
+                               device=dev, dtype=bf16)
+        cap = WINDOW if sliding else T
+        kc = torch.zeros((B, G, cap, d), dtype=bf16, device=dev)
+        vc = torch.zeros_like(kc)
+        out = torch.empty_like(x["q_pre"])
+        ws = A.workspace(A.MODE_PREFILL, B, T, H, G, d, lt, bf16, cap, dev)
+        r = rope if not sliding else A.Rope(theta=THETA)
+
+        def run(phases, x=x, kc=kc, vc=vc, out=out, ws=ws, lt=lt, r=r):
+            A.olmo3_attn_prefill(x["q_pre"], x["k_pre"], x["v"], x["q_gain"], x["k_gain"], kc, vc,
+                                 out, ws, window=WINDOW, layer_type=lt, rope=r, phases=phases)
+
+        segments.append(dict(name=f"prefill_{'sliding' if sliding else 'full'}_l{ell}", kind="prefill",
+                             sliding=sliding, run=run, phases=[A.PHASE_PROLOGUE, A.PHASE_ATTENTION],
+                             work=prefill_flops(T, H, d, WINDOW, sliding, B)))
+
+    # ---- decode layers
+    dc = wl["decode"]
+    if dc:
+        Bd, Hd, Gd, L = dc["B"], dc["H"], dc["G"], dc["L"]
+        pos = L - 1  # the cache holds positions 0 .. L-2; the new token is the L-th
+        for lt in (0, 1):
+            sliding = lt == 0
+            cap = WINDOW if sliding else L
+            print(f"[bench] filling {'ring' if sliding else 'linear'} decode cache "
+                  f"[{Bd}, {Gd}, {cap}, {d}] x2", file=sys.stderr, flush=True)
+            kc, vc = synth.cache_fill(3 if args.workload == "7b" else 4, 100 + lt, Bd, Gd, cap, d,
+                                      device=dev, dtype=bf16)
+            x = synth.layer_inputs(3 if args.workload == "7b" else 4, 200 + lt, Bd, 1, Hd, Gd, d,
+                                   device=dev, dtype=bf16)
+            q = x["q_pre"][:, 0].contiguous()
+            k = x["k_pre"][:, 0].contiguous()
+            v = x["v"][:, 0].contiguous()
+            out = torch.empty_like(q)
+            ws = A.workspace(A.MODE_DECODE, Bd, 1, Hd, Gd, d, lt, bf16, cap, dev)
+            r = rope if not sliding else A.Rope(theta=THETA)
+
+            def run(phases, q=q, k=k, v=v, x=x, kc=kc, vc=vc, out=out, ws=ws, lt=lt, r=r, pos=pos):
+                A.olmo3_attn_decode(q, k, v, x["q_gain"], x["k_gain"], kc, vc, out, ws,
+                                    window=WINDOW, layer_type=lt, rope=r, pos=pos, phases=phases)
+
+            n = decode_rows(pos, WINDOW, sliding)
+            segments.append(dict(name=f"decode_{'sliding' if sliding else 'full'}", kind="decode",
+                                 sliding=sliding, run=run,
+                                 phases=[A.PHASE_PROLOGUE, A.PHASE_ATTENTION, A.PHASE_MERGE],
+                                 work=decode_kv_bytes(Bd, Gd, d, n), rows=n))
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+
+    def step(record):
+        for seg in segments:
+            if record:
+                evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(seg["phases"]) + 1)]
+                evs[0].record(stream)
+                for i, ph in enumerate(seg["phases"]):
+                    seg["run"](ph)
+                    evs[i + 1].record(stream)
+                seg.setdefault("events", []).append(evs)
+            else:
+                seg["run"](A.PHASES_ALL if seg["kind"] == "decode" else
+                           A.PHASE_PROLOGUE | A.PHASE_ATTENTION)
+
+    print(f"[bench] warmup {args.warmup} step(s)", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    print(f"[bench] timing {args.steps} step(s)", file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    # ---- per-kernel and per-call times (ms), averaged over the timed steps
+    kernel_names = {("prefill", 0): "qknorm_rope_append_kernel", ("prefill", 1): "prefill_d128_kernel",
+                    ("decode", 0): "qknorm_rope_append_kernel", ("decode", 1): "decode_split_kernel",
+                    ("decode", 2): "decode_merge_kernel"}
+    for seg in segments:
+        per_phase = [[evs[i].elapsed_time(evs[i + 1]) for evs in seg["events"]]
+                     for i in range(len(seg["phases"]))]
+        seg["phase_ms"] = [sum(p) / len(p) for p in per_phase]
+        seg["call_ms"] = sum(seg["phase_ms"])
+    ms_per_step = wall * 1e3 / args.steps
+
+    pre = [s for s in segments if s["kind"] == "prefill"]
+    dec = [s for s in segments if s["kind"] == "decode"]
+    prefill_tflops = sum(s["work"] for s in pre) / (sum(s["call_ms"] for s in pre) * 1e-3) / 1e12
+
+    def roof(seg, phase_idx):
+        ms = seg["phase_ms"][phase_idx]
+        if seg["kind"] == "prefill":
+            ach = seg["work"] / (ms * 1e-3) / 1e12
+            return dict(kernel=kernel_names[("prefill", phase_idx)], segment=seg["name"], bound="mfma",
+                        achieved=round(ach, 2), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                        frac=round(ach / PEAK_BF16_TFLOPS, 4), traffic=None, avg_ms=round(ms, 4))
+        ach = seg["work"] / (ms * 1e-3) / 1e9
+        return dict(kernel=kernel_names[("decode", phase_idx)], segment=seg["name"], bound="hbm",
+                    achieved=round(ach, 1), peak=PEAK_HBM_GBS, unit="GB/s",
+                    frac=round(ach / PEAK_HBM_GBS, 4), traffic=None, avg_ms=round(ms, 4))
+
+    rooflines = [roof(s, 1) for s in segments]
+    dominant = max(zip(segments, rooflines), key=lambda sr: sr[0]["phase_ms"][1])[1]
+
+    result = {
+        "metric": METRIC,
+        "value": round(prefill_tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl["name"], "prefill": dict(pf, d=d, window=WINDOW, theta=THETA,
+                                                           yarn_full="factor 8, orig 8192"),
+                   "decode": (dict(dc, d=d, window=WINDOW, pos=dc["L"] - 1) if dc else None),
+                   "parallelism": "single GPU"},
+        "prefill": {"tflops": round(prefill_tflops, 2),
+                    "frac_of_peak": round(prefill_tflops / PEAK_BF16_TFLOPS, 4),
+                    "calls": {s["name"]: {"call_ms": round(s["call_ms"], 4),
+                                          "tflops": round(s["work"] / (s["call_ms"] * 1e-3) / 1e12, 2),
+                                          "flop": s["work"]} for s in pre}},
+        "roofline": dominant,
+        "rooflines": rooflines,
+    }
+    if dec:
+        gbs = sum(s["work"] for s in dec) / (sum(s["call_ms"] for s in dec) * 1e-3) / 1e9
+        result["decode"] = {"gbs": round(gbs, 1), "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4),
+                            "calls": {s["name"]: {"call_ms": round(s["call_ms"], 4),
+                                                  "gbs": round(s["work"] / (s["call_ms"] * 1e-3) / 1e9, 1),
+                                                  "kv_bytes": s["work"], "rows": s["rows"]}
+                                      for s in dec}}
+    if args.cpu_seconds > 0:
+        print(f"[bench] timing the CPU oracle for ~{args.cpu_seconds:.0f} s", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(args, wl, segments, dev)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(args, wl, segments, dev):
+    """The oracle, as it stands, on a bounded sample of the prefill workload:
+    blocks of 32 query rows of the sliding layer (all heads, the keys those
+    rows can see), spread over the sequence, until the time budget is spent.
+    FLOPs are counted like the GPU's (allowed pairs only)."""
+    import numpy as np
+    import torch
+
+    import oracle as O
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()
+                       if p.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover - informational only
+        threads = len(os.sched_getaffinity(0))
+    from global_hybrid_causal_amd import synth
+
+    pf = wl["prefill"]
+    B, T, H, G, d = 1, pf["T"], pf["H"], pf["G"], 128
+    seed = 5 if pf.get("layers") else (2 if args.workload == "7b" else 4)
+    x = synth.layer_inputs(seed, 0, B, T, H, G, d, device=dev, dtype=torch.bfloat16)
+    hx = {k: v.detach().to("cpu", torch.float64).numpy() for k, v in x.items()}
+    rope = O.RopeParams(theta=THETA)
+    rng = np.random.default_rng(0)
+    rows_per_block = 32
+    flops = 0
+    blocks = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < args.cpu_seconds:
+        t_start = int(rng.integers(0, T - rows_per_block + 1))
+        rows = np.arange(t_start, t_start + rows_per_block)
+        k_lo = max(0, t_start - WINDOW + 1)
+        keys = np.arange(k_lo, t_start + rows_per_block)
+        O.attention_rows_ref(hx["q_pre"][0, rows], rows, hx["k_pre"][0, keys],
+                             hx["v"][0, keys].reshape(len(keys), G, d), keys, hx["q_gain"],
+                             hx["k_gain"], H=H, G=G, d=d, kv_heads=range(G), kind=O.SLIDING,
+                             window=WINDOW, rope=rope)
+        flops += 4 * d * H * int(np.minimum(rows + 1, WINDOW).sum())
+        blocks += 1
+    elapsed = time.perf_counter() - t0
+    return {"value": round(flops / elapsed / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{blocks} blocks of {rows_per_block} query rows x {H} heads of the "
+                      f"{wl['name']} sliding prefill (T={T}, window {WINDOW}), fp64 NumPy, "
+                      f"{elapsed:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

@@ -26,8 +26,11 @@ OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_CAPACITY, ERR_HIP, ERR_WORKSPACE = ran
 EXPORTS = (
     "olmo3_layer_type", "olmo3_workspace_bytes", "olmo3_kv_append", "olmo3_attn_prefill",
     "olmo3_attn_decode", "olmo3_status_string", "olmo3_abi_version",
-    "olmo3_probe_prefill_visits", "olmo3_probe_decode_reads",
+    "olmo3_probe_prefill_visits", "olmo3_probe_decode_reads", "olmo3_attn_prefill_phases",
+    "olmo3_attn_decode_phases",
 )
+PHASE_PROLOGUE, PHASE_ATTENTION, PHASE_MERGE = 1, 2, 4
+PHASES_ALL = PHASE_PROLOGUE | PHASE_ATTENTION | PHASE_MERGE
 
 
 class RopeStruct(ctypes.Structure):
@@ -92,6 +95,10 @@ def lib() -> ctypes.CDLL:
         L.olmo3_attn_decode.argtypes = [_i, _i, _i, _i, _i, _i, ctypes.POINTER(RopeStruct), _f, _i64,
                                         _i, _p, _p, _p, _p, _p, _p, _p, _i64, _p, _p, _sz, _p]
         L.olmo3_attn_decode.restype = _i
+        L.olmo3_attn_prefill_phases.argtypes = [_i] + L.olmo3_attn_prefill.argtypes
+        L.olmo3_attn_prefill_phases.restype = _i
+        L.olmo3_attn_decode_phases.argtypes = [_i] + L.olmo3_attn_decode.argtypes
+        L.olmo3_attn_decode_phases.restype = _i
         L.olmo3_status_string.argtypes = [_i]
         L.olmo3_status_string.restype = ctypes.c_char_p
         L.olmo3_abi_version.argtypes = []
@@ -175,38 +182,44 @@ def olmo3_kv_append(k_pre, v, k_gain, k_cache, v_cache, *, window: int, layer_ty
 
 def olmo3_attn_prefill(q_pre, k_pre, v, q_gain, k_gain, k_cache, v_cache, out, workspace, *,
                        window: int, layer_type: int, rope: Rope, eps: float = 1e-6,
-                       pos_offset: int = 0, stream=None) -> None:
-    """Prefill: q_pre [B, T, H*d], k_pre/v [B, T, G*d] -> out [B, T, H*d]."""
+                       pos_offset: int = 0, stream=None, phases: int | None = None) -> None:
+    """Prefill: q_pre [B, T, H*d], k_pre/v [B, T, G*d] -> out [B, T, H*d].
+    ``phases`` (bit set of PHASE_*) selects olmo3_attn_prefill_phases."""
     B, G, cap, d = _cache_dims(k_cache)
     T = q_pre.shape[1]
     H = q_pre.shape[2] // d
     dt = q_pre.dtype
     r = rope.to_c()
-    st = lib().olmo3_attn_prefill(
-        B, T, H, G, d, window, layer_type, ctypes.byref(r), eps, pos_offset, _dtype_code(q_pre),
-        _ptr(q_pre, "q_pre", dt), _ptr(k_pre, "k_pre", dt), _ptr(v, "v", dt),
-        _ptr(q_gain, "q_gain", dt), _ptr(k_gain, "k_gain", dt), _ptr(k_cache, "k_cache", dt),
-        _ptr(v_cache, "v_cache", dt), cap, _ptr(out, "out", dt), _ptr(workspace, "workspace"),
-        workspace.numel() * workspace.element_size(), _stream(stream, q_pre.device))
-    _check(st, "olmo3_attn_prefill")
+    args = (B, T, H, G, d, window, layer_type, ctypes.byref(r), eps, pos_offset, _dtype_code(q_pre),
+            _ptr(q_pre, "q_pre", dt), _ptr(k_pre, "k_pre", dt), _ptr(v, "v", dt),
+            _ptr(q_gain, "q_gain", dt), _ptr(k_gain, "k_gain", dt), _ptr(k_cache, "k_cache", dt),
+            _ptr(v_cache, "v_cache", dt), cap, _ptr(out, "out", dt), _ptr(workspace, "workspace"),
+            workspace.numel() * workspace.element_size(), _stream(stream, q_pre.device))
+    if phases is None:
+        _check(lib().olmo3_attn_prefill(*args), "olmo3_attn_prefill")
+    else:
+        _check(lib().olmo3_attn_prefill_phases(phases, *args), "olmo3_attn_prefill_phases")
 
 
 def olmo3_attn_decode(q_pre, k_pre, v, q_gain, k_gain, k_cache, v_cache, out, workspace, *,
                       window: int, layer_type: int, rope: Rope, pos: int, eps: float = 1e-6,
-                      stream=None) -> None:
+                      stream=None, phases: int | None = None) -> None:
     """Decode one token per sequence at position ``pos``: q_pre [B, H*d],
-    k_pre/v [B, G*d] -> out [B, H*d]."""
+    k_pre/v [B, G*d] -> out [B, H*d].  ``phases`` selects
+    olmo3_attn_decode_phases."""
     B, G, cap, d = _cache_dims(k_cache)
     H = q_pre.shape[-1] // d
     dt = q_pre.dtype
     r = rope.to_c()
-    st = lib().olmo3_attn_decode(
-        B, H, G, d, window, layer_type, ctypes.byref(r), eps, pos, _dtype_code(q_pre),
-        _ptr(q_pre, "q_pre", dt), _ptr(k_pre, "k_pre", dt), _ptr(v, "v", dt),
-        _ptr(q_gain, "q_gain", dt), _ptr(k_gain, "k_gain", dt), _ptr(k_cache, "k_cache", dt),
-        _ptr(v_cache, "v_cache", dt), cap, _ptr(out, "out", dt), _ptr(workspace, "workspace"),
-        workspace.numel() * workspace.element_size(), _stream(stream, q_pre.device))
-    _check(st, "olmo3_attn_decode")
+    args = (B, H, G, d, window, layer_type, ctypes.byref(r), eps, pos, _dtype_code(q_pre),
+            _ptr(q_pre, "q_pre", dt), _ptr(k_pre, "k_pre", dt), _ptr(v, "v", dt),
+            _ptr(q_gain, "q_gain", dt), _ptr(k_gain, "k_gain", dt), _ptr(k_cache, "k_cache", dt),
+            _ptr(v_cache, "v_cache", dt), cap, _ptr(out, "out", dt), _ptr(workspace, "workspace"),
+            workspace.numel() * workspace.element_size(), _stream(stream, q_pre.device))
+    if phases is None:
+        _check(lib().olmo3_attn_decode(*args), "olmo3_attn_decode")
+    else:
+        _check(lib().olmo3_attn_decode_phases(phases, *args), "olmo3_attn_decode_phases")
 
 
 def workspace(mode: int, B: int, T: int, H: int, G: int, d: int, layer_type: int,

@@ -226,11 +226,14 @@ static int validate_attn(int B, int T, int H, int G, int d, int window, int laye
   return OLMO3_OK;
 }
 
-int olmo3_attn_prefill(int B, int T, int H, int G, int d, int window, int layer_type,
-                       const olmo3_rope* rope, float eps, int64_t pos_offset, int dtype,
-                       const void* q_pre, const void* k_pre, const void* v, const void* q_gain,
-                       const void* k_gain, void* k_cache, void* v_cache, int64_t cache_capacity,
-                       void* out, void* workspace, size_t workspace_bytes, void* stream) {
+int olmo3_attn_prefill_phases(int phases, int B, int T, int H, int G, int d, int window,
+                              int layer_type, const olmo3_rope* rope, float eps,
+                              int64_t pos_offset, int dtype, const void* q_pre, const void* k_pre,
+                              const void* v, const void* q_gain, const void* k_gain,
+                              void* k_cache, void* v_cache, int64_t cache_capacity, void* out,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  if (phases <= 0 || (phases & ~(OLMO3_PHASE_PROLOGUE | OLMO3_PHASE_ATTENTION | OLMO3_PHASE_MERGE)))
+    return OLMO3_ERR_INVALID_ARG;
   const size_t need = (B > 0 && T > 0 && H > 0 && G > 0 && d > 0)
                           ? prefill_ws(B, T, H, G, d, layer_type, dtype)
                           : 0;
@@ -272,8 +275,11 @@ int olmo3_attn_prefill(int B, int T, int H, int G, int d, int window, int layer_
   p.window = window;
   p.sliding = sliding;
   p.eps = eps;
-  st = hip_status(launch_prologue(p, table, dtype, d, s));
-  if (st) return st;
+  if (phases & OLMO3_PHASE_PROLOGUE) {
+    st = hip_status(launch_prologue(p, table, dtype, d, s));
+    if (st) return st;
+  }
+  if (!(phases & OLMO3_PHASE_ATTENTION)) return OLMO3_OK;
 
   AttnArgs a = {};
   a.q = q_rot;
@@ -310,11 +316,25 @@ int olmo3_attn_prefill(int B, int T, int H, int G, int d, int window, int layer_
   return hip_status(launch_attn_generic(a, dtype, d, s));
 }
 
-int olmo3_attn_decode(int B, int H, int G, int d, int window, int layer_type,
-                      const olmo3_rope* rope, float eps, int64_t pos, int dtype,
-                      const void* q_pre, const void* k_pre, const void* v, const void* q_gain,
-                      const void* k_gain, void* k_cache, void* v_cache, int64_t cache_capacity,
-                      void* out, void* workspace, size_t workspace_bytes, void* stream) {
+int olmo3_attn_prefill(int B, int T, int H, int G, int d, int window, int layer_type,
+                       const olmo3_rope* rope, float eps, int64_t pos_offset, int dtype,
+                       const void* q_pre, const void* k_pre, const void* v, const void* q_gain,
+                       const void* k_gain, void* k_cache, void* v_cache, int64_t cache_capacity,
+                       void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  return olmo3_attn_prefill_phases(OLMO3_PHASE_PROLOGUE | OLMO3_PHASE_ATTENTION, B, T, H, G, d,
+                                   window, layer_type, rope, eps, pos_offset, dtype, q_pre, k_pre,
+                                   v, q_gain, k_gain, k_cache, v_cache, cache_capacity, out,
+                                   workspace, workspace_bytes, stream);
+}
+
+int olmo3_attn_decode_phases(int phases, int B, int H, int G, int d, int window, int layer_type,
+                             const olmo3_rope* rope, float eps, int64_t pos, int dtype,
+                             const void* q_pre, const void* k_pre, const void* v,
+                             const void* q_gain, const void* k_gain, void* k_cache,
+                             void* v_cache, int64_t cache_capacity, void* out, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  if (phases <= 0 || (phases & ~(OLMO3_PHASE_PROLOGUE | OLMO3_PHASE_ATTENTION | OLMO3_PHASE_MERGE)))
+    return OLMO3_ERR_INVALID_ARG;
   const size_t need = (B > 0 && H > 0 && G > 0 && d > 0 && G <= H && cache_capacity > 0)
                           ? decode_ws(B, H, G, d, layer_type, window, dtype, cache_capacity)
                           : 0;
@@ -350,8 +370,10 @@ int olmo3_attn_decode(int B, int H, int G, int d, int window, int layer_type,
   p.window = window;
   p.sliding = sliding;
   p.eps = eps;
-  st = hip_status(launch_prologue(p, table, dtype, d, s));
-  if (st) return st;
+  if (phases & OLMO3_PHASE_PROLOGUE) {
+    st = hip_status(launch_prologue(p, table, dtype, d, s));
+    if (st) return st;
+  }
 
   const int64_t n = sliding ? std::min<int64_t>(pos + 1, window) : pos + 1;
   if (decode_uses_split(dtype, d, H, G)) {
@@ -370,8 +392,14 @@ int olmo3_attn_decode(int B, int H, int G, int d, int window, int layer_type,
     a.H = H;
     a.G = G;
     a.scale_log2 = scale_log2(d);
-    return hip_status(launch_decode_mfma(a, s));
+    if (phases & OLMO3_PHASE_ATTENTION) {
+      st = hip_status(launch_decode_split(a, s));
+      if (st) return st;
+    }
+    if (phases & OLMO3_PHASE_MERGE) return hip_status(launch_decode_merge(a, s));
+    return OLMO3_OK;
   }
+  if (!(phases & OLMO3_PHASE_ATTENTION)) return OLMO3_OK;
   AttnArgs a = {};
   a.q = q_rot;
   a.k = k_cache;
@@ -391,6 +419,17 @@ int olmo3_attn_decode(int B, int H, int G, int d, int window, int layer_type,
   a.all_visible = 1;
   a.scale_log2 = scale_log2(d);
   return hip_status(launch_attn_generic(a, dtype, d, s));
+}
+
+int olmo3_attn_decode(int B, int H, int G, int d, int window, int layer_type,
+                      const olmo3_rope* rope, float eps, int64_t pos, int dtype,
+                      const void* q_pre, const void* k_pre, const void* v, const void* q_gain,
+                      const void* k_gain, void* k_cache, void* v_cache, int64_t cache_capacity,
+                      void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  return olmo3_attn_decode_phases(OLMO3_PHASE_PROLOGUE | OLMO3_PHASE_ATTENTION | OLMO3_PHASE_MERGE,
+                                  B, H, G, d, window, layer_type, rope, eps, pos, dtype, q_pre,
+                                  k_pre, v, q_gain, k_gain, k_cache, v_cache, cache_capacity, out,
+                                  workspace, workspace_bytes, stream);
 }
 
 int olmo3_probe_prefill_visits(int T, int window, int layer_type, uint8_t* visit, void* stream) {

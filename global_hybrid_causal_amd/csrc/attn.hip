@@ -494,7 +494,7 @@ int decode_splits(int B, int G, int64_t n) {
   return (int)s;
 }
 
-hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t s) {
+hipError_t launch_decode_split(const DecodeArgs& a, hipStream_t s) {
   const int group = a.H / a.G;
   const int blocks = a.B * a.G * a.splits;
 #define OLMO3_DEC(GG) \
@@ -508,8 +508,10 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t s) {
       return hipErrorInvalidValue;
   }
 #undef OLMO3_DEC
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t s) {
   decode_merge_kernel<<<a.B * a.H, dec::kD, 0, s>>>(a);
   return hipGetLastError();
 }

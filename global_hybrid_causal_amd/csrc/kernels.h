@@ -77,7 +77,8 @@ struct DecodeArgs {
   float scale_log2;
 };
 int decode_splits(int B, int G, int64_t n);
-hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_decode_split(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t s);
 
 // Probes: the prefill kernel's tile walk and the decode kernel's row walk.
 hipError_t launch_probe_prefill(int T, int window, int sliding, uint8_t* visit, hipStream_t s);

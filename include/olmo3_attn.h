@@ -156,6 +156,37 @@ int olmo3_attn_decode(int B, int H, int G, int d, int window, int layer_type,
                       void* out, void* workspace, size_t workspace_bytes,
                       void* stream);
 
+/* Stage-by-stage variants, for callers that time or overlap the kernels of
+ * one call.  `phases` is a bit set of:
+ *   OLMO3_PHASE_PROLOGUE  (1)  QK-norm + RoPE of the new tokens, cache
+ *                              append, rotated queries (and, on sliding
+ *                              prefill, keys) written to the workspace;
+ *   OLMO3_PHASE_ATTENTION (2)  attention reading the workspace and cache;
+ *                              for decode, the split-KV partial states;
+ *   OLMO3_PHASE_MERGE     (4)  decode only: log-sum-exp merge of the
+ *                              partial states into out (a no-op when the
+ *                              decode path needs no merge).
+ * All phases together equal olmo3_attn_prefill / olmo3_attn_decode.  A later
+ * phase must follow the earlier ones on the same stream with the same
+ * arguments and workspace.  Arguments are validated as for the full call;
+ * phases == 0 or unknown bits: INVALID_ARG. */
+enum { OLMO3_PHASE_PROLOGUE = 1, OLMO3_PHASE_ATTENTION = 2, OLMO3_PHASE_MERGE = 4 };
+
+int olmo3_attn_prefill_phases(int phases, int B, int T, int H, int G, int d, int window,
+                              int layer_type, const olmo3_rope* rope, float eps,
+                              int64_t pos_offset, int dtype, const void* q_pre,
+                              const void* k_pre, const void* v, const void* q_gain,
+                              const void* k_gain, void* k_cache, void* v_cache,
+                              int64_t cache_capacity, void* out, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+int olmo3_attn_decode_phases(int phases, int B, int H, int G, int d, int window,
+                             int layer_type, const olmo3_rope* rope, float eps, int64_t pos,
+                             int dtype, const void* q_pre, const void* k_pre, const void* v,
+                             const void* q_gain, const void* k_gain, void* k_cache,
+                             void* v_cache, int64_t cache_capacity, void* out,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static text for a status code; never NULL. */
 const char* olmo3_status_string(int status);
 

@@ -453,16 +453,15 @@ def attention_rows_ref(q_pre_rows, q_rows_pos, k_pre_keys, v_keys, k_keys_pos,
     R = q_pre_rows.shape[0]
     qh = rms_norm(q_pre_rows, q_gain, eps).reshape(R, H, d)
     q_rot = rope_rotate(qh, q_rows_pos, w, m)
+    kv_heads = list(kv_heads)
     if k_is_rotated:
-        k_rot = np.asarray(k_pre_keys, dtype=np.float64)
+        sub_k = np.asarray(k_pre_keys, dtype=np.float64)[:, kv_heads, :]
     else:
         N = k_pre_keys.shape[0]
         kh = rms_norm(np.asarray(k_pre_keys, dtype=np.float64), k_gain, eps).reshape(N, G, d)
-        k_rot = rope_rotate(kh, k_keys_pos, w, m)
-    kv_heads = list(kv_heads)
+        sub_k = rope_rotate(kh[:, kv_heads, :], k_keys_pos, w, m)
     heads = [g * group + j for g in kv_heads for j in range(group)]
     sub_q = q_rot[:, heads, :]
-    sub_k = k_rot[:, kv_heads, :]
     sub_v = np.asarray(v_keys, dtype=np.float64)[:, kv_heads, :]
     return attend(sub_q, np.asarray(q_rows_pos), sub_k, sub_v,
                   np.asarray(k_keys_pos), kind, window)

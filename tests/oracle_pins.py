@@ -443,4 +443,33 @@ def check_kv_bytes_golden():
     assert abs(frac64 - frac) < 1e-15
 
 
+def check_sampled_functions_equal_whole_output():
+    """The row- and head-sampled evaluations used at full workload sizes give
+    the same numbers as the whole-output prefill and decode."""
+    rng = _rng(14)
+    T, H, G, d, w = 50, 6, 2, 8, 9
+    x = _inputs(rng, 1, T, H, G, d)
+    rows = np.array([0, 7, 8, 9, 30, 49])
+    for kind, cap in ((O.SLIDING, w), (O.FULL, T)):
+        rope = O.RopeParams(theta=1e4, yarn=True, factor=4.0, orig_ctx=16)
+        full = O.prefill_ref(**x, H=H, G=G, d=d, kind=kind, window=w, rope=rope).reshape(T, H, d)
+        got = O.attention_rows_ref(x["q_pre"][0, rows], rows, x["k_pre"][0],
+                                   x["v"][0].reshape(T, G, d), np.arange(T), x["q_gain"],
+                                   x["k_gain"], H=H, G=G, d=d, kv_heads=[1], kind=kind, window=w,
+                                   rope=rope)
+        _close(got, full[rows][:, 3:6], 1e-12, f"rows {kind}")
+        c = O.KvCacheRef(kind, w, cap, 1, G, d)
+        head = {k: (v[:, :T - 1] if v.ndim == 3 else v) for k, v in x.items()}
+        O.prefill_ref(**head, H=H, G=G, d=d, kind=kind, window=w, rope=rope, cache=c)
+        assert np.array_equal(c.pos, O.ring_positions(kind, w, cap, T - 1))
+        ck, cv, cp = c.k[0].copy(), c.v[0].copy(), c.pos.copy()
+        ref = O.decode_ref(x["q_pre"][:, T - 1], x["k_pre"][:, T - 1], x["v"][:, T - 1],
+                           x["q_gain"], x["k_gain"], H=H, G=G, d=d, kind=kind, window=w,
+                           rope=rope, pos=T - 1, cache=c)
+        got = O.decode_rows_ref(x["q_pre"][0, T - 1], x["k_pre"][0, T - 1], x["v"][0, T - 1],
+                                x["q_gain"], x["k_gain"], ck[[1]], cv[[1]], cp, H=H, G=G, d=d,
+                                kv_heads=[1], kind=kind, window=w, rope=rope, pos=T - 1)
+        _close(got, ref[0].reshape(H, d)[3:6], 1e-12, f"decode rows {kind}")
+
+
 ALL_CHECKS = [v for k, v in sorted(globals().items()) if k.startswith("check_") and callable(v)]

@@ -195,3 +195,14 @@ def test_binding_refuses_host_tensors():
     with pytest.raises(ValueError):
         A.olmo3_kv_append(x, x, torch.zeros(32, dtype=torch.bfloat16), c, c.clone(), window=4,
                           layer_type=0, rope=A.Rope())
+
+
+def test_phases_reject_bad_bits():
+    L = A.lib()
+    r = ctypes.byref(A.Rope().to_c())
+    p = [fake(i) for i in range(9)]
+    for ph in (0, 8, -1):
+        assert L.olmo3_attn_prefill_phases(ph, 1, 8, 2, 1, 128, 4, 0, r, 1e-6, 0, 0, *p[:7], 4, p[7], p[8],
+                                           1 << 30, None) == A.ERR_INVALID_ARG
+        assert L.olmo3_attn_decode_phases(ph, 1, 2, 1, 128, 4, 0, r, 1e-6, 3, 0, *p[:7], 4, p[7], p[8],
+                                          1 << 30, None) == A.ERR_INVALID_ARG

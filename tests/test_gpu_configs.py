@@ -1,0 +1,151 @@
+"""GPU parity at the full workload sizes, in the launch configuration the
+benchmark times, on outputs the oracle computes one by one: sampled query
+rows (including both window edges and the block edges) for sampled
+key/value heads, and sampled sequences for decode.  Cache slots written by
+the call are checked at the sampled heads."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from global_hybrid_causal_amd import attn as A
+from global_hybrid_causal_amd import synth
+from gpu_util import KINDS, assert_close, gpu_decode, gpu_prefill, host, inputs, oracle_rope
+
+pytestmark = pytest.mark.gpu
+
+BF16 = torch.bfloat16
+W = 4096
+YARN = A.Rope(theta=500000.0, yarn=True, factor=8.0, orig_ctx=8192)
+PLAIN = A.Rope(theta=500000.0)
+
+
+def _log(*a):
+    print(*a, flush=True)
+
+
+def _sample_rows(T, seed, n_random=20):
+    edges = [0, 1, 63, 64, 127, 128, W - 1, W, W + 1, T // 2, T - 2, T - 1]
+    rng = np.random.default_rng(seed)
+    rows = set(r for r in edges if 0 <= r < T) | set(rng.integers(0, T, n_random).tolist())
+    return np.array(sorted(rows))
+
+
+def _check_prefill_rows(x, out, kc, vc, *, T, H, G, d, lt, rope, kv_heads, seed, what):
+    kind = KINDS[lt]
+    rows = _sample_rows(T, seed)
+    q_rows = host(x["q_pre"][0, rows])
+    k_all = host(x["k_pre"][0])
+    v_all = host(x["v"][0]).reshape(T, G, d)
+    qg, kg = host(x["q_gain"]), host(x["k_gain"])
+    ref = O.attention_rows_ref(q_rows, rows, k_all, v_all, np.arange(T), qg, kg, H=H, G=G, d=d,
+                               kv_heads=kv_heads, kind=kind, window=W, rope=oracle_rope(rope))
+    group = H // G
+    heads = [g * group + j for g in kv_heads for j in range(group)]
+    got = host(out[0, rows]).reshape(len(rows), H, d)[:, heads]
+    err = assert_close(got, ref, what=what)
+    _log(f"  {what}: {len(rows)} rows x {len(heads)} heads, max abs/rel err {err}")
+    # cache slots of the sampled heads: keys rotated at their positions, values copied
+    w_, m_ = O.layer_rope(oracle_rope(rope), kind, d)
+    held = np.arange(T - W, T) if kind == O.SLIDING else np.arange(T)
+    pick = np.random.default_rng(seed + 1).choice(held, size=min(64, held.size), replace=False)
+    kh = O.rms_norm(k_all[pick], kg, 1e-6).reshape(len(pick), G, d)
+    k_ref = O.rope_rotate(kh, pick, w_, m_)
+    slots = pick % W if kind == O.SLIDING else pick
+    kc_h = host(kc[0][:, slots]).transpose(1, 0, 2)  # [n, G, d]
+    vc_h = host(vc[0][:, slots]).transpose(1, 0, 2)
+    assert np.array_equal(vc_h, v_all[pick]), f"{what}: cached values differ"
+    assert_close(kc_h, k_ref, what=f"{what} cached keys")
+
+
+@pytest.mark.parametrize("lt", [0, 1], ids=["sliding", "full_yarn"])
+@pytest.mark.parametrize("shape", [(32, 32), (40, 8)], ids=["7b", "32b"])
+def test_prefill_full_size_sampled(shape, lt):
+    """7B (H=G=32) and 32B (H=40, G=8) prefill, B=1, T=8192, window 4096."""
+    H, G = shape
+    B, T, d = 1, 8192, 128
+    rope = YARN if lt == 1 else PLAIN
+    _log(f"prefill H={H} G={G} T={T} layer_type={lt}")
+    x = inputs(2 if H == 32 else 4, lt, B, T, H, G, d, BF16)
+    cap = W if lt == 0 else T
+    kc = torch.zeros((B, G, cap, d), dtype=BF16, device="cuda")
+    vc = torch.zeros_like(kc)
+    out = gpu_prefill(x, kc, vc, window=W, layer_type=lt, rope=rope, H=H)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
+    kv_heads = [0, 13, G - 1] if G > 8 else [0, 5, G - 1]
+    _check_prefill_rows(x, out, kc, vc, T=T, H=H, G=G, d=d, lt=lt, rope=rope, kv_heads=kv_heads,
+                        seed=lt, what=f"prefill {H}/{G} lt={lt}")
+
+
+@pytest.mark.parametrize("lt", [0, 1], ids=["sliding_ring", "full_linear"])
+@pytest.mark.parametrize("shape", [(32, 32, 32, 65536), (64, 40, 8, 32768)], ids=["7b", "32b"])
+def test_decode_full_size_sampled(shape, lt):
+    """7B decode B=32 at cache length 65,536; 32B decode B=64 at 32,768.
+    The cache holds positions 0 .. L-2 (ring: the last 4096 of them); the new
+    token sits at L-1."""
+    B, H, G, L = shape
+    d = 128
+    kind = KINDS[lt]
+    pos = L - 1
+    cap = W if lt == 0 else L
+    rope = YARN if lt == 1 else PLAIN
+    _log(f"decode B={B} H={H} G={G} L={L} layer_type={lt}")
+    kc, vc = synth.cache_fill(3 if H == 32 else 4, 100 + lt, B, G, cap, d, device="cuda", dtype=BF16)
+    bs, gs = [0, B - 1], [0, G - 1]
+    before_k = {(b, g): host(kc[b, g]) for b in bs for g in gs}
+    before_v = {(b, g): host(vc[b, g]) for b in bs for g in gs}
+    x = inputs(3 if H == 32 else 4, 200 + lt, B, 1, H, G, d, BF16)
+    q, k, v = x["q_pre"][:, 0].contiguous(), x["k_pre"][:, 0].contiguous(), x["v"][:, 0].contiguous()
+    out = gpu_decode(q, k, v, x["q_gain"], x["k_gain"], kc, vc, window=W, layer_type=lt, rope=rope,
+                     pos=pos, H=H)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
+    tags = O.ring_positions(kind, W, cap, pos)
+    assert (tags >= 0).sum() == (min(pos, W) if lt == 0 else pos)
+    hq, hk, hv = host(q), host(k), host(v)
+    qg, kg = host(x["q_gain"]), host(x["k_gain"])
+    group = H // G
+    slot = pos % W if lt == 0 else pos
+    for b in bs:
+        ck = np.stack([before_k[(b, g)] for g in gs])
+        cv = np.stack([before_v[(b, g)] for g in gs])
+        ref = O.decode_rows_ref(hq[b], hk[b], hv[b], qg, kg, ck, cv, tags, H=H, G=G, d=d, kv_heads=gs,
+                                kind=kind, window=W, rope=oracle_rope(rope), pos=pos)
+        heads = [g * group + j for g in gs for j in range(group)]
+        got = host(out[b]).reshape(H, d)[heads]
+        err = assert_close(got, ref, what=f"decode b={b}")
+        _log(f"  decode b={b}: {len(heads)} heads, max abs/rel err {err}")
+        for g in gs:
+            assert np.array_equal(host(vc[b, g, slot]), hv[b].reshape(G, d)[g])
+            others = host(vc[b, g])
+            others[slot] = before_v[(b, g)][slot]
+            assert np.array_equal(others, before_v[(b, g)]), "decode wrote outside its slot"
+
+
+def test_long_context_stack_sampled():
+    """32-layer attention-only stack, 7B head shapes, B=1, T=65,536: full
+    layers (l mod 4 == 3 and the last) use YaRN (factor 8, original 8192),
+    sliding layers plain RoPE with window 4096; per-layer seeds.  Every layer
+    runs on the GPU; sampled rows of layers 0, 3, 30 and 31 are compared with
+    the oracle."""
+    B, T, H, G, d, n_layers = 1, 65536, 32, 32, 128, 32
+    kinds = O.layer_types(n_layers)
+    assert kinds.count(O.FULL) == 8
+    for ell in range(n_layers):
+        lt = A.olmo3_layer_type(ell, n_layers)
+        assert lt == O.layer_type_code(kinds[ell])
+        rope = YARN if lt == 1 else PLAIN
+        x = inputs(5 + ell, ell, B, T, H, G, d, BF16)
+        cap = W if lt == 0 else T
+        kc = torch.zeros((B, G, cap, d), dtype=BF16, device="cuda")
+        vc = torch.zeros_like(kc)
+        out = gpu_prefill(x, kc, vc, window=W, layer_type=lt, rope=rope, H=H)
+        torch.cuda.synchronize()
+        assert torch.isfinite(out).all(), f"layer {ell}"
+        if ell in (0, 3, 30, 31):
+            _log(f"long-context layer {ell} ({kinds[ell]})")
+            _check_prefill_rows(x, out, kc, vc, T=T, H=H, G=G, d=d, lt=lt, rope=rope,
+                                kv_heads=[0, 31], seed=100 + ell, what=f"long layer {ell}")
+        del x, kc, vc, out

@@ -256,3 +256,44 @@ def test_planted_value_window_edges(lt, T, w, s_star):
     assert (out[~sees] == 0.0).all(), np.nonzero((out[~sees] != 0).any(axis=1))
     want = (1024.0 / n[sees])[:, None] * np.ones((1, H * d))
     assert_close(out[sees], want, 0.0, 2 ** -8, "planted rows")
+
+
+def test_phase_entry_points_equal_one_call():
+    """Running the stages one by one gives bit-identical outputs and caches."""
+    B, T, H, G, d, w = 1, 333, 8, 2, 128, 100
+    rope = A.Rope(theta=500000.0, yarn=True, factor=8.0, orig_ctx=128)
+    x = inputs(29, 0, B, T, H, G, d, BF16)
+    for lt in (0, 1):
+        cap = w if lt == 0 else T + 1
+        outs = []
+        for phased in (False, True):
+            kc = torch.zeros((B, G, cap, d), dtype=BF16, device="cuda")
+            vc = torch.zeros_like(kc)
+            out = torch.empty_like(x["q_pre"])
+            ws = A.workspace(A.MODE_PREFILL, B, T, H, G, d, lt, BF16, cap, "cuda")
+            kw = dict(window=w, layer_type=lt, rope=rope)
+            if phased:
+                A.olmo3_attn_prefill(x["q_pre"], x["k_pre"], x["v"], x["q_gain"], x["k_gain"], kc, vc,
+                                     out, ws, phases=A.PHASE_PROLOGUE, **kw)
+                A.olmo3_attn_prefill(x["q_pre"], x["k_pre"], x["v"], x["q_gain"], x["k_gain"], kc, vc,
+                                     out, ws, phases=A.PHASE_ATTENTION, **kw)
+            else:
+                A.olmo3_attn_prefill(x["q_pre"], x["k_pre"], x["v"], x["q_gain"], x["k_gain"], kc, vc,
+                                     out, ws, **kw)
+            dq = synth.normal((2, H * d), 31, lt, 1, device="cuda")
+            dk = synth.normal((2, G * d), 31, lt, 2, device="cuda")
+            kc2 = kc.expand(2, -1, -1, -1).contiguous()
+            vc2 = vc.expand(2, -1, -1, -1).contiguous()
+            dout = torch.empty_like(dq)
+            wsd = A.workspace(A.MODE_DECODE, 2, 1, H, G, d, lt, BF16, cap, "cuda")
+            dargs = (dq, dk, dk.clone(), x["q_gain"], x["k_gain"], kc2, vc2, dout, wsd)
+            pos = T if lt == 1 else T + 50
+            if phased:
+                for ph in (A.PHASE_PROLOGUE, A.PHASE_ATTENTION, A.PHASE_MERGE):
+                    A.olmo3_attn_decode(*dargs, pos=pos, phases=ph, **kw)
+            else:
+                A.olmo3_attn_decode(*dargs, pos=pos, **kw)
+            torch.cuda.synchronize()
+            outs.append((out.clone(), kc.clone(), vc.clone(), dout.clone(), kc2.clone()))
+        for a_, b_ in zip(outs[0], outs[1]):
+            assert torch.equal(a_, b_)
