@@ -76,7 +76,24 @@ def parse():
     ap.add_argument("--workload", choices=sorted(WORKLOADS), default="7b")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="CPU time budget of the oracle baseline (0 disables it)")
+    ap.add_argument("--segments", default="",
+                    help="comma-separated subset of prefill_sliding, prefill_full, decode_sliding, "
+                         "decode_full (for profiling runs; default: all)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device-to-device copy of BYTES bytes three times "
+                         "(reference for HBM byte counters) and exit")
     return ap.parse_args()
+
+
+def copy_calibration(nbytes: int) -> None:
+    import torch
+
+    src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": nbytes, "launches": 3}), flush=True)
 
 
 def main():
@@ -92,6 +109,13 @@ def main():
     from global_hybrid_causal_amd import synth
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
+    wanted = set(filter(None, args.segments.split(",")))
+
+    def keep(kind, sliding):
+        return not wanted or f"{kind}_{'sliding' if sliding else 'full'}" in wanted
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     A.lib()  # fail loudly if the HIP library is missing
@@ -112,6 +136,8 @@ def main():
     seed_base = 5 if n_layers else (2 if args.workload == "7b" else 4)
     for ell, lt in layer_list:
         sliding = lt == 0
+        if not keep("prefill", sliding):
+            continue
         x = synth.layer_inputs(seed_base + (ell if n_layers else 0), ell, B, T, H, G, d,
                                device=dev, dtype=bf16)
         cap = WINDOW if sliding else T
@@ -136,6 +162,8 @@ def main():
         pos = L - 1  # the cache holds positions 0 .. L-2; the new token is the L-th
         for lt in (0, 1):
             sliding = lt == 0
+            if not keep("decode", sliding):
+                continue
             cap = WINDOW if sliding else L
             print(f"[bench] filling {'ring' if sliding else 'linear'} decode cache "
                   f"[{Bd}, {Gd}, {cap}, {d}] x2", file=sys.stderr, flush=True)
@@ -200,7 +228,8 @@ def main():
 
     pre = [s for s in segments if s["kind"] == "prefill"]
     dec = [s for s in segments if s["kind"] == "decode"]
-    prefill_tflops = sum(s["work"] for s in pre) / (sum(s["call_ms"] for s in pre) * 1e-3) / 1e12
+    prefill_tflops = (sum(s["work"] for s in pre) / (sum(s["call_ms"] for s in pre) * 1e-3) / 1e12
+                      if pre else 0.0)
 
     def roof(seg, phase_idx):
         ms = seg["phase_ms"][phase_idx]
@@ -249,7 +278,7 @@ def main():
                                                   "gbs": round(s["work"] / (s["call_ms"] * 1e-3) / 1e9, 1),
                                                   "kv_bytes": s["work"], "rows": s["rows"]}
                                       for s in dec}}
-    if args.cpu_seconds > 0:
+    if args.cpu_seconds > 0 and pre:
         print(f"[bench] timing the CPU oracle for ~{args.cpu_seconds:.0f} s", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(args, wl, segments, dev)
     print(json.dumps(result), flush=True)

@@ -18,7 +18,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libolmo3attn.so")
-SOURCES = ["api.hip", "prologue.hip", "attn.hip"]
+SOURCES = ["api.hip", "prologue.hip", "attn.hip", "prefill.hip"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops: keep hipcc from emitting packed fp32 VALU operations.
@@ -36,9 +36,15 @@ def hipcc() -> str:
     return path
 
 
+# The prefill kernel's maxima never see a NaN (masked scores are -inf), so
+# fmax needs no NaN quieting there.
+PER_FILE_FLAGS = {"prefill.hip": ["-fno-honor-nans"]}
+
+
 def _compile(src: str, extra: list[str]) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *COMMON_FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *COMMON_FLAGS, *PER_FILE_FLAGS.get(src, []), *extra, "-c",
+           os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{res.stdout}\n{res.stderr}")

@@ -1,6 +1,6 @@
-// Causal attention kernels: flash-style MFMA prefill (d = 128, bf16), a
-// plain per-query kernel for other head sizes and fp32, and split-KV decode
-// with a log-sum-exp merge.
+// Causal attention kernels: a plain per-query kernel for other head sizes
+// and fp32, and split-KV decode (d = 128, bf16) with a log-sum-exp merge.
+// The MFMA prefill kernel lives in prefill.hip.
 //
 // Masking follows "OLMo 3's Sliding-Window Attention Pattern", "The
 // sliding-window mask"; decode on a ring reads exactly the `window` held
@@ -15,217 +15,6 @@ namespace olmo3 {
 namespace {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
-// ---------------------------------------------------------------------------
-// Prefill, d = 128.
-//
-// Workgroup = 4 wavefronts x 32 queries of one (batch, head).  Per key tile
-// of 64 keys each wavefront computes S^T = K Q^T (two 32x32 blocks, K from
-// LDS as the A operand, its queries' Q^T held in registers as B), so a lane
-// owns one query column; it then accumulates O^T += V^T P^T with P^T taken
-// straight from the S accumulators (converted to bf16) as the B operand.
-// The key order inside each 16-key group is permuted consistently in P^T and
-// in the transposed V tile in LDS, so no data moves between lanes.  K and
-// V^T tiles are double-buffered in LDS; the next tile's global loads are in
-// flight while the current one is used.
-// LDS: K tile [64 keys][128 d] (256 B rows, 16-byte columns XOR-swizzled by
-// key), V^T tile [128 d][64 keys] (128 B rows, columns swizzled by d/2).
-// ---------------------------------------------------------------------------
-constexpr int kTileBytes = pf::kBK * pf::kD * 2;  // 16 KiB
-
-__device__ __forceinline__ int k_lds_off(int row, int c16) {
-  return row * 256 + ((c16 ^ (row & 15)) << 4);
-}
-__device__ __forceinline__ int v_lds_off(int d, int c16) {
-  return d * 128 + ((c16 ^ ((d >> 1) & 7)) << 4);
-}
-
-__global__ __launch_bounds__(256, 2) void prefill_d128_kernel(AttnArgs a) {
-  using namespace pf;
-  __shared__ __attribute__((aligned(16))) char smem[4 * kTileBytes];
-  char* const sK = smem;
-  char* const sV = smem + 2 * kTileBytes;
-
-  const int n_qblk = (a.Tq + kBQ - 1) / kBQ;
-  const Work w = work_of(blockIdx.x, gridDim.x, n_qblk, a.H);
-  const int g = w.h / (a.H / a.G);
-  const int q0 = w.qb * kBQ;
-  const int q1 = min(q0 + kBQ, a.Tq);
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int col = lane & 31, half = lane >> 5;
-  const int tq = lane_query(q0, wave, lane);
-  const int tql = min(tq, a.Tq - 1);
-
-  // Q^T operand: lane holds query tq, d = 16*ks + 8*half .. +7
-  bf16x8 qop[8];
-  {
-    const bf16* qrow = (const bf16*)a.q + ((int64_t)(w.b * a.Tq + tql) * a.H + w.h) * kD;
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) qop[ks] = *(const bf16x8*)(qrow + ks * 16 + half * 8);
-  }
-
-  const bf16* kbase = (const bf16*)a.k + w.b * a.k_sb + g * a.k_sg;
-  const bf16* vbase = (const bf16*)a.v + w.b * a.v_sb + g * a.v_sg;
-  const int last = (int)a.n_keys - 1;
-
-  // global -> registers.  K: thread -> (row tid/16 + 16 i, 16-byte column
-  // tid%16).  V: thread -> (keys 4*(tid%16) .. +3, d chunk tid/16).
-  bf16x8 kr[4], vr[4];
-  auto load_tile = [&](int k0) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key = min(k0 + (tid >> 4) + 16 * i, last);
-      kr[i] = *(const bf16x8*)(kbase + (int64_t)key * a.k_sr + (tid & 15) * 8);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key = min(k0 + 4 * (tid & 15) + i, last);
-      vr[i] = *(const bf16x8*)(vbase + (int64_t)key * a.v_sr + (tid >> 4) * 8);
-    }
-  };
-  // registers -> LDS stage st (V transposed, keys permuted within 16-groups:
-  // logical key 16c + 8q + 4hh + j sits at 16c + 8hh + 4q + j).
-  auto store_tile = [&](int st) {
-    char* k = sK + st * kTileBytes;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = (tid >> 4) + 16 * i;
-      *(bf16x8*)(k + k_lds_off(row, tid & 15)) = kr[i];
-    }
-    char* v = sV + st * kTileBytes;
-    const int kg = tid & 15, dc = tid >> 4;
-    const int pg = 4 * (kg >> 2) + 2 * (kg & 1) + ((kg & 3) >> 1);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int d = dc * 8 + e;
-      bf16x4 p4 = {vr[0][e], vr[1][e], vr[2][e], vr[3][e]};
-      *(bf16x4*)(v + v_lds_off(d, pg >> 1) + (pg & 1) * 8) = p4;
-    }
-  };
-
-  int kt0, kt1;
-  key_tiles(q0, q1, a.window, a.sliding, kt0, kt1);
-
-  f32x16 o[4];
-#pragma unroll
-  for (int db = 0; db < 4; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
-  float m = -1e30f, lsum = 0.f;
-  const float c = a.scale_log2;
-
-  load_tile(kt0 * kBK);
-  store_tile(0);
-
-  for (int kt = kt0; kt < kt1; ++kt) {
-    const int st = (kt - kt0) & 1;
-    const int k0 = kt * kBK;
-    const bool more = kt + 1 < kt1;
-    if (more) load_tile(k0 + kBK);
-    __syncthreads();
-
-    // S^T for keys k0 .. k0+63
-    const char* k = sK + st * kTileBytes;
-    f32x16 s0, s1;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) s0[r] = s1[r] = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      const bf16x8 a0 = *(const bf16x8*)(k + k_lds_off(col, 2 * ks + half));
-      const bf16x8 a1 = *(const bf16x8*)(k + k_lds_off(32 + col, 2 * ks + half));
-      s0 = mfma32(a0, qop[ks], s0);
-      s1 = mfma32(a1, qop[ks], s1);
-    }
-    if (!tile_interior(k0, q0, q1, a.window, a.sliding)) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        if (!visible(tq, lane_key(k0, 0, r, lane), a.window, a.sliding)) s0[r] = -INFINITY;
-        if (!visible(tq, lane_key(k0, 1, r, lane), a.window, a.sliding)) s1[r] = -INFINITY;
-      }
-    }
-
-    float mx = fmaxf(s0[0], s1[0]);
-#pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-    const float mnew = fmaxf(m, mx * c);
-    const float alpha = fast_exp2(m - mnew);
-    m = mnew;
-    float ps = 0.f;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      s0[r] = fast_exp2(fmaf(s0[r], c, -mnew));
-      s1[r] = fast_exp2(fmaf(s1[r], c, -mnew));
-      ps += s0[r] + s1[r];
-    }
-    lsum = lsum * alpha + ps;
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-
-    bf16x8 pk[4];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      pk[0][e] = (bf16)s0[e];
-      pk[1][e] = (bf16)s0[8 + e];
-      pk[2][e] = (bf16)s1[e];
-      pk[3][e] = (bf16)s1[8 + e];
-    }
-
-    const char* v = sV + st * kTileBytes;
-#pragma unroll
-    for (int db = 0; db < 4; ++db) {
-      const int d = db * 32 + col;
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const bf16x8 va = *(const bf16x8*)(v + v_lds_off(d, 2 * kk + half));
-        o[db] = mfma32(va, pk[kk], o[db]);
-      }
-    }
-    if (more) store_tile(st ^ 1);
-  }
-
-  lsum += __shfl_xor(lsum, 32, kWave);
-  const float inv = 1.0f / lsum;
-  if (tq < a.Tq) {
-    bf16* orow = (bf16*)a.out + ((int64_t)(w.b * a.Tq + tq) * a.H + w.h) * kD;
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        bf16x4 v4 = {(bf16)(o[db][4 * r4] * inv), (bf16)(o[db][4 * r4 + 1] * inv),
-                     (bf16)(o[db][4 * r4 + 2] * inv), (bf16)(o[db][4 * r4 + 3] * inv)};
-        *(bf16x4*)(orow + db * 32 + 8 * r4 + 4 * half) = v4;
-      }
-  }
-}
-
-__global__ __launch_bounds__(256) void probe_prefill_kernel(int T, int window, int sliding,
-                                                            uint8_t* visit) {
-  using namespace pf;
-  const int n_qblk = (T + kBQ - 1) / kBQ;
-  const Work w = work_of(blockIdx.x, gridDim.x, n_qblk, 1);
-  const int q0 = w.qb * kBQ, q1 = min(q0 + kBQ, T);
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int tq = lane_query(q0, wave, lane);
-  int kt0, kt1;
-  key_tiles(q0, q1, window, sliding, kt0, kt1);
-  for (int kt = kt0; kt < kt1; ++kt) {
-    const int k0 = kt * kBK;
-    const bool interior = tile_interior(k0, q0, q1, window, sliding);
-    for (int kb = 0; kb < 2; ++kb)
-      for (int r = 0; r < 16; ++r) {
-        const int s = lane_key(k0, kb, r, lane);
-        const bool acc = interior || visible(tq, s, window, sliding);
-        if (acc && tq < T && s < T) visit[(int64_t)tq * T + s] = 1;
-      }
-  }
-}
 
 // ---------------------------------------------------------------------------
 // Plain kernel: one thread per query row, keys streamed from global memory.
@@ -464,13 +253,6 @@ hipError_t launch_generic_t(const AttnArgs& a, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_prefill_mfma(const AttnArgs& a, hipStream_t s) {
-  const int n_qblk = (a.Tq + pf::kBQ - 1) / pf::kBQ;
-  const int blocks = n_qblk * a.H * a.B;
-  prefill_d128_kernel<<<blocks, 256, 0, s>>>(a);
-  return hipGetLastError();
-}
-
 hipError_t launch_attn_generic(const AttnArgs& a, int dtype, int d, hipStream_t s) {
 #define OLMO3_GEN(T, DD) \
   if (d == DD) return launch_generic_t<T, DD>(a, s);
@@ -513,14 +295,6 @@ hipError_t launch_decode_split(const DecodeArgs& a, hipStream_t s) {
 
 hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t s) {
   decode_merge_kernel<<<a.B * a.H, dec::kD, 0, s>>>(a);
-  return hipGetLastError();
-}
-
-hipError_t launch_probe_prefill(int T, int window, int sliding, uint8_t* visit, hipStream_t s) {
-  hipError_t e = hipMemsetAsync(visit, 0, (size_t)T * T, s);
-  if (e != hipSuccess) return e;
-  const int n_qblk = (T + pf::kBQ - 1) / pf::kBQ;
-  probe_prefill_kernel<<<n_qblk, 256, 0, s>>>(T, window, sliding, visit);
   return hipGetLastError();
 }
 

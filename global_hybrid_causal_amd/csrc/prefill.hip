@@ -1,0 +1,349 @@
+// Flash-style causal prefill, d = 128, bf16 in / out, fp32 accumulation
+// (v_mfma_f32_32x32x16_bf16), and the probe that records its tile walk.
+//
+// Masking follows "OLMo 3's Sliding-Window Attention Pattern", "The
+// sliding-window mask": key s is visible from query t iff s <= t and, on a
+// sliding layer, t - s < window.  Work per query row grows with the square
+// of the length on full layers and with the window on sliding layers (same
+// page, "The problem"); tiles with no visible key are never visited.
+#include <type_traits>
+
+#include "common.h"
+#include "kernels.h"
+#include "tiles.h"
+
+namespace olmo3 {
+
+namespace {
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// Workgroup = 4 wavefronts x 32 queries of one (batch, head).  Per key tile of
+// 64 keys each wavefront computes S^T = K Q^T (two 32x32 blocks: K from LDS as
+// the A operand, its queries' Q^T held in registers as B), so a lane owns one
+// query column, and accumulates O^T += V^T P^T with P^T taken straight from
+// the S accumulators (converted to bf16) as the B operand.
+//
+// K and V tiles go from global memory straight into LDS
+// (global_load_lds_dwordx4: lane l of a wavefront fills bytes 16 l .. 16 l + 15
+// after the wavefront's base), row-major, 256-byte rows, with XOR-swizzled
+// 16-byte columns: column c of K row r sits at c ^ (r mod 16), of V row r at
+// c ^ 4 (r mod 4).  The V^T operand is read with ds_read_b64_tr_b16: within a
+// group of 16 lanes, lane i receives element i mod 4 of the 8-byte pieces
+// addressed by lanes 4j + i/4 (j = 0..3), so lane i addressing
+// V[K0 + i/4][dbase + 4 (i mod 4)] receives d = dbase + i for keys K0 .. K0+3.
+// P^T and the V^T reads use the same key order (the MFMA output order: lane
+// half h holds keys 4h + 0..3 and 8 + 4h + 0..3 of every 16), so no data moves
+// between lanes.  Both swizzles keep these reads free of bank conflicts.
+//
+// Software pipeline, one barrier per tile: the step of tile j computes S for
+// tile j+1 while it exponentiates tile j and multiplies it into O.  K tiles
+// and V tiles each have a ring of two LDS buffers, V one tile behind K: the
+// step of tile j loads K_{j+2} and V_{j+1} into the buffers that held K_j and
+// V_{j-1}, which every wavefront was done with before that step's barrier.
+//
+// The tiles of a query block split into three runs: far window edge, interior
+// (every pair visible: no mask code at all) and diagonal.  The running maximum
+// is rescaled lazily: O and the row sum are rescaled only when a tile's
+// maximum exceeds the reference by more than 2^8 (so P <= 256), which leaves
+// the result unchanged and skips the rescale on almost every tile.  The row
+// sum adds the bf16 weights that enter P V, two at a time (v_dot2_f32_bf16).
+// ---------------------------------------------------------------------------
+constexpr int kTileBytes = pf::kBK * pf::kD * 2;  // 16 KiB
+constexpr float kRescaleSlack = 8.0f;             // log2 units
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+__device__ __forceinline__ void load_to_lds(const bf16* src, char* dst) {
+  __builtin_amdgcn_global_load_lds((const void*)src, (lds_ptr)dst, 16, 0, 0);
+}
+
+// max(x[l], x[l ^ 32]) in every lane: v_permlane32_swap exchanges the upper
+// half of its first operand with the lower half of its second, so after
+// swapping x with itself the two results hold, in every lane, the lane's own
+// value and its partner's.
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ bf16x4 lds_read_tr(const char* p) {
+  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)(p));
+  return __builtin_bit_cast(bf16x4, v);
+}
+
+__global__ __launch_bounds__(256, 2) void prefill_d128_kernel(AttnArgs a) {
+  using namespace pf;
+  __shared__ __attribute__((aligned(16))) char smem[4 * kTileBytes];
+  char* const sK = smem;                   // K ring: 2 x 16 KiB
+  char* const sV = smem + 2 * kTileBytes;  // V ring: 2 x 16 KiB
+
+  const int n_qblk = (a.Tq + kBQ - 1) / kBQ;
+  const Work w = work_of(blockIdx.x, gridDim.x, n_qblk, a.H);
+  const int g = w.h / (a.H / a.G);
+  const int q0 = w.qb * kBQ;
+  const int q1 = min(q0 + kBQ, a.Tq);
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int col = lane & 31, half = lane >> 5;
+  const int tq = lane_query(q0, wave, lane);
+  const int tql = min(tq, a.Tq - 1);
+
+  // Q^T operand: lane holds query tq, d = 16*ks + 8*half .. +7
+  bf16x8 qop[8];
+  {
+    const bf16* qrow = (const bf16*)a.q + ((int64_t)(w.b * a.Tq + tql) * a.H + w.h) * kD;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) qop[ks] = *(const bf16x8*)(qrow + ks * 16 + half * 8);
+  }
+
+  int kt0, kt1, i0, i1;
+  key_tiles(q0, q1, a.window, a.sliding, kt0, kt1);
+  interior_tiles(q0, q1, a.window, a.sliding, kt0, kt1, i0, i1);
+
+  // Direct loads: instruction i of wavefront w fills tile rows 16 i + 4 w ..
+  // +3; lane l takes row 16 i + 4 w + l/16, stored column l mod 16, i.e.
+  // logical column (l mod 16) ^ swizzle(row).  Rows past the last key are
+  // clamped to it (such keys lie past every query of the block: masked).
+  const int n_keys = (int)a.n_keys;
+  const int lrow = 4 * wave + (lane >> 4);  // row within each 16-row slab
+  const int kcol = (lane & 15) ^ (lrow & 15);
+  const int vcol = (lane & 15) ^ (4 * (lrow & 3));
+  // Uniform per-head bases plus a 32-bit per-lane element offset; only the
+  // last tile of a sequence (rows past n_keys) takes the clamped path.
+  const bf16* kbase = (const bf16*)a.k + w.b * a.k_sb + g * a.k_sg;
+  const bf16* vbase = (const bf16*)a.v + w.b * a.v_sb + g * a.v_sg;
+  const int k_lane = lrow * (int)a.k_sr + kcol * 8;
+  const int v_lane = lrow * (int)a.v_sr + vcol * 8;
+  const int slab = 4 * wave * 256;  // this wavefront's byte offset in a slab
+  auto load_rows = [&](const bf16* base, int64_t sr, int lane_off, int col8, int k0,
+                       char* dst) __attribute__((always_inline)) {
+    if (k0 + kBK <= n_keys) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        load_to_lds(base + (int64_t)(k0 + 16 * i) * sr + lane_off, dst + 16 * i * 256);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = min(k0 + 16 * i + lrow, n_keys - 1);
+        load_to_lds(base + (int64_t)row * sr + col8, dst + 16 * i * 256);
+      }
+    }
+  };
+  auto load_k = [&](int k0, int buf) __attribute__((always_inline)) {
+    load_rows(kbase, a.k_sr, k_lane, kcol * 8, k0, sK + buf * kTileBytes + slab);
+  };
+  auto load_v = [&](int k0, int buf) __attribute__((always_inline)) {
+    load_rows(vbase, a.v_sr, v_lane, vcol * 8, k0, sV + buf * kTileBytes + slab);
+  };
+
+  // LDS read offsets.  K (A operand of S^T): row 32 kb + col, column
+  // 2 ks + half.  V^T (A operand of O^T, ds_read_b64_tr_b16): row
+  // 16 kk + 8 r + 4 half + (lane mod 16)/4, d = 32 db + 16 ((lane/16) mod 2)
+  // + 4 (lane mod 4), 8-byte half (lane mod 2) of its 16-byte column.
+  int koff[8];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) koff[ks] = col * 256 + (((2 * ks + half) ^ (col & 15)) << 4);
+  const int vrow = 4 * half + ((lane & 15) >> 2);
+  int voff[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db) {
+    const int c16 = 4 * db + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+    voff[db] = vrow * 256 + ((c16 ^ (4 * (vrow & 3))) << 4) + (lane & 1) * 8;
+  }
+
+  auto qk = [&](int buf, f32x16& s0, f32x16& s1) __attribute__((always_inline)) {
+    const char* k = sK + buf * kTileBytes;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s0[r] = s1[r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const bf16x8 a0 = *(const bf16x8*)(k + koff[ks]);
+      const bf16x8 a1 = *(const bf16x8*)(k + koff[ks] + 32 * 256);
+      s0 = mfma32(a0, qop[ks], s0);
+      s1 = mfma32(a1, qop[ks], s1);
+    }
+  };
+
+  f32x16 o[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
+  float m = -1e30f, lsum = 0.f;
+  const float c = a.scale_log2;
+  f32x16 s0, s1;  // scores of the current tile
+
+  // Step of tile kt.  kMask: apply the visibility predicate per element.
+  // kBuf: buffers holding K_kt and V_kt ((kt - kt0) mod 2, known at compile
+  // time so that every LDS offset is an immediate).
+  auto step = [&](int kt, auto mask_tag, auto buf_tag) __attribute__((always_inline)) {
+    constexpr bool kMask = decltype(mask_tag)::value;
+    constexpr int jb = decltype(buf_tag)::value;
+    const int k0 = kt * kBK;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (kt + 2 < kt1) load_k(k0 + 2 * kBK, jb);
+    if (kt + 1 < kt1) load_v(k0 + kBK, jb ^ 1);
+
+    if constexpr (kMask) {
+      // key of register r of block kb = k0 + 4*half + kb*32 + 8*(r/4) + r%4,
+      // visible iff rel - window < offset <= rel (the lower bound only on
+      // sliding layers)
+      const int rel = tq - k0 - 4 * half;
+      const int lo = a.sliding ? rel - a.window : INT_MIN;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int c0 = 8 * (r >> 2) + (r & 3), c1 = 32 + c0;
+        s0[r] = ((c0 <= rel) & (c0 > lo)) ? s0[r] : -INFINITY;
+        s1[r] = ((c1 <= rel) & (c1 > lo)) ? s1[r] : -INFINITY;
+      }
+    }
+    // tile maximum: a max3 tree (depth 4), then the partner lane (l ^ 32)
+    float t1[12];
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+      t1[i] = fmaxf(fmaxf(s0[3 * i], s0[3 * i + 1]), s0[3 * i + 2]);
+      t1[5 + i] = fmaxf(fmaxf(s1[3 * i], s1[3 * i + 1]), s1[3 * i + 2]);
+    }
+    t1[10] = s0[15];
+    t1[11] = s1[15];
+    const float t2a = fmaxf(fmaxf(t1[0], t1[1]), t1[2]), t2b = fmaxf(fmaxf(t1[3], t1[4]), t1[5]);
+    const float t2c = fmaxf(fmaxf(t1[6], t1[7]), t1[8]), t2d = fmaxf(fmaxf(t1[9], t1[10]), t1[11]);
+    float mx = fmaxf(fmaxf(t2a, t2b), fmaxf(t2c, t2d));
+    mx = pair_max(mx);
+    const float mt = mx * c;
+    if (__ballot(mt > m + kRescaleSlack)) {
+      const float mn = fmaxf(m, mt);
+      float alpha = fast_exp2(m - mn);
+      // keep this a real (uniform) branch: without the barrier the compiler
+      // folds the condition into the multiplier and rescales every tile
+      asm volatile("" : "+v"(alpha));
+      m = mn;
+      lsum *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+    }
+
+    // S of the next tile (on the last tile the result is discarded)
+    f32x16 n0, n1;
+    qk(jb ^ 1, n0, n1);
+
+    const float nm = -m;
+    bf16x8 pk[4];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      pk[0][e] = (bf16)fast_exp2(fmaf(s0[e], c, nm));
+      pk[1][e] = (bf16)fast_exp2(fmaf(s0[8 + e], c, nm));
+      pk[2][e] = (bf16)fast_exp2(fmaf(s1[e], c, nm));
+      pk[3][e] = (bf16)fast_exp2(fmaf(s1[8 + e], c, nm));
+    }
+    const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const bf16x2 pr = {pk[kk][e], pk[kk][e + 1]};
+        lsum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lsum, false);
+      }
+    const char* v = sV + jb * kTileBytes;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const bf16x4 lo4 = lds_read_tr(v + voff[db] + (16 * kk) * 256);
+        const bf16x4 hi4 = lds_read_tr(v + voff[db] + (16 * kk + 8) * 256);
+        const bf16x8 va = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+        o[db] = mfma32(va, pk[kk], o[db]);
+      }
+    s0 = n0;
+    s1 = n1;
+  };
+
+  load_k(kt0 * kBK, 0);
+  load_v(kt0 * kBK, 0);
+  if (kt0 + 1 < kt1) load_k((kt0 + 1) * kBK, 1);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  qk(0, s0, s1);
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  auto run = [&](int& kt, int end, auto mask_tag) __attribute__((always_inline)) {
+    if (kt < end && ((kt - kt0) & 1)) step(kt++, mask_tag, B1{});
+    for (; kt + 1 < end; kt += 2) {
+      step(kt, mask_tag, B0{});
+      step(kt + 1, mask_tag, B1{});
+    }
+    if (kt < end) step(kt++, mask_tag, B0{});
+  };
+  int kt = kt0;
+  run(kt, i0, std::true_type{});
+  run(kt, i1, std::false_type{});
+  run(kt, kt1, std::true_type{});
+
+  lsum += __shfl_xor(lsum, 32, kWave);
+  const float inv = 1.0f / lsum;
+  if (tq < a.Tq) {
+    bf16* orow = (bf16*)a.out + ((int64_t)(w.b * a.Tq + tq) * a.H + w.h) * kD;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        bf16x4 v4 = {(bf16)(o[db][4 * r4] * inv), (bf16)(o[db][4 * r4 + 1] * inv),
+                     (bf16)(o[db][4 * r4 + 2] * inv), (bf16)(o[db][4 * r4 + 3] * inv)};
+        *(bf16x4*)(orow + db * 32 + 8 * r4 + 4 * half) = v4;
+      }
+  }
+}
+
+// Records every (query, key) pair the kernel above accumulates: the same
+// work mapping, tile runs, lane -> (query, key) map and predicate.
+__global__ __launch_bounds__(256) void probe_prefill_kernel(int T, int window, int sliding,
+                                                            uint8_t* visit) {
+  using namespace pf;
+  const int n_qblk = (T + kBQ - 1) / kBQ;
+  const Work w = work_of(blockIdx.x, gridDim.x, n_qblk, 1);
+  const int q0 = w.qb * kBQ, q1 = min(q0 + kBQ, T);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int tq = lane_query(q0, wave, lane);
+  int kt0, kt1, i0, i1;
+  key_tiles(q0, q1, window, sliding, kt0, kt1);
+  interior_tiles(q0, q1, window, sliding, kt0, kt1, i0, i1);
+  for (int kt = kt0; kt < kt1; ++kt) {
+    const int k0 = kt * kBK;
+    const bool interior = kt >= i0 && kt < i1;
+    for (int kb = 0; kb < 2; ++kb)
+      for (int r = 0; r < 16; ++r) {
+        const int s = lane_key(k0, kb, r, lane);
+        const bool acc = interior || visible(tq, s, window, sliding);
+        if (acc && tq < T && s < T) visit[(int64_t)tq * T + s] = 1;
+      }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_prefill_mfma(const AttnArgs& a, hipStream_t s) {
+  const int n_qblk = (a.Tq + pf::kBQ - 1) / pf::kBQ;
+  const int blocks = n_qblk * a.H * a.B;
+  prefill_d128_kernel<<<blocks, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_probe_prefill(int T, int window, int sliding, uint8_t* visit, hipStream_t s) {
+  hipError_t e = hipMemsetAsync(visit, 0, (size_t)T * T, s);
+  if (e != hipSuccess) return e;
+  const int n_qblk = (T + pf::kBQ - 1) / pf::kBQ;
+  probe_prefill_kernel<<<n_qblk, 256, 0, s>>>(T, window, sliding, visit);
+  return hipGetLastError();
+}
+
+}  // namespace olmo3

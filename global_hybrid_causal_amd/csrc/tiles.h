@@ -37,6 +37,24 @@ __host__ __device__ __forceinline__ bool tile_interior(int k0, int q0, int q1, i
   return k0 + kBK - 1 <= q0 && (!sliding || (q1 - 1) - k0 < window);
 }
 
+// The interior tiles of [kt0, kt1) form one run [i0, i1): the causal
+// condition holds for kt <= (q0 + 1)/kBK - 1 and the window condition for
+// kt >= ceil((q1 - window)/kBK).  Tiles [kt0, i0) lie on the window's far
+// edge and tiles [i1, kt1) on the diagonal; only those are masked.
+__host__ __device__ __forceinline__ void interior_tiles(int q0, int q1, int window, int sliding,
+                                                        int kt0, int kt1, int& i0, int& i1) {
+  i1 = (q0 + 1) / kBK;
+  if (i1 > kt1) i1 = kt1;
+  if (i1 < kt0) i1 = kt0;
+  i0 = kt0;
+  if (sliding) {
+    const int lo = q1 - window;
+    const int first = lo > 0 ? (lo + kBK - 1) / kBK : 0;
+    if (first > i0) i0 = first;
+  }
+  if (i0 > i1) i0 = i1;
+}
+
 struct Work {
   int b, h, qb;
 };
