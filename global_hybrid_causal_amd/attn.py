@@ -18,6 +18,7 @@ from . import LAYER_FULL, LAYER_SLIDING  # noqa: F401  (re-exported)
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libolmo3attn.so")
 
+ABI_VERSION = 2  # OLMO3_ABI_VERSION of include/olmo3_attn.h
 DTYPE_BF16, DTYPE_F32 = 0, 1
 MODE_PREFILL, MODE_DECODE = 0, 1
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_CAPACITY, ERR_HIP, ERR_WORKSPACE = range(6)
@@ -103,10 +104,13 @@ def lib() -> ctypes.CDLL:
         L.olmo3_status_string.restype = ctypes.c_char_p
         L.olmo3_abi_version.argtypes = []
         L.olmo3_abi_version.restype = _i
-        L.olmo3_probe_prefill_visits.argtypes = [_i, _i, _i, _p, _p]
+        L.olmo3_probe_prefill_visits.argtypes = [_i, _i64, _i, _i, _p, _p]
         L.olmo3_probe_prefill_visits.restype = _i
         L.olmo3_probe_decode_reads.argtypes = [_i, _i, _i, _i, _i, _i64, _i64, _p, _p]
         L.olmo3_probe_decode_reads.restype = _i
+        if L.olmo3_abi_version() != ABI_VERSION:
+            raise RuntimeError(f"{LIB_PATH} has ABI version {L.olmo3_abi_version()}, the binding "
+                               f"expects {ABI_VERSION}: rebuild it")
         _lib = L
     return _lib
 
@@ -232,10 +236,12 @@ def workspace(mode: int, B: int, T: int, H: int, G: int, d: int, layer_type: int
     return torch.empty(n, dtype=torch.uint8, device=device)
 
 
-def olmo3_probe_prefill_visits(T: int, window: int, layer_type: int, device="cuda") -> torch.Tensor:
-    """[T, T] uint8 table of the (query, key) pairs the prefill kernel accumulates."""
-    visit = torch.empty((T, T), dtype=torch.uint8, device=device)
-    st = lib().olmo3_probe_prefill_visits(T, window, layer_type, _ptr(visit, "visit"),
+def olmo3_probe_prefill_visits(T: int, window: int, layer_type: int, pos_offset: int = 0,
+                               device="cuda") -> torch.Tensor:
+    """[T, pos_offset + T] uint8 table of the (query, key position) pairs the
+    prefill kernel accumulates for queries at pos_offset .. pos_offset + T - 1."""
+    visit = torch.empty((T, pos_offset + T), dtype=torch.uint8, device=device)
+    st = lib().olmo3_probe_prefill_visits(T, pos_offset, window, layer_type, _ptr(visit, "visit"),
                                           _stream(None, visit.device))
     _check(st, "olmo3_probe_prefill_visits")
     return visit

@@ -17,6 +17,7 @@ namespace {
 
 constexpr double kLog2e = 1.4426950408889634;
 constexpr size_t kAlign = 256;
+constexpr int64_t kMaxPrefillPositions = (int64_t)1 << 30;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -241,10 +242,15 @@ int olmo3_attn_prefill_phases(int phases, int B, int T, int H, int G, int d, int
                          k_pre, v, q_gain, k_gain, k_cache, v_cache, cache_capacity, out,
                          workspace, workspace_bytes, need);
   if (st) return st;
-  if (pos_offset != 0) return OLMO3_ERR_UNSUPPORTED;
+  // positions are 32-bit inside the prefill kernels
+  if (pos_offset + T > kMaxPrefillPositions) return OLMO3_ERR_UNSUPPORTED;
 
   const hipStream_t s = (hipStream_t)stream;
   const bool sliding = layer_type == OLMO3_LAYER_SLIDING;
+  // A chunk on a sliding layer attends to the ring's earlier positions, and
+  // its own keys would overwrite ring slots that its first queries still
+  // read: such a chunk is stored in the ring only after the attention.
+  const bool ring_after = sliding && pos_offset > 0;
   const size_t es = elem_size(dtype);
   char* ws = (char*)workspace;
   void* q_rot = ws;
@@ -266,8 +272,10 @@ int olmo3_attn_prefill_phases(int phases, int B, int T, int H, int G, int d, int
   p.k_cache = k_cache;
   p.v_cache = v_cache;
   p.cap = cache_capacity;
-  p.pos_offset = 0;
-  p.cache_first_t = sliding ? std::max<int64_t>(0, (int64_t)T - window) : 0;
+  p.pos_offset = pos_offset;
+  // on a ring only the last `window` positions of the chunk are kept
+  const int64_t first_kept = sliding ? std::max<int64_t>(0, (int64_t)T - window) : 0;
+  p.cache_first_t = ring_after ? T : first_kept;
   p.B = B;
   p.T = T;
   p.H = H;
@@ -284,7 +292,8 @@ int olmo3_attn_prefill_phases(int phases, int B, int T, int H, int G, int d, int
   AttnArgs a = {};
   a.q = q_rot;
   if (sliding) {
-    // rotated keys from the workspace [B][G][T][d], values from the input
+    // the chunk: rotated keys from the workspace [B][G][T][d], values from
+    // the input; earlier positions (if any) from the ring
     a.k = k_rot;
     a.k_sb = (int64_t)G * T * d;
     a.k_sg = (int64_t)T * d;
@@ -293,27 +302,46 @@ int olmo3_attn_prefill_phases(int phases, int B, int T, int H, int G, int d, int
     a.v_sb = (int64_t)T * G * d;
     a.v_sg = d;
     a.v_sr = (int64_t)G * d;
+    a.main_pos0 = pos_offset;
+    if (pos_offset > 0) {
+      a.kp = k_cache;
+      a.vp = v_cache;
+      a.p_sb = (int64_t)G * cache_capacity * d;
+      a.p_sg = cache_capacity * d;
+      a.p_sr = d;
+      a.ring = window;
+    }
   } else {
-    // the linear cache now holds positions 0 .. T-1 at slots 0 .. T-1
+    // the linear cache now holds positions 0 .. pos_offset+T-1 at their slots
     a.k = k_cache;
     a.v = v_cache;
     a.k_sb = a.v_sb = (int64_t)G * cache_capacity * d;
     a.k_sg = a.v_sg = cache_capacity * d;
     a.k_sr = a.v_sr = d;
+    a.main_pos0 = 0;
   }
   a.out = out;
   a.B = B;
   a.Tq = T;
   a.H = H;
   a.G = G;
-  a.n_keys = T;
-  a.q_pos0 = 0;
+  a.n_keys = pos_offset + T;
+  a.q_pos0 = pos_offset;
   a.window = window;
   a.sliding = sliding;
   a.all_visible = 0;
   a.scale_log2 = scale_log2(d);
-  if (use_mfma(dtype, d)) return hip_status(launch_prefill_mfma(a, s));
-  return hip_status(launch_attn_generic(a, dtype, d, s));
+  st = hip_status(use_mfma(dtype, d) ? launch_prefill_mfma(a, s)
+                                     : launch_attn_generic(a, dtype, d, s));
+  if (st || !ring_after) return st;
+  // store the chunk's kept positions in the ring (keys normalised and rotated
+  // again from k_pre: the same arithmetic, so the same bits)
+  PrologueArgs r = p;
+  r.q_pre = nullptr;
+  r.q_out = nullptr;
+  r.k_out = nullptr;
+  r.cache_first_t = first_kept;
+  return hip_status(launch_prologue(r, table, dtype, d, s));
 }
 
 int olmo3_attn_prefill(int B, int T, int H, int G, int d, int window, int layer_type,
@@ -432,10 +460,12 @@ int olmo3_attn_decode(int B, int H, int G, int d, int window, int layer_type,
                                   workspace, workspace_bytes, stream);
 }
 
-int olmo3_probe_prefill_visits(int T, int window, int layer_type, uint8_t* visit, void* stream) {
-  if (T < 1 || T > 4096 || window < 1 || !visit) return OLMO3_ERR_INVALID_ARG;
+int olmo3_probe_prefill_visits(int T, int64_t pos_offset, int window, int layer_type,
+                               uint8_t* visit, void* stream) {
+  if (T < 1 || pos_offset < 0 || window < 1 || !visit) return OLMO3_ERR_INVALID_ARG;
+  if (T > 4096 || pos_offset + T > 8192) return OLMO3_ERR_UNSUPPORTED;
   if (layer_type != OLMO3_LAYER_SLIDING && layer_type != OLMO3_LAYER_FULL) return OLMO3_ERR_INVALID_ARG;
-  return hip_status(launch_probe_prefill(T, window, layer_type == OLMO3_LAYER_SLIDING, visit,
+  return hip_status(launch_probe_prefill(T, pos_offset, window, layer_type == OLMO3_LAYER_SLIDING, visit,
                                          (hipStream_t)stream));
 }
 

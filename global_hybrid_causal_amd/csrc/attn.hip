@@ -33,26 +33,37 @@ __global__ __launch_bounds__(64) void attn_generic_kernel(AttnArgs a) {
     o[e] = 0.f;
   }
   const int64_t tpos = a.q_pos0 + t;
-  int64_t r0 = 0, r1 = a.n_keys;
+  // positions [p0, p1) when masked; main rows [0, n_keys) when all visible
+  int64_t p0 = 0, p1 = a.n_keys;
   if (!a.all_visible) {
-    r1 = min(tpos + 1, a.n_keys);
-    if (a.sliding) r0 = max(tpos - a.window + 1, (int64_t)0);
+    p1 = min(tpos + 1, a.n_keys);
+    if (a.sliding) p0 = max(tpos - a.window + 1, (int64_t)0);
   }
+  const int64_t main0 = a.all_visible ? 0 : a.main_pos0;
   const T* kb = (const T*)a.k + b * a.k_sb + g * a.k_sg;
   const T* vb = (const T*)a.v + b * a.v_sb + g * a.v_sg;
+  const T* kpb = a.kp ? (const T*)a.kp + b * a.p_sb + g * a.p_sg : nullptr;
+  const T* vpb = a.kp ? (const T*)a.vp + b * a.p_sb + g * a.p_sg : nullptr;
   float m = -1e30f, l = 0.f;
-  for (int64_t r = r0; r < r1; ++r) {
-    const T* kp = kb + r * a.k_sr;
-    const T* vp = vb + r * a.v_sr;
+  for (int64_t p = p0; p < p1; ++p) {
+    const T *kp, *vp;
+    if (p >= main0) {
+      kp = kb + (p - main0) * a.k_sr;
+      vp = vb + (p - main0) * a.v_sr;
+    } else {
+      const int64_t slot = a.ring > 0 ? p % a.ring : p;
+      kp = kpb + slot * a.p_sr;
+      vp = vpb + slot * a.p_sr;
+    }
     float s = 0.f;
 #pragma unroll
     for (int e = 0; e < D; ++e) s += q[e] * (float)kp[e];
     const float mn = fmaxf(m, s);
     const float al = fast_exp2(m - mn);
-    const float p = fast_exp2(s - mn);
-    l = l * al + p;
+    const float pr = fast_exp2(s - mn);
+    l = l * al + pr;
 #pragma unroll
-    for (int e = 0; e < D; ++e) o[e] = o[e] * al + p * (float)vp[e];
+    for (int e = 0; e < D; ++e) o[e] = o[e] * al + pr * (float)vp[e];
     m = mn;
   }
   const float inv = 1.0f / l;

@@ -33,11 +33,15 @@ hipError_t launch_prologue(const PrologueArgs& a, const RopeTable& rope, int dty
                            hipStream_t s);
 int prologue_max_heads(int dtype, int d);
 
-// Attention over keys held in a strided buffer.
+// Attention over keys held in up to two strided buffers.
 //   queries  q[(b*Tq + t)*H + h][d], absolute position q_pos0 + t
-//   keys     k + b*k_sb + g*k_sg + r*k_sr, r in [0, n_keys); same for v
-//   prefill: key row r is at position r and the mask decides;
-//   decode (all_visible): every row r < n_keys is visible.
+//   keys at positions 0 .. n_keys-1:
+//     position p >= main_pos0: main row r = p - main_pos0,
+//       k + b*k_sb + g*k_sg + r*k_sr (v likewise)
+//     position p < main_pos0 (prefix, only when kp is set): ring slot
+//       p mod ring, kp + b*p_sb + g*p_sg + slot*p_sr (vp likewise)
+//   prefill: the mask decides which positions a query sees;
+//   decode (all_visible): every main row r < n_keys is visible.
 //   out[(b*Tq + t)*H*d + h*d + e]
 struct AttnArgs {
   const void* q;
@@ -45,6 +49,11 @@ struct AttnArgs {
   const void* v;
   int64_t k_sb, k_sg, k_sr;
   int64_t v_sb, v_sg, v_sr;
+  const void* kp;  // prefix keys and values (a sliding layer's ring), or null
+  const void* vp;
+  int64_t p_sb, p_sg, p_sr;
+  int64_t ring;
+  int64_t main_pos0;
   void* out;
   int B, Tq, H, G;
   int64_t n_keys;
@@ -55,8 +64,8 @@ struct AttnArgs {
   float scale_log2;  // log2(e) / sqrt(d)
 };
 
-// Flash-style prefill, d = 128, bf16, MFMA (requires q_pos0 == 0 and
-// n_keys == Tq, keys at positions 0..Tq-1).
+// Flash-style prefill, d = 128, bf16, MFMA.  Requires n_keys == q_pos0 + Tq
+// < 2^30, and main_pos0 == 0 unless a prefix is given.
 hipError_t launch_prefill_mfma(const AttnArgs& a, hipStream_t s);
 // Plain per-query kernel for the other head sizes and for fp32.
 hipError_t launch_attn_generic(const AttnArgs& a, int dtype, int d, hipStream_t s);
@@ -81,7 +90,8 @@ hipError_t launch_decode_split(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t s);
 
 // Probes: the prefill kernel's tile walk and the decode kernel's row walk.
-hipError_t launch_probe_prefill(int T, int window, int sliding, uint8_t* visit, hipStream_t s);
+hipError_t launch_probe_prefill(int T, int64_t pos_offset, int window, int sliding,
+                                uint8_t* visit, hipStream_t s);
 hipError_t launch_probe_decode(const DecodeArgs& a, int32_t* count, hipStream_t s);
 
 }  // namespace olmo3

@@ -79,6 +79,9 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const char* p) {
   return __builtin_bit_cast(bf16x4, v);
 }
 
+// kPrefix: keys before main_pos0 come from a ring (chunked prefill on a
+// sliding layer); without it every key is a main row (main_pos0 == 0).
+template <bool kPrefix>
 __global__ __launch_bounds__(256, 2) void prefill_d128_kernel(AttnArgs a) {
   using namespace pf;
   __shared__ __attribute__((aligned(16))) char smem[4 * kTileBytes];
@@ -88,12 +91,14 @@ __global__ __launch_bounds__(256, 2) void prefill_d128_kernel(AttnArgs a) {
   const int n_qblk = (a.Tq + kBQ - 1) / kBQ;
   const Work w = work_of(blockIdx.x, gridDim.x, n_qblk, a.H);
   const int g = w.h / (a.H / a.G);
-  const int q0 = w.qb * kBQ;
-  const int q1 = min(q0 + kBQ, a.Tq);
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  // positions: queries q_pos0 .. q_pos0 + Tq - 1, keys 0 .. n_keys - 1
+  const int qpos0 = (int)a.q_pos0;
+  const int q0 = qpos0 + w.qb * kBQ;
+  const int q1 = min(q0 + kBQ, qpos0 + a.Tq);
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int col = lane & 31, half = lane >> 5;
   const int tq = lane_query(q0, wave, lane);
-  const int tql = min(tq, a.Tq - 1);
+  const int tql = min(tq, q1 - 1) - qpos0;  // query row of the lane
 
   // Q^T operand: lane holds query tq, d = 16*ks + 8*half .. +7
   bf16x8 qop[8];
@@ -109,38 +114,62 @@ __global__ __launch_bounds__(256, 2) void prefill_d128_kernel(AttnArgs a) {
 
   // Direct loads: instruction i of wavefront w fills tile rows 16 i + 4 w ..
   // +3; lane l takes row 16 i + 4 w + l/16, stored column l mod 16, i.e.
-  // logical column (l mod 16) ^ swizzle(row).  Rows past the last key are
-  // clamped to it (such keys lie past every query of the block: masked).
+  // logical column (l mod 16) ^ swizzle(row).  Positions past the last key
+  // are clamped to it (such keys lie past every query of the block: masked).
   const int n_keys = (int)a.n_keys;
   const int lrow = 4 * wave + (lane >> 4);  // row within each 16-row slab
   const int kcol = (lane & 15) ^ (lrow & 15);
   const int vcol = (lane & 15) ^ (4 * (lrow & 3));
-  // Uniform per-head bases plus a 32-bit per-lane element offset; only the
-  // last tile of a sequence (rows past n_keys) takes the clamped path.
+  // Uniform per-head bases plus a 32-bit per-lane element offset.  Tiles
+  // whose 64 rows are consecutive rows of one source take the fast path;
+  // the last tile (positions past n_keys) and, with a prefix, tiles that
+  // cross the prefix/main boundary or the ring's wrap go row by row.
   const bf16* kbase = (const bf16*)a.k + w.b * a.k_sb + g * a.k_sg;
   const bf16* vbase = (const bf16*)a.v + w.b * a.v_sb + g * a.v_sg;
   const int k_lane = lrow * (int)a.k_sr + kcol * 8;
   const int v_lane = lrow * (int)a.v_sr + vcol * 8;
+  const int main0 = kPrefix ? (int)a.main_pos0 : 0;
+  const int ring = kPrefix ? (int)a.ring : 1;
+  const int64_t p_sr = a.p_sr;
+  const bf16* kpbase = kPrefix ? (const bf16*)a.kp + w.b * a.p_sb + g * a.p_sg : nullptr;
+  const bf16* vpbase = kPrefix ? (const bf16*)a.vp + w.b * a.p_sb + g * a.p_sg : nullptr;
+  const int kp_lane = kPrefix ? lrow * (int)p_sr + kcol * 8 : 0;
+  const int vp_lane = kPrefix ? lrow * (int)p_sr + vcol * 8 : 0;
   const int slab = 4 * wave * 256;  // this wavefront's byte offset in a slab
-  auto load_rows = [&](const bf16* base, int64_t sr, int lane_off, int col8, int k0,
-                       char* dst) __attribute__((always_inline)) {
-    if (k0 + kBK <= n_keys) {
+  auto load_rows = [&](const bf16* base, int64_t sr, int lane_off, const bf16* pbase,
+                       int plane_off, int col8, int k0, char* dst) __attribute__((always_inline)) {
+    if (!kPrefix || k0 >= main0) {
+      if (k0 + kBK <= n_keys) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          load_to_lds(base + (int64_t)(k0 - main0 + 16 * i) * sr + lane_off, dst + 16 * i * 256);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = min(k0 + 16 * i + lrow, n_keys - 1) - main0;
+          load_to_lds(base + (int64_t)row * sr + col8, dst + 16 * i * 256);
+        }
+      }
+    } else if (k0 + kBK <= main0 && k0 % ring + kBK <= ring) {
+      const int slot0 = k0 % ring;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        load_to_lds(base + (int64_t)(k0 + 16 * i) * sr + lane_off, dst + 16 * i * 256);
+        load_to_lds(pbase + (int64_t)(slot0 + 16 * i) * p_sr + plane_off, dst + 16 * i * 256);
     } else {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int row = min(k0 + 16 * i + lrow, n_keys - 1);
-        load_to_lds(base + (int64_t)row * sr + col8, dst + 16 * i * 256);
+        const int p = min(k0 + 16 * i + lrow, n_keys - 1);
+        const bf16* src = p >= main0 ? base + (int64_t)(p - main0) * sr + col8
+                                     : pbase + (int64_t)(p % ring) * p_sr + col8;
+        load_to_lds(src, dst + 16 * i * 256);
       }
     }
   };
   auto load_k = [&](int k0, int buf) __attribute__((always_inline)) {
-    load_rows(kbase, a.k_sr, k_lane, kcol * 8, k0, sK + buf * kTileBytes + slab);
+    load_rows(kbase, a.k_sr, k_lane, kpbase, kp_lane, kcol * 8, k0, sK + buf * kTileBytes + slab);
   };
   auto load_v = [&](int k0, int buf) __attribute__((always_inline)) {
-    load_rows(vbase, a.v_sr, v_lane, vcol * 8, k0, sV + buf * kTileBytes + slab);
+    load_rows(vbase, a.v_sr, v_lane, vpbase, vp_lane, vcol * 8, k0, sV + buf * kTileBytes + slab);
   };
 
   // LDS read offsets.  K (A operand of S^T): row 32 kb + col, column
@@ -291,8 +320,8 @@ __global__ __launch_bounds__(256, 2) void prefill_d128_kernel(AttnArgs a) {
 
   lsum += __shfl_xor(lsum, 32, kWave);
   const float inv = 1.0f / lsum;
-  if (tq < a.Tq) {
-    bf16* orow = (bf16*)a.out + ((int64_t)(w.b * a.Tq + tq) * a.H + w.h) * kD;
+  if (tq < q1) {
+    bf16* orow = (bf16*)a.out + ((int64_t)(w.b * a.Tq + (tq - qpos0)) * a.H + w.h) * kD;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -306,12 +335,15 @@ __global__ __launch_bounds__(256, 2) void prefill_d128_kernel(AttnArgs a) {
 
 // Records every (query, key) pair the kernel above accumulates: the same
 // work mapping, tile runs, lane -> (query, key) map and predicate.
-__global__ __launch_bounds__(256) void probe_prefill_kernel(int T, int window, int sliding,
-                                                            uint8_t* visit) {
+// visit[(t - pos_offset) * (pos_offset + T) + s] for query position t and key
+// position s.
+__global__ __launch_bounds__(256) void probe_prefill_kernel(int T, int pos_offset, int window,
+                                                            int sliding, uint8_t* visit) {
   using namespace pf;
   const int n_qblk = (T + kBQ - 1) / kBQ;
+  const int n_keys = pos_offset + T;
   const Work w = work_of(blockIdx.x, gridDim.x, n_qblk, 1);
-  const int q0 = w.qb * kBQ, q1 = min(q0 + kBQ, T);
+  const int q0 = pos_offset + w.qb * kBQ, q1 = min(q0 + kBQ, n_keys);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int tq = lane_query(q0, wave, lane);
   int kt0, kt1, i0, i1;
@@ -324,7 +356,7 @@ __global__ __launch_bounds__(256) void probe_prefill_kernel(int T, int window, i
       for (int r = 0; r < 16; ++r) {
         const int s = lane_key(k0, kb, r, lane);
         const bool acc = interior || visible(tq, s, window, sliding);
-        if (acc && tq < T && s < T) visit[(int64_t)tq * T + s] = 1;
+        if (acc && tq < q1 && s < n_keys) visit[(int64_t)(tq - pos_offset) * n_keys + s] = 1;
       }
   }
 }
@@ -334,15 +366,19 @@ __global__ __launch_bounds__(256) void probe_prefill_kernel(int T, int window, i
 hipError_t launch_prefill_mfma(const AttnArgs& a, hipStream_t s) {
   const int n_qblk = (a.Tq + pf::kBQ - 1) / pf::kBQ;
   const int blocks = n_qblk * a.H * a.B;
-  prefill_d128_kernel<<<blocks, 256, 0, s>>>(a);
+  if (a.kp)
+    prefill_d128_kernel<true><<<blocks, 256, 0, s>>>(a);
+  else
+    prefill_d128_kernel<false><<<blocks, 256, 0, s>>>(a);
   return hipGetLastError();
 }
 
-hipError_t launch_probe_prefill(int T, int window, int sliding, uint8_t* visit, hipStream_t s) {
-  hipError_t e = hipMemsetAsync(visit, 0, (size_t)T * T, s);
+hipError_t launch_probe_prefill(int T, int64_t pos_offset, int window, int sliding,
+                                uint8_t* visit, hipStream_t s) {
+  hipError_t e = hipMemsetAsync(visit, 0, (size_t)T * (size_t)(pos_offset + T), s);
   if (e != hipSuccess) return e;
   const int n_qblk = (T + pf::kBQ - 1) / pf::kBQ;
-  probe_prefill_kernel<<<n_qblk, 256, 0, s>>>(T, window, sliding, visit);
+  probe_prefill_kernel<<<n_qblk, 256, 0, s>>>(T, (int)pos_offset, window, sliding, visit);
   return hipGetLastError();
 }
 

@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define OLMO3_ABI_VERSION 1
+#define OLMO3_ABI_VERSION 2
 
 typedef enum olmo3_status {
   OLMO3_OK = 0,
@@ -115,7 +115,7 @@ size_t olmo3_workspace_bytes(int mode, int B, int T, int H, int G, int d,
  * [B][T][G*d].  Errors: INVALID_ARG (sizes <= 0, odd d, pos_offset < 0, bad
  * enum, null pointer, k_cache/v_cache overlapping each other or an input),
  * CAPACITY (ring size != window, or a linear cache shorter than
- * pos_offset + T), UNSUPPORTED (d not in {16, 32, 64, 128, 256}). */
+ * pos_offset + T), UNSUPPORTED (d not in {16, 32, 64, 128}). */
 int olmo3_kv_append(int B, int T, int G, int d, int window, int layer_type,
                     const olmo3_rope* rope, float eps, int64_t pos_offset,
                     int dtype, const void* k_pre, const void* v,
@@ -123,13 +123,18 @@ int olmo3_kv_append(int B, int T, int G, int d, int window, int layer_type,
                     int64_t cache_capacity, void* stream);
 
 /* Prefill: attention of T new tokens at positions pos_offset .. +T-1, which
- * are also appended to the cache.  Query t attends to the new keys s <= t
- * (and t - s < window on sliding layers).  out is fully overwritten.
- * workspace must hold olmo3_workspace_bytes(OLMO3_MODE_PREFILL, ...) bytes
- * (device memory, contents on entry ignored).  Errors: as olmo3_kv_append,
- * plus H % G != 0 (INVALID_ARG), out overlapping any other buffer
- * (INVALID_ARG), a short or null workspace (WORKSPACE), and pos_offset > 0
- * (UNSUPPORTED: attending to an earlier cached prefix is not implemented). */
+ * are also appended to the cache.  Query t attends to every key position
+ * s <= t (and t - s < window on sliding layers): the new keys and, when
+ * pos_offset > 0 (a later chunk of a prompt, or a multi-token step), the
+ * positions the cache already holds, following "Olmo-3 End-to-End
+ * Implementation", "Cache Operation Flow" (cached keys and values joined
+ * with the new ones).  The caller must have filled the cache with positions
+ * 0 .. pos_offset-1 (the ring with the last `window` of them).  out is
+ * fully overwritten.  workspace must hold
+ * olmo3_workspace_bytes(OLMO3_MODE_PREFILL, ...) bytes (device memory,
+ * contents on entry ignored).  Errors: as olmo3_kv_append, plus H % G != 0
+ * (INVALID_ARG), out overlapping any other buffer (INVALID_ARG), a short or
+ * null workspace (WORKSPACE), and pos_offset + T > 2^30 (UNSUPPORTED). */
 int olmo3_attn_prefill(int B, int T, int H, int G, int d, int window,
                        int layer_type, const olmo3_rope* rope, float eps,
                        int64_t pos_offset, int dtype, const void* q_pre,
@@ -163,6 +168,9 @@ int olmo3_attn_decode(int B, int H, int G, int d, int window, int layer_type,
  *                              prefill, keys) written to the workspace;
  *   OLMO3_PHASE_ATTENTION (2)  attention reading the workspace and cache;
  *                              for decode, the split-KV partial states;
+ *                              on a sliding-layer prefill with
+ *                              pos_offset > 0, also the ring append, which
+ *                              must follow the attention;
  *   OLMO3_PHASE_MERGE     (4)  decode only: log-sum-exp merge of the
  *                              partial states into out (a no-op when the
  *                              decode path needs no merge).
@@ -198,10 +206,12 @@ int olmo3_abi_version(void);
  * the decode kernel's own split / row enumeration, and record what those
  * visit, so that indexing can be compared bit for bit with the oracle.  */
 
-/* visit [T][T] uint8 (device): set to 1 for every (query t, key s) pair the
+/* visit [T][pos_offset + T] uint8 (device): entry (t, s) is set to 1 for
+ * every pair of query position pos_offset + t and key position s that the
  * d = 128 bf16 prefill kernel would accumulate, 0 elsewhere (the probe
- * clears it first).  T <= 4096.  Errors: INVALID_ARG, UNSUPPORTED. */
-int olmo3_probe_prefill_visits(int T, int window, int layer_type,
+ * clears it first).  T <= 4096, pos_offset + T <= 8192.
+ * Errors: INVALID_ARG, UNSUPPORTED. */
+int olmo3_probe_prefill_visits(int T, int64_t pos_offset, int window, int layer_type,
                                uint8_t* visit, void* stream);
 
 /* count [cache_capacity] int32 (device): number of times the decode kernel

@@ -55,13 +55,14 @@ def make_cache(B, G, cap, d, dtype, device, fill=None):
     return k, v
 
 
-def gpu_prefill(x, k_cache, v_cache, *, window, layer_type, rope, eps=1e-6, H):
+def gpu_prefill(x, k_cache, v_cache, *, window, layer_type, rope, eps=1e-6, H, pos_offset=0):
     B, T, _ = x["q_pre"].shape
     G, cap, d = k_cache.shape[1], k_cache.shape[2], k_cache.shape[3]
     out = torch.empty_like(x["q_pre"])
     ws = A.workspace(A.MODE_PREFILL, B, T, H, G, d, layer_type, x["q_pre"].dtype, cap, x["q_pre"].device)
     A.olmo3_attn_prefill(x["q_pre"], x["k_pre"], x["v"], x["q_gain"], x["k_gain"], k_cache, v_cache,
-                         out, ws, window=window, layer_type=layer_type, rope=rope, eps=eps)
+                         out, ws, window=window, layer_type=layer_type, rope=rope, eps=eps,
+                         pos_offset=pos_offset)
     return out
 
 

@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version():
-    assert A.olmo3_abi_version() == 1
+    assert A.olmo3_abi_version() == A.ABI_VERSION == 2
 
 
 def test_layer_type_matches_oracle_bit_exact():
@@ -129,7 +129,8 @@ def prefill_call(**kw):
     (dict(layer_type=1, cap=63), A.ERR_CAPACITY),   # linear cache shorter than T
     (dict(workspace=0), A.ERR_WORKSPACE),
     (dict(ws_bytes=100), A.ERR_WORKSPACE),
-    (dict(layer_type=1, cap=200, pos_offset=5), A.ERR_UNSUPPORTED),  # chunked prefill
+    (dict(layer_type=1, cap=100, pos_offset=40), A.ERR_CAPACITY),  # chunk past a linear cache
+    (dict(pos_offset=(1 << 30) - 63), A.ERR_UNSUPPORTED),  # positions past 2^30
     (dict(H=40 * 8, G=8), A.ERR_UNSUPPORTED),  # too many heads for one wavefront's norm
 ])
 def test_prefill_rejects(kw, status):
@@ -182,8 +183,10 @@ def test_append_rejects(kw, status):
 
 def test_probe_rejects():
     L = A.lib()
-    assert L.olmo3_probe_prefill_visits(0, 4, 0, fake(0), None) == A.ERR_INVALID_ARG
-    assert L.olmo3_probe_prefill_visits(5000, 4, 0, fake(0), None) == A.ERR_INVALID_ARG
+    assert L.olmo3_probe_prefill_visits(0, 0, 4, 0, fake(0), None) == A.ERR_INVALID_ARG
+    assert L.olmo3_probe_prefill_visits(5, -1, 4, 0, fake(0), None) == A.ERR_INVALID_ARG
+    assert L.olmo3_probe_prefill_visits(5000, 0, 4, 0, fake(0), None) == A.ERR_UNSUPPORTED
+    assert L.olmo3_probe_prefill_visits(100, 8100, 4, 0, fake(0), None) == A.ERR_UNSUPPORTED
     assert L.olmo3_probe_decode_reads(1, 1, 64, 4, 0, 3, 4, fake(0), None) == A.ERR_INVALID_ARG
     assert L.olmo3_probe_decode_reads(1, 1, 128, 4, 0, 3, 5, fake(0), None) == A.ERR_CAPACITY
 
