@@ -12,10 +12,13 @@ Workloads (synthetic, seeded, shaped like the OLMo 3 configurations):
   32b  prefill B=1, T=8192, H=40, G=8; decode B=64 at cache length 32,768
   long 32-layer attention-only stack (24 sliding, 8 full YaRN), B=1,
        T=65,536, 7B head shapes, prefill only
+  decode-stack  the same 32-layer stack decoding one token per sequence,
+       B=16 at cache length 65,536: KV bytes read per step and per token of
+       context (the per-layer-type cache of the page "Olmo 3 7B")
 
 Printed: one JSON line.  `value` is prefill TFLOP/s (algorithmic FLOPs of the
 allowed query/key pairs over the whole prefill call time); decode KV GB/s is
-in "decode".  Each kernel is bracketed by HIP events on the stream it is
+in "decode" (and is `value` for the decode-only stack workload).  Each kernel is bracketed by HIP events on the stream it is
 launched on (the stage-by-stage entry points), giving the per-kernel
 rooflines.  The CPU oracle is timed on a bounded sample of the same workload.
 """
@@ -65,7 +68,11 @@ WORKLOADS = {
                 decode=dict(B=64, H=40, G=8, L=32768)),
     "long": dict(name="olmo3-7b-long-context-stack", prefill=dict(B=1, T=65536, H=32, G=32, layers=32),
                  decode=None),
+    "decode-stack": dict(name="olmo3-7b-decode-stack", prefill=None,
+                         decode=dict(B=16, H=32, G=32, L=65536, layers=32)),
 }
+N_LAYERS_7B = 32
+NAIVE_BYTES_PER_TOKEN_7B = N_LAYERS_7B * 32 * 128 * 2 * 2  # every layer full: 524,288
 
 
 def parse():
@@ -126,11 +133,11 @@ def main():
     segments = []  # (name, kind, callable(phases), phase list, work, work unit)
 
     # ---- prefill layers
-    pf = wl["prefill"]
+    pf = wl["prefill"] or dict(B=0, T=0, H=0, G=0)
     B, T, H, G = pf["B"], pf["T"], pf["H"], pf["G"]
     n_layers = pf.get("layers", 0)
     layer_list = ([(ell, A.olmo3_layer_type(ell, n_layers)) for ell in range(n_layers)]
-                  if n_layers else [(0, 0), (3, 1)])
+                  if n_layers else [(0, 0), (3, 1)]) if wl["prefill"] else []
     print(f"[bench] workload {wl['name']}: preparing {len(layer_list)} prefill layer(s)", file=sys.stderr,
           flush=True)
     seed_base = 5 if n_layers else (2 if args.workload == "7b" else 4)
@@ -160,16 +167,20 @@ def main():
     if dc:
         Bd, Hd, Gd, L = dc["B"], dc["H"], dc["G"], dc["L"]
         pos = L - 1  # the cache holds positions 0 .. L-2; the new token is the L-th
-        for lt in (0, 1):
+        n_dec_layers = dc.get("layers", 0)
+        dec_layers = ([(ell, A.olmo3_layer_type(ell, n_dec_layers)) for ell in range(n_dec_layers)]
+                      if n_dec_layers else [(0, 0), (3, 1)])
+        dseed = 6 if n_dec_layers else (3 if args.workload == "7b" else 4)
+        for ell, lt in dec_layers:
             sliding = lt == 0
             if not keep("decode", sliding):
                 continue
             cap = WINDOW if sliding else L
-            print(f"[bench] filling {'ring' if sliding else 'linear'} decode cache "
+            print(f"[bench] filling {'ring' if sliding else 'linear'} decode cache of layer {ell} "
                   f"[{Bd}, {Gd}, {cap}, {d}] x2", file=sys.stderr, flush=True)
-            kc, vc = synth.cache_fill(3 if args.workload == "7b" else 4, 100 + lt, Bd, Gd, cap, d,
+            kc, vc = synth.cache_fill(dseed, (ell if n_dec_layers else 100 + lt), Bd, Gd, cap, d,
                                       device=dev, dtype=bf16)
-            x = synth.layer_inputs(3 if args.workload == "7b" else 4, 200 + lt, Bd, 1, Hd, Gd, d,
+            x = synth.layer_inputs(dseed, (100 + ell if n_dec_layers else 200 + lt), Bd, 1, Hd, Gd, d,
                                    device=dev, dtype=bf16)
             q = x["q_pre"][:, 0].contiguous()
             k = x["k_pre"][:, 0].contiguous()
@@ -183,8 +194,8 @@ def main():
                                     window=WINDOW, layer_type=lt, rope=r, pos=pos, phases=phases)
 
             n = decode_rows(pos, WINDOW, sliding)
-            segments.append(dict(name=f"decode_{'sliding' if sliding else 'full'}", kind="decode",
-                                 sliding=sliding, run=run,
+            name = f"decode_{'sliding' if sliding else 'full'}" + (f"_l{ell}" if n_dec_layers else "")
+            segments.append(dict(name=name, kind="decode", sliding=sliding, run=run,
                                  phases=[A.PHASE_PROLOGUE, A.PHASE_ATTENTION, A.PHASE_MERGE],
                                  work=decode_kv_bytes(Bd, Gd, d, n), rows=n))
     torch.cuda.synchronize()
@@ -246,10 +257,12 @@ def main():
     rooflines = [roof(s, 1) for s in segments]
     dominant = max(zip(segments, rooflines), key=lambda sr: sr[0]["phase_ms"][1])[1]
 
+    dec_gbs = (sum(s["work"] for s in dec) / (sum(s["call_ms"] for s in dec) * 1e-3) / 1e9
+               if dec else 0.0)
     result = {
         "metric": METRIC,
-        "value": round(prefill_tflops, 2),
-        "unit": "TFLOP/s",
+        "value": round(prefill_tflops, 2) if pre else round(dec_gbs, 1),
+        "unit": "TFLOP/s" if pre else "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -259,8 +272,9 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": wl["name"], "prefill": dict(pf, d=d, window=WINDOW, theta=THETA,
-                                                           yarn_full="factor 8, orig 8192"),
+        "config": {"workload": wl["name"],
+                   "prefill": (dict(pf, d=d, window=WINDOW, theta=THETA, yarn_full="factor 8, orig 8192")
+                               if pre else None),
                    "decode": (dict(dc, d=d, window=WINDOW, pos=dc["L"] - 1) if dc else None),
                    "parallelism": "single GPU"},
         "prefill": {"tflops": round(prefill_tflops, 2),
@@ -272,15 +286,27 @@ def main():
         "rooflines": rooflines,
     }
     if dec:
-        gbs = sum(s["work"] for s in dec) / (sum(s["call_ms"] for s in dec) * 1e-3) / 1e9
+        gbs = dec_gbs
         result["decode"] = {"gbs": round(gbs, 1), "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4),
                             "calls": {s["name"]: {"call_ms": round(s["call_ms"], 4),
                                                   "gbs": round(s["work"] / (s["call_ms"] * 1e-3) / 1e9, 1),
                                                   "kv_bytes": s["work"], "rows": s["rows"]}
                                       for s in dec}}
-    if args.cpu_seconds > 0 and pre:
+    if dc and dc.get("layers") and len(dec) == dc["layers"]:
+        # per decode step of the stack: every layer reads its whole cache once
+        kv_step = sum(s["work"] for s in dec)
+        step_ms = sum(s["call_ms"] for s in dec)
+        result["stack"] = {
+            "layers": dc["layers"], "sliding": sum(s["sliding"] for s in dec),
+            "kv_bytes_per_step": kv_step, "step_ms": round(step_ms, 4),
+            "tokens_per_s": round(dc["B"] / (step_ms * 1e-3), 1),
+            "kv_bytes_per_token_of_context": kv_step // (dc["B"] * dc["L"]),
+            "naive_bytes_per_token_of_context": NAIVE_BYTES_PER_TOKEN_7B,
+        }
+    if args.cpu_seconds > 0 and (pre or dec):
         print(f"[bench] timing the CPU oracle for ~{args.cpu_seconds:.0f} s", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(args, wl, segments, dev)
+        result["cpu_baseline"] = (cpu_baseline(args, wl, segments, dev) if pre else
+                                  cpu_baseline_decode(args, wl))
     print(json.dumps(result), flush=True)
 
 
@@ -294,12 +320,7 @@ def cpu_baseline(args, wl, segments, dev):
 
     import oracle as O
 
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()
-                       if p.get("user_api") == "blas"] or [1])
-    except Exception:  # pragma: no cover - informational only
-        threads = len(os.sched_getaffinity(0))
+    threads = _blas_threads()
     from global_hybrid_causal_amd import synth
 
     pf = wl["prefill"]
@@ -330,6 +351,52 @@ def cpu_baseline(args, wl, segments, dev):
             "sample": f"{blocks} blocks of {rows_per_block} query rows x {H} heads of the "
                       f"{wl['name']} sliding prefill (T={T}, window {WINDOW}), fp64 NumPy, "
                       f"{elapsed:.1f} s"}
+
+
+def cpu_baseline_decode(args, wl):
+    """The oracle's decode on a bounded sample of the decode workload: one
+    (sequence, key/value head) of a full layer at the workload's cache length
+    per call, seeded cache rows of the same shape, until the time budget is
+    spent.  Bytes are counted like the GPU's (the K and V rows read, bf16)."""
+    import numpy as np
+    import torch
+
+    import oracle as O
+    from global_hybrid_causal_amd import synth
+
+    threads = _blas_threads()
+    dc = wl["decode"]
+    H, G, L, d = dc["H"], dc["G"], dc["L"], 128
+    pos = L - 1
+    group = H // G
+    rope = O.RopeParams(theta=THETA, yarn=True, factor=8.0, orig_ctx=8192)
+    ck = synth.normal((1, L, d), 7, 0, synth.CACHE_K).to(torch.float64).numpy()
+    cv = synth.normal((1, L, d), 7, 0, synth.CACHE_V).to(torch.float64).numpy()
+    tags = O.ring_positions(O.FULL, WINDOW, L, pos)
+    x = synth.layer_inputs(7, 0, 1, 1, H, G, d, dtype=torch.float32)
+    hx = {k: v.to(torch.float64).numpy() for k, v in x.items()}
+    calls, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < args.cpu_seconds:
+        O.decode_rows_ref(hx["q_pre"][0, 0], hx["k_pre"][0, 0], hx["v"][0, 0], hx["q_gain"],
+                          hx["k_gain"], ck, cv, tags, H=H, G=G, d=d, kv_heads=[0], kind=O.FULL,
+                          window=WINDOW, rope=rope, pos=pos)
+        calls += 1
+    elapsed = time.perf_counter() - t0
+    nbytes = calls * L * d * 2 * 2
+    return {"value": round(nbytes / elapsed / 1e9, 3), "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{calls} decode calls of one sequence x one key/value head ({group} query "
+                      f"head{'s' if group > 1 else ''}) of a full layer at cache length {L}, fp64 "
+                      f"NumPy, {elapsed:.1f} s"}
+
+
+def _blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        return max([p.get("num_threads", 1) for p in threadpool_info()
+                    if p.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover - informational only
+        return len(os.sched_getaffinity(0))
 
 
 if __name__ == "__main__":

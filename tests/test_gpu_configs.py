@@ -149,3 +149,48 @@ def test_long_context_stack_sampled():
             _check_prefill_rows(x, out, kc, vc, T=T, H=H, G=G, d=d, lt=lt, rope=rope,
                                 kv_heads=[0, 31], seed=100 + ell, what=f"long layer {ell}")
         del x, kc, vc, out
+
+
+def test_decode_stack_reads_effective_bytes_per_token():
+    """32-layer attention-only decode stack, 7B head shapes, B=2, cache
+    length 65,536 (new token at 65,535), per-layer seeds.  Every layer's
+    decode runs on the GPU and is compared with the oracle on two key/value
+    heads of both sequences.  The rows the decode kernel reads, counted by
+    its probe and summed over the stack, give the cache bytes per token of
+    context that the page "Olmo 3 7B" states for the per-layer-type cache:
+    155,648 B at 65,536 (against 524,288 B if every layer were full)."""
+    B, H, G, d, L, n_layers = 2, 32, 32, 128, 65536, 32
+    pos = L - 1
+    kinds = O.layer_types(n_layers)
+    gs = [0, G - 1]
+    group = H // G
+    heads = [g * group + j for g in gs for j in range(group)]
+    rows_read = 0
+    for ell, kind in enumerate(kinds):
+        lt = O.layer_type_code(kind)
+        cap = W if lt == 0 else L
+        rope = YARN if lt == 1 else PLAIN
+        kc, vc = synth.cache_fill(6, ell, B, G, cap, d, device="cuda", dtype=BF16)
+        before = {b: (host(kc[b, gs]), host(vc[b, gs])) for b in range(B)}
+        x = inputs(6, 100 + ell, B, 1, H, G, d, BF16)
+        q, k, v = x["q_pre"][:, 0].contiguous(), x["k_pre"][:, 0].contiguous(), x["v"][:, 0].contiguous()
+        out = gpu_decode(q, k, v, x["q_gain"], x["k_gain"], kc, vc, window=W, layer_type=lt,
+                         rope=rope, pos=pos, H=H)
+        torch.cuda.synchronize()
+        assert torch.isfinite(out).all(), f"layer {ell}"
+        tags = O.ring_positions(kind, W, cap, pos)
+        hq, hk, hv = host(q), host(k), host(v)
+        qg, kg = host(x["q_gain"]), host(x["k_gain"])
+        for b in range(B):
+            ref = O.decode_rows_ref(hq[b], hk[b], hv[b], qg, kg, before[b][0], before[b][1], tags,
+                                    H=H, G=G, d=d, kv_heads=gs, kind=kind, window=W,
+                                    rope=oracle_rope(rope), pos=pos)
+            assert_close(host(out[b]).reshape(H, d)[heads], ref, what=f"stack layer {ell} b={b}")
+        count = A.olmo3_probe_decode_reads(B, G, d, W, lt, pos, cap).cpu().numpy()
+        assert count.max() == 1
+        rows_read += int(count.sum())
+        del kc, vc, x, out
+    _log(f"decode stack: {rows_read} rows read per (sequence, key/value head)")
+    bytes_per_token = rows_read * G * d * 2 * 2 // L
+    assert bytes_per_token == O.kv_bytes_per_token(kinds, G, d, W, L) == 155648
+    assert O.kv_bytes_per_token([O.FULL] * n_layers, G, d, W, L) == 524288
