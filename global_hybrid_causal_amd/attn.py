@@ -18,7 +18,7 @@ from . import LAYER_FULL, LAYER_SLIDING  # noqa: F401  (re-exported)
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libolmo3attn.so")
 
-ABI_VERSION = 2  # OLMO3_ABI_VERSION of include/olmo3_attn.h
+ABI_VERSION = 3  # OLMO3_ABI_VERSION of include/olmo3_attn.h
 DTYPE_BF16, DTYPE_F32 = 0, 1
 MODE_PREFILL, MODE_DECODE = 0, 1
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_CAPACITY, ERR_HIP, ERR_WORKSPACE = range(6)
@@ -28,7 +28,7 @@ EXPORTS = (
     "olmo3_layer_type", "olmo3_workspace_bytes", "olmo3_kv_append", "olmo3_attn_prefill",
     "olmo3_attn_decode", "olmo3_status_string", "olmo3_abi_version",
     "olmo3_probe_prefill_visits", "olmo3_probe_decode_reads", "olmo3_attn_prefill_phases",
-    "olmo3_attn_decode_phases",
+    "olmo3_attn_decode_phases", "olmo3_attn_prefill_ragged", "olmo3_attn_decode_ragged",
 )
 PHASE_PROLOGUE, PHASE_ATTENTION, PHASE_MERGE = 1, 2, 4
 PHASES_ALL = PHASE_PROLOGUE | PHASE_ATTENTION | PHASE_MERGE
@@ -100,6 +100,14 @@ def lib() -> ctypes.CDLL:
         L.olmo3_attn_prefill_phases.restype = _i
         L.olmo3_attn_decode_phases.argtypes = [_i] + L.olmo3_attn_decode.argtypes
         L.olmo3_attn_decode_phases.restype = _i
+        L.olmo3_attn_prefill_ragged.argtypes = [_i, _i, _i, _i64, _i, _i, _i, _i, _i,
+                                                ctypes.POINTER(RopeStruct), _f, _p, _p, _i, _p, _p,
+                                                _p, _p, _p, _p, _p, _i64, _p, _p, _sz, _p]
+        L.olmo3_attn_prefill_ragged.restype = _i
+        L.olmo3_attn_decode_ragged.argtypes = [_i, _i, _i, _i, _i, _i, ctypes.POINTER(RopeStruct),
+                                               _f, _p, _i64, _i, _p, _p, _p, _p, _p, _p, _p, _i64,
+                                               _p, _p, _sz, _p]
+        L.olmo3_attn_decode_ragged.restype = _i
         L.olmo3_status_string.argtypes = [_i]
         L.olmo3_status_string.restype = ctypes.c_char_p
         L.olmo3_abi_version.argtypes = []
@@ -224,6 +232,56 @@ def olmo3_attn_decode(q_pre, k_pre, v, q_gain, k_gain, k_cache, v_cache, out, wo
         _check(lib().olmo3_attn_decode(*args), "olmo3_attn_decode")
     else:
         _check(lib().olmo3_attn_decode_phases(phases, *args), "olmo3_attn_decode_phases")
+
+
+def _i32(t: torch.Tensor | None, name: str, n: int) -> int:
+    if t is None:
+        return 0
+    if t.dtype != torch.int32 or t.numel() != n:
+        raise ValueError(f"{name} must be an int32 device tensor of {n} elements")
+    return _ptr(t, name)
+
+
+def olmo3_attn_prefill_ragged(q_pre, k_pre, v, q_gain, k_gain, k_cache, v_cache, out, workspace,
+                              cu_seqlens, pos_offsets, *, max_len: int, max_end: int, window: int,
+                              layer_type: int, rope: Rope, eps: float = 1e-6, stream=None) -> None:
+    """Packed prefill of B sequences: q_pre [N, H*d], k_pre/v [N, G*d] ->
+    out [N, H*d]; sequence b owns rows cu_seqlens[b] .. cu_seqlens[b+1]-1
+    (int32 device tensors: cu_seqlens [B+1], pos_offsets [B] or None) and
+    uses cache k_cache[b] / v_cache[b]."""
+    B, G, cap, d = _cache_dims(k_cache)
+    N = q_pre.shape[0]
+    H = q_pre.shape[-1] // d
+    dt = q_pre.dtype
+    r = rope.to_c()
+    st = lib().olmo3_attn_prefill_ragged(
+        B, N, max_len, max_end, H, G, d, window, layer_type, ctypes.byref(r), eps,
+        _i32(cu_seqlens, "cu_seqlens", B + 1), _i32(pos_offsets, "pos_offsets", B),
+        _dtype_code(q_pre), _ptr(q_pre, "q_pre", dt), _ptr(k_pre, "k_pre", dt), _ptr(v, "v", dt),
+        _ptr(q_gain, "q_gain", dt), _ptr(k_gain, "k_gain", dt), _ptr(k_cache, "k_cache", dt),
+        _ptr(v_cache, "v_cache", dt), cap, _ptr(out, "out", dt), _ptr(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream(stream, q_pre.device))
+    _check(st, "olmo3_attn_prefill_ragged")
+
+
+def olmo3_attn_decode_ragged(q_pre, k_pre, v, q_gain, k_gain, k_cache, v_cache, out, workspace,
+                             positions, *, max_pos: int, window: int, layer_type: int, rope: Rope,
+                             eps: float = 1e-6, stream=None) -> None:
+    """Decode one token per sequence at its own position (int32 device
+    tensor positions [B], each <= max_pos): q_pre [B, H*d], k_pre/v [B, G*d]
+    -> out [B, H*d]."""
+    B, G, cap, d = _cache_dims(k_cache)
+    H = q_pre.shape[-1] // d
+    dt = q_pre.dtype
+    r = rope.to_c()
+    st = lib().olmo3_attn_decode_ragged(
+        B, H, G, d, window, layer_type, ctypes.byref(r), eps, _i32(positions, "positions", B),
+        max_pos, _dtype_code(q_pre), _ptr(q_pre, "q_pre", dt), _ptr(k_pre, "k_pre", dt),
+        _ptr(v, "v", dt), _ptr(q_gain, "q_gain", dt), _ptr(k_gain, "k_gain", dt),
+        _ptr(k_cache, "k_cache", dt), _ptr(v_cache, "v_cache", dt), cap, _ptr(out, "out", dt),
+        _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _stream(stream, q_pre.device))
+    _check(st, "olmo3_attn_decode_ragged")
 
 
 def workspace(mode: int, B: int, T: int, H: int, G: int, d: int, layer_type: int,

@@ -186,7 +186,8 @@ int olmo3_kv_append(int B, int T, int G, int d, int window, int layer_type,
   a.v_cache = v_cache;
   a.cap = cache_capacity;
   a.pos_offset = pos_offset;
-  a.cache_first_t = layer_type == OLMO3_LAYER_SLIDING ? std::max<int64_t>(0, (int64_t)T - window) : 0;
+  a.keep_last = layer_type == OLMO3_LAYER_SLIDING ? window : INT64_MAX;
+  a.store = 1;
   a.B = B;
   a.T = T;
   a.H = G;
@@ -202,18 +203,20 @@ static int validate_attn(int B, int T, int H, int G, int d, int window, int laye
                          const void* q_pre, const void* k_pre, const void* v, const void* q_gain,
                          const void* k_gain, void* k_cache, void* v_cache,
                          int64_t cache_capacity, void* out, void* workspace,
-                         size_t workspace_bytes, size_t ws_needed) {
+                         size_t workspace_bytes, size_t ws_needed, int cache_B,
+                         int64_t last_pos) {
   int st = check_common(B, T, H, G, d, window, layer_type, dtype, rope, eps, pos_offset);
   if (st) return st;
   const void* ptrs[] = {q_pre, k_pre, v, q_gain, k_gain, k_cache, v_cache, out};
   for (const void* p : ptrs)
     if (!p || !aligned16(p)) return OLMO3_ERR_INVALID_ARG;
-  st = check_capacity(layer_type, window, cache_capacity, pos_offset + T - 1);
+  st = check_capacity(layer_type, window, cache_capacity, last_pos);
   if (st) return st;
   if (!workspace || !aligned16(workspace) || workspace_bytes < ws_needed) return OLMO3_ERR_WORKSPACE;
   const size_t es = elem_size(dtype);
-  const Span kc = span(k_cache, (size_t)B * G * cache_capacity * d * es);
-  const Span vc = span(v_cache, (size_t)B * G * cache_capacity * d * es);
+  if (cache_B < 1 || (int64_t)cache_B * G > 65535 * 64) return OLMO3_ERR_INVALID_ARG;
+  const Span kc = span(k_cache, (size_t)cache_B * G * cache_capacity * d * es);
+  const Span vc = span(v_cache, (size_t)cache_B * G * cache_capacity * d * es);
   const Span o = span(out, (size_t)B * T * H * d * es);
   const Span ws = span(workspace, ws_needed);
   const Span in[] = {span(q_pre, (size_t)B * T * H * d * es), span(k_pre, (size_t)B * T * G * d * es),
@@ -226,6 +229,142 @@ static int validate_attn(int B, int T, int H, int G, int d, int window, int laye
     if (overlap(s, kc) || overlap(s, vc) || overlap(s, o) || overlap(s, ws)) return OLMO3_ERR_INVALID_ARG;
   return OLMO3_OK;
 }
+
+}  // extern "C"
+
+namespace {
+
+// The sequences of one prefill call.  Uniform: B sequences of T rows at
+// positions pos_offset .. pos_offset+T-1.  Packed: B sequences in n_rows
+// rows, sequence b at rows cu_seqlens[b] .. cu_seqlens[b+1]-1 and positions
+// from pos_offsets[b] (device arrays), at most T = max_len rows each.
+struct PrefillShape {
+  int B, T;
+  int64_t n_rows;
+  int64_t pos_offset;
+  const int32_t* cu_seqlens;
+  const int32_t* pos_offsets;
+};
+
+int prefill_impl(int phases, const PrefillShape& sh, int H, int G, int d, int window,
+                 int layer_type, const olmo3_rope* rope, float eps, int dtype, const void* q_pre,
+                 const void* k_pre, const void* v, const void* q_gain, const void* k_gain,
+                 void* k_cache, void* v_cache, int64_t cache_capacity, void* out,
+                 void* workspace, hipStream_t s) {
+  const bool packed = sh.cu_seqlens != nullptr;
+  const bool sliding = layer_type == OLMO3_LAYER_SLIDING;
+  const int B = sh.B, T = sh.T;
+  const int64_t N = sh.n_rows;
+  // A chunk on a sliding layer attends to the ring's earlier positions, and
+  // its own keys would overwrite ring slots that its first queries still
+  // read: such a chunk is stored in the ring only after the attention.  A
+  // packed call may hold such chunks in any sequence.
+  const bool ring_after = sliding && (packed || sh.pos_offset > 0);
+  const size_t es = elem_size(dtype);
+  char* ws = (char*)workspace;
+  void* q_rot = ws;
+  void* k_rot = sliding ? ws + align_up((size_t)N * H * d * es) : nullptr;
+
+  RopeTable table;
+  rope_table(rope, layer_type, d, &table);
+  PrologueArgs p = {};
+  p.q_pre = q_pre;
+  p.k_pre = k_pre;
+  p.v = v;
+  p.q_gain = q_gain;
+  p.k_gain = k_gain;
+  p.q_out = q_rot;
+  // rotated keys: [B][G][T][d], or [G][rows][d] when packed
+  p.k_out = k_rot;
+  p.k_sb = packed ? 0 : (int64_t)G * T * d;
+  p.k_sg = (packed ? N : (int64_t)T) * d;
+  p.k_st = d;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.cap = cache_capacity;
+  p.pos_offset = sh.pos_offset;
+  p.keep_last = sliding ? window : INT64_MAX;  // a ring keeps the last `window`
+  p.store = !ring_after;
+  p.seq_pos = sh.pos_offsets;
+  p.cu_seqlens = sh.cu_seqlens;
+  p.n_rows = N;
+  p.B = B;
+  p.T = T;
+  p.H = H;
+  p.G = G;
+  p.window = window;
+  p.sliding = sliding;
+  p.eps = eps;
+  int st;
+  if (phases & OLMO3_PHASE_PROLOGUE) {
+    st = hip_status(launch_prologue(p, table, dtype, d, s));
+    if (st) return st;
+  }
+  if (!(phases & OLMO3_PHASE_ATTENTION)) return OLMO3_OK;
+
+  AttnArgs a = {};
+  a.q = q_rot;
+  if (sliding) {
+    // the chunk: rotated keys from the workspace, values from the input;
+    // earlier positions (if any) from the ring
+    a.k = k_rot;
+    a.k_sb = p.k_sb;
+    a.k_sg = p.k_sg;
+    a.k_sr = d;
+    a.v = v;
+    a.v_sb = packed ? 0 : (int64_t)T * G * d;
+    a.v_sg = d;
+    a.v_sr = (int64_t)G * d;
+    a.main_pos0 = sh.pos_offset;
+    a.main_packed = packed;
+    if (ring_after) {
+      a.kp = k_cache;
+      a.vp = v_cache;
+      a.p_sb = (int64_t)G * cache_capacity * d;
+      a.p_sg = cache_capacity * d;
+      a.p_sr = d;
+      a.ring = window;
+    }
+  } else {
+    // the linear cache now holds every position up to the chunk's last
+    a.k = k_cache;
+    a.v = v_cache;
+    a.k_sb = a.v_sb = (int64_t)G * cache_capacity * d;
+    a.k_sg = a.v_sg = cache_capacity * d;
+    a.k_sr = a.v_sr = d;
+    a.main_pos0 = 0;
+  }
+  a.out = out;
+  a.B = B;
+  a.Tq = T;
+  a.H = H;
+  a.G = G;
+  a.n_keys = sh.pos_offset + T;
+  a.q_pos0 = sh.pos_offset;
+  a.window = window;
+  a.sliding = sliding;
+  a.all_visible = 0;
+  a.scale_log2 = scale_log2(d);
+  a.cu_seqlens = sh.cu_seqlens;
+  a.seq_pos = sh.pos_offsets;
+  a.n_rows = N;
+  a.key_limit = sliding ? kMaxPrefillPositions : cache_capacity;
+  st = hip_status(use_mfma(dtype, d) ? launch_prefill_mfma(a, s)
+                                     : launch_attn_generic(a, dtype, d, s));
+  if (st || !ring_after) return st;
+  // store the chunk's kept positions in the ring (keys normalised and rotated
+  // again from k_pre: the same arithmetic, so the same bits)
+  PrologueArgs r = p;
+  r.q_pre = nullptr;
+  r.q_out = nullptr;
+  r.k_out = nullptr;
+  r.store = 1;
+  return hip_status(launch_prologue(r, table, dtype, d, s));
+}
+
+}  // namespace
+
+extern "C" {
 
 int olmo3_attn_prefill_phases(int phases, int B, int T, int H, int G, int d, int window,
                               int layer_type, const olmo3_rope* rope, float eps,
@@ -240,108 +379,39 @@ int olmo3_attn_prefill_phases(int phases, int B, int T, int H, int G, int d, int
                           : 0;
   int st = validate_attn(B, T, H, G, d, window, layer_type, rope, eps, pos_offset, dtype, q_pre,
                          k_pre, v, q_gain, k_gain, k_cache, v_cache, cache_capacity, out,
-                         workspace, workspace_bytes, need);
+                         workspace, workspace_bytes, need, B, pos_offset + T - 1);
   if (st) return st;
   // positions are 32-bit inside the prefill kernels
   if (pos_offset + T > kMaxPrefillPositions) return OLMO3_ERR_UNSUPPORTED;
+  const PrefillShape sh = {B, T, (int64_t)B * T, pos_offset, nullptr, nullptr};
+  return prefill_impl(phases, sh, H, G, d, window, layer_type, rope, eps, dtype, q_pre, k_pre, v,
+                      q_gain, k_gain, k_cache, v_cache, cache_capacity, out, workspace,
+                      (hipStream_t)stream);
+}
 
-  const hipStream_t s = (hipStream_t)stream;
-  const bool sliding = layer_type == OLMO3_LAYER_SLIDING;
-  // A chunk on a sliding layer attends to the ring's earlier positions, and
-  // its own keys would overwrite ring slots that its first queries still
-  // read: such a chunk is stored in the ring only after the attention.
-  const bool ring_after = sliding && pos_offset > 0;
-  const size_t es = elem_size(dtype);
-  char* ws = (char*)workspace;
-  void* q_rot = ws;
-  void* k_rot = sliding ? ws + align_up((size_t)B * T * H * d * es) : nullptr;
-
-  RopeTable table;
-  rope_table(rope, layer_type, d, &table);
-  PrologueArgs p = {};
-  p.q_pre = q_pre;
-  p.k_pre = k_pre;
-  p.v = v;
-  p.q_gain = q_gain;
-  p.k_gain = k_gain;
-  p.q_out = q_rot;
-  p.k_out = k_rot;
-  p.k_sb = (int64_t)G * T * d;
-  p.k_sg = (int64_t)T * d;
-  p.k_st = d;
-  p.k_cache = k_cache;
-  p.v_cache = v_cache;
-  p.cap = cache_capacity;
-  p.pos_offset = pos_offset;
-  // on a ring only the last `window` positions of the chunk are kept
-  const int64_t first_kept = sliding ? std::max<int64_t>(0, (int64_t)T - window) : 0;
-  p.cache_first_t = ring_after ? T : first_kept;
-  p.B = B;
-  p.T = T;
-  p.H = H;
-  p.G = G;
-  p.window = window;
-  p.sliding = sliding;
-  p.eps = eps;
-  if (phases & OLMO3_PHASE_PROLOGUE) {
-    st = hip_status(launch_prologue(p, table, dtype, d, s));
-    if (st) return st;
-  }
-  if (!(phases & OLMO3_PHASE_ATTENTION)) return OLMO3_OK;
-
-  AttnArgs a = {};
-  a.q = q_rot;
-  if (sliding) {
-    // the chunk: rotated keys from the workspace [B][G][T][d], values from
-    // the input; earlier positions (if any) from the ring
-    a.k = k_rot;
-    a.k_sb = (int64_t)G * T * d;
-    a.k_sg = (int64_t)T * d;
-    a.k_sr = d;
-    a.v = v;
-    a.v_sb = (int64_t)T * G * d;
-    a.v_sg = d;
-    a.v_sr = (int64_t)G * d;
-    a.main_pos0 = pos_offset;
-    if (pos_offset > 0) {
-      a.kp = k_cache;
-      a.vp = v_cache;
-      a.p_sb = (int64_t)G * cache_capacity * d;
-      a.p_sg = cache_capacity * d;
-      a.p_sr = d;
-      a.ring = window;
-    }
-  } else {
-    // the linear cache now holds positions 0 .. pos_offset+T-1 at their slots
-    a.k = k_cache;
-    a.v = v_cache;
-    a.k_sb = a.v_sb = (int64_t)G * cache_capacity * d;
-    a.k_sg = a.v_sg = cache_capacity * d;
-    a.k_sr = a.v_sr = d;
-    a.main_pos0 = 0;
-  }
-  a.out = out;
-  a.B = B;
-  a.Tq = T;
-  a.H = H;
-  a.G = G;
-  a.n_keys = pos_offset + T;
-  a.q_pos0 = pos_offset;
-  a.window = window;
-  a.sliding = sliding;
-  a.all_visible = 0;
-  a.scale_log2 = scale_log2(d);
-  st = hip_status(use_mfma(dtype, d) ? launch_prefill_mfma(a, s)
-                                     : launch_attn_generic(a, dtype, d, s));
-  if (st || !ring_after) return st;
-  // store the chunk's kept positions in the ring (keys normalised and rotated
-  // again from k_pre: the same arithmetic, so the same bits)
-  PrologueArgs r = p;
-  r.q_pre = nullptr;
-  r.q_out = nullptr;
-  r.k_out = nullptr;
-  r.cache_first_t = first_kept;
-  return hip_status(launch_prologue(r, table, dtype, d, s));
+int olmo3_attn_prefill_ragged(int B, int n_tokens, int max_len, int64_t max_end, int H, int G,
+                              int d, int window, int layer_type, const olmo3_rope* rope,
+                              float eps, const int32_t* cu_seqlens, const int32_t* pos_offsets,
+                              int dtype, const void* q_pre, const void* k_pre, const void* v,
+                              const void* q_gain, const void* k_gain, void* k_cache,
+                              void* v_cache, int64_t cache_capacity, void* out, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  if (B < 1 || n_tokens < 1 || max_len < 1 || max_len > n_tokens || max_end < max_len)
+    return OLMO3_ERR_INVALID_ARG;
+  if (!cu_seqlens || ((uintptr_t)cu_seqlens & 3) || ((uintptr_t)pos_offsets & 3))
+    return OLMO3_ERR_INVALID_ARG;
+  const size_t need = (H > 0 && G > 0 && d > 0) ? prefill_ws(1, n_tokens, H, G, d, layer_type, dtype)
+                                                : 0;
+  // the rows as one sequence for the input sizes; the caches hold B sequences
+  int st = validate_attn(1, n_tokens, H, G, d, window, layer_type, rope, eps, 0, dtype, q_pre,
+                         k_pre, v, q_gain, k_gain, k_cache, v_cache, cache_capacity, out,
+                         workspace, workspace_bytes, need, B, max_end - 1);
+  if (st) return st;
+  if (max_end > kMaxPrefillPositions) return OLMO3_ERR_UNSUPPORTED;
+  const PrefillShape sh = {B, max_len, n_tokens, 0, cu_seqlens, pos_offsets};
+  return prefill_impl(OLMO3_PHASE_PROLOGUE | OLMO3_PHASE_ATTENTION, sh, H, G, d, window,
+                      layer_type, rope, eps, dtype, q_pre, k_pre, v, q_gain, k_gain, k_cache,
+                      v_cache, cache_capacity, out, workspace, (hipStream_t)stream);
 }
 
 int olmo3_attn_prefill(int B, int T, int H, int G, int d, int window, int layer_type,
@@ -355,23 +425,17 @@ int olmo3_attn_prefill(int B, int T, int H, int G, int d, int window, int layer_
                                    workspace, workspace_bytes, stream);
 }
 
-int olmo3_attn_decode_phases(int phases, int B, int H, int G, int d, int window, int layer_type,
-                             const olmo3_rope* rope, float eps, int64_t pos, int dtype,
-                             const void* q_pre, const void* k_pre, const void* v,
-                             const void* q_gain, const void* k_gain, void* k_cache,
-                             void* v_cache, int64_t cache_capacity, void* out, void* workspace,
-                             size_t workspace_bytes, void* stream) {
-  if (phases <= 0 || (phases & ~(OLMO3_PHASE_PROLOGUE | OLMO3_PHASE_ATTENTION | OLMO3_PHASE_MERGE)))
-    return OLMO3_ERR_INVALID_ARG;
-  const size_t need = (B > 0 && H > 0 && G > 0 && d > 0 && G <= H && cache_capacity > 0)
-                          ? decode_ws(B, H, G, d, layer_type, window, dtype, cache_capacity)
-                          : 0;
-  int st = validate_attn(B, 1, H, G, d, window, layer_type, rope, eps, pos, dtype, q_pre, k_pre,
-                         v, q_gain, k_gain, k_cache, v_cache, cache_capacity, out, workspace,
-                         workspace_bytes, need);
-  if (st) return st;
+}  // extern "C"
 
-  const hipStream_t s = (hipStream_t)stream;
+namespace {
+
+// Decode of one token per sequence: at position `pos` for every sequence, or
+// at positions[b] (device array, each at most max_pos) when positions is set.
+int decode_impl(int phases, int B, int H, int G, int d, int window, int layer_type,
+                const olmo3_rope* rope, float eps, int64_t pos, const int32_t* positions,
+                int64_t max_pos, int dtype, const void* q_pre, const void* k_pre, const void* v,
+                const void* q_gain, const void* k_gain, void* k_cache, void* v_cache,
+                int64_t cache_capacity, void* out, void* workspace, hipStream_t s) {
   const bool sliding = layer_type == OLMO3_LAYER_SLIDING;
   const size_t es = elem_size(dtype);
   char* ws = (char*)workspace;
@@ -390,7 +454,9 @@ int olmo3_attn_decode_phases(int phases, int B, int H, int G, int d, int window,
   p.v_cache = v_cache;
   p.cap = cache_capacity;
   p.pos_offset = pos;
-  p.cache_first_t = 0;
+  p.keep_last = INT64_MAX;
+  p.store = 1;
+  p.seq_pos = positions;
   p.B = B;
   p.T = 1;
   p.H = H;
@@ -398,12 +464,15 @@ int olmo3_attn_decode_phases(int phases, int B, int H, int G, int d, int window,
   p.window = window;
   p.sliding = sliding;
   p.eps = eps;
+  int st;
   if (phases & OLMO3_PHASE_PROLOGUE) {
     st = hip_status(launch_prologue(p, table, dtype, d, s));
     if (st) return st;
   }
 
-  const int64_t n = sliding ? std::min<int64_t>(pos + 1, window) : pos + 1;
+  // rows read: the filled ring slots or slots 0 .. pos (the largest over the
+  // batch when positions differ; each sequence then reads its own count)
+  const int64_t n = sliding ? std::min<int64_t>(max_pos + 1, window) : max_pos + 1;
   if (decode_uses_split(dtype, d, H, G)) {
     DecodeArgs a = {};
     a.q = q_rot;
@@ -420,6 +489,9 @@ int olmo3_attn_decode_phases(int phases, int B, int H, int G, int d, int window,
     a.H = H;
     a.G = G;
     a.scale_log2 = scale_log2(d);
+    a.seq_pos = positions;
+    a.window = window;
+    a.sliding = sliding;
     if (phases & OLMO3_PHASE_ATTENTION) {
       st = hip_status(launch_decode_split(a, s));
       if (st) return st;
@@ -446,7 +518,54 @@ int olmo3_attn_decode_phases(int phases, int B, int H, int G, int d, int window,
   a.sliding = sliding;
   a.all_visible = 1;
   a.scale_log2 = scale_log2(d);
+  a.seq_pos = positions;
+  a.key_limit = cache_capacity;
   return hip_status(launch_attn_generic(a, dtype, d, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+int olmo3_attn_decode_phases(int phases, int B, int H, int G, int d, int window, int layer_type,
+                             const olmo3_rope* rope, float eps, int64_t pos, int dtype,
+                             const void* q_pre, const void* k_pre, const void* v,
+                             const void* q_gain, const void* k_gain, void* k_cache,
+                             void* v_cache, int64_t cache_capacity, void* out, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  if (phases <= 0 || (phases & ~(OLMO3_PHASE_PROLOGUE | OLMO3_PHASE_ATTENTION | OLMO3_PHASE_MERGE)))
+    return OLMO3_ERR_INVALID_ARG;
+  const size_t need = (B > 0 && H > 0 && G > 0 && d > 0 && G <= H && cache_capacity > 0)
+                          ? decode_ws(B, H, G, d, layer_type, window, dtype, cache_capacity)
+                          : 0;
+  int st = validate_attn(B, 1, H, G, d, window, layer_type, rope, eps, pos, dtype, q_pre, k_pre,
+                         v, q_gain, k_gain, k_cache, v_cache, cache_capacity, out, workspace,
+                         workspace_bytes, need, B, pos);
+  if (st) return st;
+  return decode_impl(phases, B, H, G, d, window, layer_type, rope, eps, pos, nullptr, pos, dtype,
+                     q_pre, k_pre, v, q_gain, k_gain, k_cache, v_cache, cache_capacity, out,
+                     workspace, (hipStream_t)stream);
+}
+
+int olmo3_attn_decode_ragged(int B, int H, int G, int d, int window, int layer_type,
+                             const olmo3_rope* rope, float eps, const int32_t* positions,
+                             int64_t max_pos, int dtype, const void* q_pre, const void* k_pre,
+                             const void* v, const void* q_gain, const void* k_gain,
+                             void* k_cache, void* v_cache, int64_t cache_capacity, void* out,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  if (!positions || ((uintptr_t)positions & 3) || max_pos < 0 || max_pos > INT32_MAX)
+    return OLMO3_ERR_INVALID_ARG;
+  const size_t need = (B > 0 && H > 0 && G > 0 && d > 0 && G <= H && cache_capacity > 0)
+                          ? decode_ws(B, H, G, d, layer_type, window, dtype, cache_capacity)
+                          : 0;
+  int st = validate_attn(B, 1, H, G, d, window, layer_type, rope, eps, max_pos, dtype, q_pre,
+                         k_pre, v, q_gain, k_gain, k_cache, v_cache, cache_capacity, out,
+                         workspace, workspace_bytes, need, B, max_pos);
+  if (st) return st;
+  return decode_impl(OLMO3_PHASE_PROLOGUE | OLMO3_PHASE_ATTENTION | OLMO3_PHASE_MERGE, B, H, G,
+                     d, window, layer_type, rope, eps, 0, positions, max_pos, dtype, q_pre, k_pre,
+                     v, q_gain, k_gain, k_cache, v_cache, cache_capacity, out, workspace,
+                     (hipStream_t)stream);
 }
 
 int olmo3_attn_decode(int B, int H, int G, int d, int window, int layer_type,

@@ -23,25 +23,41 @@ template <typename T, int D>
 __global__ __launch_bounds__(64) void attn_generic_kernel(AttnArgs a) {
   const int t = blockIdx.x * 64 + threadIdx.x;
   const int h = blockIdx.y, b = blockIdx.z;
-  if (t >= a.Tq) return;
+  // this sequence: query rows row0 .. row0 + len - 1 at positions qpos0 ..
+  int64_t row0 = (int64_t)b * a.Tq, len = a.Tq, qpos0 = a.q_pos0, n_keys = a.n_keys;
+  if (a.cu_seqlens) {
+    const int64_t c0 = min(max((int64_t)a.cu_seqlens[b], (int64_t)0), a.n_rows);
+    const int64_t c1 = min(max((int64_t)a.cu_seqlens[b + 1], c0), a.n_rows);
+    row0 = c0;
+    len = min(c1 - c0, (int64_t)a.Tq);
+    qpos0 = a.seq_pos ? max((int64_t)a.seq_pos[b], (int64_t)0) : 0;
+    if (qpos0 + len > a.key_limit) return;
+    n_keys = qpos0 + len;
+  } else if (a.all_visible && a.seq_pos) {
+    // decode, per-sequence positions: rows of the ring or the linear cache
+    const int64_t p = max((int64_t)a.seq_pos[b], (int64_t)0);
+    n_keys = min(a.sliding ? min(p + 1, (int64_t)a.window) : p + 1, a.key_limit);
+  }
+  if (t >= len) return;
   const int g = h / (a.H / a.G);
-  const T* qp = (const T*)a.q + ((int64_t)(b * a.Tq + t) * a.H + h) * D;
+  const T* qp = (const T*)a.q + ((row0 + t) * a.H + h) * D;
   float q[D], o[D];
 #pragma unroll
   for (int e = 0; e < D; ++e) {
     q[e] = (float)qp[e] * a.scale_log2;
     o[e] = 0.f;
   }
-  const int64_t tpos = a.q_pos0 + t;
+  const int64_t tpos = qpos0 + t;
   // positions [p0, p1) when masked; main rows [0, n_keys) when all visible
-  int64_t p0 = 0, p1 = a.n_keys;
+  int64_t p0 = 0, p1 = n_keys;
   if (!a.all_visible) {
-    p1 = min(tpos + 1, a.n_keys);
+    p1 = min(tpos + 1, n_keys);
     if (a.sliding) p0 = max(tpos - a.window + 1, (int64_t)0);
   }
-  const int64_t main0 = a.all_visible ? 0 : a.main_pos0;
-  const T* kb = (const T*)a.k + b * a.k_sb + g * a.k_sg;
-  const T* vb = (const T*)a.v + b * a.v_sb + g * a.v_sg;
+  const bool packed_main = a.cu_seqlens && a.main_packed;
+  const int64_t main0 = a.all_visible ? 0 : (a.cu_seqlens ? (packed_main ? qpos0 : 0) : a.main_pos0);
+  const T* kb = (const T*)a.k + (packed_main ? row0 * a.k_sr : b * a.k_sb) + g * a.k_sg;
+  const T* vb = (const T*)a.v + (packed_main ? row0 * a.v_sr : b * a.v_sb) + g * a.v_sg;
   const T* kpb = a.kp ? (const T*)a.kp + b * a.p_sb + g * a.p_sg : nullptr;
   const T* vpb = a.kp ? (const T*)a.vp + b * a.p_sb + g * a.p_sg : nullptr;
   float m = -1e30f, l = 0.f;
@@ -67,7 +83,7 @@ __global__ __launch_bounds__(64) void attn_generic_kernel(AttnArgs a) {
     m = mn;
   }
   const float inv = 1.0f / l;
-  T* op = (T*)a.out + ((int64_t)(b * a.Tq + t) * a.H + h) * D;
+  T* op = (T*)a.out + ((row0 + t) * a.H + h) * D;
 #pragma unroll
   for (int e = 0; e < D; ++e) op[e] = (T)(o[e] * inv);
 }
@@ -87,8 +103,14 @@ __global__ __launch_bounds__(dec::kThreads) void decode_split_kernel(DecodeArgs 
   const int sp = blockIdx.x % a.splits;
   const int bg = blockIdx.x / a.splits;
   const int g = bg % a.G, b = bg / a.G;
-  const int64_t r0 = (int64_t)sp * a.rows_per_split;
-  const int64_t r1 = min(a.n, r0 + a.rows_per_split);
+  int64_t n = a.n, rps = a.rows_per_split;
+  if (a.seq_pos) {  // this sequence's rows, split evenly
+    const int64_t p = max((int64_t)a.seq_pos[b], (int64_t)0);
+    n = min(a.sliding ? min(p + 1, (int64_t)a.window) : p + 1, a.cap);
+    rps = ((n + a.splits - 1) / a.splits + kRowsPerIter - 1) / kRowsPerIter * kRowsPerIter;
+  }
+  const int64_t r0 = (int64_t)sp * rps;
+  const int64_t r1 = min(n, r0 + rps);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int li = lane & 15;
   const int grp = tid >> 4;

@@ -8,24 +8,37 @@
 
 namespace olmo3 {
 
-// QK-norm + RoPE + cache append over B*T token rows.
+// QK-norm + RoPE + cache append over token rows.
+//   uniform batch: B*T rows, row = b*T + t, position pos_offset + t (or
+//     seq_pos[b] + t when seq_pos is set: per-sequence positions);
+//   packed (cu_seqlens set): n_rows rows, sequence b owns rows
+//     cu_seqlens[b] .. cu_seqlens[b+1]-1, t = row - cu_seqlens[b], position
+//     (seq_pos ? seq_pos[b] : 0) + t.
+// Row t of a sequence of `len` rows is stored in the cache when `store` is
+// set and len - t <= keep_last (a ring keeps the last `window` rows), at slot
+// pos (linear; skipped if pos >= cap) or pos mod window (ring).
 struct PrologueArgs {
-  const void* q_pre;   // [B][T][H*d] or null (keys/values only)
-  const void* k_pre;   // [B][T][G*d]
-  const void* v;       // [B][T][G*d]
+  const void* q_pre;   // [rows][H*d] or null (keys/values only)
+  const void* k_pre;   // [rows][G*d]
+  const void* v;       // [rows][G*d]
   const void* q_gain;  // [H*d]
   const void* k_gain;  // [G*d]
-  void* q_out;         // [B][T][H][d] rotated queries (when q_pre is set)
-  void* k_out;         // rotated keys at b*k_sb + g*k_sg + t*k_st, or null
+  void* q_out;         // [rows][H][d] rotated queries (when q_pre is set)
+  void* k_out;         // rotated keys at b*k_sb + g*k_sg + t*k_st (packed:
+                       // g*k_sg + row*k_st), or null
   int64_t k_sb, k_sg, k_st;
   void* k_cache;       // [B][G][cap][d]
   void* v_cache;
   int64_t cap;
   int64_t pos_offset;
-  int64_t cache_first_t;  // rows t >= this are stored in the cache
+  int64_t keep_last;
+  const int32_t* seq_pos;     // [B] device, or null
+  const int32_t* cu_seqlens;  // [B+1] device, or null
+  int64_t n_rows;             // packed rows
   int B, T, H, G;
   int window;
   int sliding;
+  int store;
   float eps;
 };
 
@@ -62,6 +75,22 @@ struct AttnArgs {
   int sliding;
   int all_visible;
   float scale_log2;  // log2(e) / sqrt(d)
+  // Packed batch (cu_seqlens set): sequence b's queries are rows
+  // cu_seqlens[b] .. cu_seqlens[b+1]-1 (at most Tq of them, rows < n_rows)
+  // of q and out, at positions seq_pos[b] + t (0 + t without seq_pos); its
+  // keys are positions 0 .. seq_pos[b] + len - 1: with main_packed the
+  // positions from seq_pos[b] on are its packed rows (k_sb, v_sb unused) and
+  // earlier ones come from the prefix ring; otherwise main row = position in
+  // sequence b's buffer.  A sequence whose keys would pass key_limit is
+  // skipped.  Decode (all_visible) with seq_pos: sequence b
+  // reads main rows 0 .. n_b - 1, n_b = min(seq_pos[b]+1, window) on a ring,
+  // seq_pos[b]+1 on a linear cache, at most key_limit.
+  const int32_t* cu_seqlens;
+  const int32_t* seq_pos;
+  int64_t n_rows;
+  int64_t key_limit;
+  int main_packed;  // packed batch: main rows are the sequence's packed rows
+                    // (main_pos0 = its first position) instead of b*k_sb rows
 };
 
 // Flash-style prefill, d = 128, bf16, MFMA.  Requires n_keys == q_pos0 + Tq
@@ -84,6 +113,12 @@ struct DecodeArgs {
   void* out;           // [B][H*d]
   int B, H, G, splits;
   float scale_log2;
+  // per-sequence positions (device [B]) or null: sequence b reads
+  // n_b = min(seq_pos[b]+1, window) (ring) or seq_pos[b]+1 (linear) rows,
+  // at most cap, split evenly over the `splits` workgroups
+  const int32_t* seq_pos;
+  int window;
+  int sliding;
 };
 int decode_splits(int B, int G, int64_t n);
 hipError_t launch_decode_split(const DecodeArgs& a, hipStream_t s);

@@ -81,7 +81,9 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const char* p) {
 
 // kPrefix: keys before main_pos0 come from a ring (chunked prefill on a
 // sliding layer); without it every key is a main row (main_pos0 == 0).
-template <bool kPrefix>
+// kPacked: sequences of different lengths and offsets packed row after row
+// (cu_seqlens, seq_pos); a workgroup past its sequence's end exits.
+template <bool kPrefix, bool kPacked>
 __global__ __launch_bounds__(256, 2) void prefill_d128_kernel(AttnArgs a) {
   using namespace pf;
   __shared__ __attribute__((aligned(16))) char smem[4 * kTileBytes];
@@ -91,10 +93,21 @@ __global__ __launch_bounds__(256, 2) void prefill_d128_kernel(AttnArgs a) {
   const int n_qblk = (a.Tq + kBQ - 1) / kBQ;
   const Work w = work_of(blockIdx.x, gridDim.x, n_qblk, a.H);
   const int g = w.h / (a.H / a.G);
-  // positions: queries q_pos0 .. q_pos0 + Tq - 1, keys 0 .. n_keys - 1
-  const int qpos0 = (int)a.q_pos0;
+  // this sequence: query rows row0 .. row0 + len - 1 at positions qpos0 ..,
+  // keys at positions 0 .. n_keys - 1
+  int64_t row0 = (int64_t)w.b * a.Tq;
+  int len = a.Tq, qpos0 = (int)a.q_pos0, n_keys = (int)a.n_keys;
+  if constexpr (kPacked) {
+    const int64_t c0 = min(max((int64_t)a.cu_seqlens[w.b], (int64_t)0), a.n_rows);
+    const int64_t c1 = min(max((int64_t)a.cu_seqlens[w.b + 1], c0), a.n_rows);
+    row0 = c0;
+    len = (int)min(c1 - c0, (int64_t)a.Tq);
+    qpos0 = a.seq_pos ? max(a.seq_pos[w.b], 0) : 0;
+    if (w.qb * kBQ >= len || (int64_t)qpos0 + len > a.key_limit) return;
+    n_keys = qpos0 + len;
+  }
   const int q0 = qpos0 + w.qb * kBQ;
-  const int q1 = min(q0 + kBQ, qpos0 + a.Tq);
+  const int q1 = min(q0 + kBQ, qpos0 + len);
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int col = lane & 31, half = lane >> 5;
   const int tq = lane_query(q0, wave, lane);
@@ -103,7 +116,7 @@ __global__ __launch_bounds__(256, 2) void prefill_d128_kernel(AttnArgs a) {
   // Q^T operand: lane holds query tq, d = 16*ks + 8*half .. +7
   bf16x8 qop[8];
   {
-    const bf16* qrow = (const bf16*)a.q + ((int64_t)(w.b * a.Tq + tql) * a.H + w.h) * kD;
+    const bf16* qrow = (const bf16*)a.q + ((row0 + tql) * a.H + w.h) * kD;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) qop[ks] = *(const bf16x8*)(qrow + ks * 16 + half * 8);
   }
@@ -116,7 +129,6 @@ __global__ __launch_bounds__(256, 2) void prefill_d128_kernel(AttnArgs a) {
   // +3; lane l takes row 16 i + 4 w + l/16, stored column l mod 16, i.e.
   // logical column (l mod 16) ^ swizzle(row).  Positions past the last key
   // are clamped to it (such keys lie past every query of the block: masked).
-  const int n_keys = (int)a.n_keys;
   const int lrow = 4 * wave + (lane >> 4);  // row within each 16-row slab
   const int kcol = (lane & 15) ^ (lrow & 15);
   const int vcol = (lane & 15) ^ (4 * (lrow & 3));
@@ -124,11 +136,12 @@ __global__ __launch_bounds__(256, 2) void prefill_d128_kernel(AttnArgs a) {
   // whose 64 rows are consecutive rows of one source take the fast path;
   // the last tile (positions past n_keys) and, with a prefix, tiles that
   // cross the prefix/main boundary or the ring's wrap go row by row.
-  const bf16* kbase = (const bf16*)a.k + w.b * a.k_sb + g * a.k_sg;
-  const bf16* vbase = (const bf16*)a.v + w.b * a.v_sb + g * a.v_sg;
+  const bool packed_main = kPacked && a.main_packed;
+  const bf16* kbase = (const bf16*)a.k + (packed_main ? row0 * a.k_sr : w.b * a.k_sb) + g * a.k_sg;
+  const bf16* vbase = (const bf16*)a.v + (packed_main ? row0 * a.v_sr : w.b * a.v_sb) + g * a.v_sg;
   const int k_lane = lrow * (int)a.k_sr + kcol * 8;
   const int v_lane = lrow * (int)a.v_sr + vcol * 8;
-  const int main0 = kPrefix ? (int)a.main_pos0 : 0;
+  const int main0 = kPacked ? (packed_main ? qpos0 : 0) : (kPrefix ? (int)a.main_pos0 : 0);
   const int ring = kPrefix ? (int)a.ring : 1;
   const int64_t p_sr = a.p_sr;
   const bf16* kpbase = kPrefix ? (const bf16*)a.kp + w.b * a.p_sb + g * a.p_sg : nullptr;
@@ -321,7 +334,7 @@ __global__ __launch_bounds__(256, 2) void prefill_d128_kernel(AttnArgs a) {
   lsum += __shfl_xor(lsum, 32, kWave);
   const float inv = 1.0f / lsum;
   if (tq < q1) {
-    bf16* orow = (bf16*)a.out + ((int64_t)(w.b * a.Tq + (tq - qpos0)) * a.H + w.h) * kD;
+    bf16* orow = (bf16*)a.out + ((row0 + (tq - qpos0)) * a.H + w.h) * kD;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -366,10 +379,16 @@ __global__ __launch_bounds__(256) void probe_prefill_kernel(int T, int pos_offse
 hipError_t launch_prefill_mfma(const AttnArgs& a, hipStream_t s) {
   const int n_qblk = (a.Tq + pf::kBQ - 1) / pf::kBQ;
   const int blocks = n_qblk * a.H * a.B;
-  if (a.kp)
-    prefill_d128_kernel<true><<<blocks, 256, 0, s>>>(a);
-  else
-    prefill_d128_kernel<false><<<blocks, 256, 0, s>>>(a);
+  if (a.cu_seqlens) {
+    if (a.kp)
+      prefill_d128_kernel<true, true><<<blocks, 256, 0, s>>>(a);
+    else
+      prefill_d128_kernel<false, true><<<blocks, 256, 0, s>>>(a);
+  } else if (a.kp) {
+    prefill_d128_kernel<true, false><<<blocks, 256, 0, s>>>(a);
+  } else {
+    prefill_d128_kernel<false, false><<<blocks, 256, 0, s>>>(a);
+  }
   return hipGetLastError();
 }
 

@@ -1,4 +1,5 @@
-// Fused QK-norm + RoPE + KV-cache append (one wavefront per token).
+// Fused QK-norm + RoPE + KV-cache append (one wavefront per token), for a
+// uniform batch, per-sequence positions or packed sequences of any length.
 //
 // QK-norm: one RMS statistic over the token's whole query vector (H*d
 // features) and one over its whole key vector (G*d features), then a
@@ -108,6 +109,19 @@ __device__ __forceinline__ void norm_rope_row(const T* __restrict__ src, const T
   }
 }
 
+// Sequence of packed row `row`: the number of b >= 1 with cu[b] <= row
+// (cu[0] = 0), counted 64 entries at a time with a ballot; clamped to
+// [0, B-1].  Uniform across the wavefront.
+__device__ __forceinline__ int packed_sequence(const int32_t* cu, int B, int64_t row, int lane) {
+  int b = 0;
+  for (int j0 = 1; j0 <= B; j0 += kWave) {
+    const int j = j0 + lane;
+    const bool le = j <= B && (int64_t)cu[j] <= row;
+    b += __popcll(__ballot(le));
+  }
+  return min(b, B - 1);
+}
+
 template <typename T, int D>
 __global__ __launch_bounds__(kWave * kTokensPerBlock) void qknorm_rope_append_kernel(
     PrologueArgs a, RopeTable rope) {
@@ -115,15 +129,30 @@ __global__ __launch_bounds__(kWave * kTokensPerBlock) void qknorm_rope_append_ke
   constexpr int kVec = Io<T>::kVec;
   const int lane = threadIdx.x % kWave;
   const int64_t row = (int64_t)blockIdx.x * kTokensPerBlock + threadIdx.x / kWave;
-  if (row >= (int64_t)a.B * a.T) return;
-  const int b = (int)(row / a.T);
-  const int t = (int)(row % a.T);
-  const int64_t pos = a.pos_offset + t;
+  // (sequence, index in it, its length, absolute position) of this row
+  int b;
+  int64_t t, len, pos;
+  if (a.cu_seqlens) {
+    if (row >= a.n_rows) return;
+    b = packed_sequence(a.cu_seqlens, a.B, row, lane);
+    const int64_t first = a.cu_seqlens[b];
+    t = row - first;
+    len = (int64_t)a.cu_seqlens[b + 1] - first;
+    if (t < 0 || t >= len) return;  // inconsistent offsets: row belongs to no sequence
+    pos = (a.seq_pos ? (int64_t)a.seq_pos[b] : 0) + t;
+  } else {
+    if (row >= (int64_t)a.B * a.T) return;
+    b = (int)(row / a.T);
+    t = row % a.T;
+    len = a.T;
+    pos = (a.seq_pos ? (int64_t)a.seq_pos[b] : a.pos_offset) + t;
+  }
+  if (pos < 0) return;
 
   float cs[kVec], sn[kVec];
   rope_angles<T, D>(lane, pos, rope, cs, sn);
 
-  // queries -> q_out [B][T][H][D]
+  // queries -> q_out [rows][H][D]
   if (a.q_pre) {
     const T* src = (const T*)a.q_pre + row * a.H * D;
     T* qo = (T*)a.q_out + row * a.H * D;
@@ -132,8 +161,10 @@ __global__ __launch_bounds__(kWave * kTokensPerBlock) void qknorm_rope_append_ke
                         [&](int) -> T* { return nullptr; });
   }
 
-  const bool to_cache = t >= a.cache_first_t;
   const int64_t slot = a.sliding ? pos % a.window : pos;
+  const bool to_cache = a.store && len - t <= a.keep_last && slot < a.cap;
+  // rotated-key copy: [b][g][t] strided, or [g][row] for packed rows
+  const int64_t kb_idx = a.cu_seqlens ? 0 : b, kt_idx = a.cu_seqlens ? row : t;
 
   // keys -> optional strided copy (prefill workspace) and the cache slot
   {
@@ -143,7 +174,7 @@ __global__ __launch_bounds__(kWave * kTokensPerBlock) void qknorm_rope_append_ke
     norm_rope_row<T, D>(
         src, (const T*)a.k_gain, a.G, a.eps, lane, cs, sn, rope.mscale,
         [&](int h) -> T* {
-          return ko ? ko + b * a.k_sb + h * a.k_sg + (int64_t)t * a.k_st : nullptr;
+          return ko ? ko + kb_idx * a.k_sb + h * a.k_sg + kt_idx * a.k_st : nullptr;
         },
         [&](int h) -> T* {
           return to_cache ? kc + (((int64_t)b * a.G + h) * a.cap + slot) * D : nullptr;
@@ -165,7 +196,7 @@ __global__ __launch_bounds__(kWave * kTokensPerBlock) void qknorm_rope_append_ke
 
 template <typename T, int D>
 hipError_t launch_prologue_t(const PrologueArgs& a, const RopeTable& rope, hipStream_t s) {
-  const int64_t rows = (int64_t)a.B * a.T;
+  const int64_t rows = a.cu_seqlens ? a.n_rows : (int64_t)a.B * a.T;
   const int blocks = (int)((rows + kTokensPerBlock - 1) / kTokensPerBlock);
   qknorm_rope_append_kernel<T, D><<<blocks, kWave * kTokensPerBlock, 0, s>>>(a, rope);
   return hipGetLastError();

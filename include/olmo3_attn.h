@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define OLMO3_ABI_VERSION 2
+#define OLMO3_ABI_VERSION 3
 
 typedef enum olmo3_status {
   OLMO3_OK = 0,
@@ -160,6 +160,47 @@ int olmo3_attn_decode(int B, int H, int G, int d, int window, int layer_type,
                       void* k_cache, void* v_cache, int64_t cache_capacity,
                       void* out, void* workspace, size_t workspace_bytes,
                       void* stream);
+
+/* Ragged batches: several prompts served together ("Olmo-3 End-to-End
+ * Implementation", "Next Steps": batch processing), whose sequences differ in
+ * length and position.  Per-sequence values live in DEVICE int32 arrays (they stay
+ * on the GPU between steps); the host passes bounds that size the launch
+ * and the checks.  Device values that break the stated bounds leave the
+ * affected sequences' outputs and cache rows unspecified, but no kernel
+ * reads or writes outside the buffers the host arguments describe. */
+
+/* Ragged prefill: B sequences packed row after row.  Sequence b owns rows
+ * cu_seqlens[b] .. cu_seqlens[b+1]-1 of q_pre [n_tokens][H*d], k_pre and v
+ * [n_tokens][G*d] and out [n_tokens][H*d]; its tokens sit at positions
+ * pos_offsets[b] .. pos_offsets[b] + len_b - 1 (pos_offsets NULL: all 0) and
+ * attend, as in olmo3_attn_prefill, to the positions its cache
+ * k_cache[b] / v_cache[b] already holds and to each other.  Device arrays:
+ * cu_seqlens [B+1] nondecreasing from 0 to n_tokens with every len_b <=
+ * max_len; pos_offsets [B] >= 0 with pos_offsets[b] + len_b <= max_end.
+ * workspace: olmo3_workspace_bytes(OLMO3_MODE_PREFILL, 1, n_tokens, ...).
+ * Errors: as olmo3_attn_prefill with positions up to max_end - 1 (a linear
+ * cache needs max_end slots), plus INVALID_ARG for B, n_tokens or max_len
+ * < 1, max_len > n_tokens, max_end < max_len, a null or misaligned
+ * cu_seqlens, a misaligned pos_offsets. */
+int olmo3_attn_prefill_ragged(int B, int n_tokens, int max_len, int64_t max_end, int H, int G,
+                              int d, int window, int layer_type, const olmo3_rope* rope,
+                              float eps, const int32_t* cu_seqlens, const int32_t* pos_offsets,
+                              int dtype, const void* q_pre, const void* k_pre, const void* v,
+                              const void* q_gain, const void* k_gain, void* k_cache,
+                              void* v_cache, int64_t cache_capacity, void* out, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+/* Ragged decode: as olmo3_attn_decode, but sequence b's new token sits at
+ * positions[b] (device int32 [B], each in [0, max_pos]); each sequence reads
+ * its own min(positions[b]+1, window) ring slots or positions[b]+1 linear
+ * slots.  Errors: as olmo3_attn_decode at pos = max_pos, plus INVALID_ARG for
+ * a null or misaligned positions array or max_pos outside [0, 2^31). */
+int olmo3_attn_decode_ragged(int B, int H, int G, int d, int window, int layer_type,
+                             const olmo3_rope* rope, float eps, const int32_t* positions,
+                             int64_t max_pos, int dtype, const void* q_pre, const void* k_pre,
+                             const void* v, const void* q_gain, const void* k_gain,
+                             void* k_cache, void* v_cache, int64_t cache_capacity, void* out,
+                             void* workspace, size_t workspace_bytes, void* stream);
 
 /* Stage-by-stage variants, for callers that time or overlap the kernels of
  * one call.  `phases` is a bit set of:

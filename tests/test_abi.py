@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version():
-    assert A.olmo3_abi_version() == A.ABI_VERSION == 2
+    assert A.olmo3_abi_version() == A.ABI_VERSION == 3
 
 
 def test_layer_type_matches_oracle_bit_exact():
@@ -209,3 +209,56 @@ def test_phases_reject_bad_bits():
                                            1 << 30, None) == A.ERR_INVALID_ARG
         assert L.olmo3_attn_decode_phases(ph, 1, 2, 1, 128, 4, 0, r, 1e-6, 3, 0, *p[:7], 4, p[7], p[8],
                                           1 << 30, None) == A.ERR_INVALID_ARG
+
+
+def ragged_prefill_call(**kw):
+    a = dict(B=3, N=64, max_len=40, max_end=100, H=4, G=2, d=128, window=16, layer_type=0,
+             eps=1e-6, dtype=0, cap=16, cu=fake(9), pos=fake(10))
+    a.update(kw)
+    p = [fake(i) for i in range(9)]
+    r = ctypes.byref(A.Rope(theta=1e4).to_c())
+    return A.lib().olmo3_attn_prefill_ragged(
+        a["B"], a["N"], a["max_len"], a["max_end"], a["H"], a["G"], a["d"], a["window"],
+        a["layer_type"], r, a["eps"], a["cu"], a["pos"], a["dtype"], *p[:7], a["cap"], p[7], p[8],
+        1 << 34, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), A.ERR_INVALID_ARG),
+    (dict(N=0), A.ERR_INVALID_ARG),
+    (dict(max_len=0), A.ERR_INVALID_ARG),
+    (dict(max_len=65), A.ERR_INVALID_ARG),        # longer than all rows
+    (dict(max_end=39), A.ERR_INVALID_ARG),        # shorter than the longest sequence
+    (dict(cu=0), A.ERR_INVALID_ARG),
+    (dict(cu=fake(9) + 2), A.ERR_INVALID_ARG),    # misaligned device array
+    (dict(pos=fake(10) + 1), A.ERR_INVALID_ARG),
+    (dict(cap=17), A.ERR_CAPACITY),               # ring must equal window
+    (dict(layer_type=1, cap=99), A.ERR_CAPACITY),  # linear cache shorter than max_end
+    (dict(max_end=(1 << 30) + 1), A.ERR_UNSUPPORTED),
+    (dict(H=3), A.ERR_INVALID_ARG),
+])
+def test_ragged_prefill_rejects(kw, status):
+    assert ragged_prefill_call(**kw) == status
+
+
+def ragged_decode_call(**kw):
+    a = dict(B=3, H=4, G=2, d=128, window=16, layer_type=0, eps=1e-6, pos=fake(10), max_pos=50,
+             dtype=0, cap=16)
+    a.update(kw)
+    p = [fake(i) for i in range(9)]
+    r = ctypes.byref(A.Rope(theta=1e4).to_c())
+    return A.lib().olmo3_attn_decode_ragged(
+        a["B"], a["H"], a["G"], a["d"], a["window"], a["layer_type"], r, a["eps"], a["pos"],
+        a["max_pos"], a["dtype"], *p[:7], a["cap"], p[7], p[8], 1 << 34, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(pos=0), A.ERR_INVALID_ARG),
+    (dict(pos=fake(10) + 2), A.ERR_INVALID_ARG),
+    (dict(max_pos=-1), A.ERR_INVALID_ARG),
+    (dict(max_pos=1 << 31), A.ERR_INVALID_ARG),
+    (dict(layer_type=1, cap=50), A.ERR_CAPACITY),  # needs max_pos + 1 slots
+    (dict(B=0), A.ERR_INVALID_ARG),
+])
+def test_ragged_decode_rejects(kw, status):
+    assert ragged_decode_call(**kw) == status
