@@ -15,6 +15,7 @@ Workloads (synthetic, seeded, shaped like the OLMo 3 configurations):
   decode-stack  the same 32-layer stack decoding one token per sequence,
        B=16 at cache length 65,536: KV bytes read per step and per token of
        context (the per-layer-type cache of the page "Olmo 3 7B")
+  7b-e4m3  7B decode (B=32 at 65,536) against e4m3 caches (1-byte codes)
 
 Printed: one JSON line.  `value` is prefill TFLOP/s (algorithmic FLOPs of the
 allowed query/key pairs over the whole prefill call time); decode KV GB/s is
@@ -103,7 +104,10 @@ WORKLOADS = {
                  decode=None),
     "decode-stack": dict(name="olmo3-7b-decode-stack", prefill=None,
                          decode=dict(B=16, H=32, G=32, L=65536, layers=32)),
+    "7b-e4m3": dict(name="olmo3-7b-decode-e4m3", prefill=None,
+                    decode=dict(B=32, H=32, G=32, L=65536, e4m3=True)),
 }
+E4M3_SCALES = (1.0 / 16, 1.0 / 16)  # k_scale, v_scale of the e4m3 workload
 N_LAYERS_7B = 32
 NAIVE_BYTES_PER_TOKEN_7B = N_LAYERS_7B * 32 * 128 * 2 * 2  # every layer full: 524,288
 
@@ -211,26 +215,39 @@ def main():
             cap = WINDOW if sliding else L
             print(f"[bench] filling {'ring' if sliding else 'linear'} decode cache of layer {ell} "
                   f"[{Bd}, {Gd}, {cap}, {d}] x2", file=sys.stderr, flush=True)
-            kc, vc = synth.cache_fill(dseed, (ell if n_dec_layers else 100 + lt), Bd, Gd, cap, d,
-                                      device=dev, dtype=bf16)
+            e4m3 = dc.get("e4m3", False)
+            if e4m3:
+                kc, vc = synth.e4m3_cache_fill(dseed, 100 + lt, Bd, Gd, cap, d, device=dev)
+            else:
+                kc, vc = synth.cache_fill(dseed, (ell if n_dec_layers else 100 + lt), Bd, Gd, cap, d,
+                                          device=dev, dtype=bf16)
             x = synth.layer_inputs(dseed, (100 + ell if n_dec_layers else 200 + lt), Bd, 1, Hd, Gd, d,
                                    device=dev, dtype=bf16)
             q = x["q_pre"][:, 0].contiguous()
             k = x["k_pre"][:, 0].contiguous()
             v = x["v"][:, 0].contiguous()
             out = torch.empty_like(q)
-            ws = A.workspace(A.MODE_DECODE, Bd, 1, Hd, Gd, d, lt, bf16, cap, dev)
+            ws = A.workspace(A.MODE_DECODE, Bd, 1, Hd, Gd, d, lt,
+                             A.DTYPE_BF16_E4M3 if e4m3 else bf16, cap, dev)
             r = rope if not sliding else A.Rope(theta=THETA)
 
-            def run(phases, q=q, k=k, v=v, x=x, kc=kc, vc=vc, out=out, ws=ws, lt=lt, r=r, pos=pos):
-                A.olmo3_attn_decode(q, k, v, x["q_gain"], x["k_gain"], kc, vc, out, ws,
-                                    window=WINDOW, layer_type=lt, rope=r, pos=pos, phases=phases)
+            def run(phases, q=q, k=k, v=v, x=x, kc=kc, vc=vc, out=out, ws=ws, lt=lt, r=r, pos=pos,
+                    e4m3=e4m3):
+                if e4m3:
+                    A.olmo3_attn_decode_e4m3(q, k, v, x["q_gain"], x["k_gain"], kc, vc, out, ws,
+                                             k_scale=E4M3_SCALES[0], v_scale=E4M3_SCALES[1],
+                                             window=WINDOW, layer_type=lt, rope=r, pos=pos,
+                                             phases=phases)
+                else:
+                    A.olmo3_attn_decode(q, k, v, x["q_gain"], x["k_gain"], kc, vc, out, ws,
+                                        window=WINDOW, layer_type=lt, rope=r, pos=pos, phases=phases)
 
             n = decode_rows(pos, WINDOW, sliding)
             name = f"decode_{'sliding' if sliding else 'full'}" + (f"_l{ell}" if n_dec_layers else "")
             segments.append(dict(name=name, kind="decode", sliding=sliding, run=run,
                                  phases=[A.PHASE_PROLOGUE, A.PHASE_ATTENTION, A.PHASE_MERGE],
-                                 work=decode_kv_bytes(Bd, Gd, d, n), rows=n))
+                                 work=decode_kv_bytes(Bd, Gd, d, n, elem=1 if e4m3 else 2),
+                                 rows=n))
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream(dev)
@@ -344,6 +361,10 @@ def main():
         print(f"[bench] timing the CPU oracle for ~{args.cpu_seconds:.0f} s", file=sys.stderr, flush=True)
         result["cpu_baseline"] = (cpu_baseline(args, wl, segments, dev) if pre else
                                   cpu_baseline_decode(args, wl))
+    if dc and dec:
+        result["decode"]["tokens_per_s"] = round(
+            dc["B"] / (sum(s["call_ms"] for s in dec) * 1e-3), 1)
+        result["decode"]["cache_dtype"] = "e4m3" if dc.get("e4m3") else "bf16"
     print(json.dumps(result), flush=True)
 
 
@@ -406,9 +427,15 @@ def cpu_baseline_decode(args, wl):
     H, G, L, d = dc["H"], dc["G"], dc["L"], 128
     pos = L - 1
     group = H // G
+    e4m3 = dc.get("e4m3", False)
     rope = O.RopeParams(theta=THETA, yarn=True, factor=8.0, orig_ctx=8192)
-    ck = synth.normal((1, L, d), 7, 0, synth.CACHE_K).to(torch.float64).numpy()
-    cv = synth.normal((1, L, d), 7, 0, synth.CACHE_V).to(torch.float64).numpy()
+    if e4m3:  # the codes' values, as the oracle's e4m3 cache holds them
+        table = O.e4m3_values()
+        ck = table[synth.e4m3_codes((1, L, d), 7, 0, synth.CACHE_K).numpy()] * E4M3_SCALES[0]
+        cv = table[synth.e4m3_codes((1, L, d), 7, 0, synth.CACHE_V).numpy()] * E4M3_SCALES[1]
+    else:
+        ck = synth.normal((1, L, d), 7, 0, synth.CACHE_K).to(torch.float64).numpy()
+        cv = synth.normal((1, L, d), 7, 0, synth.CACHE_V).to(torch.float64).numpy()
     tags = O.ring_positions(O.FULL, WINDOW, L, pos)
     x = synth.layer_inputs(7, 0, 1, 1, H, G, d, dtype=torch.float32)
     hx = {k: v.to(torch.float64).numpy() for k, v in x.items()}
@@ -419,7 +446,7 @@ def cpu_baseline_decode(args, wl):
                           window=WINDOW, rope=rope, pos=pos)
         calls += 1
     elapsed = time.perf_counter() - t0
-    nbytes = calls * L * d * 2 * 2
+    nbytes = calls * L * d * 2 * (1 if e4m3 else 2)
     return {"value": round(nbytes / elapsed / 1e9, 3), "unit": "GB/s", "cores": int(threads),
             "kind": "oracle",
             "sample": f"{calls} decode calls of one sequence x one key/value head ({group} query "

@@ -18,8 +18,8 @@ from . import LAYER_FULL, LAYER_SLIDING  # noqa: F401  (re-exported)
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libolmo3attn.so")
 
-ABI_VERSION = 3  # OLMO3_ABI_VERSION of include/olmo3_attn.h
-DTYPE_BF16, DTYPE_F32 = 0, 1
+ABI_VERSION = 4  # OLMO3_ABI_VERSION of include/olmo3_attn.h
+DTYPE_BF16, DTYPE_F32, DTYPE_BF16_E4M3 = 0, 1, 2
 MODE_PREFILL, MODE_DECODE = 0, 1
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_CAPACITY, ERR_HIP, ERR_WORKSPACE = range(6)
 
@@ -29,6 +29,8 @@ EXPORTS = (
     "olmo3_attn_decode", "olmo3_status_string", "olmo3_abi_version",
     "olmo3_probe_prefill_visits", "olmo3_probe_decode_reads", "olmo3_attn_prefill_phases",
     "olmo3_attn_decode_phases", "olmo3_attn_prefill_ragged", "olmo3_attn_decode_ragged",
+    "olmo3_kv_append_e4m3", "olmo3_attn_prefill_e4m3", "olmo3_attn_decode_e4m3",
+    "olmo3_attn_decode_e4m3_phases",
 )
 PHASE_PROLOGUE, PHASE_ATTENTION, PHASE_MERGE = 1, 2, 4
 PHASES_ALL = PHASE_PROLOGUE | PHASE_ATTENTION | PHASE_MERGE
@@ -108,6 +110,18 @@ def lib() -> ctypes.CDLL:
                                                _f, _p, _i64, _i, _p, _p, _p, _p, _p, _p, _p, _i64,
                                                _p, _p, _sz, _p]
         L.olmo3_attn_decode_ragged.restype = _i
+        R = ctypes.POINTER(RopeStruct)
+        L.olmo3_kv_append_e4m3.argtypes = [_i, _i, _i, _i, _i, _i, R, _f, _i64, _p, _p, _p, _p, _p,
+                                           _f, _f, _i64, _p]
+        L.olmo3_kv_append_e4m3.restype = _i
+        L.olmo3_attn_prefill_e4m3.argtypes = [_i, _i, _i, _i, _i, _i, _i, R, _f, _p, _p, _p, _p,
+                                              _p, _p, _p, _f, _f, _i64, _p, _p, _sz, _p]
+        L.olmo3_attn_prefill_e4m3.restype = _i
+        L.olmo3_attn_decode_e4m3.argtypes = [_i, _i, _i, _i, _i, _i, R, _f, _i64, _p, _p, _p, _p,
+                                             _p, _p, _p, _f, _f, _i64, _p, _p, _sz, _p]
+        L.olmo3_attn_decode_e4m3.restype = _i
+        L.olmo3_attn_decode_e4m3_phases.argtypes = [_i] + L.olmo3_attn_decode_e4m3.argtypes
+        L.olmo3_attn_decode_e4m3_phases.restype = _i
         L.olmo3_status_string.argtypes = [_i]
         L.olmo3_status_string.restype = ctypes.c_char_p
         L.olmo3_abi_version.argtypes = []
@@ -284,11 +298,75 @@ def olmo3_attn_decode_ragged(q_pre, k_pre, v, q_gain, k_gain, k_cache, v_cache, 
     _check(st, "olmo3_attn_decode_ragged")
 
 
+def _e4m3_caches(k_cache, v_cache):
+    for t, name in ((k_cache, "k_cache"), (v_cache, "v_cache")):
+        if t.dtype != torch.uint8:
+            raise TypeError(f"{name} must hold e4m3 codes as torch.uint8")
+    return _ptr(k_cache, "k_cache"), _ptr(v_cache, "v_cache")
+
+
+def olmo3_kv_append_e4m3(k_pre, v, k_gain, k_cache, v_cache, *, k_scale: float, v_scale: float,
+                         window: int, layer_type: int, rope: Rope, eps: float = 1e-6,
+                         pos_offset: int = 0, stream=None) -> None:
+    """Append k_pre/v [B, T, G*d] (bf16) to e4m3 caches [B, G, capacity, d] (uint8)."""
+    B, G, cap, d = _cache_dims(k_cache)
+    T = k_pre.shape[1]
+    dt = torch.bfloat16
+    kc, vc = _e4m3_caches(k_cache, v_cache)
+    r = rope.to_c()
+    st = lib().olmo3_kv_append_e4m3(B, T, G, d, window, layer_type, ctypes.byref(r), eps,
+                                    pos_offset, _ptr(k_pre, "k_pre", dt), _ptr(v, "v", dt),
+                                    _ptr(k_gain, "k_gain", dt), kc, vc, k_scale, v_scale, cap,
+                                    _stream(stream, k_pre.device))
+    _check(st, "olmo3_kv_append_e4m3")
+
+
+def olmo3_attn_prefill_e4m3(q_pre, k_pre, v, q_gain, k_gain, k_cache, v_cache, out, workspace, *,
+                            k_scale: float, v_scale: float, window: int, layer_type: int,
+                            rope: Rope, eps: float = 1e-6, stream=None) -> None:
+    """First-chunk prefill (positions 0..T-1) into e4m3 caches (uint8)."""
+    B, G, cap, d = _cache_dims(k_cache)
+    T = q_pre.shape[1]
+    H = q_pre.shape[2] // d
+    dt = torch.bfloat16
+    kc, vc = _e4m3_caches(k_cache, v_cache)
+    r = rope.to_c()
+    st = lib().olmo3_attn_prefill_e4m3(
+        B, T, H, G, d, window, layer_type, ctypes.byref(r), eps, _ptr(q_pre, "q_pre", dt),
+        _ptr(k_pre, "k_pre", dt), _ptr(v, "v", dt), _ptr(q_gain, "q_gain", dt),
+        _ptr(k_gain, "k_gain", dt), kc, vc, k_scale, v_scale, cap, _ptr(out, "out", dt),
+        _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _stream(stream, q_pre.device))
+    _check(st, "olmo3_attn_prefill_e4m3")
+
+
+def olmo3_attn_decode_e4m3(q_pre, k_pre, v, q_gain, k_gain, k_cache, v_cache, out, workspace, *,
+                           k_scale: float, v_scale: float, window: int, layer_type: int,
+                           rope: Rope, pos: int, eps: float = 1e-6, stream=None,
+                           phases: int | None = None) -> None:
+    """Decode against e4m3 caches (uint8): q_pre [B, H*d], k_pre/v [B, G*d]
+    -> out [B, H*d].  ``phases`` selects olmo3_attn_decode_e4m3_phases."""
+    B, G, cap, d = _cache_dims(k_cache)
+    H = q_pre.shape[-1] // d
+    dt = torch.bfloat16
+    kc, vc = _e4m3_caches(k_cache, v_cache)
+    r = rope.to_c()
+    args = (B, H, G, d, window, layer_type, ctypes.byref(r), eps, pos, _ptr(q_pre, "q_pre", dt),
+            _ptr(k_pre, "k_pre", dt), _ptr(v, "v", dt), _ptr(q_gain, "q_gain", dt),
+            _ptr(k_gain, "k_gain", dt), kc, vc, k_scale, v_scale, cap, _ptr(out, "out", dt),
+            _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+            _stream(stream, q_pre.device))
+    if phases is None:
+        _check(lib().olmo3_attn_decode_e4m3(*args), "olmo3_attn_decode_e4m3")
+    else:
+        _check(lib().olmo3_attn_decode_e4m3_phases(phases, *args), "olmo3_attn_decode_e4m3_phases")
+
+
 def workspace(mode: int, B: int, T: int, H: int, G: int, d: int, layer_type: int,
               dtype: torch.dtype, cache_capacity: int, device) -> torch.Tensor:
     """Device byte buffer of the size ``olmo3_workspace_bytes`` asks for."""
-    n = olmo3_workspace_bytes(mode, B, T, H, G, d, layer_type,
-                              DTYPE_BF16 if dtype == torch.bfloat16 else DTYPE_F32, cache_capacity)
+    code = dtype if isinstance(dtype, int) else (DTYPE_BF16 if dtype == torch.bfloat16 else DTYPE_F32)
+    n = olmo3_workspace_bytes(mode, B, T, H, G, d, layer_type, code, cache_capacity)
     if n == 0:
         raise Olmo3Error(ERR_INVALID_ARG, "olmo3_workspace_bytes")
     return torch.empty(n, dtype=torch.uint8, device=device)

@@ -21,7 +21,8 @@ constexpr int64_t kMaxPrefillPositions = (int64_t)1 << 30;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
-size_t elem_size(int dtype) { return dtype == OLMO3_DTYPE_BF16 ? 2 : 4; }
+// bytes of an activation element (the e4m3 mode keeps bf16 activations)
+size_t elem_size(int dtype) { return dtype == OLMO3_DTYPE_F32 ? 4 : 2; }
 
 bool supported_d(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 
@@ -91,16 +92,19 @@ void rope_table(const olmo3_rope* rope, int layer_type, int d, RopeTable* t) {
 
 float scale_log2(int d) { return (float)(kLog2e / sqrt((double)d)); }
 
-bool use_mfma(int dtype, int d) { return dtype == OLMO3_DTYPE_BF16 && d == 128; }
+bool use_mfma(int dtype, int d) { return dtype != OLMO3_DTYPE_F32 && d == 128; }
 
 bool decode_uses_split(int dtype, int d, int H, int G) {
   return use_mfma(dtype, d) && H / G <= 8;
 }
 
+// Rotated queries, plus rotated keys where the attention cannot read them
+// from the cache: a ring shorter than the call, or an e4m3 cache.
 size_t prefill_ws(int B, int T, int H, int G, int d, int layer_type, int dtype) {
   const size_t es = elem_size(dtype);
   size_t bytes = align_up((size_t)B * T * H * d * es);
-  if (layer_type == OLMO3_LAYER_SLIDING) bytes += align_up((size_t)B * G * T * d * es);
+  if (layer_type == OLMO3_LAYER_SLIDING || dtype == OLMO3_DTYPE_BF16_E4M3)
+    bytes += align_up((size_t)B * G * T * d * es);
   return bytes;
 }
 
@@ -116,6 +120,68 @@ size_t decode_ws(int B, int H, int G, int d, int layer_type, int window, int dty
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? OLMO3_OK : OLMO3_ERR_HIP; }
+
+// Element format of the caches: bf16 (or fp32) rows, or e4m3 codes whose
+// values are code * k_scale (keys) and code * v_scale (values).
+struct CacheFormat {
+  int e4m3;
+  float k_scale, v_scale;
+};
+constexpr CacheFormat kPlainCache = {0, 1.f, 1.f};
+
+void set_cache_format(PrologueArgs& p, const CacheFormat& cf) {
+  p.cache_fp8 = cf.e4m3;
+  p.k_inv_scale = (float)(1.0 / (double)cf.k_scale);
+  p.v_inv_scale = (float)(1.0 / (double)cf.v_scale);
+}
+
+bool valid_scale(float x) { return x > 0.f && isfinite(x) && isfinite(1.0f / x); }
+
+// QK-norm + RoPE + store of keys and values only (no attention).
+int kv_append_impl(int B, int T, int G, int d, int window, int layer_type,
+                   const olmo3_rope* rope, float eps, int64_t pos_offset, int dtype,
+                   const void* k_pre, const void* v, const void* k_gain, void* k_cache,
+                   void* v_cache, int64_t cache_capacity, hipStream_t stream,
+                   const CacheFormat& cf) {
+  int st = check_common(B, T, G, G, d, window, layer_type, dtype, rope, eps, pos_offset);
+  if (st) return st;
+  if (!k_pre || !v || !k_gain || !k_cache || !v_cache) return OLMO3_ERR_INVALID_ARG;
+  if (!aligned16(k_pre) || !aligned16(v) || !aligned16(k_gain) || !aligned16(k_cache) ||
+      !aligned16(v_cache))
+    return OLMO3_ERR_INVALID_ARG;
+  st = check_capacity(layer_type, window, cache_capacity, pos_offset + T - 1);
+  if (st) return st;
+  const size_t es = elem_size(dtype), ces = cf.e4m3 ? 1 : es;
+  const Span kc = span(k_cache, (size_t)B * G * cache_capacity * d * ces);
+  const Span vc = span(v_cache, (size_t)B * G * cache_capacity * d * ces);
+  const Span in[] = {span(k_pre, (size_t)B * T * G * d * es), span(v, (size_t)B * T * G * d * es),
+                     span(k_gain, (size_t)G * d * es)};
+  if (overlap(kc, vc)) return OLMO3_ERR_INVALID_ARG;
+  for (const Span& sp : in)
+    if (overlap(sp, kc) || overlap(sp, vc)) return OLMO3_ERR_INVALID_ARG;
+
+  RopeTable table;
+  rope_table(rope, layer_type, d, &table);
+  PrologueArgs a = {};
+  a.k_pre = k_pre;
+  a.v = v;
+  a.k_gain = k_gain;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.cap = cache_capacity;
+  a.pos_offset = pos_offset;
+  a.keep_last = layer_type == OLMO3_LAYER_SLIDING ? window : INT64_MAX;
+  a.store = 1;
+  a.B = B;
+  a.T = T;
+  a.H = G;
+  a.G = G;
+  a.window = window;
+  a.sliding = layer_type == OLMO3_LAYER_SLIDING;
+  a.eps = eps;
+  set_cache_format(a, cf);
+  return hip_status(launch_prologue(a, table, dtype, d, stream));
+}
 
 }  // namespace
 
@@ -144,7 +210,8 @@ size_t olmo3_workspace_bytes(int mode, int B, int T, int H, int G, int d, int la
                              int dtype, int64_t cache_capacity) {
   olmo3_rope plain = {10000.0, 0, 1.0, 1, 32.0, 1.0, 0.0};
   if (mode == OLMO3_MODE_DECODE) T = 1;
-  if (check_common(B, T, H, G, d, 1, layer_type, dtype, &plain, 0.f, 0) != OLMO3_OK) return 0;
+  const int act = dtype == OLMO3_DTYPE_BF16_E4M3 ? OLMO3_DTYPE_BF16 : dtype;
+  if (check_common(B, T, H, G, d, 1, layer_type, act, &plain, 0.f, 0) != OLMO3_OK) return 0;
   if (mode == OLMO3_MODE_PREFILL) return prefill_ws(B, T, H, G, d, layer_type, dtype);
   if (mode == OLMO3_MODE_DECODE) {
     if (cache_capacity < 1) return 0;
@@ -159,43 +226,19 @@ int olmo3_kv_append(int B, int T, int G, int d, int window, int layer_type,
                     const olmo3_rope* rope, float eps, int64_t pos_offset, int dtype,
                     const void* k_pre, const void* v, const void* k_gain, void* k_cache,
                     void* v_cache, int64_t cache_capacity, void* stream) {
-  int st = check_common(B, T, G, G, d, window, layer_type, dtype, rope, eps, pos_offset);
-  if (st) return st;
-  if (!k_pre || !v || !k_gain || !k_cache || !v_cache) return OLMO3_ERR_INVALID_ARG;
-  if (!aligned16(k_pre) || !aligned16(v) || !aligned16(k_gain) || !aligned16(k_cache) ||
-      !aligned16(v_cache))
-    return OLMO3_ERR_INVALID_ARG;
-  st = check_capacity(layer_type, window, cache_capacity, pos_offset + T - 1);
-  if (st) return st;
-  const size_t es = elem_size(dtype);
-  const Span kc = span(k_cache, (size_t)B * G * cache_capacity * d * es);
-  const Span vc = span(v_cache, (size_t)B * G * cache_capacity * d * es);
-  const Span in[] = {span(k_pre, (size_t)B * T * G * d * es), span(v, (size_t)B * T * G * d * es),
-                     span(k_gain, (size_t)G * d * es)};
-  if (overlap(kc, vc)) return OLMO3_ERR_INVALID_ARG;
-  for (const Span& s : in)
-    if (overlap(s, kc) || overlap(s, vc)) return OLMO3_ERR_INVALID_ARG;
+  return kv_append_impl(B, T, G, d, window, layer_type, rope, eps, pos_offset, dtype, k_pre, v,
+                        k_gain, k_cache, v_cache, cache_capacity, (hipStream_t)stream,
+                        kPlainCache);
+}
 
-  RopeTable table;
-  rope_table(rope, layer_type, d, &table);
-  PrologueArgs a = {};
-  a.k_pre = k_pre;
-  a.v = v;
-  a.k_gain = k_gain;
-  a.k_cache = k_cache;
-  a.v_cache = v_cache;
-  a.cap = cache_capacity;
-  a.pos_offset = pos_offset;
-  a.keep_last = layer_type == OLMO3_LAYER_SLIDING ? window : INT64_MAX;
-  a.store = 1;
-  a.B = B;
-  a.T = T;
-  a.H = G;
-  a.G = G;
-  a.window = window;
-  a.sliding = layer_type == OLMO3_LAYER_SLIDING;
-  a.eps = eps;
-  return hip_status(launch_prologue(a, table, dtype, d, (hipStream_t)stream));
+int olmo3_kv_append_e4m3(int B, int T, int G, int d, int window, int layer_type,
+                         const olmo3_rope* rope, float eps, int64_t pos_offset, const void* k_pre,
+                         const void* v, const void* k_gain, void* k_cache, void* v_cache,
+                         float k_scale, float v_scale, int64_t cache_capacity, void* stream) {
+  if (!valid_scale(k_scale) || !valid_scale(v_scale)) return OLMO3_ERR_INVALID_ARG;
+  return kv_append_impl(B, T, G, d, window, layer_type, rope, eps, pos_offset, OLMO3_DTYPE_BF16,
+                        k_pre, v, k_gain, k_cache, v_cache, cache_capacity, (hipStream_t)stream,
+                        CacheFormat{1, k_scale, v_scale});
 }
 
 static int validate_attn(int B, int T, int H, int G, int d, int window, int layer_type,
@@ -204,7 +247,7 @@ static int validate_attn(int B, int T, int H, int G, int d, int window, int laye
                          const void* k_gain, void* k_cache, void* v_cache,
                          int64_t cache_capacity, void* out, void* workspace,
                          size_t workspace_bytes, size_t ws_needed, int cache_B,
-                         int64_t last_pos) {
+                         int64_t last_pos, size_t cache_es = 0) {
   int st = check_common(B, T, H, G, d, window, layer_type, dtype, rope, eps, pos_offset);
   if (st) return st;
   const void* ptrs[] = {q_pre, k_pre, v, q_gain, k_gain, k_cache, v_cache, out};
@@ -215,8 +258,9 @@ static int validate_attn(int B, int T, int H, int G, int d, int window, int laye
   if (!workspace || !aligned16(workspace) || workspace_bytes < ws_needed) return OLMO3_ERR_WORKSPACE;
   const size_t es = elem_size(dtype);
   if (cache_B < 1 || (int64_t)cache_B * G > 65535 * 64) return OLMO3_ERR_INVALID_ARG;
-  const Span kc = span(k_cache, (size_t)cache_B * G * cache_capacity * d * es);
-  const Span vc = span(v_cache, (size_t)cache_B * G * cache_capacity * d * es);
+  const size_t ces = cache_es ? cache_es : es;
+  const Span kc = span(k_cache, (size_t)cache_B * G * cache_capacity * d * ces);
+  const Span vc = span(v_cache, (size_t)cache_B * G * cache_capacity * d * ces);
   const Span o = span(out, (size_t)B * T * H * d * es);
   const Span ws = span(workspace, ws_needed);
   const Span in[] = {span(q_pre, (size_t)B * T * H * d * es), span(k_pre, (size_t)B * T * G * d * es),
@@ -250,7 +294,7 @@ int prefill_impl(int phases, const PrefillShape& sh, int H, int G, int d, int wi
                  int layer_type, const olmo3_rope* rope, float eps, int dtype, const void* q_pre,
                  const void* k_pre, const void* v, const void* q_gain, const void* k_gain,
                  void* k_cache, void* v_cache, int64_t cache_capacity, void* out,
-                 void* workspace, hipStream_t s) {
+                 void* workspace, hipStream_t s, const CacheFormat& cf = kPlainCache) {
   const bool packed = sh.cu_seqlens != nullptr;
   const bool sliding = layer_type == OLMO3_LAYER_SLIDING;
   const int B = sh.B, T = sh.T;
@@ -263,7 +307,11 @@ int prefill_impl(int phases, const PrefillShape& sh, int H, int G, int d, int wi
   const size_t es = elem_size(dtype);
   char* ws = (char*)workspace;
   void* q_rot = ws;
-  void* k_rot = sliding ? ws + align_up((size_t)N * H * d * es) : nullptr;
+  // the attention reads the new keys from the workspace and the new values
+  // from the input, except on a full layer with a bf16 cache, which it reads
+  // straight after the prologue has filled it
+  const bool kv_from_ws = sliding || cf.e4m3;
+  void* k_rot = kv_from_ws ? ws + align_up((size_t)N * H * d * es) : nullptr;
 
   RopeTable table;
   rope_table(rope, layer_type, d, &table);
@@ -295,6 +343,7 @@ int prefill_impl(int phases, const PrefillShape& sh, int H, int G, int d, int wi
   p.window = window;
   p.sliding = sliding;
   p.eps = eps;
+  set_cache_format(p, cf);
   int st;
   if (phases & OLMO3_PHASE_PROLOGUE) {
     st = hip_status(launch_prologue(p, table, dtype, d, s));
@@ -304,7 +353,7 @@ int prefill_impl(int phases, const PrefillShape& sh, int H, int G, int d, int wi
 
   AttnArgs a = {};
   a.q = q_rot;
-  if (sliding) {
+  if (kv_from_ws) {
     // the chunk: rotated keys from the workspace, values from the input;
     // earlier positions (if any) from the ring
     a.k = k_rot;
@@ -435,7 +484,8 @@ int decode_impl(int phases, int B, int H, int G, int d, int window, int layer_ty
                 const olmo3_rope* rope, float eps, int64_t pos, const int32_t* positions,
                 int64_t max_pos, int dtype, const void* q_pre, const void* k_pre, const void* v,
                 const void* q_gain, const void* k_gain, void* k_cache, void* v_cache,
-                int64_t cache_capacity, void* out, void* workspace, hipStream_t s) {
+                int64_t cache_capacity, void* out, void* workspace, hipStream_t s,
+                const CacheFormat& cf = kPlainCache) {
   const bool sliding = layer_type == OLMO3_LAYER_SLIDING;
   const size_t es = elem_size(dtype);
   char* ws = (char*)workspace;
@@ -464,6 +514,7 @@ int decode_impl(int phases, int B, int H, int G, int d, int window, int layer_ty
   p.window = window;
   p.sliding = sliding;
   p.eps = eps;
+  set_cache_format(p, cf);
   int st;
   if (phases & OLMO3_PHASE_PROLOGUE) {
     st = hip_status(launch_prologue(p, table, dtype, d, s));
@@ -492,6 +543,9 @@ int decode_impl(int phases, int B, int H, int G, int d, int window, int layer_ty
     a.seq_pos = positions;
     a.window = window;
     a.sliding = sliding;
+    a.fp8 = cf.e4m3;
+    a.k_scale = cf.k_scale;
+    a.v_scale = cf.v_scale;
     if (phases & OLMO3_PHASE_ATTENTION) {
       st = hip_status(launch_decode_split(a, s));
       if (st) return st;
@@ -577,6 +631,66 @@ int olmo3_attn_decode(int B, int H, int G, int d, int window, int layer_type,
                                   B, H, G, d, window, layer_type, rope, eps, pos, dtype, q_pre,
                                   k_pre, v, q_gain, k_gain, k_cache, v_cache, cache_capacity, out,
                                   workspace, workspace_bytes, stream);
+}
+
+int olmo3_attn_prefill_e4m3(int B, int T, int H, int G, int d, int window, int layer_type,
+                            const olmo3_rope* rope, float eps, const void* q_pre,
+                            const void* k_pre, const void* v, const void* q_gain,
+                            const void* k_gain, void* k_cache, void* v_cache, float k_scale,
+                            float v_scale, int64_t cache_capacity, void* out, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  if (!valid_scale(k_scale) || !valid_scale(v_scale)) return OLMO3_ERR_INVALID_ARG;
+  const size_t need = (B > 0 && T > 0 && H > 0 && G > 0 && d > 0)
+                          ? prefill_ws(B, T, H, G, d, layer_type, OLMO3_DTYPE_BF16_E4M3)
+                          : 0;
+  int st = validate_attn(B, T, H, G, d, window, layer_type, rope, eps, 0, OLMO3_DTYPE_BF16,
+                         q_pre, k_pre, v, q_gain, k_gain, k_cache, v_cache, cache_capacity, out,
+                         workspace, workspace_bytes, need, B, (int64_t)T - 1, 1);
+  if (st) return st;
+  if (T > kMaxPrefillPositions) return OLMO3_ERR_UNSUPPORTED;
+  const PrefillShape sh = {B, T, (int64_t)B * T, 0, nullptr, nullptr};
+  return prefill_impl(OLMO3_PHASE_PROLOGUE | OLMO3_PHASE_ATTENTION, sh, H, G, d, window,
+                      layer_type, rope, eps, OLMO3_DTYPE_BF16, q_pre, k_pre, v, q_gain, k_gain,
+                      k_cache, v_cache, cache_capacity, out, workspace, (hipStream_t)stream,
+                      CacheFormat{1, k_scale, v_scale});
+}
+
+int olmo3_attn_decode_e4m3_phases(int phases, int B, int H, int G, int d, int window,
+                                  int layer_type, const olmo3_rope* rope, float eps, int64_t pos,
+                                  const void* q_pre, const void* k_pre, const void* v,
+                                  const void* q_gain, const void* k_gain, void* k_cache,
+                                  void* v_cache, float k_scale, float v_scale,
+                                  int64_t cache_capacity, void* out, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  if (phases <= 0 || (phases & ~(OLMO3_PHASE_PROLOGUE | OLMO3_PHASE_ATTENTION | OLMO3_PHASE_MERGE)))
+    return OLMO3_ERR_INVALID_ARG;
+  if (!valid_scale(k_scale) || !valid_scale(v_scale)) return OLMO3_ERR_INVALID_ARG;
+  const size_t need = (B > 0 && H > 0 && G > 0 && d > 0 && G <= H && cache_capacity > 0)
+                          ? decode_ws(B, H, G, d, layer_type, window, OLMO3_DTYPE_BF16_E4M3,
+                                      cache_capacity)
+                          : 0;
+  int st = validate_attn(B, 1, H, G, d, window, layer_type, rope, eps, pos, OLMO3_DTYPE_BF16,
+                         q_pre, k_pre, v, q_gain, k_gain, k_cache, v_cache, cache_capacity, out,
+                         workspace, workspace_bytes, need, B, pos, 1);
+  if (st) return st;
+  // the e4m3 cache is read by the split-KV kernel only
+  if (!decode_uses_split(OLMO3_DTYPE_BF16_E4M3, d, H, G)) return OLMO3_ERR_UNSUPPORTED;
+  return decode_impl(phases, B, H, G, d, window, layer_type, rope, eps, pos, nullptr, pos,
+                     OLMO3_DTYPE_BF16, q_pre, k_pre, v, q_gain, k_gain, k_cache, v_cache,
+                     cache_capacity, out, workspace, (hipStream_t)stream,
+                     CacheFormat{1, k_scale, v_scale});
+}
+
+int olmo3_attn_decode_e4m3(int B, int H, int G, int d, int window, int layer_type,
+                           const olmo3_rope* rope, float eps, int64_t pos, const void* q_pre,
+                           const void* k_pre, const void* v, const void* q_gain,
+                           const void* k_gain, void* k_cache, void* v_cache, float k_scale,
+                           float v_scale, int64_t cache_capacity, void* out, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  return olmo3_attn_decode_e4m3_phases(
+      OLMO3_PHASE_PROLOGUE | OLMO3_PHASE_ATTENTION | OLMO3_PHASE_MERGE, B, H, G, d, window,
+      layer_type, rope, eps, pos, q_pre, k_pre, v, q_gain, k_gain, k_cache, v_cache, k_scale,
+      v_scale, cache_capacity, out, workspace, workspace_bytes, stream);
 }
 
 int olmo3_probe_prefill_visits(int T, int64_t pos_offset, int window, int layer_type,

@@ -6,6 +6,8 @@
 // sliding-window mask"; decode on a ring reads exactly the `window` held
 // entries ("Olmo 3 7B", "SERVICEABILITY JOIN").  Softmax uses base-2
 // exponentials with log2(e)/sqrt(d) folded into the scores.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 #include "tiles.h"
@@ -97,7 +99,10 @@ __global__ __launch_bounds__(64) void attn_generic_kernel(AttnArgs a) {
 // the 4 groups of a wavefront with lane exchanges and then across
 // wavefronts in LDS, into one partial (m, l, o) per head and split.
 // ---------------------------------------------------------------------------
-template <int GRP>
+// kFp8: the caches hold e4m3 codes (a 128-byte row, 8 bytes per lane);
+// k_scale is folded into the query and v_scale into the partial output, so
+// each scale multiplies the result exactly once.
+template <int GRP, bool kFp8>
 __global__ __launch_bounds__(dec::kThreads) void decode_split_kernel(DecodeArgs a) {
   using namespace dec;
   const int sp = blockIdx.x % a.splits;
@@ -116,11 +121,12 @@ __global__ __launch_bounds__(dec::kThreads) void decode_split_kernel(DecodeArgs 
   const int grp = tid >> 4;
 
   float q[GRP][8];
+  const float qs = kFp8 ? a.scale_log2 * a.k_scale : a.scale_log2;
 #pragma unroll
   for (int j = 0; j < GRP; ++j) {
     const bf16x8 qv = *(const bf16x8*)((const bf16*)a.q + ((int64_t)b * a.H + g * GRP + j) * kD + li * 8);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) q[j][e] = (float)qv[e] * a.scale_log2;
+    for (int e = 0; e < 8; ++e) q[j][e] = (float)qv[e] * qs;
   }
   float m[GRP], l[GRP], o[GRP][8];
 #pragma unroll
@@ -130,27 +136,46 @@ __global__ __launch_bounds__(dec::kThreads) void decode_split_kernel(DecodeArgs 
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[j][e] = 0.f;
   }
-  const bf16* kb = (const bf16*)a.k_cache + ((int64_t)b * a.G + g) * a.cap * kD + li * 8;
-  const bf16* vb = (const bf16*)a.v_cache + ((int64_t)b * a.G + g) * a.cap * kD + li * 8;
+  // row r of this (sequence, head): element offset (bf16) or byte offset (e4m3)
+  const int64_t base = ((int64_t)b * a.G + g) * a.cap * kD + li * 8;
+  const bf16* kb = (const bf16*)a.k_cache + base;
+  const bf16* vb = (const bf16*)a.v_cache + base;
+  const uint8_t* kb8 = (const uint8_t*)a.k_cache + base;
+  const uint8_t* vb8 = (const uint8_t*)a.v_cache + base;
+  typedef typename std::conditional<kFp8, u32x2, bf16x8>::type Chunk;
+  auto load = [&](const bf16* p16, const uint8_t* p8, int64_t r) -> Chunk {
+    if constexpr (kFp8)
+      return *(const u32x2*)(p8 + r * kD);
+    else
+      return *(const bf16x8*)(p16 + r * kD);
+  };
+  auto widen = [&](const Chunk& c, float* f) {
+    if constexpr (kFp8) {
+      e4m3x4_to_f32(c[0], f);
+      e4m3x4_to_f32(c[1], f + 4);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) f[e] = (float)c[e];
+    }
+  };
 
   const int64_t n_iter = r1 > r0 ? (r1 - r0 + kRowsPerIter - 1) / kRowsPerIter : 0;
   for (int64_t i = 0; i < n_iter; ++i) {
-    bf16x8 kr[kUnroll], vr[kUnroll];
+    Chunk kr[kUnroll], vr[kUnroll];
     bool ok[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int64_t r = row_of(r0, i, u, grp);
       ok[u] = r < r1;
       const int64_t rc = ok[u] ? r : r0;
-      kr[u] = *(const bf16x8*)(kb + rc * kD);
-      vr[u] = *(const bf16x8*)(vb + rc * kD);
+      kr[u] = load(kb, kb8, rc);
+      vr[u] = load(vb, vb8, rc);
     }
     float s[kUnroll][GRP];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       float kf[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) kf[e] = (float)kr[u][e];
+      widen(kr[u], kf);
 #pragma unroll
       for (int j = 0; j < GRP; ++j) {
         float acc = 0.f;
@@ -183,12 +208,25 @@ __global__ __launch_bounds__(dec::kThreads) void decode_split_kernel(DecodeArgs 
         ps += p[u];
       }
       l[j] = l[j] * al + ps;
+      if constexpr (kFp8) {
+        float vf[kUnroll][8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float acc = o[j][e] * al;
+        for (int u = 0; u < kUnroll; ++u) widen(vr[u], vf[u]);
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) acc = fmaf(p[u], (float)vr[u][e], acc);
-        o[j][e] = acc;
+        for (int e = 0; e < 8; ++e) {
+          float acc = o[j][e] * al;
+#pragma unroll
+          for (int u = 0; u < kUnroll; ++u) acc = fmaf(p[u], vf[u][e], acc);
+          o[j][e] = acc;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          float acc = o[j][e] * al;
+#pragma unroll
+          for (int u = 0; u < kUnroll; ++u) acc = fmaf(p[u], (float)vr[u][e], acc);
+          o[j][e] = acc;
+        }
       }
     }
   }
@@ -243,7 +281,7 @@ __global__ __launch_bounds__(dec::kThreads) void decode_split_kernel(DecodeArgs 
       pp[0] = M;
       pp[1] = L;
     }
-    pp[2 + d] = O;
+    pp[2 + d] = kFp8 ? O * a.v_scale : O;
   }
 }
 
@@ -312,9 +350,12 @@ int decode_splits(int B, int G, int64_t n) {
 hipError_t launch_decode_split(const DecodeArgs& a, hipStream_t s) {
   const int group = a.H / a.G;
   const int blocks = a.B * a.G * a.splits;
-#define OLMO3_DEC(GG) \
-  case GG:            \
-    decode_split_kernel<GG><<<blocks, dec::kThreads, 0, s>>>(a); \
+#define OLMO3_DEC(GG)                                                      \
+  case GG:                                                                 \
+    if (a.fp8)                                                             \
+      decode_split_kernel<GG, true><<<blocks, dec::kThreads, 0, s>>>(a);   \
+    else                                                                   \
+      decode_split_kernel<GG, false><<<blocks, dec::kThreads, 0, s>>>(a);  \
     break;
   switch (group) {
     OLMO3_DEC(1) OLMO3_DEC(2) OLMO3_DEC(3) OLMO3_DEC(4)

@@ -59,6 +59,33 @@ template <> struct Io<float> {
   }
 };
 
+// OCP e4m3 (sign, 4 exponent bits with bias 7, 3 mantissa bits, no
+// infinities, largest finite value 448), converted in hardware on gfx950.
+// The hardware rounds to nearest even but turns values past the largest
+// finite one into NaN, so inputs are clamped to +-448 first (saturation).
+constexpr float kE4m3Max = 448.f;
+
+// Four fp32 values -> four e4m3 codes, first value in the low byte.
+__device__ __forceinline__ uint32_t f32x4_to_e4m3(float a, float b, float c, float d) {
+  a = fminf(fmaxf(a, -kE4m3Max), kE4m3Max);
+  b = fminf(fmaxf(b, -kE4m3Max), kE4m3Max);
+  c = fminf(fmaxf(c, -kE4m3Max), kE4m3Max);
+  d = fminf(fmaxf(d, -kE4m3Max), kE4m3Max);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return (uint32_t)w;
+}
+
+// Four e4m3 codes (low byte first) -> four fp32 values.
+__device__ __forceinline__ void e4m3x4_to_f32(uint32_t w, float* f) {
+  const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+  const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+  f[0] = lo[0];
+  f[1] = lo[1];
+  f[2] = hi[0];
+  f[3] = hi[1];
+}
+
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, kWave);

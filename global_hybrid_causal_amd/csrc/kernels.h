@@ -40,6 +40,9 @@ struct PrologueArgs {
   int sliding;
   int store;
   float eps;
+  // e4m3 caches (bf16 rows only): code = e4m3(value * inv_scale)
+  int cache_fp8;
+  float k_inv_scale, v_inv_scale;
 };
 
 hipError_t launch_prologue(const PrologueArgs& a, const RopeTable& rope, int dtype, int d,
@@ -119,6 +122,10 @@ struct DecodeArgs {
   const int32_t* seq_pos;
   int window;
   int sliding;
+  // e4m3 caches: a row holds codes c, values c * k_scale (keys) and
+  // c * v_scale (values)
+  int fp8;
+  float k_scale, v_scale;
 };
 int decode_splits(int B, int G, int64_t n);
 hipError_t launch_decode_split(const DecodeArgs& a, hipStream_t s);

@@ -49,12 +49,12 @@ __device__ __forceinline__ void rope_angles(int lane, int64_t pos, const RopeTab
 }
 
 // Normalise, rotate and emit the `nheads` heads of one token row.
-// dst0(h) and dst1(h) return where head h goes (the start of its d
-// elements), or nullptr to skip that destination.
-template <typename T, int D, typename Dst0, typename Dst1>
+// emit(h, j, y0, y1) receives pair chunk j of head h: elements j*kVec ..
+// j*kVec + kVec-1 of the head (y0) and the same offsets past d/2 (y1).
+template <typename T, int D, typename Emit>
 __device__ __forceinline__ void norm_rope_row(const T* __restrict__ src, const T* __restrict__ gain,
                                               int nheads, float eps, int lane, const float* cs,
-                                              const float* sn, float mscale, Dst0 dst0, Dst1 dst1) {
+                                              const float* sn, float mscale, Emit emit) {
   typedef typename Io<T>::vec vec;
   constexpr int kVec = Io<T>::kVec;
   constexpr int kPerHead = PairChunks<T, D>::kPerHead;
@@ -96,17 +96,22 @@ __device__ __forceinline__ void norm_rope_row(const T* __restrict__ src, const T
         y0[e] = (u * cs[e] - w * sn[e]) * mscale;
         y1[e] = (w * cs[e] + u * sn[e]) * mscale;
       }
-      const vec v0 = Io<T>::from_f32(y0), v1 = Io<T>::from_f32(y1);
-      if (T* d = dst0(h)) {
-        *(vec*)(d + j * kVec) = v0;
-        *(vec*)(d + D / 2 + j * kVec) = v1;
-      }
-      if (T* d = dst1(h)) {
-        *(vec*)(d + j * kVec) = v0;
-        *(vec*)(d + D / 2 + j * kVec) = v1;
-      }
+      emit(h, j, y0, y1);
     }
   }
+}
+
+// kVec consecutive values of one head: as T, or (e4m3 cache, T = bf16) as
+// codes of value * inv_scale.
+template <typename T>
+__device__ __forceinline__ void store_chunk(T* dst, const float* y) {
+  *(typename Io<T>::vec*)dst = Io<T>::from_f32(y);
+}
+__device__ __forceinline__ void store_chunk_e4m3(uint8_t* dst, const float* y, float inv_scale) {
+  u32x2 w;
+  w[0] = f32x4_to_e4m3(y[0] * inv_scale, y[1] * inv_scale, y[2] * inv_scale, y[3] * inv_scale);
+  w[1] = f32x4_to_e4m3(y[4] * inv_scale, y[5] * inv_scale, y[6] * inv_scale, y[7] * inv_scale);
+  *(u32x2*)dst = w;
 }
 
 // Sequence of packed row `row`: the number of b >= 1 with cu[b] <= row
@@ -157,39 +162,66 @@ __global__ __launch_bounds__(kWave * kTokensPerBlock) void qknorm_rope_append_ke
     const T* src = (const T*)a.q_pre + row * a.H * D;
     T* qo = (T*)a.q_out + row * a.H * D;
     norm_rope_row<T, D>(src, (const T*)a.q_gain, a.H, a.eps, lane, cs, sn, rope.mscale,
-                        [&](int h) -> T* { return qo + h * D; },
-                        [&](int) -> T* { return nullptr; });
+                        [&](int h, int j, const float* y0, const float* y1) {
+                          store_chunk(qo + h * D + j * kVec, y0);
+                          store_chunk(qo + h * D + D / 2 + j * kVec, y1);
+                        });
   }
 
   const int64_t slot = a.sliding ? pos % a.window : pos;
   const bool to_cache = a.store && len - t <= a.keep_last && slot < a.cap;
   // rotated-key copy: [b][g][t] strided, or [g][row] for packed rows
   const int64_t kb_idx = a.cu_seqlens ? 0 : b, kt_idx = a.cu_seqlens ? row : t;
+  constexpr bool kCanFp8 = kVec == 8;  // e4m3 caches hold bf16 rows only
+  const bool fp8 = a.cache_fp8;
 
   // keys -> optional strided copy (prefill workspace) and the cache slot
   {
     const T* src = (const T*)a.k_pre + row * a.G * D;
     T* ko = (T*)a.k_out;
-    T* kc = (T*)a.k_cache;
     norm_rope_row<T, D>(
         src, (const T*)a.k_gain, a.G, a.eps, lane, cs, sn, rope.mscale,
-        [&](int h) -> T* {
-          return ko ? ko + kb_idx * a.k_sb + h * a.k_sg + kt_idx * a.k_st : nullptr;
-        },
-        [&](int h) -> T* {
-          return to_cache ? kc + (((int64_t)b * a.G + h) * a.cap + slot) * D : nullptr;
+        [&](int h, int j, const float* y0, const float* y1) {
+          if (ko) {
+            T* d = ko + kb_idx * a.k_sb + h * a.k_sg + kt_idx * a.k_st;
+            store_chunk(d + j * kVec, y0);
+            store_chunk(d + D / 2 + j * kVec, y1);
+          }
+          if (!to_cache) return;
+          const int64_t off = (((int64_t)b * a.G + h) * a.cap + slot) * D;
+          if constexpr (kCanFp8) {
+            if (fp8) {
+              uint8_t* d = (uint8_t*)a.k_cache + off;
+              store_chunk_e4m3(d + j * kVec, y0, a.k_inv_scale);
+              store_chunk_e4m3(d + D / 2 + j * kVec, y1, a.k_inv_scale);
+              return;
+            }
+          }
+          {
+            T* d = (T*)a.k_cache + off;
+            store_chunk(d + j * kVec, y0);
+            store_chunk(d + D / 2 + j * kVec, y1);
+          }
         });
   }
 
-  // values -> cache slot, unchanged
+  // values -> cache slot, unchanged (or as e4m3 codes of value / scale)
   if (to_cache) {
     const T* src = (const T*)a.v + row * a.G * D;
-    T* vc = (T*)a.v_cache;
     const int n_vec = a.G * D / kVec;
     for (int c = lane; c < n_vec; c += kWave) {
       const int h = c / (D / kVec), e = c % (D / kVec);
-      *(vec*)(vc + (((int64_t)b * a.G + h) * a.cap + slot) * D + e * kVec) =
-          *(const vec*)(src + c * kVec);
+      const int64_t off = (((int64_t)b * a.G + h) * a.cap + slot) * D + e * kVec;
+      const vec x = *(const vec*)(src + c * kVec);
+      if constexpr (kCanFp8) {
+        if (fp8) {
+          float f[kVec];
+          Io<T>::to_f32(x, f);
+          store_chunk_e4m3((uint8_t*)a.v_cache + off, f, a.v_inv_scale);
+          continue;
+        }
+      }
+      *(vec*)((T*)a.v_cache + off) = x;
     }
   }
 }

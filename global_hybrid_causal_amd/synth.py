@@ -69,6 +69,25 @@ def layer_inputs(seed: int, layer: int, B: int, T: int, H: int, G: int, d: int,
     }
 
 
+def e4m3_codes(shape, seed: int, *keys: int, device="cpu", exp_lo: int = 5,
+               exp_hi: int = 8) -> torch.Tensor:
+    """Random e4m3 bytes (uint8): uniform sign bit, exponent field uniform in
+    [exp_lo, exp_hi], uniform 3-bit mantissa.  The default fields give
+    magnitudes 0.25 .. 3.75; no NaN code is drawn."""
+    g = _generator(device, seed, keys)
+    sign = torch.randint(0, 2, shape, generator=g, device=device, dtype=torch.int32)
+    exp = torch.randint(exp_lo, exp_hi + 1, shape, generator=g, device=device, dtype=torch.int32)
+    man = torch.randint(0, 8, shape, generator=g, device=device, dtype=torch.int32)
+    return ((sign << 7) | (exp << 3) | man).to(torch.uint8)
+
+
+def e4m3_cache_fill(seed: int, layer: int, B: int, G: int, capacity: int, d: int,
+                    device="cpu") -> tuple[torch.Tensor, torch.Tensor]:
+    """Pre-filled e4m3 K and V caches [B, G, capacity, d] of random codes."""
+    return (e4m3_codes((B, G, capacity, d), seed, layer, CACHE_K, device=device),
+            e4m3_codes((B, G, capacity, d), seed, layer, CACHE_V, device=device))
+
+
 def cache_fill(seed: int, layer: int, B: int, G: int, capacity: int, d: int,
                device="cpu", dtype=torch.bfloat16) -> tuple[torch.Tensor, torch.Tensor]:
     """Pre-filled K and V caches [B, G, capacity, d] ~ N(0, 1)."""

@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define OLMO3_ABI_VERSION 3
+#define OLMO3_ABI_VERSION 4
 
 typedef enum olmo3_status {
   OLMO3_OK = 0,
@@ -70,7 +70,10 @@ typedef enum olmo3_status {
 } olmo3_status;
 
 enum { OLMO3_LAYER_SLIDING = 0, OLMO3_LAYER_FULL = 1 };
-enum { OLMO3_DTYPE_BF16 = 0, OLMO3_DTYPE_F32 = 1 };
+/* Element types.  OLMO3_DTYPE_BF16_E4M3 (bf16 activations with e4m3 caches)
+ * is accepted by olmo3_workspace_bytes only; the e4m3 entry points below
+ * imply it. */
+enum { OLMO3_DTYPE_BF16 = 0, OLMO3_DTYPE_F32 = 1, OLMO3_DTYPE_BF16_E4M3 = 2 };
 enum { OLMO3_MODE_PREFILL = 0, OLMO3_MODE_DECODE = 1 };
 
 /* RoPE / YaRN settings ("Case Study: OLMo 3", items 3 and 7).
@@ -201,6 +204,56 @@ int olmo3_attn_decode_ragged(int B, int H, int G, int d, int window, int layer_t
                              const void* v, const void* q_gain, const void* k_gain,
                              void* k_cache, void* v_cache, int64_t cache_capacity, void* out,
                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---- e4m3 key/value caches ----------------------------------------------
+ * Half the cache bytes of bf16, for decode, which streams the cache ("Olmo-3
+ * End-to-End Implementation", "Next Steps" lists quantization; "Olmo 3 7B",
+ * "SERVICEABILITY JOIN" records that sliding-window layers with a quantized
+ * cache break when the scales are applied twice or the window position is
+ * mishandled).  A cache element is one byte, an OCP e4m3 code c (sign, 4
+ * exponent bits with bias 7, 3 mantissa bits, largest finite 448, no
+ * infinities); it stands for c * k_scale in k_cache and c * v_scale in
+ * v_cache.  A key or value x is stored as the code nearest to
+ * x * (1/scale) (fp32 product, ties to even, saturated to +-448), keys taken
+ * after QK-norm and RoPE in fp32.  Activations are bf16.  Layouts, slots and
+ * errors as the bf16 entry points, with 1-byte cache elements; scales must
+ * be finite and > 0 (INVALID_ARG). */
+
+/* Append keys and values to e4m3 caches (as olmo3_kv_append). */
+int olmo3_kv_append_e4m3(int B, int T, int G, int d, int window, int layer_type,
+                         const olmo3_rope* rope, float eps, int64_t pos_offset, const void* k_pre,
+                         const void* v, const void* k_gain, void* k_cache, void* v_cache,
+                         float k_scale, float v_scale, int64_t cache_capacity, void* stream);
+
+/* Prefill of a first chunk (positions 0 .. T-1) into e4m3 caches: the
+ * attention uses the chunk's own rotated keys and values at bf16 precision;
+ * the cache receives their codes.  workspace:
+ * olmo3_workspace_bytes(OLMO3_MODE_PREFILL, ..., OLMO3_DTYPE_BF16_E4M3, ...). */
+int olmo3_attn_prefill_e4m3(int B, int T, int H, int G, int d, int window, int layer_type,
+                            const olmo3_rope* rope, float eps, const void* q_pre,
+                            const void* k_pre, const void* v, const void* q_gain,
+                            const void* k_gain, void* k_cache, void* v_cache, float k_scale,
+                            float v_scale, int64_t cache_capacity, void* out, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/* Decode against e4m3 caches: the new token's key and value are stored as
+ * codes first, then the query attends to the cache rows as stored (the new
+ * token's included), as olmo3_attn_decode does.  Requires d = 128 and
+ * H/G <= 8 (UNSUPPORTED otherwise).  The _phases form takes the phase bits
+ * of olmo3_attn_decode_phases. */
+int olmo3_attn_decode_e4m3(int B, int H, int G, int d, int window, int layer_type,
+                           const olmo3_rope* rope, float eps, int64_t pos, const void* q_pre,
+                           const void* k_pre, const void* v, const void* q_gain,
+                           const void* k_gain, void* k_cache, void* v_cache, float k_scale,
+                           float v_scale, int64_t cache_capacity, void* out, void* workspace,
+                           size_t workspace_bytes, void* stream);
+int olmo3_attn_decode_e4m3_phases(int phases, int B, int H, int G, int d, int window,
+                                  int layer_type, const olmo3_rope* rope, float eps, int64_t pos,
+                                  const void* q_pre, const void* k_pre, const void* v,
+                                  const void* q_gain, const void* k_gain, void* k_cache,
+                                  void* v_cache, float k_scale, float v_scale,
+                                  int64_t cache_capacity, void* out, void* workspace,
+                                  size_t workspace_bytes, void* stream);
 
 /* Stage-by-stage variants, for callers that time or overlap the kernels of
  * one call.  `phases` is a bit set of:

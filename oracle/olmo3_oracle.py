@@ -38,7 +38,10 @@ Parity unpinned by the pages: the rotation direction, the GQA grouping order,
 the YaRN ramp parameters and the softmax scale are shared conventions.
 
 No intermediate is rounded: inputs are taken exactly as given (bf16 values
-are exactly representable in fp64) and everything is computed in fp64.
+are exactly representable in fp64) and everything is computed in fp64.  The
+one exception is the optional e4m3 cache: a stored code is an integer that
+floating point decides, so it is decided as the kernels decide it (the fp32
+product of the value and 1/scale, then the nearest code), see ``e4m3_encode``.
 """
 
 from __future__ import annotations
@@ -55,6 +58,7 @@ __all__ = [
     "RopeParams", "layer_rope", "rope_rotate", "KvCacheRef", "cache_entries",
     "kv_bytes_per_token", "attend", "prefill_ref", "decode_ref",
     "attention_rows_ref", "decode_rows_ref", "ring_positions",
+    "E4M3_MAX", "e4m3_value", "e4m3_values", "e4m3_encode", "e4m3_store", "decode_e4m3_ref",
 ]
 
 SLIDING = "sliding"
@@ -263,6 +267,65 @@ def rope_rotate(x: np.ndarray, positions: np.ndarray, inv_freq: np.ndarray,
 
 
 # --------------------------------------------------------------------------
+# e4m3 cache codes
+# --------------------------------------------------------------------------
+# The pages name quantization only as a next step (page "Olmo-3 End-to-End
+# Implementation", "Next Steps") and as a failure mode of quantized caches on
+# sliding-window layers (page "Olmo 3 7B", "SERVICEABILITY JOIN"); they fix
+# no format.  The format used is the 8-bit E4M3 format of the OCP 8-bit
+# floating point specification: sign bit, 4 exponent bits with bias 7, 3
+# mantissa bits; exponent field 0 holds subnormals m/8 * 2^-6; the all-ones
+# exponent with mantissa 7 is NaN; there are no infinities, so the largest
+# finite value is 1.75 * 2^8 = 448.
+
+E4M3_MAX = 448.0
+
+
+def e4m3_value(code: int) -> float:
+    """The value a code stands for, from its bit fields."""
+    code = int(code) & 0xFF
+    sign = -1.0 if code & 0x80 else 1.0
+    exp = (code >> 3) & 0xF
+    man = code & 0x7
+    if exp == 0xF and man == 0x7:
+        return math.nan
+    if exp == 0:
+        return sign * (man / 8.0) * 2.0 ** -6
+    return sign * (1.0 + man / 8.0) * 2.0 ** (exp - 7)
+
+
+def e4m3_values() -> np.ndarray:
+    """Values of all 256 codes (NaN for the two NaN codes)."""
+    return np.array([e4m3_value(c) for c in range(256)])
+
+
+def e4m3_encode(x) -> np.ndarray:
+    """Nearest code to each value, as uint8.  Magnitudes above 448 saturate to
+    448; a value halfway between two codes takes the one whose mantissa is
+    even (consecutive non-negative codes differ by one in their low bit); the
+    sign bit is the value's sign (so -0.0 and small negatives give 0x80).
+    Brute force: compare against all 127 finite non-negative codes."""
+    x = np.asarray(x, dtype=np.float64)
+    mag = np.minimum(np.abs(x), E4M3_MAX)
+    codes = np.arange(0x7F)                      # 0x00 .. 0x7E, increasing values
+    vals = np.array([e4m3_value(c) for c in codes])
+    dist = np.abs(mag[..., None] - vals)         # [..., 127]
+    best = dist.min(axis=-1, keepdims=True)
+    cand = dist == best                          # one code, or two on a tie
+    even = cand & (codes % 2 == 0)
+    pick = np.where(even.any(axis=-1), np.argmax(even, axis=-1), np.argmax(cand, axis=-1))
+    out = codes[pick].astype(np.uint8)
+    return np.where(np.signbit(x), out | 0x80, out).astype(np.uint8)
+
+
+def e4m3_store(x, scale: float) -> np.ndarray:
+    """Code stored for value x with cache scale `scale`: the kernels form the
+    fp32 product x * fp32(1/scale) and take its nearest code."""
+    inv = np.float32(1.0 / np.float64(scale))
+    return e4m3_encode(np.asarray(x, dtype=np.float32) * inv)
+
+
+# --------------------------------------------------------------------------
 # Per-layer-type KV cache
 # --------------------------------------------------------------------------
 
@@ -296,11 +359,14 @@ class KvCacheRef:
     """
 
     def __init__(self, kind: str, window: int, capacity: int, B: int, G: int,
-                 d: int, rotated: bool = True):
+                 d: int, rotated: bool = True, e4m3_scales: tuple | None = None):
         if kind == SLIDING and capacity != window:
             raise ValueError("a sliding layer's ring has exactly `window` slots")
         self.kind, self.window, self.capacity = kind, window, capacity
         self.B, self.G, self.d, self.rotated = B, G, d, rotated
+        # e4m3 storage: (k_scale, v_scale); a stored key is the value of its
+        # code times k_scale (see e4m3_store), a value likewise
+        self.e4m3_scales = e4m3_scales
         self.k = np.zeros((B, G, capacity, d))
         self.v = np.zeros((B, G, capacity, d))
         self.pos = np.full(capacity, -1, dtype=np.int64)
@@ -313,6 +379,11 @@ class KvCacheRef:
 
     def append(self, k: np.ndarray, v: np.ndarray, positions: np.ndarray) -> None:
         """k, v: [B, n, G, d] for the absolute ``positions`` (length n)."""
+        if self.e4m3_scales is not None:
+            ks, vs = self.e4m3_scales
+            table = e4m3_values()
+            k = table[e4m3_store(k, ks)] * ks
+            v = table[e4m3_store(v, vs)] * vs
         for j, p in enumerate(np.asarray(positions, dtype=np.int64)):
             s = self.slot(int(p))
             self.k[:, :, s, :] = k[:, j]
@@ -430,6 +501,31 @@ def decode_ref(q_pre, k_pre, v, q_gain, k_gain, *, H: int, G: int, d: int,
     out = prefill_ref(q_pre, k_pre, v, q_gain, k_gain, H=H, G=G, d=d, kind=kind,
                       window=window, rope=rope, eps=eps, pos_offset=pos, cache=cache)
     return out[:, 0, :]
+
+
+def decode_e4m3_ref(q_pre, k_pre, v, q_gain, k_gain, *, H: int, G: int, d: int,
+                    kind: str, window: int, rope: RopeParams, eps: float = 1e-6,
+                    pos: int, cache: KvCacheRef) -> np.ndarray:
+    """Single-token decode against an e4m3 cache: the token's rotated key and
+    its value are stored as codes at the slot of ``pos`` first, and the query
+    then attends to the cache as stored, the new token's dequantized key and
+    value included.  q_pre [B, H*d], k_pre and v [B, G*d]; returns [B, H*d]."""
+    if cache.e4m3_scales is None:
+        raise ValueError("decode_e4m3_ref needs a cache with e4m3 storage")
+    q_pre = np.asarray(q_pre, dtype=np.float64)[:, None, :]
+    k_pre = np.asarray(k_pre, dtype=np.float64)[:, None, :]
+    v = np.asarray(v, dtype=np.float64)[:, None, :]
+    B = q_pre.shape[0]
+    qh, kh, vh = _project_heads(q_pre, k_pre, v, q_gain, k_gain, H, G, d, eps)
+    w, m = layer_rope(rope, kind, d)
+    p = np.array([pos], dtype=np.int64)
+    q_rot = rope_rotate(qh, p, w, m)
+    cache.append(rope_rotate(kh, p, w, m), vh, p)
+    keys, vals, key_pos = cache.contents()
+    out = np.zeros((B, 1, H, d))
+    for b in range(B):
+        out[b] = attend(q_rot[b], p, keys[b], vals[b], key_pos, kind, window)
+    return out.reshape(B, H * d)
 
 
 def attention_rows_ref(q_pre_rows, q_rows_pos, k_pre_keys, v_keys, k_keys_pos,

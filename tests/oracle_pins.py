@@ -472,4 +472,110 @@ def check_sampled_functions_equal_whole_output():
         _close(got, ref[0].reshape(H, d)[3:6], 1e-12, f"decode rows {kind}")
 
 
+# ------------------------------------------------------------- e4m3 cache
+# The format is the OCP 8-bit floating point E4M3 format (the pages fix none):
+# its table and its round-to-nearest-even encoding are pinned to torch's own
+# float8_e4m3fn conversion, an implementation independent of the oracle's
+# brute force, and to closed forms of the format's definition.
+
+def check_e4m3_table_matches_torch():
+    codes = torch.arange(256, dtype=torch.uint8)
+    want = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = O.e4m3_values()
+    assert np.array_equal(np.isnan(got), np.isnan(want))
+    fin = ~np.isnan(want)
+    assert np.array_equal(got[fin], want[fin])
+
+
+def check_e4m3_encode_matches_torch_in_range():
+    rng = _rng(71)
+    table = O.e4m3_values()
+    pos_vals = np.sort(table[:0x7F])
+    mids = (pos_vals[:-1] + pos_vals[1:]) / 2          # exact ties
+    x = np.concatenate([rng.normal(0, 1, 2000), rng.normal(0, 100, 2000),
+                        rng.normal(0, 0.01, 2000), rng.uniform(-448, 448, 2000),
+                        mids, -mids, pos_vals, -pos_vals, [0.0, -0.0, 448.0, -448.0]])
+    x = x[np.abs(x) <= 448.0].astype(np.float32)        # in range: no saturation
+    want = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = O.e4m3_encode(x.astype(np.float64))
+    assert np.array_equal(got, want), np.argwhere(got != want)[:5]
+
+
+def check_e4m3_closed_forms():
+    v = O.e4m3_value
+    assert v(0x7E) == 1.75 * 2 ** 8 == O.E4M3_MAX
+    assert v(0x01) == 2.0 ** -9 and v(0x08) == 2.0 ** -6 and v(0x38) == 1.0
+    assert v(0x07) == 7 * 2.0 ** -9 and v(0xB8) == -1.0
+    assert math.isnan(v(0x7F)) and math.isnan(v(0xFF))
+    table = O.e4m3_values()
+    assert len(set(table[~np.isnan(table)].tolist())) == 253   # 254 finite codes, +-0 equal
+    enc = O.e4m3_encode
+    assert list(enc([1e6, -1e6, 449.0, 463.9, 464.0, 1e30])) == [0x7E, 0xFE, 0x7E, 0x7E, 0x7E, 0x7E]
+    # ties go to the even mantissa: 1 + 1/16 -> 1.0, 1 + 3/16 -> 1.25, 2^-10 -> 0
+    assert list(enc([1.0625, 1.1875, 2.0 ** -10, 3 * 2.0 ** -10])) == [0x38, 0x3A, 0x00, 0x02]
+    # half-ulp error: relative 2^-4 on normals, absolute 2^-10 on subnormals
+    rng = _rng(73)
+    x = np.concatenate([rng.uniform(2.0 ** -6, 448, 5000), rng.uniform(0, 2.0 ** -6, 5000)])
+    err = np.abs(table[enc(x)] - x)
+    normal = x >= 2.0 ** -6
+    assert (err[normal] <= 2.0 ** -4 * x[normal]).all()
+    assert (err[~normal] <= 2.0 ** -10).all()
+
+
+def check_e4m3_cache_stores_scale_once():
+    """A value that is exactly code * scale is stored exactly: a scale applied
+    twice, or not at all, moves it (x * fp32(1/3) lands within 3e-8 relative of
+    the code, far from any tie)."""
+    rng = _rng(79)
+    table = O.e4m3_values()
+    B, G, d, w = 1, 2, 8, 4
+    for ks, vs in ((0.5, 3.0), (3.0, 0.5)):
+        c = O.KvCacheRef(O.SLIDING, w, w, B, G, d, e4m3_scales=(ks, vs))
+        ck = rng.integers(0, 0x7F, (B, 3, G, d)) | rng.integers(0, 2, (B, 3, G, d)) * 0x80
+        cv = rng.integers(0, 0x7F, (B, 3, G, d)) | rng.integers(0, 2, (B, 3, G, d)) * 0x80
+        k, v = table[ck] * ks, table[cv] * vs
+        c.append(k, v, np.array([5, 6, 7]))
+        kk, vv, pos = c.contents()
+        order = np.argsort(pos)
+        assert np.array_equal(kk[:, order], k) and np.array_equal(vv[:, order], v)
+        assert list(pos[order]) == [5, 6, 7]
+    # and an arbitrary value lands within half a step of the grid times the scale
+    c = O.KvCacheRef(O.FULL, w, 8, 1, 1, 4, e4m3_scales=(0.37, 0.37))
+    x = rng.normal(0, 1, (1, 1, 1, 4))
+    c.append(x, x, np.array([0]))
+    assert (np.abs(c.k[0, 0, 0] - x[0, 0, 0]) <= 2.0 ** -4 * np.abs(x[0, 0, 0]) + 0.37 * 2.0 ** -10).all()
+
+
+def check_decode_e4m3_equals_decode_on_the_grid():
+    """When every cached row and the new token's key and value are exact
+    e4m3 multiples of the scales (the new key is zero: k_pre = 0 normalises to
+    0), storing codes changes nothing, so e4m3 decode equals plain decode;
+    it also means the new token is stored before the attention reads."""
+    rng = _rng(83)
+    table = O.e4m3_values()
+    B, H, G, d, w, pos = 2, 4, 2, 16, 6, 9
+    rope = O.RopeParams(theta=10000.0)
+    for kind in (O.SLIDING, O.FULL):
+        cap = w if kind == O.SLIDING else pos + 1
+        ks, vs = 0.25, 2.0
+        ck = rng.integers(0x20, 0x48, (B, G, cap, d)) | rng.integers(0, 2, (B, G, cap, d)) * 0x80
+        cv = rng.integers(0x20, 0x48, (B, G, cap, d)) | rng.integers(0, 2, (B, G, cap, d)) * 0x80
+        caches = []
+        for e4 in (False, True):
+            c = O.KvCacheRef(kind, w, cap, B, G, d, e4m3_scales=(ks, vs) if e4 else None)
+            c.k[:] = table[ck] * ks
+            c.v[:] = table[cv] * vs
+            c.pos[:] = O.ring_positions(kind, w, cap, pos)
+            caches.append(c)
+        q = rng.normal(0, 1, (B, H * d))
+        k0 = np.zeros((B, G * d))
+        v_new = table[rng.integers(0x20, 0x48, (B, G * d))] * vs
+        qg, kg = rng.uniform(0.5, 1.5, H * d), rng.uniform(0.5, 1.5, G * d)
+        a = O.decode_ref(q, k0, v_new, qg, kg, H=H, G=G, d=d, kind=kind, window=w, rope=rope,
+                         pos=pos, cache=caches[0])
+        b = O.decode_e4m3_ref(q, k0, v_new, qg, kg, H=H, G=G, d=d, kind=kind, window=w,
+                              rope=rope, pos=pos, cache=caches[1])
+        _close(a, b, 1e-12, f"e4m3 decode on the grid, {kind}")
+
+
 ALL_CHECKS = [v for k, v in sorted(globals().items()) if k.startswith("check_") and callable(v)]

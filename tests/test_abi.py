@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version():
-    assert A.olmo3_abi_version() == A.ABI_VERSION == 3
+    assert A.olmo3_abi_version() == A.ABI_VERSION == 4
 
 
 def test_layer_type_matches_oracle_bit_exact():
@@ -262,3 +262,38 @@ def ragged_decode_call(**kw):
 ])
 def test_ragged_decode_rejects(kw, status):
     assert ragged_decode_call(**kw) == status
+
+
+def e4m3_decode_call(**kw):
+    a = dict(B=2, H=4, G=2, d=128, window=16, layer_type=0, eps=1e-6, pos=20, cap=16,
+             ks=0.5, vs=0.5)
+    a.update(kw)
+    p = [fake(i) for i in range(9)]
+    r = ctypes.byref(A.Rope(theta=1e4).to_c())
+    return A.lib().olmo3_attn_decode_e4m3(
+        a["B"], a["H"], a["G"], a["d"], a["window"], a["layer_type"], r, a["eps"], a["pos"],
+        *p[:7], a["ks"], a["vs"], a["cap"], p[7], p[8], 1 << 34, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ks=0.0), A.ERR_INVALID_ARG),
+    (dict(vs=-1.0), A.ERR_INVALID_ARG),
+    (dict(ks=float("inf")), A.ERR_INVALID_ARG),
+    (dict(vs=float("nan")), A.ERR_INVALID_ARG),
+    (dict(ks=1e-45), A.ERR_INVALID_ARG),          # 1/scale overflows
+    (dict(d=64), A.ERR_UNSUPPORTED),              # split kernel only
+    (dict(H=18, G=2), A.ERR_UNSUPPORTED),         # 9 query heads per key/value head
+    (dict(cap=15), A.ERR_CAPACITY),
+    (dict(pos=-1), A.ERR_INVALID_ARG),
+])
+def test_e4m3_decode_rejects(kw, status):
+    assert e4m3_decode_call(**kw) == status
+
+
+def test_e4m3_workspace_adds_rotated_keys_on_full_layers():
+    L = A.lib()
+    plain = L.olmo3_workspace_bytes(0, 1, 100, 4, 2, 128, 1, A.DTYPE_BF16, 100)
+    e4m3 = L.olmo3_workspace_bytes(0, 1, 100, 4, 2, 128, 1, A.DTYPE_BF16_E4M3, 100)
+    assert e4m3 - plain >= 100 * 2 * 128 * 2
+    assert L.olmo3_workspace_bytes(0, 1, 100, 4, 2, 128, 0, A.DTYPE_BF16_E4M3, 16) == \
+        L.olmo3_workspace_bytes(0, 1, 100, 4, 2, 128, 0, A.DTYPE_BF16, 16)

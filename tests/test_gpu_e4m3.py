@@ -1,0 +1,200 @@
+"""e4m3 key/value caches: stored codes and decode outputs against the fp64
+oracle, with scales that are not powers of two so that a scale applied twice
+or not at all shows, and decode positions on both sides of the ring's window
+boundary (the failure mode of quantized caches on sliding-window layers that
+the page "Olmo 3 7B" records, "SERVICEABILITY JOIN").
+
+Value codes are compared bit for bit: both sides decide them in fp32 from
+the same bf16 input.  Key codes come from rotated keys that the kernel
+computes in fp32 and the oracle in fp64, so a code may differ from the
+oracle's by one step, and only where the key lies at a rounding midpoint."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from global_hybrid_causal_amd import attn as A
+from global_hybrid_causal_amd import synth
+from gpu_util import KINDS, assert_close, host, host_inputs, inputs, oracle_rope
+
+pytestmark = pytest.mark.gpu
+
+BF16 = torch.bfloat16
+KS, VS = 0.37, 1.9
+TABLE = O.e4m3_values()
+
+
+def _log(*a):
+    print(*a, flush=True)
+
+
+def _codes(t):
+    return t.cpu().numpy()
+
+
+def _key_x32(k_rot, scale):
+    """The fp32 quantity whose nearest code is stored (as the kernel forms it)."""
+    return np.asarray(k_rot, dtype=np.float32) * np.float32(1.0 / np.float64(scale))
+
+
+def _check_key_codes(got, x32, what):
+    want = O.e4m3_encode(x32)
+    diff = got != want
+    if not diff.any():
+        return
+    mid = (TABLE[got[diff]] + TABLE[want[diff]]) / 2
+    x = x32[diff].astype(np.float64)
+    assert (np.abs(x - mid) <= 1e-4 * np.abs(x) + 1e-6).all(), f"{what}: key codes off a midpoint differ"
+    assert diff.mean() < 1e-3, f"{what}: {int(diff.sum())} key codes differ"
+
+
+def _rotated_keys(hx, kind, rope, positions, G, d):
+    w_, m_ = O.layer_rope(oracle_rope(rope), kind, d)
+    B, T = hx["k_pre"].shape[:2]
+    kh = O.rms_norm(hx["k_pre"], hx["k_gain"], 1e-6).reshape(B, T, G, d)
+    return O.rope_rotate(kh, np.asarray(positions), w_, m_)
+
+
+def _check_slots(kc, vc, before_k, before_v, slots, k_rot, v_new, what):
+    """slots[j] holds position j of k_rot / v_new [B, n, G, d]; other slots keep their bytes."""
+    gk, gv = _codes(kc), _codes(vc)
+    slots = np.asarray(slots)
+    got_v = gv[:, :, slots].transpose(0, 2, 1, 3)
+    assert np.array_equal(got_v, O.e4m3_store(v_new, VS)), f"{what}: value codes"
+    _check_key_codes(gk[:, :, slots].transpose(0, 2, 1, 3), _key_x32(k_rot, KS), what)
+    rest = np.setdiff1d(np.arange(gk.shape[2]), slots)
+    assert np.array_equal(gk[:, :, rest], before_k[:, :, rest]), f"{what}: key slot overwritten"
+    assert np.array_equal(gv[:, :, rest], before_v[:, :, rest]), f"{what}: value slot overwritten"
+
+
+@pytest.mark.parametrize("lt,T,pos_offset,cap", [(0, 50, 0, 16), (0, 5, 30, 16), (1, 50, 5, 60)])
+def test_e4m3_append(lt, T, pos_offset, cap):
+    B, G, d, w = 2, 2, 128, 16
+    kind = KINDS[lt]
+    rope = A.Rope(theta=500000.0, yarn=True, factor=4.0, orig_ctx=64)
+    x = inputs(61, lt, B, T, G, G, d, BF16)
+    kc, vc = synth.e4m3_cache_fill(61, lt, B, G, cap, d, device="cuda")
+    bk, bv = _codes(kc), _codes(vc)
+    A.olmo3_kv_append_e4m3(x["k_pre"], x["v"], x["k_gain"], kc, vc, k_scale=KS, v_scale=VS,
+                           window=w, layer_type=lt, rope=rope, pos_offset=pos_offset)
+    hx = host_inputs(x)
+    positions = pos_offset + np.arange(T)
+    keep = positions[-w:] if kind == O.SLIDING else positions
+    idx = keep - pos_offset
+    slots = keep % w if kind == O.SLIDING else keep
+    k_rot = _rotated_keys(hx, kind, rope, positions, G, d)[:, idx]
+    v_new = hx["v"].reshape(B, T, G, d)[:, idx]
+    _check_slots(kc, vc, bk, bv, slots, k_rot, v_new, f"append {lt} {T} {pos_offset}")
+
+
+PREFILL = [
+    # B, T, H, G, window, layer_type, yarn
+    (1, 300, 4, 4, 64, 0, False),
+    (2, 129, 10, 2, 4096, 1, True),
+    (1, 1000, 8, 8, 4096, 1, True),
+    (2, 77, 4, 2, 100, 0, False),
+]
+
+
+@pytest.mark.parametrize("case", PREFILL, ids=[str(c) for c in PREFILL])
+def test_e4m3_prefill_vs_oracle(case):
+    """The chunk attends to its own keys at bf16 precision and stores codes."""
+    B, T, H, G, w, lt, yarn = case
+    d = 128
+    _log("e4m3 prefill", case)
+    kind = KINDS[lt]
+    rope = A.Rope(theta=500000.0, yarn=yarn, factor=8.0, orig_ctx=256)
+    cap = w if kind == O.SLIDING else T + 3
+    x = inputs(67, lt, B, T, H, G, d, BF16)
+    kc, vc = synth.e4m3_cache_fill(67, lt, B, G, cap, d, device="cuda")
+    bk, bv = _codes(kc), _codes(vc)
+    out = torch.empty_like(x["q_pre"])
+    ws = A.workspace(A.MODE_PREFILL, B, T, H, G, d, lt, A.DTYPE_BF16_E4M3, cap, "cuda")
+    A.olmo3_attn_prefill_e4m3(x["q_pre"], x["k_pre"], x["v"], x["q_gain"], x["k_gain"], kc, vc,
+                              out, ws, k_scale=KS, v_scale=VS, window=w, layer_type=lt, rope=rope)
+    hx = host_inputs(x)
+    ref_cache = O.KvCacheRef(kind, w, cap, B, G, d, e4m3_scales=(KS, VS))
+    ref = O.prefill_ref(**hx, H=H, G=G, d=d, kind=kind, window=w, rope=oracle_rope(rope),
+                        cache=ref_cache)
+    err = assert_close(host(out), ref, what=f"e4m3 prefill {case}")
+    _log("  max abs / rel err", err)
+    positions = np.arange(T)
+    keep = positions[-w:] if kind == O.SLIDING else positions
+    slots = keep % w if kind == O.SLIDING else keep
+    k_rot = _rotated_keys(hx, kind, rope, positions, G, d)[:, keep]
+    _check_slots(kc, vc, bk, bv, slots, k_rot, hx["v"].reshape(B, T, G, d)[:, keep],
+                 f"e4m3 prefill {case}")
+
+
+DECODE = [
+    # B, H, G, window, layer_type, pos, cap
+    *[(3, 8, 2, 128, 0, p, 128) for p in (0, 126, 127, 128, 129, 255, 256, 1000)],
+    (2, 10, 2, 4096, 1, 399, 400),        # group 5, linear
+    (4, 16, 2, 300, 0, 5000, 300),        # group 8
+    (1, 4, 1, 4096, 1, 19999, 20000),     # 64 splits
+    (2, 8, 8, 4096, 0, 4096, 4096),       # the 7B window, first wrap
+]
+
+
+@pytest.mark.parametrize("case", DECODE, ids=[str(c) for c in DECODE])
+def test_e4m3_decode_vs_oracle(case):
+    B, H, G, w, lt, pos, cap = case
+    d = 128
+    _log("e4m3 decode", case)
+    kind = KINDS[lt]
+    rope = A.Rope(theta=500000.0, yarn=True, factor=8.0, orig_ctx=512)
+    kc, vc = synth.e4m3_cache_fill(71, lt, B, G, cap, d, device="cuda")
+    bk, bv = _codes(kc), _codes(vc)
+    x = inputs(71, 10 + lt, B, 1, H, G, d, BF16)
+    q, k, v = x["q_pre"][:, 0].contiguous(), x["k_pre"][:, 0].contiguous(), x["v"][:, 0].contiguous()
+    out = torch.empty_like(q)
+    ws = A.workspace(A.MODE_DECODE, B, 1, H, G, d, lt, A.DTYPE_BF16_E4M3, cap, "cuda")
+    A.olmo3_attn_decode_e4m3(q, k, v, x["q_gain"], x["k_gain"], kc, vc, out, ws, k_scale=KS,
+                             v_scale=VS, window=w, layer_type=lt, rope=rope, pos=pos)
+    hx = host_inputs(x)
+    ref_cache = O.KvCacheRef(kind, w, cap, B, G, d, e4m3_scales=(KS, VS))
+    ref_cache.k[:] = TABLE[bk] * KS
+    ref_cache.v[:] = TABLE[bv] * VS
+    ref_cache.pos[:] = O.ring_positions(kind, w, cap, pos)
+    ref = O.decode_e4m3_ref(hx["q_pre"][:, 0], hx["k_pre"][:, 0], hx["v"][:, 0], hx["q_gain"],
+                            hx["k_gain"], H=H, G=G, d=d, kind=kind, window=w,
+                            rope=oracle_rope(rope), pos=pos, cache=ref_cache)
+    err = assert_close(host(out), ref, what=f"e4m3 decode {case}")
+    _log("  max abs / rel err", err)
+    slot = pos % w if kind == O.SLIDING else pos
+    k_rot = _rotated_keys({"k_pre": hx["k_pre"], "k_gain": hx["k_gain"]}, kind, rope, [pos], G, d)
+    _check_slots(kc, vc, bk, bv, [slot], k_rot, hx["v"].reshape(B, 1, G, d), f"e4m3 decode {case}")
+
+
+@pytest.mark.parametrize("lt,w,pos,back", [
+    (0, 128, 127, 127), (0, 128, 128, 127), (0, 128, 129, 127), (0, 128, 401, 127),
+    (0, 128, 128, 128), (0, 128, 401, 128),      # the evicted position: its slot holds the new token
+    (0, 128, 300, 0), (1, 128, 300, 300), (1, 128, 300, 0), (1, 128, 300, 1)])
+def test_e4m3_window_edge_planted_value(lt, w, pos, back):
+    """q = 0 makes the weights uniform over the rows the decode reads.  Every
+    value code is 0 except one planted at the slot of position pos - back, and
+    the new token's value is 0, so each output is exactly v_scale * 2 / n when
+    the planted row is read (n = min(pos+1, w) on the ring, pos+1 on the
+    linear cache) and 0 when its slot now holds the new token: this fixes the
+    window edge and that v_scale is applied once."""
+    B, H, G, d = 2, 4, 2, 128
+    kind = KINDS[lt]
+    cap = w if lt == 0 else pos + 1
+    kc, _ = synth.e4m3_cache_fill(73, lt, B, G, cap, d, device="cuda")
+    vc = torch.zeros_like(kc)
+    p_star = pos - back
+    vc[:, :, p_star % cap] = 0x40  # code 0x40 = 2.0
+    x = inputs(73, lt, B, 1, H, G, d, BF16)
+    q = torch.zeros_like(x["q_pre"][:, 0])
+    k = x["k_pre"][:, 0].contiguous()
+    v = torch.zeros_like(x["v"][:, 0])
+    out = torch.empty_like(q)
+    ws = A.workspace(A.MODE_DECODE, B, 1, H, G, d, lt, A.DTYPE_BF16_E4M3, cap, "cuda")
+    A.olmo3_attn_decode_e4m3(q, k, v, x["q_gain"], x["k_gain"], kc, vc, out, ws, k_scale=KS,
+                             v_scale=VS, window=w, layer_type=lt, rope=A.Rope(), pos=pos)
+    got = host(out)
+    n = min(pos + 1, w) if lt == 0 else pos + 1
+    overwritten = p_star % cap == pos % cap  # the new token (value 0) took the slot
+    want = 0.0 if overwritten else 2.0 * VS / n
+    assert_close(got, np.full_like(got, want), 0.0, 2.0 ** -8, f"planted {lt} {pos} {back}")

@@ -152,6 +152,52 @@ def _cache_entries_all(kind, window, context):
     return context
 
 
+def _e4m3_value_bias8(code):
+    code = int(code) & 0xFF
+    sign = -1.0 if code & 0x80 else 1.0
+    exp, man = (code >> 3) & 0xF, code & 0x7
+    if exp == 0xF and man == 0x7:
+        return math.nan
+    if exp == 0:
+        return sign * (man / 8.0) * 2.0 ** -7
+    return sign * (1.0 + man / 8.0) * 2.0 ** (exp - 8)
+
+
+def _e4m3_encode_factory(mode):
+    def enc(x):
+        x = np.asarray(x, dtype=np.float64)
+        mag = np.minimum(np.abs(x), 448.0)
+        codes = np.arange(0x7F)
+        vals = np.array([_orig["e4m3_value"](c) for c in codes])
+        if mode == "truncate":
+            pick = np.searchsorted(vals, mag, side="right") - 1
+        else:  # ties away from zero
+            dist = np.abs(mag[..., None] - vals)
+            best = dist.min(axis=-1, keepdims=True)
+            pick = vals.size - 1 - np.argmax((dist == best)[..., ::-1], axis=-1)
+        out = codes[pick].astype(np.uint8)
+        return np.where(np.signbit(x), out | 0x80, out).astype(np.uint8)
+    return enc
+
+
+def _e4m3_store_twice(x, scale):
+    inv = np.float32(1.0 / np.float64(scale))
+    return _orig["e4m3_encode"](np.asarray(x, dtype=np.float32) * inv * inv)
+
+
+def _decode_e4m3_drops_new_token(q_pre, k_pre, v, q_gain, k_gain, *, H, G, d, kind, window, rope,
+                                 eps=1e-6, pos, cache):
+    keys, vals, key_pos = cache.contents()
+    q_pre = np.asarray(q_pre, dtype=np.float64)[:, None, :]
+    B = q_pre.shape[0]
+    qh = O.rms_norm(q_pre, q_gain, eps).reshape(B, 1, H, d)
+    w, m = O.layer_rope(rope, kind, d)
+    p = np.array([pos])
+    q_rot = O.rope_rotate(qh, p, w, m)
+    return np.stack([O.attend(q_rot[b], p, keys[b], vals[b], key_pos, kind, window)
+                     for b in range(B)]).reshape(B, H * d)
+
+
 MUTANTS = {
     "mask t-s <= window": dict(sliding_window_mask=_mask_le_window, mask_at_positions=_mask_at_le_window),
     "mask not causal": dict(mask_at_positions=_mask_at_noncausal),
@@ -175,6 +221,11 @@ MUTANTS = {
     "ring slot p mod (w+1)": dict(KvCacheRef=_RingOffByOne),
     "ring keeps first writer": dict(KvCacheRef=_RingKeepsFirst),
     "no window bound on cache": dict(cache_entries=_cache_entries_all),
+    "e4m3 exponent bias 8": dict(e4m3_value=_e4m3_value_bias8),
+    "e4m3 truncates": dict(e4m3_encode=_e4m3_encode_factory("truncate")),
+    "e4m3 ties away from zero": dict(e4m3_encode=_e4m3_encode_factory("away")),
+    "e4m3 scale applied twice": dict(e4m3_store=_e4m3_store_twice),
+    "e4m3 decode drops the new token": dict(decode_e4m3_ref=_decode_e4m3_drops_new_token),
 }
 
 
