@@ -127,13 +127,20 @@ __device__ __forceinline__ int packed_sequence(const int32_t* cu, int B, int64_t
   return min(b, B - 1);
 }
 
-template <typename T, int D>
+// kRoles: one workgroup per token and one wavefront per part of it (queries,
+// keys, values), so that the three dependent load / reduce / store chains of
+// a token overlap; used when there are too few tokens to fill the GPU (decode).
+// Otherwise one wavefront per token handles all three parts in turn.
+template <typename T, int D, bool kRoles>
 __global__ __launch_bounds__(kWave * kTokensPerBlock) void qknorm_rope_append_kernel(
     PrologueArgs a, RopeTable rope) {
   typedef typename Io<T>::vec vec;
   constexpr int kVec = Io<T>::kVec;
   const int lane = threadIdx.x % kWave;
-  const int64_t row = (int64_t)blockIdx.x * kTokensPerBlock + threadIdx.x / kWave;
+  const int64_t row = kRoles ? (int64_t)blockIdx.x
+                             : (int64_t)blockIdx.x * kTokensPerBlock + threadIdx.x / kWave;
+  const int role = kRoles ? (int)(threadIdx.x / kWave) : -1;
+  const bool do_q = !kRoles || role == 0, do_k = !kRoles || role == 1, do_v = !kRoles || role == 2;
   // (sequence, index in it, its length, absolute position) of this row
   int b;
   int64_t t, len, pos;
@@ -155,10 +162,10 @@ __global__ __launch_bounds__(kWave * kTokensPerBlock) void qknorm_rope_append_ke
   if (pos < 0) return;
 
   float cs[kVec], sn[kVec];
-  rope_angles<T, D>(lane, pos, rope, cs, sn);
+  if (do_q || do_k) rope_angles<T, D>(lane, pos, rope, cs, sn);
 
   // queries -> q_out [rows][H][D]
-  if (a.q_pre) {
+  if (do_q && a.q_pre) {
     const T* src = (const T*)a.q_pre + row * a.H * D;
     T* qo = (T*)a.q_out + row * a.H * D;
     norm_rope_row<T, D>(src, (const T*)a.q_gain, a.H, a.eps, lane, cs, sn, rope.mscale,
@@ -176,7 +183,7 @@ __global__ __launch_bounds__(kWave * kTokensPerBlock) void qknorm_rope_append_ke
   const bool fp8 = a.cache_fp8;
 
   // keys -> optional strided copy (prefill workspace) and the cache slot
-  {
+  if (do_k) {
     const T* src = (const T*)a.k_pre + row * a.G * D;
     T* ko = (T*)a.k_out;
     norm_rope_row<T, D>(
@@ -206,7 +213,7 @@ __global__ __launch_bounds__(kWave * kTokensPerBlock) void qknorm_rope_append_ke
   }
 
   // values -> cache slot, unchanged (or as e4m3 codes of value / scale)
-  if (to_cache) {
+  if (do_v && to_cache) {
     const T* src = (const T*)a.v + row * a.G * D;
     const int n_vec = a.G * D / kVec;
     for (int c = lane; c < n_vec; c += kWave) {
@@ -226,11 +233,18 @@ __global__ __launch_bounds__(kWave * kTokensPerBlock) void qknorm_rope_append_ke
   }
 }
 
+// Up to this many tokens the per-part wavefronts are used.
+constexpr int64_t kRolesMaxRows = 2048;
+
 template <typename T, int D>
 hipError_t launch_prologue_t(const PrologueArgs& a, const RopeTable& rope, hipStream_t s) {
   const int64_t rows = a.cu_seqlens ? a.n_rows : (int64_t)a.B * a.T;
-  const int blocks = (int)((rows + kTokensPerBlock - 1) / kTokensPerBlock);
-  qknorm_rope_append_kernel<T, D><<<blocks, kWave * kTokensPerBlock, 0, s>>>(a, rope);
+  if (rows <= kRolesMaxRows) {
+    qknorm_rope_append_kernel<T, D, true><<<(int)rows, kWave * 3, 0, s>>>(a, rope);
+  } else {
+    const int blocks = (int)((rows + kTokensPerBlock - 1) / kTokensPerBlock);
+    qknorm_rope_append_kernel<T, D, false><<<blocks, kWave * kTokensPerBlock, 0, s>>>(a, rope);
+  }
   return hipGetLastError();
 }
 
