@@ -99,11 +99,43 @@ __global__ __launch_bounds__(64) void attn_generic_kernel(AttnArgs a) {
 // the 4 groups of a wavefront with lane exchanges and then across
 // wavefronts in LDS, into one partial (m, l, o) per head and split.
 // ---------------------------------------------------------------------------
+// Sum over the 16 lanes of a DPP row, returned in all of them: neighbours,
+// pairs of neighbours, the two quads of each half row (mirrored), then the
+// two half rows (mirrored); each step is one add with a DPP operand.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_operand(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), kCtrl,
+                                                              0xF, 0xF, false));
+}
+__device__ __forceinline__ float row16_sum(float x) {
+  x += dpp_operand<0xB1>(x);   // quad_perm [1, 0, 3, 2]
+  x += dpp_operand<0x4E>(x);   // quad_perm [2, 3, 0, 1]
+  x += dpp_operand<0x141>(x);  // row_half_mirror
+  x += dpp_operand<0x140>(x);  // row_mirror
+  return x;
+}
+
+__device__ __forceinline__ float dot2(bf16x2 a, bf16x2 b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(a, b, c, false);
+}
+__device__ __forceinline__ bf16x2 pair(const bf16x8& v, int i) {
+  return bf16x2{v[2 * i], v[2 * i + 1]};
+}
+
 // kFp8: the caches hold e4m3 codes (a 128-byte row, 8 bytes per lane);
 // k_scale is folded into the query and v_scale into the partial output, so
 // each scale multiplies the result exactly once.
+// Waves per SIMD the register budget is held to: enough rows in flight per
+// CU to cover HBM latency (each wavefront streams 8 KiB per iteration).
 template <int GRP, bool kFp8>
-__global__ __launch_bounds__(dec::kThreads) void decode_split_kernel(DecodeArgs a) {
+constexpr int decode_waves_per_eu() {
+  return kFp8 ? (GRP <= 2 ? 6 : (GRP <= 3 ? 4 : 2)) : (GRP <= 1 ? 8 : (GRP <= 5 ? 4 : 2));
+}
+
+template <int GRP, bool kFp8>
+__global__ __launch_bounds__(dec::kThreads)
+__attribute__((amdgpu_waves_per_eu(decode_waves_per_eu<GRP, kFp8>()))) void decode_split_kernel(
+    DecodeArgs a) {
   using namespace dec;
   const int sp = blockIdx.x % a.splits;
   const int bg = blockIdx.x / a.splits;
@@ -120,14 +152,19 @@ __global__ __launch_bounds__(dec::kThreads) void decode_split_kernel(DecodeArgs 
   const int li = lane & 15;
   const int grp = tid >> 4;
 
-  float q[GRP][8];
-  const float qs = kFp8 ? a.scale_log2 * a.k_scale : a.scale_log2;
+  static_assert(kUnroll == 4, "rows are paired for the bf16 dot products");
+  // queries: bf16 pairs (bf16 caches), or fp32 scaled by k_scale (e4m3)
+  bf16x8 qv[GRP];
+  float qf[kFp8 ? GRP : 1][8];
 #pragma unroll
   for (int j = 0; j < GRP; ++j) {
-    const bf16x8 qv = *(const bf16x8*)((const bf16*)a.q + ((int64_t)b * a.H + g * GRP + j) * kD + li * 8);
+    qv[j] = *(const bf16x8*)((const bf16*)a.q + ((int64_t)b * a.H + g * GRP + j) * kD + li * 8);
+    if constexpr (kFp8) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) q[j][e] = (float)qv[e] * qs;
+      for (int e = 0; e < 8; ++e) qf[j][e] = (float)qv[j][e] * a.k_scale;
+    }
   }
+  const float c = a.scale_log2;
   float m[GRP], l[GRP], o[GRP][8];
 #pragma unroll
   for (int j = 0; j < GRP; ++j) {
@@ -149,15 +186,7 @@ __global__ __launch_bounds__(dec::kThreads) void decode_split_kernel(DecodeArgs 
     else
       return *(const bf16x8*)(p16 + r * kD);
   };
-  auto widen = [&](const Chunk& c, float* f) {
-    if constexpr (kFp8) {
-      e4m3x4_to_f32(c[0], f);
-      e4m3x4_to_f32(c[1], f + 4);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) f[e] = (float)c[e];
-    }
-  };
+  const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
 
   const int64_t n_iter = r1 > r0 ? (r1 - r0 + kRowsPerIter - 1) / kRowsPerIter : 0;
   for (int64_t i = 0; i < n_iter; ++i) {
@@ -171,25 +200,49 @@ __global__ __launch_bounds__(dec::kThreads) void decode_split_kernel(DecodeArgs 
       kr[u] = load(kb, kb8, rc);
       vr[u] = load(vb, vb8, rc);
     }
+    // scores in log2 units: this lane's 8 elements, then the row's 16 lanes
     float s[kUnroll][GRP];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      float kf[8];
-      widen(kr[u], kf);
+      if constexpr (kFp8) {
+        float kf[8];
+        e4m3x4_to_f32(kr[u][0], kf);
+        e4m3x4_to_f32(kr[u][1], kf + 4);
 #pragma unroll
-      for (int j = 0; j < GRP; ++j) {
-        float acc = 0.f;
+        for (int j = 0; j < GRP; ++j) {
+          float acc = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc = fmaf(q[j][e], kf[e], acc);
-        s[u][j] = acc;
+          for (int e = 0; e < 8; ++e) acc = fmaf(qf[j][e], kf[e], acc);
+          s[u][j] = acc;
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < GRP; ++j) {
+          float acc = dot2(pair(kr[u], 0), pair(qv[j], 0), 0.f);
+#pragma unroll
+          for (int e = 1; e < 4; ++e) acc = dot2(pair(kr[u], e), pair(qv[j], e), acc);
+          s[u][j] = acc;
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < GRP; ++j) s[u][j] = row16_sum(s[u][j]) * c;
+    }
+    // values: fp32 (e4m3 codes), or bf16 pairs of rows (0, 1) and (2, 3)
+    float vf[kFp8 ? kUnroll : 1][8];
+    bf16x2 v01[8], v23[8];
+    if constexpr (kFp8) {
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        e4m3x4_to_f32(vr[u][0], vf[u]);
+        e4m3x4_to_f32(vr[u][1], vf[u] + 4);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        v01[e] = bf16x2{vr[0][e], vr[1][e]};
+        v23[e] = bf16x2{vr[2][e], vr[3][e]};
       }
     }
-#pragma unroll
-    for (int off = 8; off > 0; off >>= 1)
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u)
-#pragma unroll
-        for (int j = 0; j < GRP; ++j) s[u][j] += __shfl_xor(s[u][j], off, kWave);
 #pragma unroll
     for (int j = 0; j < GRP; ++j) {
       float mx = -INFINITY;
@@ -201,17 +254,11 @@ __global__ __launch_bounds__(dec::kThreads) void decode_split_kernel(DecodeArgs 
       const float mn = fmaxf(m[j], mx);
       const float al = fast_exp2(m[j] - mn);
       m[j] = mn;
-      float p[kUnroll], ps = 0.f;
+      float p[kUnroll];
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        p[u] = fast_exp2(s[u][j] - mn);
-        ps += p[u];
-      }
-      l[j] = l[j] * al + ps;
+      for (int u = 0; u < kUnroll; ++u) p[u] = fast_exp2(s[u][j] - mn);
       if constexpr (kFp8) {
-        float vf[kUnroll][8];
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) widen(vr[u], vf[u]);
+        l[j] = l[j] * al + ((p[0] + p[1]) + (p[2] + p[3]));
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           float acc = o[j][e] * al;
@@ -220,13 +267,11 @@ __global__ __launch_bounds__(dec::kThreads) void decode_split_kernel(DecodeArgs 
           o[j][e] = acc;
         }
       } else {
+        // the weights enter P V as bf16; the row sum adds those same values
+        const bf16x2 p01 = {(bf16)p[0], (bf16)p[1]}, p23 = {(bf16)p[2], (bf16)p[3]};
+        l[j] = dot2(p23, ones, dot2(p01, ones, l[j] * al));
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          float acc = o[j][e] * al;
-#pragma unroll
-          for (int u = 0; u < kUnroll; ++u) acc = fmaf(p[u], (float)vr[u][e], acc);
-          o[j][e] = acc;
-        }
+        for (int e = 0; e < 8; ++e) o[j][e] = dot2(p23, v23[e], dot2(p01, v01[e], o[j][e] * al));
       }
     }
   }
