@@ -53,10 +53,10 @@ KERNEL_SOURCES = {
     "decode_split_kernel": ["attn.hip", "tiles.h", "common.h", "kernels.h"],
 }
 MEASURED_TRAFFIC = {
-    ("olmo3-7b-layer", "prefill_sliding_l0"): dict(bytes=681875100, sources="4aaacfb7637e6341"),
-    ("olmo3-7b-layer", "prefill_full_l3"): dict(bytes=287196383, sources="4aaacfb7637e6341"),
-    ("olmo3-7b-layer", "decode_sliding"): dict(bytes=2149406565, sources="92c8df7991a3b01f"),
-    ("olmo3-7b-layer", "decode_full"): dict(bytes=34360963592, sources="92c8df7991a3b01f"),
+    ("olmo3-7b-layer", "prefill_sliding_l0"): dict(bytes=694921097, sources="29f457aeb048a41d"),
+    ("olmo3-7b-layer", "prefill_full_l3"): dict(bytes=287857439, sources="29f457aeb048a41d"),
+    ("olmo3-7b-layer", "decode_sliding"): dict(bytes=2149531756, sources="860e3c9b483c47a1"),
+    ("olmo3-7b-layer", "decode_full"): dict(bytes=34360978594, sources="860e3c9b483c47a1"),
 }
 
 
