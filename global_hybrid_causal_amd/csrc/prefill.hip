@@ -306,6 +306,22 @@ __global__ __launch_bounds__(256, 2) void prefill_d128_kernel(AttnArgs a) {
         const bf16x8 va = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
         o[db] = mfma32(va, pk[kk], o[db]);
       }
+    // Scheduling shape of the step: each QK MFMA followed by one LDS read
+    // and four softmax VALU instructions, each PV MFMA by two transposed
+    // reads and two VALU instructions, so that the MFMA pipe is fed evenly
+    // (the default schedule bunches the exponentials).
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+    }
     s0 = n0;
     s1 = n1;
   };
