@@ -35,6 +35,13 @@ def test_every_declared_symbol_is_exported():
     assert sorted(A.EXPORTS) == syms
 
 
+def test_header_binding_and_library_versions_agree():
+    import re
+    text = open(os.path.join(os.path.dirname(__file__), "..", "include", "olmo3_attn.h")).read()
+    header = int(re.search(r"#define OLMO3_ABI_VERSION (\d+)", text).group(1))
+    assert header == A.ABI_VERSION == A.olmo3_abi_version()
+
+
 def test_abi_version():
     assert A.olmo3_abi_version() == A.ABI_VERSION == 4
 
