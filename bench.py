@@ -16,6 +16,7 @@ Workloads (synthetic, seeded, shaped like the OLMo 3 configurations):
        B=16 at cache length 65,536: KV bytes read per step and per token of
        context (the per-layer-type cache of the page "Olmo 3 7B")
   7b-e4m3  7B decode (B=32 at 65,536) against e4m3 caches (1-byte codes)
+  decode-stack-e4m3  the decode stack against e4m3 caches
 
 Printed: one JSON line.  `value` is prefill TFLOP/s (algorithmic FLOPs of the
 allowed query/key pairs over the whole prefill call time); decode KV GB/s is
@@ -106,6 +107,8 @@ WORKLOADS = {
                          decode=dict(B=16, H=32, G=32, L=65536, layers=32)),
     "7b-e4m3": dict(name="olmo3-7b-decode-e4m3", prefill=None,
                     decode=dict(B=32, H=32, G=32, L=65536, e4m3=True)),
+    "decode-stack-e4m3": dict(name="olmo3-7b-decode-stack-e4m3", prefill=None,
+                              decode=dict(B=16, H=32, G=32, L=65536, layers=32, e4m3=True)),
 }
 E4M3_SCALES = (1.0 / 16, 1.0 / 16)  # k_scale, v_scale of the e4m3 workload
 N_LAYERS_7B = 32
@@ -217,7 +220,8 @@ def main():
                   f"[{Bd}, {Gd}, {cap}, {d}] x2", file=sys.stderr, flush=True)
             e4m3 = dc.get("e4m3", False)
             if e4m3:
-                kc, vc = synth.e4m3_cache_fill(dseed, 100 + lt, Bd, Gd, cap, d, device=dev)
+                kc, vc = synth.e4m3_cache_fill(dseed, (ell if n_dec_layers else 100 + lt), Bd, Gd,
+                                               cap, d, device=dev)
             else:
                 kc, vc = synth.cache_fill(dseed, (ell if n_dec_layers else 100 + lt), Bd, Gd, cap, d,
                                           device=dev, dtype=bf16)
@@ -355,7 +359,7 @@ def main():
             "kv_bytes_per_step": kv_step, "step_ms": round(step_ms, 4),
             "tokens_per_s": round(dc["B"] / (step_ms * 1e-3), 1),
             "kv_bytes_per_token_of_context": kv_step // (dc["B"] * dc["L"]),
-            "naive_bytes_per_token_of_context": NAIVE_BYTES_PER_TOKEN_7B,
+            "naive_bytes_per_token_of_context": NAIVE_BYTES_PER_TOKEN_7B // (2 if dc.get("e4m3") else 1),
         }
     if args.cpu_seconds > 0 and (pre or dec):
         print(f"[bench] timing the CPU oracle for ~{args.cpu_seconds:.0f} s", file=sys.stderr, flush=True)

@@ -1,0 +1,55 @@
+"""Host-side logic of bench.py, without a GPU: the algorithmic work it
+divides by (checked against the oracle's explicit masks and cache
+accounting), the refusal of more than one GPU, and the guard that drops a
+recorded traffic figure once its kernel's sources change."""
+
+import os
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+
+import bench
+import oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.mark.parametrize("T,window", [(1, 4), (5, 2), (64, 16), (300, 64), (257, 1000), (4096, 4096)])
+def test_prefill_pairs_count_the_mask(T, window):
+    assert bench.prefill_pairs(T, window, True) == int(O.sliding_window_mask(T, window).sum())
+    assert bench.prefill_pairs(T, window, False) == int(O.causal_mask(T).sum())
+
+
+def test_prefill_flops_at_the_7b_config():
+    # 4 * d * H per allowed pair: 4.1235e11 (sliding) and 5.4982e11 (full) at T = 8192
+    assert bench.prefill_flops(8192, 32, 128, 4096, True) == 412350414848
+    assert bench.prefill_flops(8192, 32, 128, 4096, False) == 549822922752
+
+
+def test_decode_bytes_match_the_cache_accounting():
+    kinds = O.layer_types(32)
+    L, G, d = 65536, 32, 128
+    per_seq = sum(bench.decode_kv_bytes(1, G, d, bench.decode_rows(L - 1, 4096, k == O.SLIDING))
+                  for k in kinds)
+    assert per_seq // L == O.kv_bytes_per_token(kinds, G, d, 4096, L) == 155648
+    assert bench.decode_kv_bytes(32, 32, 128, 65536) == 34359738368
+    assert bench.decode_kv_bytes(32, 32, 128, 65536, elem=1) == 34359738368 // 2
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_recorded_traffic_needs_unchanged_sources(monkeypatch):
+    key = ("olmo3-7b-layer", "decode_full")
+    entry = dict(bench.MEASURED_TRAFFIC[key])
+    monkeypatch.setitem(bench.MEASURED_TRAFFIC, key, dict(entry, sources="0" * 16))
+    assert bench.measured_traffic(*key, "decode_split_kernel") is None
+    monkeypatch.setitem(bench.MEASURED_TRAFFIC, key,
+                        dict(entry, sources=bench.sources_digest("decode_split_kernel")))
+    assert bench.measured_traffic(*key, "decode_split_kernel") == entry["bytes"]
+    assert bench.measured_traffic("olmo3-7b-layer", "no such segment", "decode_split_kernel") is None
