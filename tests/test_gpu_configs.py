@@ -194,3 +194,97 @@ def test_decode_stack_reads_effective_bytes_per_token():
     bytes_per_token = rows_read * G * d * 2 * 2 // L
     assert bytes_per_token == O.kv_bytes_per_token(kinds, G, d, W, L) == 155648
     assert O.kv_bytes_per_token([O.FULL] * n_layers, G, d, W, L) == 524288
+
+
+def _rotated_keys_of(k_pre_rows, positions, k_gain, kind, rope, G, d):
+    """The oracle's rotated keys for projected key rows [n, G*d] at `positions`."""
+    w_, m_ = O.layer_rope(oracle_rope(rope), kind, d)
+    kh = O.rms_norm(k_pre_rows, k_gain, 1e-6).reshape(len(positions), G, d)
+    return O.rope_rotate(kh, np.asarray(positions), w_, m_)
+
+
+def _chunk_rows_ref(x, b, row0, n_rows, P, rows, pre_k, pre_v, tags, gs, kind, rope, H, G, d):
+    """Oracle outputs of chunk rows `rows` (within the chunk) of sequence b:
+    queries and keys rows row0 .. row0 + n_rows - 1 of x at positions P ..,
+    attending to the cache's held rows pre_k / pre_v [len(gs), cap, d]
+    (positions `tags`) and to the chunk, for key/value heads gs."""
+    held = np.nonzero(tags >= 0)[0]
+    n = held.size + n_rows
+    sl = slice(row0, row0 + n_rows)
+    k_chunk = _rotated_keys_of(host(x["k_pre"][b, sl]), P + np.arange(n_rows), host(x["k_gain"]),
+                               kind, rope, G, d)
+    keys = np.zeros((n, G, d))   # only the sampled heads are filled
+    vals = np.zeros((n, G, d))
+    keys[:, gs] = np.concatenate([pre_k[:, held].transpose(1, 0, 2), k_chunk[:, gs]], axis=0)
+    vals[:, gs] = np.concatenate([pre_v[:, held].transpose(1, 0, 2),
+                                  host(x["v"][b, sl]).reshape(n_rows, G, d)[:, gs]], axis=0)
+    key_pos = np.concatenate([tags[held], P + np.arange(n_rows)])
+    return O.attention_rows_ref(host(x["q_pre"][b, row0 + rows]), P + rows, keys, vals, key_pos,
+                                host(x["q_gain"]), host(x["k_gain"]), H=H, G=G, d=d,
+                                kv_heads=gs, kind=kind, window=W, rope=oracle_rope(rope),
+                                k_is_rotated=True)
+
+
+@pytest.mark.parametrize("lt", [0, 1], ids=["sliding_ring", "full_linear"])
+def test_chunked_prefill_full_size_sampled(lt):
+    """7B shapes: a 4096-token chunk at positions 8192 .. 12287 onto a cache
+    pre-filled with seeded rows (the ring holds 4096 .. 8191), as the bench's
+    kernels run it; sampled query rows (both window edges, the chunk edges)
+    of two key/value heads against the oracle."""
+    B, P, T, H, G, d = 1, 8192, 4096, 32, 32, 128
+    kind = KINDS[lt]
+    rope = YARN if lt == 1 else PLAIN
+    cap = W if lt == 0 else P + T
+    kc, vc = synth.cache_fill(8, lt, B, G, cap, d, device="cuda", dtype=BF16)
+    gs = [0, G - 1]
+    pre_k, pre_v = host(kc[0, gs]), host(vc[0, gs])           # [2, cap, d], before the call
+    tags = O.ring_positions(kind, W, cap, P)
+    x = inputs(8, 30 + lt, B, T, H, G, d, BF16)
+    out = gpu_prefill(x, kc, vc, window=W, layer_type=lt, rope=rope, H=H, pos_offset=P)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
+    rows = np.array(sorted({0, 1, 63, 64, 127, 128, T // 2, T - 2, T - 1} |
+                           set(np.random.default_rng(9).integers(0, T, 12).tolist())))
+    # keys: the held prefix (rotated, as stored) and the chunk (rotated by the oracle)
+    got = host(out[0, rows]).reshape(len(rows), H, d)[:, gs]
+    ref = _chunk_rows_ref(x, 0, 0, T, P, rows, pre_k, pre_v, tags, gs, kind, rope, H, G, d)
+    err = assert_close(got, ref, what=f"chunked prefill {kind}")
+    _log(f"chunked prefill {kind}: {len(rows)} rows, max abs/rel err {err}")
+
+
+@pytest.mark.parametrize("lt", [0, 1], ids=["sliding_ring", "full_linear"])
+def test_ragged_prefill_7b_shapes_sampled(lt):
+    """7B heads, three packed sequences of 2000, 100 and 3000 tokens at
+    position offsets 5000, 0 and 300 onto seeded caches; sampled rows of each
+    sequence against the oracle run on that sequence alone."""
+    H, G, d = 32, 32, 128
+    lengths, offsets = [2000, 100, 3000], [5000, 0, 300]
+    B, N = len(lengths), sum(lengths)
+    kind = KINDS[lt]
+    rope = YARN if lt == 1 else PLAIN
+    max_end = max(p + n for p, n in zip(offsets, lengths))
+    cap = W if lt == 0 else max_end
+    kc, vc = synth.cache_fill(9, lt, B, G, cap, d, device="cuda", dtype=BF16)
+    gs = [0, G - 1]
+    pre = [(host(kc[b, gs]), host(vc[b, gs])) for b in range(B)]
+    x = inputs(9, 40 + lt, 1, N, H, G, d, BF16)
+    flat = {k: (v[0] if v.dim() == 3 else v) for k, v in x.items()}
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lengths)]), dtype=torch.int32, device="cuda")
+    po = torch.tensor(offsets, dtype=torch.int32, device="cuda")
+    out = torch.empty_like(flat["q_pre"])
+    ws = A.workspace(A.MODE_PREFILL, 1, N, H, G, d, lt, BF16, cap, "cuda")
+    A.olmo3_attn_prefill_ragged(flat["q_pre"], flat["k_pre"], flat["v"], flat["q_gain"],
+                                flat["k_gain"], kc, vc, out, ws, cu, po, max_len=max(lengths),
+                                max_end=max_end, window=W, layer_type=lt, rope=rope)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
+    row0 = 0
+    for b, (n, P) in enumerate(zip(lengths, offsets)):
+        rows = np.array(sorted({0, n - 1, n // 2} | set(np.random.default_rng(b).integers(0, n, 6).tolist())))
+        tags = O.ring_positions(kind, W, cap, P)
+        ref = _chunk_rows_ref(x, 0, row0, n, P, rows, pre[b][0], pre[b][1], tags, gs, kind, rope,
+                              H, G, d)
+        got = host(out[row0 + rows]).reshape(len(rows), H, d)[:, gs]
+        err = assert_close(got, ref, what=f"ragged sequence {b} ({kind})")
+        _log(f"ragged {kind} sequence {b}: {len(rows)} rows, max abs/rel err {err}")
+        row0 += n
