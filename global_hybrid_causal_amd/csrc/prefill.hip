@@ -132,30 +132,38 @@ __global__ __launch_bounds__(256, 2) void prefill_d128_kernel(AttnArgs a) {
   const int lrow = 4 * wave + (lane >> 4);  // row within each 16-row slab
   const int kcol = (lane & 15) ^ (lrow & 15);
   const int vcol = (lane & 15) ^ (4 * (lrow & 3));
-  // Uniform per-head bases plus a 32-bit per-lane element offset.  Tiles
+  // Uniform per-head bases plus 32-bit per-lane byte offsets.  Tiles
   // whose 64 rows are consecutive rows of one source take the fast path;
   // the last tile (positions past n_keys) and, with a prefix, tiles that
   // cross the prefix/main boundary or the ring's wrap go row by row.
   const bool packed_main = kPacked && a.main_packed;
   const bf16* kbase = (const bf16*)a.k + (packed_main ? row0 * a.k_sr : w.b * a.k_sb) + g * a.k_sg;
   const bf16* vbase = (const bf16*)a.v + (packed_main ? row0 * a.v_sr : w.b * a.v_sb) + g * a.v_sg;
-  const int k_lane = lrow * (int)a.k_sr + kcol * 8;
-  const int v_lane = lrow * (int)a.v_sr + vcol * 8;
   const int main0 = kPacked ? (packed_main ? qpos0 : 0) : (kPrefix ? (int)a.main_pos0 : 0);
   const int ring = kPrefix ? (int)a.ring : 1;
   const int64_t p_sr = a.p_sr;
   const bf16* kpbase = kPrefix ? (const bf16*)a.kp + w.b * a.p_sb + g * a.p_sg : nullptr;
   const bf16* vpbase = kPrefix ? (const bf16*)a.vp + w.b * a.p_sb + g * a.p_sg : nullptr;
-  const int kp_lane = kPrefix ? lrow * (int)p_sr + kcol * 8 : 0;
-  const int vp_lane = kPrefix ? lrow * (int)p_sr + vcol * 8 : 0;
+  // Byte offsets of this lane's rows 16 i + lrow in a run of 64 rows, so that
+  // a tile's loads are one uniform base plus these.  Row strides are at most
+  // G * d elements and G is capped by the prologue's head limit, so 64 rows
+  // span a few MiB at most and the offsets fit 32 bits.
+  uint32_t k_off[4], v_off[4], kp_off[4], vp_off[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    k_off[i] = (uint32_t)(((16 * i + lrow) * (int)a.k_sr + kcol * 8) * 2);
+    v_off[i] = (uint32_t)(((16 * i + lrow) * (int)a.v_sr + vcol * 8) * 2);
+    kp_off[i] = kPrefix ? (uint32_t)(((16 * i + lrow) * (int)p_sr + kcol * 8) * 2) : 0u;
+    vp_off[i] = kPrefix ? (uint32_t)(((16 * i + lrow) * (int)p_sr + vcol * 8) * 2) : 0u;
+  }
   const int slab = 4 * wave * 256;  // this wavefront's byte offset in a slab
-  auto load_rows = [&](const bf16* base, int64_t sr, int lane_off, const bf16* pbase,
-                       int plane_off, int col8, int k0, char* dst) __attribute__((always_inline)) {
+  auto load_rows = [&](const bf16* base, int64_t sr, const uint32_t* off, const bf16* pbase,
+                       const uint32_t* poff, int col8, int k0, char* dst) __attribute__((always_inline)) {
     if (!kPrefix || k0 >= main0) {
       if (k0 + kBK <= n_keys) {
+        const char* tb = (const char*)(base + (int64_t)(k0 - main0) * sr);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          load_to_lds(base + (int64_t)(k0 - main0 + 16 * i) * sr + lane_off, dst + 16 * i * 256);
+        for (int i = 0; i < 4; ++i) load_to_lds((const bf16*)(tb + off[i]), dst + 16 * i * 256);
       } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -164,10 +172,9 @@ __global__ __launch_bounds__(256, 2) void prefill_d128_kernel(AttnArgs a) {
         }
       }
     } else if (k0 + kBK <= main0 && k0 % ring + kBK <= ring) {
-      const int slot0 = k0 % ring;
+      const char* tb = (const char*)(pbase + (int64_t)(k0 % ring) * p_sr);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        load_to_lds(pbase + (int64_t)(slot0 + 16 * i) * p_sr + plane_off, dst + 16 * i * 256);
+      for (int i = 0; i < 4; ++i) load_to_lds((const bf16*)(tb + poff[i]), dst + 16 * i * 256);
     } else {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -179,10 +186,10 @@ __global__ __launch_bounds__(256, 2) void prefill_d128_kernel(AttnArgs a) {
     }
   };
   auto load_k = [&](int k0, int buf) __attribute__((always_inline)) {
-    load_rows(kbase, a.k_sr, k_lane, kpbase, kp_lane, kcol * 8, k0, sK + buf * kTileBytes + slab);
+    load_rows(kbase, a.k_sr, k_off, kpbase, kp_off, kcol * 8, k0, sK + buf * kTileBytes + slab);
   };
   auto load_v = [&](int k0, int buf) __attribute__((always_inline)) {
-    load_rows(vbase, a.v_sr, v_lane, vpbase, vp_lane, vcol * 8, k0, sV + buf * kTileBytes + slab);
+    load_rows(vbase, a.v_sr, v_off, vpbase, vp_off, vcol * 8, k0, sV + buf * kTileBytes + slab);
   };
 
   // LDS read offsets.  K (A operand of S^T): row 32 kb + col, column
