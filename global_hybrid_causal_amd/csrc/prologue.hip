@@ -40,9 +40,17 @@ __device__ __forceinline__ void rope_angles(int lane, int64_t pos, const RopeTab
   const int j = lane % PairChunks<T, D>::kPerHead;
   constexpr double kTwoPi = 6.283185307179586;
   constexpr double kInvTwoPi = 0.15915494309189535;
+  typedef double f64x2 __attribute__((ext_vector_type(2)));
+  double f[kVec];
+#pragma unroll
+  for (int e = 0; e < kVec; e += 2) {
+    const f64x2 v = *(const f64x2*)&rope.inv_freq[j * kVec + e];
+    f[e] = v[0];
+    f[e + 1] = v[1];
+  }
 #pragma unroll
   for (int e = 0; e < kVec; ++e) {
-    const double a = (double)pos * rope.inv_freq[j * kVec + e];
+    const double a = (double)pos * f[e];
     const double r = a - kTwoPi * rint(a * kInvTwoPi);  // |r| <= pi
     sincosf((float)r, &sn[e], &cs[e]);
   }
@@ -51,30 +59,48 @@ __device__ __forceinline__ void rope_angles(int lane, int64_t pos, const RopeTab
 // Normalise, rotate and emit the `nheads` heads of one token row.
 // emit(h, j, y0, y1) receives pair chunk j of head h: elements j*kVec ..
 // j*kVec + kVec-1 of the head (y0) and the same offsets past d/2 (y1).
-template <typename T, int D, typename Emit>
+// With kAngles, angles() runs once the row's loads are issued and fills cs
+// and sn; otherwise they are already there.
+template <typename T, int D, bool kAngles, typename Angles, typename Emit>
 __device__ __forceinline__ void norm_rope_row(const T* __restrict__ src, const T* __restrict__ gain,
                                               int nheads, float eps, int lane, const float* cs,
-                                              const float* sn, float mscale, Emit emit) {
+                                              const float* sn, float mscale, Angles angles,
+                                              Emit emit) {
   typedef typename Io<T>::vec vec;
   constexpr int kVec = Io<T>::kVec;
   constexpr int kPerHead = PairChunks<T, D>::kPerHead;
   const int n_chunks = nheads * kPerHead;
   vec a0[kMaxChunksPerLane], a1[kMaxChunksPerLane];
-  float ss = 0.f;
-#pragma unroll
-  for (int k = 0; k < kMaxChunksPerLane; ++k) {
+  auto load = [&](int k) __attribute__((always_inline)) {
     const int pc = lane + kWave * k;
-    if (pc < n_chunks) {
-      const int h = pc / kPerHead, j = pc % kPerHead;
-      const T* p = src + h * D + j * kVec;
-      a0[k] = *(const vec*)p;
-      a1[k] = *(const vec*)(p + D / 2);
-      float f0[kVec], f1[kVec];
-      Io<T>::to_f32(a0[k], f0);
-      Io<T>::to_f32(a1[k], f1);
+    const int h = pc / kPerHead, j = pc % kPerHead;
+    const T* p = src + h * D + j * kVec;
+    a0[k] = *(const vec*)p;
+    a1[k] = *(const vec*)(p + D / 2);
+  };
+  float ss = 0.f;
+  auto accumulate = [&](int k) __attribute__((always_inline)) {
+    float f0[kVec], f1[kVec];
+    Io<T>::to_f32(a0[k], f0);
+    Io<T>::to_f32(a1[k], f1);
 #pragma unroll
-      for (int e = 0; e < kVec; ++e) ss += f0[e] * f0[e] + f1[e] * f1[e];
-    }
+    for (int e = 0; e < kVec; ++e) ss += f0[e] * f0[e] + f1[e] * f1[e];
+  };
+  if constexpr (kAngles) {  // every load issued before the angle arithmetic
+#pragma unroll
+    for (int k = 0; k < kMaxChunksPerLane; ++k)
+      if (lane + kWave * k < n_chunks) load(k);
+    angles();
+#pragma unroll
+    for (int k = 0; k < kMaxChunksPerLane; ++k)
+      if (lane + kWave * k < n_chunks) accumulate(k);
+  } else {
+#pragma unroll
+    for (int k = 0; k < kMaxChunksPerLane; ++k)
+      if (lane + kWave * k < n_chunks) {
+        load(k);
+        accumulate(k);
+      }
   }
   ss = wave_sum(ss);
   const float r = 1.0f / sqrtf(ss / (float)(nheads * D) + eps);
@@ -131,7 +157,10 @@ __device__ __forceinline__ int packed_sequence(const int32_t* cu, int B, int64_t
 // keys, values), so that the three dependent load / reduce / store chains of
 // a token overlap; used when there are too few tokens to fill the GPU (decode).
 // Otherwise one wavefront per token handles all three parts in turn.
-template <typename T, int D, bool kRoles>
+// kEarly (with kRoles, for a few hundred tokens at most): a wavefront issues
+// its row's loads before the RoPE angle arithmetic, so that the two overlap;
+// it keeps more registers live, which larger grids cannot afford.
+template <typename T, int D, bool kRoles, bool kEarly>
 __global__ __launch_bounds__(kWave * kTokensPerBlock) void qknorm_rope_append_kernel(
     PrologueArgs a, RopeTable rope) {
   typedef typename Io<T>::vec vec;
@@ -161,18 +190,23 @@ __global__ __launch_bounds__(kWave * kTokensPerBlock) void qknorm_rope_append_ke
   }
   if (pos < 0) return;
 
+  // RoPE angles, once per wavefront: first, or (kEarly) once the row's loads
+  // are issued.
   float cs[kVec], sn[kVec];
-  if (do_q || do_k) rope_angles<T, D>(lane, pos, rope, cs, sn);
+  if (!kEarly && (do_q || do_k)) rope_angles<T, D>(lane, pos, rope, cs, sn);
+  auto angles = [&]() __attribute__((always_inline)) {
+    if constexpr (kEarly) rope_angles<T, D>(lane, pos, rope, cs, sn);
+  };
 
   // queries -> q_out [rows][H][D]
   if (do_q && a.q_pre) {
     const T* src = (const T*)a.q_pre + row * a.H * D;
     T* qo = (T*)a.q_out + row * a.H * D;
-    norm_rope_row<T, D>(src, (const T*)a.q_gain, a.H, a.eps, lane, cs, sn, rope.mscale,
-                        [&](int h, int j, const float* y0, const float* y1) {
-                          store_chunk(qo + h * D + j * kVec, y0);
-                          store_chunk(qo + h * D + D / 2 + j * kVec, y1);
-                        });
+    norm_rope_row<T, D, kEarly>(src, (const T*)a.q_gain, a.H, a.eps, lane, cs, sn, rope.mscale,
+                                angles, [&](int h, int j, const float* y0, const float* y1) {
+                                  store_chunk(qo + h * D + j * kVec, y0);
+                                  store_chunk(qo + h * D + D / 2 + j * kVec, y1);
+                                });
   }
 
   const int64_t slot = a.sliding ? pos % a.window : pos;
@@ -186,8 +220,8 @@ __global__ __launch_bounds__(kWave * kTokensPerBlock) void qknorm_rope_append_ke
   if (do_k) {
     const T* src = (const T*)a.k_pre + row * a.G * D;
     T* ko = (T*)a.k_out;
-    norm_rope_row<T, D>(
-        src, (const T*)a.k_gain, a.G, a.eps, lane, cs, sn, rope.mscale,
+    norm_rope_row<T, D, kEarly>(
+        src, (const T*)a.k_gain, a.G, a.eps, lane, cs, sn, rope.mscale, angles,
         [&](int h, int j, const float* y0, const float* y1) {
           if (ko) {
             T* d = ko + kb_idx * a.k_sb + h * a.k_sg + kt_idx * a.k_st;
@@ -233,17 +267,21 @@ __global__ __launch_bounds__(kWave * kTokensPerBlock) void qknorm_rope_append_ke
   }
 }
 
-// Up to this many tokens the per-part wavefronts are used.
+// Up to this many tokens the per-part wavefronts are used, and up to the
+// smaller bound they issue their loads before the angle arithmetic.
 constexpr int64_t kRolesMaxRows = 2048;
+constexpr int64_t kEarlyMaxRows = 512;
 
 template <typename T, int D>
 hipError_t launch_prologue_t(const PrologueArgs& a, const RopeTable& rope, hipStream_t s) {
   const int64_t rows = a.cu_seqlens ? a.n_rows : (int64_t)a.B * a.T;
-  if (rows <= kRolesMaxRows) {
-    qknorm_rope_append_kernel<T, D, true><<<(int)rows, kWave * 3, 0, s>>>(a, rope);
+  if (rows <= kEarlyMaxRows) {
+    qknorm_rope_append_kernel<T, D, true, true><<<(int)rows, kWave * 3, 0, s>>>(a, rope);
+  } else if (rows <= kRolesMaxRows) {
+    qknorm_rope_append_kernel<T, D, true, false><<<(int)rows, kWave * 3, 0, s>>>(a, rope);
   } else {
     const int blocks = (int)((rows + kTokensPerBlock - 1) / kTokensPerBlock);
-    qknorm_rope_append_kernel<T, D, false><<<blocks, kWave * kTokensPerBlock, 0, s>>>(a, rope);
+    qknorm_rope_append_kernel<T, D, false, false><<<blocks, kWave * kTokensPerBlock, 0, s>>>(a, rope);
   }
   return hipGetLastError();
 }
