@@ -127,6 +127,8 @@ __device__ __forceinline__ bf16x2 pair(const bf16x8& v, int i) {
 // each scale multiplies the result exactly once.
 // Waves per SIMD the register budget is held to: enough rows in flight per
 // CU to cover HBM latency (each wavefront streams 8 KiB per iteration).
+constexpr float kSlack = 8.0f;  // log2 units: bf16-cache weights at most 2^8 before a rescale
+
 template <int GRP, bool kFp8>
 constexpr int decode_waves_per_eu() {
   return kFp8 ? (GRP <= 2 ? 6 : (GRP <= 3 ? 4 : 2)) : (GRP <= 1 ? 8 : (GRP <= 5 ? 4 : 2));
@@ -245,25 +247,57 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_eu<GRP, kFp8>()))) void deco
         v23[e] = bf16x2{vr[2][e], vr[3][e]};
       }
     }
+    // Online softmax per head.  bf16 caches: lazy rescale, m[j] a reference
+    // maximum moved (and o, l rescaled) only when a score passes it by more
+    // than 2^kSlack, so the weights stay at most 2^kSlack; the merges below
+    // accept any reference.  e4m3 caches (half the bytes per row, so the
+    // branch weighs more): exact running maximum, rescaled every iteration.
+    float mx[GRP];
 #pragma unroll
     for (int j = 0; j < GRP; ++j) {
-      float mx = -INFINITY;
+      mx[j] = -INFINITY;
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
         if (!ok[u]) s[u][j] = -INFINITY;
-        mx = fmaxf(mx, s[u][j]);
+        mx[j] = fmaxf(mx[j], s[u][j]);
       }
-      const float mn = fmaxf(m[j], mx);
-      const float al = fast_exp2(m[j] - mn);
-      m[j] = mn;
+    }
+    float al[GRP];
+    if constexpr (kFp8) {
+#pragma unroll
+      for (int j = 0; j < GRP; ++j) {
+        const float mn = fmaxf(m[j], mx[j]);
+        al[j] = fast_exp2(m[j] - mn);
+        m[j] = mn;
+      }
+    } else {
+      bool grow = false;
+#pragma unroll
+      for (int j = 0; j < GRP; ++j) grow |= mx[j] > m[j] + kSlack;
+      if (__ballot(grow)) {
+#pragma unroll
+        for (int j = 0; j < GRP; ++j) {
+          const float mn = fmaxf(m[j], mx[j]);
+          float a1 = fast_exp2(m[j] - mn);
+          // keep this a real (uniform) branch rather than a multiply per tile
+          asm volatile("" : "+v"(a1));
+          m[j] = mn;
+          l[j] *= a1;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) o[j][e] *= a1;
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < GRP; ++j) {
       float p[kUnroll];
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) p[u] = fast_exp2(s[u][j] - mn);
+      for (int u = 0; u < kUnroll; ++u) p[u] = fast_exp2(s[u][j] - m[j]);
       if constexpr (kFp8) {
-        l[j] = l[j] * al + ((p[0] + p[1]) + (p[2] + p[3]));
+        l[j] = l[j] * al[j] + ((p[0] + p[1]) + (p[2] + p[3]));
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          float acc = o[j][e] * al;
+          float acc = o[j][e] * al[j];
 #pragma unroll
           for (int u = 0; u < kUnroll; ++u) acc = fmaf(p[u], vf[u][e], acc);
           o[j][e] = acc;
@@ -271,9 +305,9 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_eu<GRP, kFp8>()))) void deco
       } else {
         // the weights enter P V as bf16; the row sum adds those same values
         const bf16x2 p01 = {(bf16)p[0], (bf16)p[1]}, p23 = {(bf16)p[2], (bf16)p[3]};
-        l[j] = dot2(p23, ones, dot2(p01, ones, l[j] * al));
+        l[j] = dot2(p23, ones, dot2(p01, ones, l[j]));
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o[j][e] = dot2(p23, v23[e], dot2(p01, v01[e], o[j][e] * al));
+        for (int e = 0; e < 8; ++e) o[j][e] = dot2(p23, v23[e], dot2(p01, v01[e], o[j][e]));
       }
     }
   }
