@@ -193,22 +193,25 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_eu<GRP, kFp8>()))) void deco
   const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
 
   const int64_t n_iter = r1 > r0 ? (r1 - r0 + kRowsPerIter - 1) / kRowsPerIter : 0;
-  for (int64_t i = 0; i < n_iter; ++i) {
-    Chunk kr[kUnroll], vr[kUnroll];
-    bool ok[kUnroll];
+  if constexpr (kFp8) {
+    // e4m3 codes: keys and values converted to fp32, exact running maximum
+    // rescaled every iteration, every row masked against r1 (the loop shape
+    // that measured fastest for these half-size rows)
+    for (int64_t i = 0; i < n_iter; ++i) {
+      Chunk kr[kUnroll], vr[kUnroll];
+      bool ok[kUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int64_t r = row_of(r0, i, u, grp);
-      ok[u] = r < r1;
-      const int64_t rc = ok[u] ? r : r0;
-      kr[u] = load(kb, kb8, rc);
-      vr[u] = load(vb, vb8, rc);
-    }
-    // scores in log2 units: this lane's 8 elements, then the row's 16 lanes
-    float s[kUnroll][GRP];
+      for (int u = 0; u < kUnroll; ++u) {
+        const int64_t r = row_of(r0, i, u, grp);
+        ok[u] = r < r1;
+        const int64_t rc = ok[u] ? r : r0;
+        kr[u] = load(kb, kb8, rc);
+        vr[u] = load(vb, vb8, rc);
+      }
+      // scores in log2 units: this lane's 8 elements, then the row's 16 lanes
+      float s[kUnroll][GRP];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      if constexpr (kFp8) {
+      for (int u = 0; u < kUnroll; ++u) {
         float kf[8];
         e4m3x4_to_f32(kr[u][0], kf);
         e4m3x4_to_f32(kr[u][1], kf + 4);
@@ -219,65 +222,104 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_eu<GRP, kFp8>()))) void deco
           for (int e = 0; e < 8; ++e) acc = fmaf(qf[j][e], kf[e], acc);
           s[u][j] = acc;
         }
-      } else {
 #pragma unroll
-        for (int j = 0; j < GRP; ++j) {
-          float acc = dot2(pair(kr[u], 0), pair(qv[j], 0), 0.f);
-#pragma unroll
-          for (int e = 1; e < 4; ++e) acc = dot2(pair(kr[u], e), pair(qv[j], e), acc);
-          s[u][j] = acc;
-        }
+        for (int j = 0; j < GRP; ++j) s[u][j] = row16_sum(s[u][j]) * c;
       }
-#pragma unroll
-      for (int j = 0; j < GRP; ++j) s[u][j] = row16_sum(s[u][j]) * c;
-    }
-    // values: fp32 (e4m3 codes), or bf16 pairs of rows (0, 1) and (2, 3)
-    float vf[kFp8 ? kUnroll : 1][8];
-    bf16x2 v01[8], v23[8];
-    if constexpr (kFp8) {
+      float vf[kUnroll][8];
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
         e4m3x4_to_f32(vr[u][0], vf[u]);
         e4m3x4_to_f32(vr[u][1], vf[u] + 4);
       }
-    } else {
+      float mx[GRP];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        v01[e] = bf16x2{vr[0][e], vr[1][e]};
-        v23[e] = bf16x2{vr[2][e], vr[3][e]};
+      for (int j = 0; j < GRP; ++j) {
+        mx[j] = -INFINITY;
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+          if (!ok[u]) s[u][j] = -INFINITY;
+          mx[j] = fmaxf(mx[j], s[u][j]);
+        }
       }
-    }
-    // Online softmax per head.  bf16 caches: lazy rescale, m[j] a reference
-    // maximum moved (and o, l rescaled) only when a score passes it by more
-    // than 2^kSlack, so the weights stay at most 2^kSlack; the merges below
-    // accept any reference.  e4m3 caches (half the bytes per row, so the
-    // branch weighs more): exact running maximum, rescaled every iteration.
-    float mx[GRP];
-#pragma unroll
-    for (int j = 0; j < GRP; ++j) {
-      mx[j] = -INFINITY;
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        if (!ok[u]) s[u][j] = -INFINITY;
-        mx[j] = fmaxf(mx[j], s[u][j]);
-      }
-    }
-    float al[GRP];
-    if constexpr (kFp8) {
+      float al[GRP];
 #pragma unroll
       for (int j = 0; j < GRP; ++j) {
         const float mn = fmaxf(m[j], mx[j]);
         al[j] = fast_exp2(m[j] - mn);
         m[j] = mn;
       }
-    } else {
+#pragma unroll
+      for (int j = 0; j < GRP; ++j) {
+        float p[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) p[u] = fast_exp2(s[u][j] - m[j]);
+        l[j] = l[j] * al[j] + ((p[0] + p[1]) + (p[2] + p[3]));
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          float acc = o[j][e] * al[j];
+#pragma unroll
+          for (int u = 0; u < kUnroll; ++u) acc = fmaf(p[u], vf[u][e], acc);
+          o[j][e] = acc;
+        }
+      }
+    }
+  } else {
+    // bf16 rows.  One iteration: 4 rows per lane group; only the last
+    // iteration of a split can hold rows past r1 (kTail: rows clamped to r0
+    // and masked).  Scores stay unscaled until the exponent, c * s - m in one
+    // fma.  Lazy rescale: m[j] is a reference maximum, moved (and o, l
+    // rescaled) only when a scaled score passes it by more than 2^kSlack, so
+    // the weights stay at most 2^kSlack; the merges below accept any
+    // reference.
+    auto iteration = [&](int64_t i, auto tail_tag) __attribute__((always_inline)) {
+      constexpr bool kTail = decltype(tail_tag)::value;
+      Chunk kr[kUnroll], vr[kUnroll];
+      bool ok[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int64_t r = row_of(r0, i, u, grp);
+        ok[u] = !kTail || r < r1;
+        const int64_t rc = ok[u] ? r : r0;
+        kr[u] = load(kb, kb8, rc);
+        vr[u] = load(vb, vb8, rc);
+      }
+      // scores: this lane's 8 elements, then the row's 16 lanes
+      float s[kUnroll][GRP];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+#pragma unroll
+        for (int j = 0; j < GRP; ++j) {
+          float acc = dot2(pair(kr[u], 0), pair(qv[j], 0), 0.f);
+#pragma unroll
+          for (int e = 1; e < 4; ++e) acc = dot2(pair(kr[u], e), pair(qv[j], e), acc);
+          s[u][j] = row16_sum(acc);
+        }
+      }
+      // values as bf16 pairs of rows (0, 1) and (2, 3)
+      bf16x2 v01[8], v23[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        v01[e] = bf16x2{vr[0][e], vr[1][e]};
+        v23[e] = bf16x2{vr[2][e], vr[3][e]};
+      }
       bool grow = false;
 #pragma unroll
-      for (int j = 0; j < GRP; ++j) grow |= mx[j] > m[j] + kSlack;
+      for (int j = 0; j < GRP; ++j) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+          if (kTail && !ok[u]) s[u][j] = -INFINITY;
+          mx = fmaxf(mx, s[u][j]);
+        }
+        grow |= mx * c > m[j] + kSlack;
+      }
       if (__ballot(grow)) {
 #pragma unroll
         for (int j = 0; j < GRP; ++j) {
-          const float mn = fmaxf(m[j], mx[j]);
+          float mx = -INFINITY;
+#pragma unroll
+          for (int u = 0; u < kUnroll; ++u) mx = fmaxf(mx, s[u][j]);
+          const float mn = fmaxf(m[j], mx * c);
           float a1 = fast_exp2(m[j] - mn);
           // keep this a real (uniform) branch rather than a multiply per tile
           asm volatile("" : "+v"(a1));
@@ -287,29 +329,20 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_eu<GRP, kFp8>()))) void deco
           for (int e = 0; e < 8; ++e) o[j][e] *= a1;
         }
       }
-    }
 #pragma unroll
-    for (int j = 0; j < GRP; ++j) {
-      float p[kUnroll];
+      for (int j = 0; j < GRP; ++j) {
+        float p[kUnroll];
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) p[u] = fast_exp2(s[u][j] - m[j]);
-      if constexpr (kFp8) {
-        l[j] = l[j] * al[j] + ((p[0] + p[1]) + (p[2] + p[3]));
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          float acc = o[j][e] * al[j];
-#pragma unroll
-          for (int u = 0; u < kUnroll; ++u) acc = fmaf(p[u], vf[u][e], acc);
-          o[j][e] = acc;
-        }
-      } else {
+        for (int u = 0; u < kUnroll; ++u) p[u] = fast_exp2(fmaf(s[u][j], c, -m[j]));
         // the weights enter P V as bf16; the row sum adds those same values
         const bf16x2 p01 = {(bf16)p[0], (bf16)p[1]}, p23 = {(bf16)p[2], (bf16)p[3]};
         l[j] = dot2(p23, ones, dot2(p01, ones, l[j]));
 #pragma unroll
         for (int e = 0; e < 8; ++e) o[j][e] = dot2(p23, v23[e], dot2(p01, v01[e], o[j][e]));
       }
-    }
+    };
+    for (int64_t i = 0; i + 1 < n_iter; ++i) iteration(i, std::false_type{});
+    if (n_iter > 0) iteration(n_iter - 1, std::true_type{});
   }
 
   // merge the 4 lane groups of this wavefront (lanes l, l^16, l^32, l^48)
