@@ -54,10 +54,10 @@ KERNEL_SOURCES = {
     "decode_split_kernel": ["attn.hip", "tiles.h", "common.h", "kernels.h"],
 }
 MEASURED_TRAFFIC = {
-    ("olmo3-7b-layer", "prefill_sliding_l0"): dict(bytes=693325625, sources="7f2f5107ac811bb8"),
-    ("olmo3-7b-layer", "prefill_full_l3"): dict(bytes=303818114, sources="7f2f5107ac811bb8"),
-    ("olmo3-7b-layer", "decode_sliding"): dict(bytes=2149190490, sources="08c6d3bbf272cadc"),
-    ("olmo3-7b-layer", "decode_full"): dict(bytes=34360635680, sources="08c6d3bbf272cadc"),
+    ("olmo3-7b-layer", "prefill_sliding_l0"): dict(bytes=706134217, sources="7f2f5107ac811bb8"),
+    ("olmo3-7b-layer", "prefill_full_l3"): dict(bytes=297171648, sources="7f2f5107ac811bb8"),
+    ("olmo3-7b-layer", "decode_sliding"): dict(bytes=2149194501, sources="415111273ea86b7f"),
+    ("olmo3-7b-layer", "decode_full"): dict(bytes=34360676474, sources="415111273ea86b7f"),
 }
 
 
