@@ -18,7 +18,7 @@ from . import LAYER_FULL, LAYER_SLIDING  # noqa: F401  (re-exported)
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libolmo3attn.so")
 
-ABI_VERSION = 4  # OLMO3_ABI_VERSION of include/olmo3_attn.h
+ABI_VERSION = 5  # OLMO3_ABI_VERSION of include/olmo3_attn.h
 DTYPE_BF16, DTYPE_F32, DTYPE_BF16_E4M3 = 0, 1, 2
 MODE_PREFILL, MODE_DECODE = 0, 1
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_CAPACITY, ERR_HIP, ERR_WORKSPACE = range(6)
@@ -128,7 +128,7 @@ def lib() -> ctypes.CDLL:
         L.olmo3_abi_version.restype = _i
         L.olmo3_probe_prefill_visits.argtypes = [_i, _i64, _i, _i, _p, _p]
         L.olmo3_probe_prefill_visits.restype = _i
-        L.olmo3_probe_decode_reads.argtypes = [_i, _i, _i, _i, _i, _i64, _i64, _p, _p]
+        L.olmo3_probe_decode_reads.argtypes = [_i, _i, _i, _i, _i, _i, _i, _i64, _i64, _p, _p]
         L.olmo3_probe_decode_reads.restype = _i
         if L.olmo3_abi_version() != ABI_VERSION:
             raise RuntimeError(f"{LIB_PATH} has ABI version {L.olmo3_abi_version()}, the binding "
@@ -383,11 +383,13 @@ def olmo3_probe_prefill_visits(T: int, window: int, layer_type: int, pos_offset:
     return visit
 
 
-def olmo3_probe_decode_reads(B: int, G: int, d: int, window: int, layer_type: int, pos: int,
-                             cache_capacity: int, device="cuda") -> torch.Tensor:
-    """[cache_capacity] int32 count of reads per slot by the decode kernel."""
+def olmo3_probe_decode_reads(B: int, H: int, G: int, d: int, window: int, layer_type: int,
+                             pos: int, cache_capacity: int, dtype: int = DTYPE_BF16,
+                             device="cuda") -> torch.Tensor:
+    """[cache_capacity] int32 count of reads per slot by the decode kernel that
+    serves these arguments (dtype: DTYPE_BF16 or DTYPE_BF16_E4M3)."""
     count = torch.empty(cache_capacity, dtype=torch.int32, device=device)
-    st = lib().olmo3_probe_decode_reads(B, G, d, window, layer_type, pos, cache_capacity,
+    st = lib().olmo3_probe_decode_reads(B, H, G, d, window, layer_type, dtype, pos, cache_capacity,
                                         _ptr(count, "count"), _stream(None, count.device))
     _check(st, "olmo3_probe_decode_reads")
     return count

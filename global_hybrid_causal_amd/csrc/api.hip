@@ -702,9 +702,11 @@ int olmo3_probe_prefill_visits(int T, int64_t pos_offset, int window, int layer_
                                          (hipStream_t)stream));
 }
 
-int olmo3_probe_decode_reads(int B, int G, int d, int window, int layer_type, int64_t pos,
-                             int64_t cache_capacity, int32_t* count, void* stream) {
-  if (B < 1 || G < 1 || d != 128 || window < 1 || pos < 0 || !count) return OLMO3_ERR_INVALID_ARG;
+int olmo3_probe_decode_reads(int B, int H, int G, int d, int window, int layer_type, int dtype,
+                             int64_t pos, int64_t cache_capacity, int32_t* count, void* stream) {
+  if (B < 1 || G < 1 || H < G || H % G || d != 128 || window < 1 || pos < 0 || !count)
+    return OLMO3_ERR_INVALID_ARG;
+  if (dtype != OLMO3_DTYPE_BF16 && dtype != OLMO3_DTYPE_BF16_E4M3) return OLMO3_ERR_INVALID_ARG;
   if (layer_type != OLMO3_LAYER_SLIDING && layer_type != OLMO3_LAYER_FULL) return OLMO3_ERR_INVALID_ARG;
   int st = check_capacity(layer_type, window, cache_capacity, pos);
   if (st) return st;
@@ -716,7 +718,9 @@ int olmo3_probe_decode_reads(int B, int G, int d, int window, int layer_type, in
   const int64_t per = (a.n + a.splits - 1) / a.splits;
   a.rows_per_split = (per + dec::kRowsPerIter - 1) / dec::kRowsPerIter * dec::kRowsPerIter;
   a.B = B;
+  a.H = H;
   a.G = G;
+  a.fp8 = dtype == OLMO3_DTYPE_BF16_E4M3;
   return hip_status(launch_probe_decode(a, count, (hipStream_t)stream));
 }
 

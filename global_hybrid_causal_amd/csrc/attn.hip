@@ -399,6 +399,219 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_eu<GRP, kFp8>()))) void deco
   }
 }
 
+// Split-KV decode on MFMA, bf16 caches, GRP = H/G >= 2 query heads per
+// key/value head.  Same split of the rows [r0, r1) over workgroups and the
+// same partial (m, l, o) per head as decode_split_kernel; inside a split the
+// 4 wavefronts take 16-row stages in turn (stage t -> wavefront t mod 4).
+// Per stage a wavefront
+//   - loads the stage's K straight into the MFMA A-operand layout (lane l:
+//     key l mod 16, d = 32 kk + 8 (l/16) + 0..7) and its V rows coalesced
+//     (lane l: row 4 i + l/16, 16-byte column l mod 16), two stages ahead
+//     of the arithmetic (non-temporal: every row is read once);
+//   - S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (B = Q^T: lane l holds
+//     query l mod 16, zero past GRP), 4 blocks over d = 128; lane l ends with
+//     query l mod 16 and keys 4 (l/16) + 0..3;
+//   - softmax over the stage's 16 keys per query (maximum over the lane's 4
+//     values, then lanes l ^ 16 and l ^ 32), with the lazy reference maximum
+//     of the VALU kernel;
+//   - writes V to its LDS tile (16-byte columns XOR-swizzled by 2 (r mod 8)
+//     so the transposed reads are conflict-free) and forms O += P V with
+//     v_mfma_f32_16x16x16_bf16: A = P, already in its layout (query l mod 16,
+//     keys 4 (l/16) + 0..3), B = 16 keys x 16 d of V read with
+//     ds_read_b64_tr_b16 (lane 4 j + t of a 16-lane group addresses row
+//     4 (l/16) + j, d = 16 blk + 4 t .. + 3, and receives V[4 (l/16) + j]
+//     [16 blk + l mod 16], j = 0..3), 8 blocks over d.
+// Lane l then holds O for queries 4 (l/16) + r, d = 16 blk + l mod 16.
+constexpr int kStageRows = 16;
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+struct DecStage {
+  bf16x8 k[4];  // A operand of block kk
+  bf16x8 v[4];  // rows 4 i + l/16, column l mod 16
+};
+
+// Two wavefronts per SIMD: the three stages in registers (96 VGPRs of K and V)
+// leave no room for a third.
+template <int GRP>
+__global__ __launch_bounds__(dec::kThreads, 2) void decode_mfma_kernel(DecodeArgs a) {
+  using namespace dec;
+  static_assert(GRP >= 2 && GRP <= 16, "query heads per key/value head");
+  __shared__ __attribute__((aligned(16))) char vtile[4][kStageRows * kD * 2];  // per wavefront
+  __shared__ float sm[4][GRP], sl[4][GRP];
+  __shared__ float so[4][GRP][kD];
+
+  const int sp = blockIdx.x % a.splits;
+  const int bg = blockIdx.x / a.splits;
+  const int g = bg % a.G, b = bg / a.G;
+  int64_t n = a.n, rps = a.rows_per_split;
+  if (a.seq_pos) {  // this sequence's rows, split evenly
+    const int64_t p = max((int64_t)a.seq_pos[b], (int64_t)0);
+    n = min(a.sliding ? min(p + 1, (int64_t)a.window) : p + 1, a.cap);
+    rps = ((n + a.splits - 1) / a.splits + kRowsPerIter - 1) / kRowsPerIter * kRowsPerIter;
+  }
+  const int64_t r0 = (int64_t)sp * rps;
+  const int64_t r1 = min(n, r0 + rps);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 15, quad = lane >> 4;
+
+  // Q^T operand: query col (zero past GRP), d = 32 kk + 8 quad .. + 7
+  bf16x8 qop[4];
+  {
+    const bool real = col < GRP;
+    const bf16* qrow = (const bf16*)a.q + ((int64_t)b * a.H + g * GRP + (real ? col : 0)) * kD;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const bf16x8 v = *(const bf16x8*)(qrow + 32 * kk + 8 * quad);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qop[kk][e] = real ? v[e] : (bf16)0.0f;
+    }
+  }
+
+  // (sequence, head) bases, uniform; rows as 32-bit byte offsets (the
+  // launcher takes this kernel only while cap * 256 B fits 32 bits)
+  const char* kb = (const char*)a.k_cache + ((int64_t)b * a.G + g) * a.cap * kD * 2;
+  const char* vb = (const char*)a.v_cache + ((int64_t)b * a.G + g) * a.cap * kD * 2;
+  const uint32_t rlast = (uint32_t)(r1 - 1);
+  auto fetch = [&](int64_t t, DecStage& st) __attribute__((always_inline)) {
+    const uint32_t base = (uint32_t)(r0 + t * kStageRows);
+    const uint32_t koff = min(base + col, rlast) * (kD * 2) + 16 * quad;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+      st.k[kk] = __builtin_bit_cast(bf16x8, __builtin_nontemporal_load((const u32x4*)(kb + koff + 64 * kk)));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t voff = min(base + 4 * i + quad, rlast) * (kD * 2) + 16 * col;
+      st.v[i] = __builtin_bit_cast(bf16x8, __builtin_nontemporal_load((const u32x4*)(vb + voff)));
+    }
+  };
+
+  f32x4 o[kD / 16];
+#pragma unroll
+  for (int i = 0; i < kD / 16; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m = -1e30f, lsum = 0.f;  // of query col
+  const float c = a.scale_log2;
+  const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
+  char* const vt = vtile[wave];
+  // transposed-read address of V block blk: row 4 quad + col / 4, d = 16 blk + 4 (col mod 4)
+  const int vr = 4 * quad + (col >> 2);
+  const int vsw = 2 * (vr & 7);
+
+  auto compute = [&](const DecStage& st, int64_t t) __attribute__((always_inline)) {
+    f32x4 s4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) s4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(st.k[kk], qop[kk], s4, 0, 0, 0);
+    const int64_t key0 = r0 + t * kStageRows + 4 * quad;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (key0 + r >= r1) s4[r] = -INFINITY;
+    float mx = fmaxf(fmaxf(s4[0], s4[1]), fmaxf(s4[2], s4[3]));
+    {
+      const auto x16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      mx = fmaxf(__uint_as_float(x16[0]), __uint_as_float(x16[1]));
+      const auto x32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      mx = fmaxf(__uint_as_float(x32[0]), __uint_as_float(x32[1]));
+    }
+    const float mt = mx * c;
+    if (__ballot(mt > m + kSlack)) {
+      const float mn = fmaxf(m, mt);
+      float al = fast_exp2(m - mn);
+      asm volatile("" : "+v"(al));
+      m = mn;
+      lsum *= al;
+      // O rows are queries 4 quad + r, whose factors sit in lanes col = 4 quad + r
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float ar = __shfl(al, 4 * quad + r, kWave);
+#pragma unroll
+        for (int i2 = 0; i2 < kD / 16; ++i2) o[i2][r] *= ar;
+      }
+    }
+    const float nm = -m;
+    bf16x4 pa;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) pa[r] = (bf16)fast_exp2(fmaf(s4[r], c, nm));
+    // the weights enter P V as bf16; the row sum adds those same values
+    lsum = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pa[0], pa[1]}, ones, lsum, false);
+    lsum = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pa[2], pa[3]}, ones, lsum, false);
+    const i16x4 pai = __builtin_bit_cast(i16x4, pa);
+    // V tile: row r, 16-byte column c stored at c ^ 2 (r mod 8)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 4 * i + quad;
+      *(bf16x8*)(vt + r * 256 + ((col ^ (2 * (r & 7))) * 16)) = st.v[i];
+    }
+#pragma unroll
+    for (int blk = 0; blk < kD / 16; ++blk) {
+      const int d0 = 16 * blk + 4 * (col & 3);
+      const char* pv = vt + vr * 256 + (((d0 >> 3) ^ vsw) * 16) + (d0 & 7) * 2;
+      const i16x4 vv = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4*)(pv));
+      o[blk] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pai, vv, o[blk], 0, 0, 0);
+    }
+  };
+
+  const int64_t n_stages = r1 > r0 ? (r1 - r0 + kStageRows - 1) / kStageRows : 0;
+  const int64_t n_mine = n_stages > wave ? (n_stages - wave + 3) / 4 : 0;
+  // Three stages in registers: one being used, two in flight.  The steady
+  // loop has no branches, so every fetch is issued two stages ahead; fetches
+  // past the wavefront's last stage read (clamped) rows that are not used.
+  if (n_mine > 0) {
+    DecStage s0, s1, s2;
+    fetch(wave, s0);
+    fetch(wave + 4, s1);
+    int64_t i = 0;
+    for (; i + 3 <= n_mine; i += 3) {
+      const int64_t t = wave + 4 * i;
+      fetch(t + 8, s2);
+      compute(s0, t);
+      fetch(t + 12, s0);
+      compute(s1, t + 4);
+      fetch(t + 16, s1);
+      compute(s2, t + 8);
+    }
+    if (i < n_mine) compute(s0, wave + 4 * i);
+    if (i + 1 < n_mine) compute(s1, wave + 4 * (i + 1));
+  }
+
+  // this wavefront's (m, l) per query (col) and O rows (queries 4 quad + r)
+  lsum += __shfl_xor(lsum, 16, kWave);
+  lsum += __shfl_xor(lsum, 32, kWave);
+  if (quad == 0 && col < GRP) {
+    sm[wave][col] = m;
+    sl[wave][col] = lsum;
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int q = 4 * quad + r;
+    if (q < GRP) {
+#pragma unroll
+      for (int blk = 0; blk < kD / 16; ++blk) so[wave][q][16 * blk + col] = o[blk][r];
+    }
+  }
+  __syncthreads();
+  for (int idx = tid; idx < GRP * kD; idx += kThreads) {
+    const int j = idx / kD, d = idx % kD;
+    float M = sm[0][j];
+#pragma unroll
+    for (int w2 = 1; w2 < 4; ++w2) M = fmaxf(M, sm[w2][j]);
+    float L = 0.f, O = 0.f;
+#pragma unroll
+    for (int w2 = 0; w2 < 4; ++w2) {
+      const float f = fast_exp2(sm[w2][j] - M);
+      L += sl[w2][j] * f;
+      O += so[w2][j][d] * f;
+    }
+    float* pp = a.part + (((int64_t)b * a.H + g * GRP + j) * a.splits + sp) * (kD + 2);
+    if (d == 0) {
+      pp[0] = M;
+      pp[1] = L;
+    }
+    pp[2 + d] = O;
+  }
+}
+
 __global__ __launch_bounds__(128) void decode_merge_kernel(DecodeArgs a) {
   using namespace dec;
   const int bh = blockIdx.x;
@@ -413,6 +626,23 @@ __global__ __launch_bounds__(128) void decode_merge_kernel(DecodeArgs a) {
     O += p[s * (kD + 2) + 2 + d] * f;
   }
   ((bf16*)a.out)[(int64_t)bh * kD + d] = (bf16)(O / L);
+}
+
+// The grouped MFMA kernel's walk: 16-row stages of the split, stage t taken
+// by wavefront t mod 4.
+__global__ __launch_bounds__(dec::kThreads) void probe_decode_mfma_kernel(DecodeArgs a,
+                                                                         int32_t* count) {
+  using namespace dec;
+  const int sp = blockIdx.x;
+  const int64_t r0 = (int64_t)sp * a.rows_per_split;
+  const int64_t r1 = min(a.n, r0 + a.rows_per_split);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t n_stages = r1 > r0 ? (r1 - r0 + kStageRows - 1) / kStageRows : 0;
+  const int64_t n_mine = n_stages > wave ? (n_stages - wave + 3) / 4 : 0;
+  for (int64_t i = 0; i < n_mine; ++i) {
+    const int64_t r = r0 + (wave + 4 * i) * kStageRows + lane;
+    if (lane < kStageRows && r < r1) atomicAdd(&count[r], 1);
+  }
 }
 
 __global__ __launch_bounds__(dec::kThreads) void probe_decode_kernel(DecodeArgs a, int32_t* count) {
@@ -461,6 +691,12 @@ int decode_splits(int B, int G, int64_t n) {
   return (int)s;
 }
 
+// The grouped MFMA kernel serves bf16 caches with H/G >= 2 whose rows fit
+// 32-bit byte offsets; the per-row kernel the rest.
+bool uses_decode_mfma(const DecodeArgs& a) {
+  return !a.fp8 && a.H / a.G >= 2 && a.cap < ((int64_t)1 << 24);
+}
+
 hipError_t launch_decode_split(const DecodeArgs& a, hipStream_t s) {
   const int group = a.H / a.G;
   const int blocks = a.B * a.G * a.splits;
@@ -468,6 +704,8 @@ hipError_t launch_decode_split(const DecodeArgs& a, hipStream_t s) {
   case GG:                                                                 \
     if (a.fp8)                                                             \
       decode_split_kernel<GG, true><<<blocks, dec::kThreads, 0, s>>>(a);   \
+    else if (uses_decode_mfma(a))                                          \
+      decode_mfma_kernel<(GG >= 2 ? GG : 2)><<<blocks, dec::kThreads, 0, s>>>(a); \
     else                                                                   \
       decode_split_kernel<GG, false><<<blocks, dec::kThreads, 0, s>>>(a);  \
     break;
@@ -489,7 +727,10 @@ hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t s) {
 hipError_t launch_probe_decode(const DecodeArgs& a, int32_t* count, hipStream_t s) {
   hipError_t e = hipMemsetAsync(count, 0, (size_t)a.cap * sizeof(int32_t), s);
   if (e != hipSuccess) return e;
-  probe_decode_kernel<<<a.splits, dec::kThreads, 0, s>>>(a, count);
+  if (uses_decode_mfma(a))
+    probe_decode_mfma_kernel<<<a.splits, dec::kThreads, 0, s>>>(a, count);
+  else
+    probe_decode_kernel<<<a.splits, dec::kThreads, 0, s>>>(a, count);
   return hipGetLastError();
 }
 

@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define OLMO3_ABI_VERSION 4
+#define OLMO3_ABI_VERSION 5
 
 typedef enum olmo3_status {
   OLMO3_OK = 0,
@@ -309,11 +309,14 @@ int olmo3_probe_prefill_visits(int T, int64_t pos_offset, int window, int layer_
                                uint8_t* visit, void* stream);
 
 /* count [cache_capacity] int32 (device): number of times the decode kernel
- * at position `pos` reads each cache slot of one (sequence, KV head), for
- * the split count it would choose for batch B and G key/value heads.
+ * at position `pos` reads each cache slot of one (sequence, KV head) into
+ * its result, for the split count it would choose for batch B, H query and G
+ * key/value heads, and cache element type `dtype` (OLMO3_DTYPE_BF16 or
+ * OLMO3_DTYPE_BF16_E4M3): the row walk of the kernel those select (the
+ * grouped MFMA kernel for bf16 caches with H/G >= 2, else the per-row one).
  * Errors: INVALID_ARG, CAPACITY.  */
-int olmo3_probe_decode_reads(int B, int G, int d, int window, int layer_type,
-                             int64_t pos, int64_t cache_capacity,
+int olmo3_probe_decode_reads(int B, int H, int G, int d, int window, int layer_type,
+                             int dtype, int64_t pos, int64_t cache_capacity,
                              int32_t* count, void* stream);
 
 #ifdef __cplusplus

@@ -43,7 +43,7 @@ def test_header_binding_and_library_versions_agree():
 
 
 def test_abi_version():
-    assert A.olmo3_abi_version() == A.ABI_VERSION == 4
+    assert A.olmo3_abi_version() == A.ABI_VERSION == 5
 
 
 def test_layer_type_matches_oracle_bit_exact():
@@ -194,8 +194,10 @@ def test_probe_rejects():
     assert L.olmo3_probe_prefill_visits(5, -1, 4, 0, fake(0), None) == A.ERR_INVALID_ARG
     assert L.olmo3_probe_prefill_visits(5000, 0, 4, 0, fake(0), None) == A.ERR_UNSUPPORTED
     assert L.olmo3_probe_prefill_visits(100, 8100, 4, 0, fake(0), None) == A.ERR_UNSUPPORTED
-    assert L.olmo3_probe_decode_reads(1, 1, 64, 4, 0, 3, 4, fake(0), None) == A.ERR_INVALID_ARG
-    assert L.olmo3_probe_decode_reads(1, 1, 128, 4, 0, 3, 5, fake(0), None) == A.ERR_CAPACITY
+    assert L.olmo3_probe_decode_reads(1, 1, 1, 64, 4, 0, 0, 3, 4, fake(0), None) == A.ERR_INVALID_ARG
+    assert L.olmo3_probe_decode_reads(1, 3, 2, 128, 4, 0, 0, 3, 4, fake(0), None) == A.ERR_INVALID_ARG
+    assert L.olmo3_probe_decode_reads(1, 2, 1, 128, 4, 0, 1, 3, 4, fake(0), None) == A.ERR_INVALID_ARG
+    assert L.olmo3_probe_decode_reads(1, 1, 1, 128, 4, 0, 0, 3, 5, fake(0), None) == A.ERR_CAPACITY
 
 
 def test_binding_refuses_host_tensors():

@@ -186,7 +186,7 @@ def test_decode_stack_reads_effective_bytes_per_token():
                                     H=H, G=G, d=d, kv_heads=gs, kind=kind, window=W,
                                     rope=oracle_rope(rope), pos=pos)
             assert_close(host(out[b]).reshape(H, d)[heads], ref, what=f"stack layer {ell} b={b}")
-        count = A.olmo3_probe_decode_reads(B, G, d, W, lt, pos, cap).cpu().numpy()
+        count = A.olmo3_probe_decode_reads(B, H, G, d, W, lt, pos, cap).cpu().numpy()
         assert count.max() == 1
         rows_read += int(count.sum())
         del kc, vc, x, out

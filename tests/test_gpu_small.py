@@ -219,13 +219,18 @@ def test_probe_prefill_visits_bit_exact(T, window):
         assert np.array_equal(got, want), (T, window, lt, np.argwhere(got != want)[:5])
 
 
-@pytest.mark.parametrize("B,G,window,lt,pos,cap", [
-    (32, 32, 4096, 0, 65535, 4096), (32, 32, 4096, 1, 65535, 65536), (64, 8, 4096, 0, 32767, 4096),
-    (64, 8, 4096, 1, 32767, 32768), (1, 1, 4096, 0, 10, 4096), (1, 1, 4096, 1, 0, 1),
-    (1, 4, 4096, 1, 19999, 20000), (3, 2, 128, 0, 127, 128), (3, 2, 128, 0, 128, 128),
+# (B, H, G, ...): H = G is the per-row kernel's walk, H/G >= 2 with bf16 caches
+# the grouped MFMA kernel's, with e4m3 caches the per-row kernel's again
+@pytest.mark.parametrize("B,H,G,window,lt,pos,cap,dtype", [
+    (32, 32, 32, 4096, 0, 65535, 4096, 0), (32, 32, 32, 4096, 1, 65535, 65536, 0),
+    (64, 40, 8, 4096, 0, 32767, 4096, 0), (64, 40, 8, 4096, 1, 32767, 32768, 0),
+    (64, 40, 8, 4096, 0, 32767, 4096, 2), (64, 40, 8, 4096, 1, 32767, 32768, 2),
+    (1, 1, 1, 4096, 0, 10, 4096, 0), (1, 1, 1, 4096, 1, 0, 1, 0), (1, 2, 1, 4096, 1, 0, 1, 0),
+    (1, 8, 4, 4096, 1, 19999, 20000, 0), (3, 6, 2, 128, 0, 127, 128, 0), (3, 6, 2, 128, 0, 128, 128, 0),
+    (2, 40, 8, 4096, 1, 100, 1000, 0), (5, 14, 2, 4096, 1, 1000, 1001, 0),
 ])
-def test_probe_decode_reads_each_held_slot_once(B, G, window, lt, pos, cap):
-    got = A.olmo3_probe_decode_reads(B, G, 128, window, lt, pos, cap).cpu().numpy()
+def test_probe_decode_reads_each_held_slot_once(B, H, G, window, lt, pos, cap, dtype):
+    got = A.olmo3_probe_decode_reads(B, H, G, 128, window, lt, pos, cap, dtype=dtype).cpu().numpy()
     kind = KINDS[lt]
     n = O.cache_entries(kind, window, pos + 1)
     assert n == (min(pos + 1, window) if lt == 0 else pos + 1)
