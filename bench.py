@@ -52,7 +52,14 @@ THETA = 500000.0
 KERNEL_SOURCES = {
     "prefill_d128_kernel": ["prefill.hip", "tiles.h", "common.h", "kernels.h"],
     "decode_split_kernel": ["attn.hip", "tiles.h", "common.h", "kernels.h"],
+    "decode_mfma_kernel": ["attn.hip", "tiles.h", "common.h", "kernels.h"],
 }
+
+
+def decode_kernel(H: int, G: int, e4m3: bool) -> str:
+    """The split kernel the library runs: the grouped MFMA one for bf16
+    caches with H/G >= 2, else the per-row one."""
+    return "decode_mfma_kernel" if not e4m3 and H // G >= 2 else "decode_split_kernel"
 MEASURED_TRAFFIC = {
     ("olmo3-7b-layer", "prefill_sliding_l0"): dict(bytes=706134217, sources="7f2f5107ac811bb8"),
     ("olmo3-7b-layer", "prefill_full_l3"): dict(bytes=297171648, sources="7f2f5107ac811bb8"),
@@ -281,8 +288,11 @@ def main():
     wall = time.perf_counter() - t0
 
     # ---- per-kernel and per-call times (ms), averaged over the timed steps
+    dcfg = wl["decode"] or {}
     kernel_names = {("prefill", 0): "qknorm_rope_append_kernel", ("prefill", 1): "prefill_d128_kernel",
-                    ("decode", 0): "qknorm_rope_append_kernel", ("decode", 1): "decode_split_kernel",
+                    ("decode", 0): "qknorm_rope_append_kernel",
+                    ("decode", 1): decode_kernel(dcfg.get("H", 1), dcfg.get("G", 1),
+                                                 bool(dcfg.get("e4m3"))),
                     ("decode", 2): "decode_merge_kernel"}
     for seg in segments:
         per_phase = [[evs[i].elapsed_time(evs[i + 1]) for evs in seg["events"]]

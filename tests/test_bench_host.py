@@ -53,3 +53,10 @@ def test_recorded_traffic_needs_unchanged_sources(monkeypatch):
                         dict(entry, sources=bench.sources_digest("decode_split_kernel")))
     assert bench.measured_traffic(*key, "decode_split_kernel") == entry["bytes"]
     assert bench.measured_traffic("olmo3-7b-layer", "no such segment", "decode_split_kernel") is None
+
+
+def test_decode_kernel_label():
+    assert bench.decode_kernel(32, 32, False) == "decode_split_kernel"
+    assert bench.decode_kernel(40, 8, False) == "decode_mfma_kernel"
+    assert bench.decode_kernel(40, 8, True) == "decode_split_kernel"
+    assert bench.decode_kernel(32, 32, True) == "decode_split_kernel"
