@@ -44,11 +44,12 @@ WINDOW = 4096
 THETA = 500000.0
 
 
-# HBM bytes per launch of the timed kernels, from two rocprofv3 --pmc runs of
-# this script (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled by
-# what the same counter reads for a 1 GiB device-to-device copy on the same
-# GPU (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0).  An entry holds only while the
-# kernel's sources hash to `sources`; otherwise the figure is reported null.
+# HBM bytes per launch of the timed kernels (7B and 32B layer workloads), from
+# two rocprofv3 --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE, KiB per
+# dispatch), each scaled by what the same counter reads for a 1 GiB
+# device-to-device copy on the same GPU (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0).
+# An entry holds only while the kernel's sources hash to `sources`; otherwise
+# the figure is reported null.
 KERNEL_SOURCES = {
     "prefill_d128_kernel": ["prefill.hip", "tiles.h", "common.h", "kernels.h"],
     "decode_split_kernel": ["attn.hip", "tiles.h", "common.h", "kernels.h"],
@@ -60,11 +61,17 @@ def decode_kernel(H: int, G: int, e4m3: bool) -> str:
     """The split kernel the library runs: the grouped MFMA one for bf16
     caches with H/G >= 2, else the per-row one."""
     return "decode_mfma_kernel" if not e4m3 and H // G >= 2 else "decode_split_kernel"
+
+
 MEASURED_TRAFFIC = {
-    ("olmo3-7b-layer", "prefill_sliding_l0"): dict(bytes=706134217, sources="7f2f5107ac811bb8"),
-    ("olmo3-7b-layer", "prefill_full_l3"): dict(bytes=297171648, sources="7f2f5107ac811bb8"),
-    ("olmo3-7b-layer", "decode_sliding"): dict(bytes=2149194501, sources="415111273ea86b7f"),
-    ("olmo3-7b-layer", "decode_full"): dict(bytes=34360676474, sources="415111273ea86b7f"),
+    ("olmo3-7b-layer", "prefill_sliding_l0"): dict(bytes=710944943, sources="7f2f5107ac811bb8"),
+    ("olmo3-7b-layer", "prefill_full_l3"): dict(bytes=296485791, sources="7f2f5107ac811bb8"),
+    ("olmo3-7b-layer", "decode_sliding"): dict(bytes=2149210591, sources="fad8070f0b61442d"),
+    ("olmo3-7b-layer", "decode_full"): dict(bytes=34360685972, sources="fad8070f0b61442d"),
+    ("olmo3-32b-layer", "prefill_sliding_l0"): dict(bytes=323849758, sources="7f2f5107ac811bb8"),
+    ("olmo3-32b-layer", "prefill_full_l3"): dict(bytes=319625280, sources="7f2f5107ac811bb8"),
+    ("olmo3-32b-layer", "decode_sliding"): dict(bytes=1089779665, sources="fad8070f0b61442d"),
+    ("olmo3-32b-layer", "decode_full"): dict(bytes=8643026345, sources="fad8070f0b61442d"),
 }
 
 
