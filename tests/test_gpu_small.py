@@ -123,6 +123,10 @@ DECODE_CASES = [
     (2, 10, 2, 128, 4096, 1, 0, 400),
     (1, 4, 1, 128, 4096, 1, 19999, 20000),  # 64 splits
     (4, 16, 2, 128, 300, 0, 5000, 300),     # group 8
+    (2, 4, 2, 128, 4096, 1, 777, 1000),     # group 2
+    (2, 6, 2, 128, 256, 0, 300, 256),       # group 3
+    (1, 12, 2, 128, 4096, 1, 2048, 3000),   # group 6
+    (2, 14, 2, 128, 100, 0, 500, 100),      # group 7
     (2, 6, 2, 64, 64, 0, 100, 64),          # plain kernel
     (2, 6, 6, 32, 4096, 1, 70, 100),
 ]
