@@ -18,7 +18,7 @@ from . import LAYER_FULL, LAYER_SLIDING  # noqa: F401  (re-exported)
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libolmo3attn.so")
 
-ABI_VERSION = 5  # OLMO3_ABI_VERSION of include/olmo3_attn.h
+ABI_VERSION = 6  # OLMO3_ABI_VERSION of include/olmo3_attn.h
 DTYPE_BF16, DTYPE_F32, DTYPE_BF16_E4M3 = 0, 1, 2
 MODE_PREFILL, MODE_DECODE = 0, 1
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_CAPACITY, ERR_HIP, ERR_WORKSPACE = range(6)
@@ -114,8 +114,8 @@ def lib() -> ctypes.CDLL:
         L.olmo3_kv_append_e4m3.argtypes = [_i, _i, _i, _i, _i, _i, R, _f, _i64, _p, _p, _p, _p, _p,
                                            _f, _f, _i64, _p]
         L.olmo3_kv_append_e4m3.restype = _i
-        L.olmo3_attn_prefill_e4m3.argtypes = [_i, _i, _i, _i, _i, _i, _i, R, _f, _p, _p, _p, _p,
-                                              _p, _p, _p, _f, _f, _i64, _p, _p, _sz, _p]
+        L.olmo3_attn_prefill_e4m3.argtypes = [_i, _i, _i, _i, _i, _i, _i, R, _f, _i64, _p, _p,
+                                              _p, _p, _p, _p, _p, _f, _f, _i64, _p, _p, _sz, _p]
         L.olmo3_attn_prefill_e4m3.restype = _i
         L.olmo3_attn_decode_e4m3.argtypes = [_i, _i, _i, _i, _i, _i, R, _f, _i64, _p, _p, _p, _p,
                                              _p, _p, _p, _f, _f, _i64, _p, _p, _sz, _p]
@@ -323,8 +323,9 @@ def olmo3_kv_append_e4m3(k_pre, v, k_gain, k_cache, v_cache, *, k_scale: float, 
 
 def olmo3_attn_prefill_e4m3(q_pre, k_pre, v, q_gain, k_gain, k_cache, v_cache, out, workspace, *,
                             k_scale: float, v_scale: float, window: int, layer_type: int,
-                            rope: Rope, eps: float = 1e-6, stream=None) -> None:
-    """First-chunk prefill (positions 0..T-1) into e4m3 caches (uint8)."""
+                            rope: Rope, eps: float = 1e-6, pos_offset: int = 0,
+                            stream=None) -> None:
+    """Prefill of positions pos_offset..pos_offset+T-1 into e4m3 caches (uint8)."""
     B, G, cap, d = _cache_dims(k_cache)
     T = q_pre.shape[1]
     H = q_pre.shape[2] // d
@@ -332,9 +333,10 @@ def olmo3_attn_prefill_e4m3(q_pre, k_pre, v, q_gain, k_gain, k_cache, v_cache, o
     kc, vc = _e4m3_caches(k_cache, v_cache)
     r = rope.to_c()
     st = lib().olmo3_attn_prefill_e4m3(
-        B, T, H, G, d, window, layer_type, ctypes.byref(r), eps, _ptr(q_pre, "q_pre", dt),
-        _ptr(k_pre, "k_pre", dt), _ptr(v, "v", dt), _ptr(q_gain, "q_gain", dt),
-        _ptr(k_gain, "k_gain", dt), kc, vc, k_scale, v_scale, cap, _ptr(out, "out", dt),
+        B, T, H, G, d, window, layer_type, ctypes.byref(r), eps, pos_offset,
+        _ptr(q_pre, "q_pre", dt), _ptr(k_pre, "k_pre", dt), _ptr(v, "v", dt),
+        _ptr(q_gain, "q_gain", dt), _ptr(k_gain, "k_gain", dt), kc, vc, k_scale, v_scale, cap,
+        _ptr(out, "out", dt),
         _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
         _stream(stream, q_pre.device))
     _check(st, "olmo3_attn_prefill_e4m3")

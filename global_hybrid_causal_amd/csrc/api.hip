@@ -108,6 +108,18 @@ size_t prefill_ws(int B, int T, int H, int G, int d, int layer_type, int dtype) 
   return bytes;
 }
 
+// A later chunk of a prefill into e4m3 caches reads the cache's earlier rows
+// through a bf16 copy of them (keys and values, `rows` per (sequence, head)).
+size_t stage_ws(int B, int G, int d, int64_t rows) {
+  return 2 * align_up((size_t)B * G * rows * d * sizeof(uint16_t));
+}
+
+// Rows of that copy: the whole ring (slot order kept) or positions
+// 0 .. pos_offset-1 of a linear cache.
+int64_t stage_rows(int layer_type, int window, int64_t pos_offset) {
+  return layer_type == OLMO3_LAYER_SLIDING ? window : pos_offset;
+}
+
 size_t decode_ws(int B, int H, int G, int d, int layer_type, int window, int dtype, int64_t cap) {
   const size_t es = elem_size(dtype);
   size_t bytes = align_up((size_t)B * H * d * es);
@@ -212,7 +224,12 @@ size_t olmo3_workspace_bytes(int mode, int B, int T, int H, int G, int d, int la
   if (mode == OLMO3_MODE_DECODE) T = 1;
   const int act = dtype == OLMO3_DTYPE_BF16_E4M3 ? OLMO3_DTYPE_BF16 : dtype;
   if (check_common(B, T, H, G, d, 1, layer_type, act, &plain, 0.f, 0) != OLMO3_OK) return 0;
-  if (mode == OLMO3_MODE_PREFILL) return prefill_ws(B, T, H, G, d, layer_type, dtype);
+  if (mode == OLMO3_MODE_PREFILL) {
+    size_t bytes = prefill_ws(B, T, H, G, d, layer_type, dtype);
+    // e4m3: room for a bf16 copy of every cache row, for chunks after the first
+    if (dtype == OLMO3_DTYPE_BF16_E4M3 && cache_capacity > 0) bytes += stage_ws(B, G, d, cache_capacity);
+    return bytes;
+  }
   if (mode == OLMO3_MODE_DECODE) {
     if (cache_capacity < 1) return 0;
     // a sliding layer's ring holds cache_capacity == window slots
@@ -312,6 +329,12 @@ int prefill_impl(int phases, const PrefillShape& sh, int H, int G, int d, int wi
   // straight after the prologue has filled it
   const bool kv_from_ws = sliding || cf.e4m3;
   void* k_rot = kv_from_ws ? ws + align_up((size_t)N * H * d * es) : nullptr;
+  // a later chunk with e4m3 caches reads the earlier positions from a bf16
+  // copy of the cache rows that hold them, placed after the rotated keys
+  const bool stage = cf.e4m3 && !packed && sh.pos_offset > 0;
+  const int64_t st_rows = stage ? stage_rows(layer_type, window, sh.pos_offset) : 0;
+  char* k_stage = stage ? (char*)k_rot + align_up((size_t)B * G * T * d * es) : nullptr;
+  char* v_stage = stage ? k_stage + stage_ws(B, G, d, st_rows) / 2 : nullptr;
 
   RopeTable table;
   rope_table(rope, layer_type, d, &table);
@@ -350,6 +373,24 @@ int prefill_impl(int phases, const PrefillShape& sh, int H, int G, int d, int wi
     if (st) return st;
   }
   if (!(phases & OLMO3_PHASE_ATTENTION)) return OLMO3_OK;
+  if (stage) {
+    // before the chunk's own positions enter a ring (they are stored after
+    // the attention); on a linear cache they lie past the copied rows
+    E4m3StageArgs sa = {};
+    sa.k_codes = k_cache;
+    sa.v_codes = v_cache;
+    sa.k_out = k_stage;
+    sa.v_out = v_stage;
+    sa.cap = cache_capacity;
+    sa.rows = st_rows;
+    sa.n = std::min<int64_t>(sh.pos_offset, st_rows);
+    sa.BG = B * G;
+    sa.d = d;
+    sa.k_scale = cf.k_scale;
+    sa.v_scale = cf.v_scale;
+    st = hip_status(launch_e4m3_rows_to_bf16(sa, s));
+    if (st) return st;
+  }
 
   AttnArgs a = {};
   a.q = q_rot;
@@ -366,7 +407,16 @@ int prefill_impl(int phases, const PrefillShape& sh, int H, int G, int d, int wi
     a.v_sr = (int64_t)G * d;
     a.main_pos0 = sh.pos_offset;
     a.main_packed = packed;
-    if (ring_after) {
+    if (stage) {
+      // earlier positions from the bf16 copy: slot = position mod window on
+      // a ring, row = position on a linear cache (all below st_rows)
+      a.kp = k_stage;
+      a.vp = v_stage;
+      a.p_sb = (int64_t)G * st_rows * d;
+      a.p_sg = st_rows * d;
+      a.p_sr = d;
+      a.ring = st_rows;
+    } else if (ring_after) {
       a.kp = k_cache;
       a.vp = v_cache;
       a.p_sb = (int64_t)G * cache_capacity * d;
@@ -634,21 +684,22 @@ int olmo3_attn_decode(int B, int H, int G, int d, int window, int layer_type,
 }
 
 int olmo3_attn_prefill_e4m3(int B, int T, int H, int G, int d, int window, int layer_type,
-                            const olmo3_rope* rope, float eps, const void* q_pre,
-                            const void* k_pre, const void* v, const void* q_gain,
-                            const void* k_gain, void* k_cache, void* v_cache, float k_scale,
-                            float v_scale, int64_t cache_capacity, void* out, void* workspace,
-                            size_t workspace_bytes, void* stream) {
+                            const olmo3_rope* rope, float eps, int64_t pos_offset,
+                            const void* q_pre, const void* k_pre, const void* v,
+                            const void* q_gain, const void* k_gain, void* k_cache,
+                            void* v_cache, float k_scale, float v_scale, int64_t cache_capacity,
+                            void* out, void* workspace, size_t workspace_bytes, void* stream) {
   if (!valid_scale(k_scale) || !valid_scale(v_scale)) return OLMO3_ERR_INVALID_ARG;
-  const size_t need = (B > 0 && T > 0 && H > 0 && G > 0 && d > 0)
-                          ? prefill_ws(B, T, H, G, d, layer_type, OLMO3_DTYPE_BF16_E4M3)
-                          : 0;
-  int st = validate_attn(B, T, H, G, d, window, layer_type, rope, eps, 0, OLMO3_DTYPE_BF16,
-                         q_pre, k_pre, v, q_gain, k_gain, k_cache, v_cache, cache_capacity, out,
-                         workspace, workspace_bytes, need, B, (int64_t)T - 1, 1);
+  const bool sizes_ok = B > 0 && T > 0 && H > 0 && G > 0 && d > 0 && window > 0 && pos_offset >= 0;
+  size_t need = sizes_ok ? prefill_ws(B, T, H, G, d, layer_type, OLMO3_DTYPE_BF16_E4M3) : 0;
+  if (sizes_ok && pos_offset > 0) need += stage_ws(B, G, d, stage_rows(layer_type, window, pos_offset));
+  int st = validate_attn(B, T, H, G, d, window, layer_type, rope, eps, pos_offset,
+                         OLMO3_DTYPE_BF16, q_pre, k_pre, v, q_gain, k_gain, k_cache, v_cache,
+                         cache_capacity, out, workspace, workspace_bytes, need, B,
+                         pos_offset + T - 1, 1);
   if (st) return st;
-  if (T > kMaxPrefillPositions) return OLMO3_ERR_UNSUPPORTED;
-  const PrefillShape sh = {B, T, (int64_t)B * T, 0, nullptr, nullptr};
+  if (pos_offset + T > kMaxPrefillPositions) return OLMO3_ERR_UNSUPPORTED;
+  const PrefillShape sh = {B, T, (int64_t)B * T, pos_offset, nullptr, nullptr};
   return prefill_impl(OLMO3_PHASE_PROLOGUE | OLMO3_PHASE_ATTENTION, sh, H, G, d, window,
                       layer_type, rope, eps, OLMO3_DTYPE_BF16, q_pre, k_pre, v, q_gain, k_gain,
                       k_cache, v_cache, cache_capacity, out, workspace, (hipStream_t)stream,

@@ -49,6 +49,21 @@ hipError_t launch_prologue(const PrologueArgs& a, const RopeTable& rope, int dty
                            hipStream_t s);
 int prologue_max_heads(int dtype, int d);
 
+// bf16 image of e4m3 cache rows: rows 0 .. n-1 of each of the BG
+// (sequence, head) pairs of k_codes / v_codes ([BG][cap][d] codes) become
+// k_out / v_out [BG][rows][d] with value code * scale (fp32 product rounded
+// to bf16).  d must be a multiple of 16 and n <= min(rows, cap).
+struct E4m3StageArgs {
+  const void* k_codes;
+  const void* v_codes;
+  void* k_out;
+  void* v_out;
+  int64_t cap, rows, n;
+  int BG, d;
+  float k_scale, v_scale;
+};
+hipError_t launch_e4m3_rows_to_bf16(const E4m3StageArgs& a, hipStream_t s);
+
 // Attention over keys held in up to two strided buffers.
 //   queries  q[(b*Tq + t)*H + h][d], absolute position q_pos0 + t
 //   keys at positions 0 .. n_keys-1:

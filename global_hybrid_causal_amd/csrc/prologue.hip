@@ -286,7 +286,47 @@ hipError_t launch_prologue_t(const PrologueArgs& a, const RopeTable& rope, hipSt
   return hipGetLastError();
 }
 
+// bf16 copy of the first n rows of each (sequence, head) of an e4m3 cache.
+// One thread per 16 codes: one 16-byte load, two 16-byte stores; blockIdx.y
+// picks keys (0) or values (1).
+__global__ __launch_bounds__(256) void e4m3_rows_to_bf16_kernel(E4m3StageArgs a) {
+  const bool val = blockIdx.y != 0;
+  const uint8_t* src = (const uint8_t*)(val ? a.v_codes : a.k_codes);
+  bf16* dst = (bf16*)(val ? a.v_out : a.k_out);
+  const float scale = val ? a.v_scale : a.k_scale;
+  const int per_row = a.d / 16;
+  const int64_t per_head = a.n * per_row;
+  const int64_t items = (int64_t)a.BG * per_head;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < items;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t bg = i / per_head, rem = i - bg * per_head;
+    const int64_t row = rem / per_row;
+    const int c = (int)(rem - row * per_row) * 16;
+    const u32x4 w = *(const u32x4*)(src + (bg * a.cap + row) * a.d + c);
+    bf16x8 h[2];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float f[4];
+      e4m3x4_to_f32(w[j], f);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) h[j >> 1][4 * (j & 1) + e] = (bf16)(f[e] * scale);
+    }
+    bf16x8* o = (bf16x8*)(dst + (bg * a.rows + row) * a.d + c);
+    o[0] = h[0];
+    o[1] = h[1];
+  }
+}
+
 }  // namespace
+
+hipError_t launch_e4m3_rows_to_bf16(const E4m3StageArgs& a, hipStream_t s) {
+  if (a.d % 16 || a.n < 0 || a.n > a.rows || a.n > a.cap) return hipErrorInvalidValue;
+  const int64_t items = (int64_t)a.BG * a.n * (a.d / 16);
+  if (items == 0) return hipSuccess;
+  const int blocks = (int)std::min<int64_t>((items + 255) / 256, 8192);
+  e4m3_rows_to_bf16_kernel<<<dim3(blocks, 2), 256, 0, s>>>(a);
+  return hipGetLastError();
+}
 
 int prologue_max_heads(int dtype, int d) {
   const int vec = dtype == 0 ? 8 : 4;

@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define OLMO3_ABI_VERSION 5
+#define OLMO3_ABI_VERSION 6
 
 typedef enum olmo3_status {
   OLMO3_OK = 0,
@@ -107,8 +107,10 @@ int olmo3_layer_type(int layer, int n_layers);
 
 /* Device workspace, in bytes, that olmo3_attn_prefill (mode 0, T tokens) or
  * olmo3_attn_decode (mode 1, T ignored) needs for these sizes; the decode
- * figure covers every position that fits `cache_capacity`.  Returns 0 for
- * invalid sizes. */
+ * figure covers every position that fits `cache_capacity`.  With e4m3 caches
+ * (dtype OLMO3_DTYPE_BF16_E4M3) the prefill figure includes a bf16 copy of
+ * `cache_capacity` cache rows, which chunks at pos_offset > 0 need; a first
+ * chunk may pass cache_capacity = 0.  Returns 0 for invalid sizes. */
 size_t olmo3_workspace_bytes(int mode, int B, int T, int H, int G, int d,
                              int layer_type, int dtype, int64_t cache_capacity);
 
@@ -225,16 +227,20 @@ int olmo3_kv_append_e4m3(int B, int T, int G, int d, int window, int layer_type,
                          const void* v, const void* k_gain, void* k_cache, void* v_cache,
                          float k_scale, float v_scale, int64_t cache_capacity, void* stream);
 
-/* Prefill of a first chunk (positions 0 .. T-1) into e4m3 caches: the
- * attention uses the chunk's own rotated keys and values at bf16 precision;
- * the cache receives their codes.  workspace:
- * olmo3_workspace_bytes(OLMO3_MODE_PREFILL, ..., OLMO3_DTYPE_BF16_E4M3, ...). */
+/* Prefill of positions pos_offset .. pos_offset+T-1 into e4m3 caches (as
+ * olmo3_attn_prefill): the attention uses the chunk's own rotated keys and
+ * values at bf16 precision and, when pos_offset > 0, the positions the cache
+ * already holds as stored (code * scale, rounded to bf16: the library first
+ * copies the ring, or rows 0 .. pos_offset-1 of a linear cache, into the
+ * workspace); the cache then receives the chunk's codes.  workspace:
+ * olmo3_workspace_bytes(OLMO3_MODE_PREFILL, ..., OLMO3_DTYPE_BF16_E4M3,
+ * cache_capacity) bytes (with cache_capacity = 0 when pos_offset = 0). */
 int olmo3_attn_prefill_e4m3(int B, int T, int H, int G, int d, int window, int layer_type,
-                            const olmo3_rope* rope, float eps, const void* q_pre,
-                            const void* k_pre, const void* v, const void* q_gain,
-                            const void* k_gain, void* k_cache, void* v_cache, float k_scale,
-                            float v_scale, int64_t cache_capacity, void* out, void* workspace,
-                            size_t workspace_bytes, void* stream);
+                            const olmo3_rope* rope, float eps, int64_t pos_offset,
+                            const void* q_pre, const void* k_pre, const void* v,
+                            const void* q_gain, const void* k_gain, void* k_cache,
+                            void* v_cache, float k_scale, float v_scale, int64_t cache_capacity,
+                            void* out, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Decode against e4m3 caches: the new token's key and value are stored as
  * codes first, then the query attends to the cache rows as stored (the new

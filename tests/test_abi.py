@@ -43,7 +43,7 @@ def test_header_binding_and_library_versions_agree():
 
 
 def test_abi_version():
-    assert A.olmo3_abi_version() == A.ABI_VERSION == 5
+    assert A.olmo3_abi_version() == A.ABI_VERSION == 6
 
 
 def test_layer_type_matches_oracle_bit_exact():
@@ -304,5 +304,49 @@ def test_e4m3_workspace_adds_rotated_keys_on_full_layers():
     plain = L.olmo3_workspace_bytes(0, 1, 100, 4, 2, 128, 1, A.DTYPE_BF16, 100)
     e4m3 = L.olmo3_workspace_bytes(0, 1, 100, 4, 2, 128, 1, A.DTYPE_BF16_E4M3, 100)
     assert e4m3 - plain >= 100 * 2 * 128 * 2
-    assert L.olmo3_workspace_bytes(0, 1, 100, 4, 2, 128, 0, A.DTYPE_BF16_E4M3, 16) == \
+    # a first chunk (capacity 0): the same as bf16 on a sliding layer
+    assert L.olmo3_workspace_bytes(0, 1, 100, 4, 2, 128, 0, A.DTYPE_BF16_E4M3, 0) == \
         L.olmo3_workspace_bytes(0, 1, 100, 4, 2, 128, 0, A.DTYPE_BF16, 16)
+
+
+def test_e4m3_workspace_adds_cache_copy_for_later_chunks():
+    # room for a bf16 copy of every key and value row of the cache
+    L = A.lib()
+    for lt, cap in ((0, 16), (1, 300)):
+        first = L.olmo3_workspace_bytes(0, 3, 100, 4, 2, 128, lt, A.DTYPE_BF16_E4M3, 0)
+        later = L.olmo3_workspace_bytes(0, 3, 100, 4, 2, 128, lt, A.DTYPE_BF16_E4M3, cap)
+        assert later - first == 2 * 3 * 2 * cap * 128 * 2
+
+
+def e4m3_prefill_call(ws_bytes=1 << 34, **kw):
+    a = dict(B=1, T=8, H=4, G=2, d=128, window=16, layer_type=1, eps=1e-6, pos=40, cap=64,
+             ks=0.5, vs=0.5)
+    a.update(kw)
+    p = [fake(i) for i in range(9)]
+    r = ctypes.byref(A.Rope(theta=1e4).to_c())
+    return A.lib().olmo3_attn_prefill_e4m3(
+        a["B"], a["T"], a["H"], a["G"], a["d"], a["window"], a["layer_type"], r, a["eps"],
+        a["pos"], *p[:7], a["ks"], a["vs"], a["cap"], p[7], p[8], ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(pos=-1), A.ERR_INVALID_ARG),
+    (dict(ks=0.0), A.ERR_INVALID_ARG),
+    (dict(cap=47), A.ERR_CAPACITY),               # positions 40 .. 47 need 48 slots
+    (dict(layer_type=0, cap=15), A.ERR_CAPACITY),  # ring size != window
+    (dict(pos=(1 << 30) - 7), A.ERR_CAPACITY),
+    (dict(d=20), A.ERR_UNSUPPORTED),
+])
+def test_e4m3_prefill_rejects(kw, status):
+    assert e4m3_prefill_call(**kw) == status
+
+
+@pytest.mark.parametrize("lt,rows", [(1, 40), (0, 16)])
+def test_e4m3_prefill_later_chunk_needs_the_copy(lt, rows):
+    # a chunk at pos_offset 40 needs the first-chunk workspace plus a bf16
+    # copy of 40 linear rows, or of the 16-slot ring
+    L = A.lib()
+    first = L.olmo3_workspace_bytes(0, 1, 8, 4, 2, 128, lt, A.DTYPE_BF16_E4M3, 0)
+    need = first + 2 * 2 * rows * 128 * 2
+    cap = 64 if lt == 1 else 16
+    assert e4m3_prefill_call(ws_bytes=need - 1, layer_type=lt, cap=cap) == A.ERR_WORKSPACE

@@ -127,6 +127,53 @@ def test_e4m3_prefill_vs_oracle(case):
                  f"e4m3 prefill {case}")
 
 
+CHUNKED = [
+    # B, T, H, G, d, window, layer_type, pos_offset, yarn
+    (1, 200, 4, 4, 128, 64, 0, 300, False),    # wrapped ring, chunk longer than the window
+    (2, 40, 6, 2, 128, 100, 0, 30, False),     # ring partly filled
+    (2, 77, 8, 2, 128, 128, 0, 250, False),    # wrapped ring, tiles cross the wrap
+    (2, 129, 10, 2, 128, 4096, 1, 500, True),  # linear cache, group 5
+    (1, 300, 8, 8, 128, 4096, 1, 1000, True),  # linear cache, MHA
+    (1, 1, 4, 2, 128, 4096, 1, 77, True),      # one token
+    (1, 50, 4, 2, 64, 40, 0, 77, False),       # plain kernel, ring
+]
+
+
+@pytest.mark.parametrize("case", CHUNKED, ids=[str(c) for c in CHUNKED])
+def test_e4m3_chunked_prefill_vs_oracle(case):
+    """A later chunk: earlier positions are read from the cache as stored
+    (code times scale), the chunk's own keys and values at bf16 precision;
+    the chunk's codes then land in their slots and no other slot changes."""
+    B, T, H, G, d, w, lt, P, yarn = case
+    _log("e4m3 chunked prefill", case)
+    kind = KINDS[lt]
+    rope = A.Rope(theta=500000.0, yarn=yarn, factor=8.0, orig_ctx=256)
+    cap = w if kind == O.SLIDING else P + T + 3
+    x = inputs(79, lt, B, T, H, G, d, BF16)
+    kc, vc = synth.e4m3_cache_fill(79, lt, B, G, cap, d, device="cuda")
+    bk, bv = _codes(kc), _codes(vc)
+    out = torch.empty_like(x["q_pre"])
+    ws = A.workspace(A.MODE_PREFILL, B, T, H, G, d, lt, A.DTYPE_BF16_E4M3, cap, "cuda")
+    A.olmo3_attn_prefill_e4m3(x["q_pre"], x["k_pre"], x["v"], x["q_gain"], x["k_gain"], kc, vc,
+                              out, ws, k_scale=KS, v_scale=VS, window=w, layer_type=lt, rope=rope,
+                              pos_offset=P)
+    hx = host_inputs(x)
+    ref_cache = O.KvCacheRef(kind, w, cap, B, G, d, e4m3_scales=(KS, VS))
+    ref_cache.k[:] = TABLE[bk] * KS
+    ref_cache.v[:] = TABLE[bv] * VS
+    ref_cache.pos[:] = O.ring_positions(kind, w, cap, P)
+    ref = O.prefill_ref(**hx, H=H, G=G, d=d, kind=kind, window=w, rope=oracle_rope(rope),
+                        pos_offset=P, cache=ref_cache)
+    err = assert_close(host(out), ref, what=f"e4m3 chunked prefill {case}")
+    _log("  max abs / rel err", err)
+    positions = P + np.arange(T)
+    keep = positions[-w:] if kind == O.SLIDING else positions
+    slots = keep % w if kind == O.SLIDING else keep
+    k_rot = _rotated_keys(hx, kind, rope, positions, G, d)[:, keep - P]
+    _check_slots(kc, vc, bk, bv, slots, k_rot, hx["v"].reshape(B, T, G, d)[:, keep - P],
+                 f"e4m3 chunked prefill {case}")
+
+
 DECODE = [
     # B, H, G, window, layer_type, pos, cap
     *[(3, 8, 2, 128, 0, p, 128) for p in (0, 126, 127, 128, 129, 255, 256, 1000)],
