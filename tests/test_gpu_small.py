@@ -267,6 +267,57 @@ def test_planted_value_window_edges(lt, T, w, s_star):
     assert_close(out[sees], want, 0.0, 2 ** -8, "planted rows")
 
 
+WHOLE_VS_PHASES = [
+    # B, H, G, window, layer_type, pos, cap, e4m3
+    (3, 8, 8, 128, 0, 500, 128, False),        # per-row kernel, one query head per group
+    (2, 40, 8, 4096, 1, 19999, 20001, False),  # grouped MFMA kernel, group 5, many splits
+    (2, 8, 2, 4096, 1, 5000, 5002, True),      # e4m3 caches, group 4
+    (1, 4, 4, 64, 0, 3, 64, False),            # four rows: one split
+]
+
+
+@pytest.mark.parametrize("case", WHOLE_VS_PHASES, ids=[str(c) for c in WHOLE_VS_PHASES])
+def test_decode_whole_call_equals_phases(case):
+    """A whole decode call and the three phase entry points run one after the
+    other give the same bits, for each decode kernel, on two calls in a row
+    that share one workspace which starts as 0xff bytes (nothing may depend
+    on its contents on entry)."""
+    B, H, G, w, lt, pos, cap, e4m3 = case
+    d = 128
+    _log("whole call vs phases", case)
+    rope = A.Rope(theta=500000.0, yarn=lt == 1, factor=8.0, orig_ctx=512)
+    kw = dict(window=w, layer_type=lt, rope=rope)
+    if e4m3:
+        kc0, vc0 = synth.e4m3_cache_fill(83, lt, B, G, cap, d, device="cuda")
+        decode, dt, kw = A.olmo3_attn_decode_e4m3, A.DTYPE_BF16_E4M3, dict(kw, k_scale=0.37, v_scale=1.9)
+    else:
+        kc0, vc0 = synth.cache_fill(83, lt, B, G, cap, d, device="cuda")
+        decode, dt = A.olmo3_attn_decode, BF16
+    xs = [inputs(83, 30 + i, B, 1, H, G, d, BF16) for i in range(2)]
+    toks = [(x["q_pre"][:, 0].contiguous(), x["k_pre"][:, 0].contiguous(), x["v"][:, 0].contiguous(),
+             x["q_gain"], x["k_gain"]) for x in xs]
+    results = []
+    for phased in (False, True):
+        kc, vc = kc0.clone(), vc0.clone()
+        ws = A.workspace(A.MODE_DECODE, B, 1, H, G, d, lt, dt, cap, "cuda")
+        ws.fill_(255)
+        outs = []
+        for i, (q, k, v, qg, kg) in enumerate(toks):
+            out = torch.empty_like(q)
+            args = (q, k, v, qg, kg, kc, vc, out, ws)
+            if phased:
+                for ph in (A.PHASE_PROLOGUE, A.PHASE_ATTENTION, A.PHASE_MERGE):
+                    decode(*args, pos=pos + i, phases=ph, **kw)
+            else:
+                decode(*args, pos=pos + i, **kw)
+            outs.append(out)
+        torch.cuda.synchronize()
+        results.append([o.clone() for o in outs] + [kc.clone(), vc.clone()])
+    for a_, b_ in zip(*results):
+        assert torch.equal(a_, b_)
+    assert torch.isfinite(results[0][0].float()).all()
+
+
 def test_phase_entry_points_equal_one_call():
     """Running the stages one by one gives bit-identical outputs and caches."""
     B, T, H, G, d, w = 1, 333, 8, 2, 128, 100
