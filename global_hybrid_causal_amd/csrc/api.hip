@@ -600,7 +600,8 @@ int decode_impl(int phases, int B, int H, int G, int d, int window, int layer_ty
       st = hip_status(launch_decode_split(a, s));
       if (st) return st;
     }
-    if (phases & OLMO3_PHASE_MERGE) return hip_status(launch_decode_merge(a, s));
+    // one split: the split kernel has written the output rows
+    if ((phases & OLMO3_PHASE_MERGE) && a.splits > 1) return hip_status(launch_decode_merge(a, s));
     return OLMO3_OK;
   }
   if (!(phases & OLMO3_PHASE_ATTENTION)) return OLMO3_OK;

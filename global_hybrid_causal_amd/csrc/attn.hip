@@ -390,12 +390,19 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_eu<GRP, kFp8>()))) void deco
       L += sl[w2][j] * f;
       O += so[w2][j][d] * f;
     }
-    float* pp = a.part + (((int64_t)b * a.H + g * GRP + j) * a.splits + sp) * (kD + 2);
+    const float Ov = kFp8 ? O * a.v_scale : O;
+    const int64_t bh = (int64_t)b * a.H + g * GRP + j;
+    if (a.splits == 1) {
+      // the whole key range: the output row itself (the merge of one state)
+      ((bf16*)a.out)[bh * kD + d] = (bf16)(Ov / L);
+      continue;
+    }
+    float* pp = a.part + (bh * a.splits + sp) * (kD + 2);
     if (d == 0) {
       pp[0] = M;
       pp[1] = L;
     }
-    pp[2 + d] = kFp8 ? O * a.v_scale : O;
+    pp[2 + d] = Ov;
   }
 }
 
@@ -603,7 +610,12 @@ __global__ __launch_bounds__(dec::kThreads, 2) void decode_mfma_kernel(DecodeArg
       L += sl[w2][j] * f;
       O += so[w2][j][d] * f;
     }
-    float* pp = a.part + (((int64_t)b * a.H + g * GRP + j) * a.splits + sp) * (kD + 2);
+    const int64_t bh = (int64_t)b * a.H + g * GRP + j;
+    if (a.splits == 1) {
+      ((bf16*)a.out)[bh * kD + d] = (bf16)(O / L);
+      continue;
+    }
+    float* pp = a.part + (bh * a.splits + sp) * (kD + 2);
     if (d == 0) {
       pp[0] = M;
       pp[1] = L;

@@ -92,7 +92,11 @@ constexpr int kUnroll = 4;                   // steps per loop iteration
 constexpr int kRowsPerIter = kGroups * kUnroll;
 constexpr int kMaxSplits = 64;
 constexpr int64_t kMinRowsPerSplit = 256;
-constexpr int64_t kTargetWorkgroups = 2048;
+// Splits per (sequence, key/value head): enough for about this many
+// workgroups.  Few long workgroups stream as fast as many short ones (at
+// B*G >= 512 every pair is one workgroup, which then writes its output rows
+// itself and no merge runs), and fewer reach the end of the stream together.
+constexpr int64_t kTargetWorkgroups = 512;
 
 // Rows of a split at iteration i, step u, for lane group grp.
 __host__ __device__ __forceinline__ int64_t row_of(int64_t r0, int64_t i, int u, int grp) {
