@@ -267,6 +267,154 @@ __global__ __launch_bounds__(kWave * kTokensPerBlock) void qknorm_rope_append_ke
   }
 }
 
+// Decode prologue (bf16 rows, d = 128, one token per sequence): one
+// workgroup of 8 wavefronts per token.  The token's query, key and value rows
+// are cut into pair chunks (8 values of a head and the 8 values d/2 further
+// on, the halves that RoPE rotates together), dealt out over the 512
+// threads; each thread adds up its squares, the workgroup adds the
+// wavefronts' sums through LDS, and the 64 rotation angles of the token's
+// position are computed once, one per lane of wavefront 0, into LDS.  Each
+// thread then handles a few pair chunks instead of a wavefront a whole row,
+// which shortens the token's dependent chain (a decode batch has too few
+// tokens to hide it).  The squares are added in another order than in the
+// row kernel above, so a key may round differently in its last place.
+constexpr int kDecProThreads = 512;
+constexpr int kDecProItems = 3;  // pair chunks per thread: 8 (H + 2G) <= 1536
+
+__global__ __launch_bounds__(kDecProThreads) void decode_prologue_kernel(PrologueArgs a,
+                                                                         RopeTable rope) {
+  constexpr int D = 128, kVec = 8, kPer = D / (2 * kVec);  // 8 pair chunks per head
+  constexpr int kWaves = kDecProThreads / kWave;
+  __shared__ float s_cs[D / 2], s_sn[D / 2];
+  __shared__ float s_ss[kWaves][2];
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int b = blockIdx.x;
+  const int64_t pos = a.seq_pos ? (int64_t)a.seq_pos[b] : a.pos_offset;
+  if (pos < 0) return;  // the whole workgroup: no position for this sequence
+  const int nq = a.H * kPer, nk = a.G * kPer, n = nq + 2 * nk;
+  const bf16* src[3] = {(const bf16*)a.q_pre + (int64_t)b * a.H * D,
+                        (const bf16*)a.k_pre + (int64_t)b * a.G * D,
+                        (const bf16*)a.v + (int64_t)b * a.G * D};
+  const bf16* gain[2] = {(const bf16*)a.q_gain, (const bf16*)a.k_gain};
+  // item it -> part (0 queries, 1 keys, 2 values) and pair chunk pc
+  auto item = [&](int it, int& part, int& pc) __attribute__((always_inline)) {
+    part = it < nq ? 0 : (it < nq + nk ? 1 : 2);
+    pc = it - (part == 0 ? 0 : (part == 1 ? nq : nq + nk));
+  };
+  bf16x8 x0[kDecProItems], x1[kDecProItems], g0[kDecProItems], g1[kDecProItems];
+#pragma unroll
+  for (int i = 0; i < kDecProItems; ++i) {
+    const int it = tid + kDecProThreads * i;
+    if (it < n) {
+      int part, pc;
+      item(it, part, pc);
+      const int off = (pc / kPer) * D + (pc % kPer) * kVec;
+      x0[i] = *(const bf16x8*)(src[part] + off);
+      x1[i] = *(const bf16x8*)(src[part] + off + D / 2);
+      if (part < 2) {
+        g0[i] = *(const bf16x8*)(gain[part] + off);
+        g1[i] = *(const bf16x8*)(gain[part] + off + D / 2);
+      }
+    }
+  }
+  if (wave == 0) {  // angle of rate `lane` at this position, as in rope_angles
+    constexpr double kTwoPi = 6.283185307179586;
+    constexpr double kInvTwoPi = 0.15915494309189535;
+    const double ang = (double)pos * rope.inv_freq[lane];
+    const double r = ang - kTwoPi * rint(ang * kInvTwoPi);
+    float sv, cv;
+    sincosf((float)r, &sv, &cv);
+    s_cs[lane] = cv;
+    s_sn[lane] = sv;
+  }
+  float ss[2] = {0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < kDecProItems; ++i) {
+    const int it = tid + kDecProThreads * i;
+    if (it < nq + nk) {
+      float t = 0.f;
+#pragma unroll
+      for (int e = 0; e < kVec; ++e) {
+        const float f0 = (float)x0[i][e], f1 = (float)x1[i][e];
+        t += f0 * f0 + f1 * f1;
+      }
+      ss[it < nq ? 0 : 1] += t;
+    }
+  }
+  ss[0] = wave_sum(ss[0]);
+  ss[1] = wave_sum(ss[1]);
+  if (lane == 0) {
+    s_ss[wave][0] = ss[0];
+    s_ss[wave][1] = ss[1];
+  }
+  __syncthreads();
+  float tot[2] = {0.f, 0.f};
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    tot[0] += s_ss[w][0];
+    tot[1] += s_ss[w][1];
+  }
+  const float rn[2] = {1.0f / sqrtf(tot[0] / (float)(a.H * D) + a.eps),
+                       1.0f / sqrtf(tot[1] / (float)(a.G * D) + a.eps)};
+  const int64_t slot = a.sliding ? pos % a.window : pos;
+  const bool to_cache = a.store && slot < a.cap;
+  const bool fp8 = a.cache_fp8;
+#pragma unroll
+  for (int i = 0; i < kDecProItems; ++i) {
+    const int it = tid + kDecProThreads * i;
+    if (it >= n) continue;
+    int part, pc;
+    item(it, part, pc);
+    const int h = pc / kPer, j = pc % kPer;
+    if (part == 2) {  // values -> cache slot, unchanged (or as e4m3 codes)
+      if (!to_cache) continue;
+      const int64_t off = (((int64_t)b * a.G + h) * a.cap + slot) * D + j * kVec;
+      if (fp8) {
+        float f0[kVec], f1[kVec];
+        Io<bf16>::to_f32(x0[i], f0);
+        Io<bf16>::to_f32(x1[i], f1);
+        store_chunk_e4m3((uint8_t*)a.v_cache + off, f0, a.v_inv_scale);
+        store_chunk_e4m3((uint8_t*)a.v_cache + off + D / 2, f1, a.v_inv_scale);
+      } else {
+        *(bf16x8*)((bf16*)a.v_cache + off) = x0[i];
+        *(bf16x8*)((bf16*)a.v_cache + off + D / 2) = x1[i];
+      }
+      continue;
+    }
+    float y0[kVec], y1[kVec];
+    const float r = rn[part];
+#pragma unroll
+    for (int e = 0; e < kVec; ++e) {
+      const float cs = s_cs[j * kVec + e], sn = s_sn[j * kVec + e];
+      const float u = (float)x0[i][e] * r * (float)g0[i][e];
+      const float w = (float)x1[i][e] * r * (float)g1[i][e];
+      y0[e] = (u * cs - w * sn) * rope.mscale;
+      y1[e] = (w * cs + u * sn) * rope.mscale;
+    }
+    if (part == 0) {
+      bf16* qo = (bf16*)a.q_out + ((int64_t)b * a.H + h) * D + j * kVec;
+      store_chunk(qo, y0);
+      store_chunk(qo + D / 2, y1);
+    } else if (to_cache) {
+      const int64_t off = (((int64_t)b * a.G + h) * a.cap + slot) * D + j * kVec;
+      if (fp8) {
+        store_chunk_e4m3((uint8_t*)a.k_cache + off, y0, a.k_inv_scale);
+        store_chunk_e4m3((uint8_t*)a.k_cache + off + D / 2, y1, a.k_inv_scale);
+      } else {
+        store_chunk((bf16*)a.k_cache + off, y0);
+        store_chunk((bf16*)a.k_cache + off + D / 2, y1);
+      }
+    }
+  }
+}
+
+// Whether decode_prologue_kernel serves this call: one bf16 token per
+// sequence with d = 128, queries present, no rotated-key copy.
+bool decode_prologue_fits(const PrologueArgs& a, int dtype, int d) {
+  return dtype == 0 && d == 128 && a.T == 1 && !a.cu_seqlens && a.q_pre && !a.k_out &&
+         8 * (a.H + 2 * a.G) <= kDecProThreads * kDecProItems;
+}
+
 // Up to this many tokens the per-part wavefronts are used, and up to the
 // smaller bound they issue their loads before the angle arithmetic.
 constexpr int64_t kRolesMaxRows = 2048;
@@ -336,6 +484,10 @@ int prologue_max_heads(int dtype, int d) {
 
 hipError_t launch_prologue(const PrologueArgs& a, const RopeTable& rope, int dtype, int d,
                            hipStream_t s) {
+  if (decode_prologue_fits(a, dtype, d)) {
+    decode_prologue_kernel<<<a.B, kDecProThreads, 0, s>>>(a, rope);
+    return hipGetLastError();
+  }
 #define OLMO3_PRO(T, DD) \
   if (d == DD) return launch_prologue_t<T, DD>(a, rope, s);
   if (dtype == 0) {
