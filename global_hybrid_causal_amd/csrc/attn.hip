@@ -437,10 +437,29 @@ struct DecStage {
   bf16x8 k[4];  // A operand of block kk
   bf16x8 v[4];  // rows 4 i + l/16, column l mod 16
 };
+// e4m3 caches: the same elements as codes, 8 bytes per lane and block
+struct DecStage8 {
+  u32x2 k[4];
+  u32x2 v[4];
+};
+
+// Eight e4m3 codes -> their values as bf16 (exact: every e4m3 value is a
+// bf16 value).
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16(u32x2 w) {
+  float f[8];
+  e4m3x4_to_f32(w[0], f);
+  e4m3x4_to_f32(w[1], f + 4);
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = (bf16)f[e];
+  return r;
+}
 
 // Two wavefronts per SIMD: the three stages in registers (96 VGPRs of K and V)
-// leave no room for a third.
-template <int GRP>
+// leave no room for a third.  kFp8: e4m3 caches, converted to bf16 in
+// registers (keys as the MFMA operand, values before their LDS tile);
+// k_scale multiplies the softmax scale and v_scale the output.
+template <int GRP, bool kFp8>
 __global__ __launch_bounds__(dec::kThreads, 2) void decode_mfma_kernel(DecodeArgs a) {
   using namespace dec;
   static_assert(GRP >= 2 && GRP <= 16, "query heads per key/value head");
@@ -478,37 +497,61 @@ __global__ __launch_bounds__(dec::kThreads, 2) void decode_mfma_kernel(DecodeArg
 
   // (sequence, head) bases, uniform; rows as 32-bit byte offsets (the
   // launcher takes this kernel only while cap * 256 B fits 32 bits)
-  const char* kb = (const char*)a.k_cache + ((int64_t)b * a.G + g) * a.cap * kD * 2;
-  const char* vb = (const char*)a.v_cache + ((int64_t)b * a.G + g) * a.cap * kD * 2;
+  constexpr int kEs = kFp8 ? 1 : 2;  // bytes per cache element
+  // stages in flight per wavefront (8 KiB of K and V each with bf16 rows,
+  // 4 KiB with e4m3 codes; 4 or 5 e4m3 stages measured no faster)
+  constexpr int kStages = 3;
+  typedef typename std::conditional<kFp8, DecStage8, DecStage>::type Stage;
+  const char* kb = (const char*)a.k_cache + ((int64_t)b * a.G + g) * a.cap * kD * kEs;
+  const char* vb = (const char*)a.v_cache + ((int64_t)b * a.G + g) * a.cap * kD * kEs;
   const uint32_t rlast = (uint32_t)(r1 - 1);
-  auto fetch = [&](int64_t t, DecStage& st) __attribute__((always_inline)) {
+  auto fetch = [&](int64_t t, Stage& st) __attribute__((always_inline)) {
     const uint32_t base = (uint32_t)(r0 + t * kStageRows);
-    const uint32_t koff = min(base + col, rlast) * (kD * 2) + 16 * quad;
+    const uint32_t koff = min(base + col, rlast) * (kD * kEs) + 8 * kEs * quad;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-      st.k[kk] = __builtin_bit_cast(bf16x8, __builtin_nontemporal_load((const u32x4*)(kb + koff + 64 * kk)));
+    for (int kk = 0; kk < 4; ++kk) {
+      if constexpr (kFp8)
+        st.k[kk] = __builtin_nontemporal_load((const u32x2*)(kb + koff + 32 * kk));
+      else
+        st.k[kk] = __builtin_bit_cast(bf16x8, __builtin_nontemporal_load((const u32x4*)(kb + koff + 64 * kk)));
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const uint32_t voff = min(base + 4 * i + quad, rlast) * (kD * 2) + 16 * col;
-      st.v[i] = __builtin_bit_cast(bf16x8, __builtin_nontemporal_load((const u32x4*)(vb + voff)));
+      const uint32_t voff = min(base + 4 * i + quad, rlast) * (kD * kEs) + 8 * kEs * col;
+      if constexpr (kFp8)
+        st.v[i] = __builtin_nontemporal_load((const u32x2*)(vb + voff));
+      else
+        st.v[i] = __builtin_bit_cast(bf16x8, __builtin_nontemporal_load((const u32x4*)(vb + voff)));
     }
+  };
+  auto kop = [&](const Stage& st, int kk) __attribute__((always_inline)) -> bf16x8 {
+    if constexpr (kFp8)
+      return e4m3x8_to_bf16(st.k[kk]);
+    else
+      return st.k[kk];
+  };
+  auto vrow = [&](const Stage& st, int i) __attribute__((always_inline)) -> bf16x8 {
+    if constexpr (kFp8)
+      return e4m3x8_to_bf16(st.v[i]);
+    else
+      return st.v[i];
   };
 
   f32x4 o[kD / 16];
 #pragma unroll
   for (int i = 0; i < kD / 16; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m = -1e30f, lsum = 0.f;  // of query col
-  const float c = a.scale_log2;
+  const float c = kFp8 ? a.scale_log2 * a.k_scale : a.scale_log2;
   const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
   char* const vt = vtile[wave];
   // transposed-read address of V block blk: row 4 quad + col / 4, d = 16 blk + 4 (col mod 4)
   const int vr = 4 * quad + (col >> 2);
   const int vsw = 2 * (vr & 7);
 
-  auto compute = [&](const DecStage& st, int64_t t) __attribute__((always_inline)) {
+  auto compute = [&](const Stage& st, int64_t t) __attribute__((always_inline)) {
     f32x4 s4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) s4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(st.k[kk], qop[kk], s4, 0, 0, 0);
+    for (int kk = 0; kk < 4; ++kk) s4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop(st, kk), qop[kk], s4, 0, 0, 0);
     const int64_t key0 = r0 + t * kStageRows + 4 * quad;
 #pragma unroll
     for (int r = 0; r < 4; ++r)
@@ -547,7 +590,7 @@ __global__ __launch_bounds__(dec::kThreads, 2) void decode_mfma_kernel(DecodeArg
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 4 * i + quad;
-      *(bf16x8*)(vt + r * 256 + ((col ^ (2 * (r & 7))) * 16)) = st.v[i];
+      *(bf16x8*)(vt + r * 256 + ((col ^ (2 * (r & 7))) * 16)) = vrow(st, i);
     }
 #pragma unroll
     for (int blk = 0; blk < kD / 16; ++blk) {
@@ -564,8 +607,14 @@ __global__ __launch_bounds__(dec::kThreads, 2) void decode_mfma_kernel(DecodeArg
   // Three stages in registers: one being used, two in flight.  The steady
   // loop has no branches, so every fetch is issued two stages ahead; fetches
   // past the wavefront's last stage read (clamped) rows that are not used.
+  // Three stages in registers, named (an array of them was not kept in
+  // registers): at the top of a trip stage i + j sits in s_j; each step
+  // fetches two stages ahead (past the split's end, rows are clamped to its
+  // last) into the register set just computed.  The trip is branch-free so
+  // that every wait is an exact vmcnt.
+  static_assert(kStages == 3, "the loop below holds three stages");
   if (n_mine > 0) {
-    DecStage s0, s1, s2;
+    Stage s0, s1, s2;
     fetch(wave, s0);
     fetch(wave + 4, s1);
     int64_t i = 0;
@@ -610,6 +659,7 @@ __global__ __launch_bounds__(dec::kThreads, 2) void decode_mfma_kernel(DecodeArg
       L += sl[w2][j] * f;
       O += so[w2][j][d] * f;
     }
+    if constexpr (kFp8) O *= a.v_scale;
     const int64_t bh = (int64_t)b * a.H + g * GRP + j;
     if (a.splits == 1) {
       ((bf16*)a.out)[bh * kD + d] = (bf16)(O / L);
@@ -703,23 +753,27 @@ int decode_splits(int B, int G, int64_t n) {
   return (int)s;
 }
 
-// The grouped MFMA kernel serves bf16 caches with H/G >= 2 whose rows fit
+// The grouped MFMA kernel serves bf16 and e4m3 caches with H/G >= 2 whose rows fit
 // 32-bit byte offsets; the per-row kernel the rest.
 bool uses_decode_mfma(const DecodeArgs& a) {
-  return !a.fp8 && a.H / a.G >= 2 && a.cap < ((int64_t)1 << 24);
+  return a.H / a.G >= 2 && a.cap < ((int64_t)1 << 24);
 }
 
 hipError_t launch_decode_split(const DecodeArgs& a, hipStream_t s) {
   const int group = a.H / a.G;
   const int blocks = a.B * a.G * a.splits;
-#define OLMO3_DEC(GG)                                                      \
-  case GG:                                                                 \
-    if (a.fp8)                                                             \
-      decode_split_kernel<GG, true><<<blocks, dec::kThreads, 0, s>>>(a);   \
-    else if (uses_decode_mfma(a))                                          \
-      decode_mfma_kernel<(GG >= 2 ? GG : 2)><<<blocks, dec::kThreads, 0, s>>>(a); \
-    else                                                                   \
-      decode_split_kernel<GG, false><<<blocks, dec::kThreads, 0, s>>>(a);  \
+#define OLMO3_DEC(GG)                                                                     \
+  case GG:                                                                                \
+    if (uses_decode_mfma(a)) {                                                            \
+      if (a.fp8)                                                                          \
+        decode_mfma_kernel<(GG >= 2 ? GG : 2), true><<<blocks, dec::kThreads, 0, s>>>(a); \
+      else                                                                                \
+        decode_mfma_kernel<(GG >= 2 ? GG : 2), false><<<blocks, dec::kThreads, 0, s>>>(a); \
+    } else if (a.fp8) {                                                                   \
+      decode_split_kernel<GG, true><<<blocks, dec::kThreads, 0, s>>>(a);                  \
+    } else {                                                                              \
+      decode_split_kernel<GG, false><<<blocks, dec::kThreads, 0, s>>>(a);                 \
+    }                                                                                     \
     break;
   switch (group) {
     OLMO3_DEC(1) OLMO3_DEC(2) OLMO3_DEC(3) OLMO3_DEC(4)

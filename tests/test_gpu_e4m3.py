@@ -181,6 +181,9 @@ DECODE = [
     (4, 16, 2, 300, 0, 5000, 300),        # group 8
     (1, 4, 1, 4096, 1, 19999, 20000),     # 64 splits
     (2, 8, 8, 4096, 0, 4096, 4096),       # the 7B window, first wrap
+    (1, 12, 2, 4096, 1, 2046, 3000),      # group 6, several splits, ragged last stage
+    (2, 14, 2, 100, 0, 500, 100),         # group 7, ring of 100 slots
+    (3, 40, 8, 4096, 0, 5000, 4096),      # the 32B grouping on the 7B window
 ]
 
 
