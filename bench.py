@@ -22,7 +22,9 @@ Printed: one JSON line.  `value` is prefill TFLOP/s (algorithmic FLOPs of the
 allowed query/key pairs over the whole prefill call time); decode KV GB/s is
 in "decode" (and is `value` for the decode-only stack workload).  Each kernel is bracketed by HIP events on the stream it is
 launched on (the stage-by-stage entry points), giving the per-kernel
-rooflines.  The CPU oracle is timed on a bounded sample of the same workload.
+rooflines; a decode call's merge stage shares its attention stage's events
+(at these batch sizes each (sequence, key/value head) is one workgroup of the
+split kernel, which writes the output itself, and no merge kernel runs).  The CPU oracle is timed on a bounded sample of the same workload.
 """
 
 from __future__ import annotations
@@ -263,7 +265,10 @@ def main():
             n = decode_rows(pos, WINDOW, sliding)
             name = f"decode_{'sliding' if sliding else 'full'}" + (f"_l{ell}" if n_dec_layers else "")
             segments.append(dict(name=name, kind="decode", sliding=sliding, run=run,
-                                 phases=[A.PHASE_PROLOGUE, A.PHASE_ATTENTION, A.PHASE_MERGE],
+                                 # the merge (a kernel only when a key range is split,
+                                 # which these batch sizes never need) shares the
+                                 # attention stage's events: one event pair fewer
+                                 phases=[A.PHASE_PROLOGUE, A.PHASE_ATTENTION | A.PHASE_MERGE],
                                  work=decode_kv_bytes(Bd, Gd, d, n, elem=1 if e4m3 else 2),
                                  rows=n))
     torch.cuda.synchronize()
@@ -299,8 +304,7 @@ def main():
     kernel_names = {("prefill", 0): "qknorm_rope_append_kernel", ("prefill", 1): "prefill_d128_kernel",
                     ("decode", 0): "decode_prologue_kernel",
                     ("decode", 1): decode_kernel(dcfg.get("H", 1), dcfg.get("G", 1),
-                                                 bool(dcfg.get("e4m3"))),
-                    ("decode", 2): "decode_merge_kernel"}
+                                                 bool(dcfg.get("e4m3")))}
     for seg in segments:
         per_phase = [[evs[i].elapsed_time(evs[i + 1]) for evs in seg["events"]]
                      for i in range(len(seg["phases"]))]
