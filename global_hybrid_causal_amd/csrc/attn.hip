@@ -437,10 +437,14 @@ struct DecStage {
   bf16x8 k[4];  // A operand of block kk
   bf16x8 v[4];  // rows 4 i + l/16, column l mod 16
 };
-// e4m3 caches: the same elements as codes, 8 bytes per lane and block
+// e4m3 caches: 16-byte loads (half as many load instructions per byte as
+// 8-byte ones).  k: the lane's 32 code bytes of its key row (d = 32 quad ..
+// +31, block kk taking d = 32 quad + 8 kk .. +7; the Q operand is loaded
+// with the same d order, which the sum over d does not see); v: code bytes
+// 16 (col mod 8) .. +15 of rows 8 i + 2 quad + col / 8.
 struct DecStage8 {
-  u32x2 k[4];
-  u32x2 v[4];
+  u32x4 k[2];
+  u32x4 v[2];
 };
 
 // Eight e4m3 codes -> their values as bf16 (exact: every e4m3 value is a
@@ -483,13 +487,15 @@ __global__ __launch_bounds__(dec::kThreads, 2) void decode_mfma_kernel(DecodeArg
   const int col = lane & 15, quad = lane >> 4;
 
   // Q^T operand: query col (zero past GRP), d = 32 kk + 8 quad .. + 7
+  // (e4m3 caches: d = 32 quad + 8 kk .. + 7, the order of the key codes)
   bf16x8 qop[4];
   {
     const bool real = col < GRP;
     const bf16* qrow = (const bf16*)a.q + ((int64_t)b * a.H + g * GRP + (real ? col : 0)) * kD;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      const bf16x8 v = *(const bf16x8*)(qrow + 32 * kk + 8 * quad);
+      const int d0 = kFp8 ? 32 * quad + 8 * kk : 32 * kk + 8 * quad;
+      const bf16x8 v = *(const bf16x8*)(qrow + d0);
 #pragma unroll
       for (int e = 0; e < 8; ++e) qop[kk][e] = real ? v[e] : (bf16)0.0f;
     }
@@ -507,34 +513,34 @@ __global__ __launch_bounds__(dec::kThreads, 2) void decode_mfma_kernel(DecodeArg
   const uint32_t rlast = (uint32_t)(r1 - 1);
   auto fetch = [&](int64_t t, Stage& st) __attribute__((always_inline)) {
     const uint32_t base = (uint32_t)(r0 + t * kStageRows);
-    const uint32_t koff = min(base + col, rlast) * (kD * kEs) + 8 * kEs * quad;
+    if constexpr (kFp8) {
+      const uint32_t koff = min(base + col, rlast) * kD + 32 * quad;
+      st.k[0] = __builtin_nontemporal_load((const u32x4*)(kb + koff));
+      st.k[1] = __builtin_nontemporal_load((const u32x4*)(kb + koff + 16));
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      if constexpr (kFp8)
-        st.k[kk] = __builtin_nontemporal_load((const u32x2*)(kb + koff + 32 * kk));
-      else
+      for (int i = 0; i < 2; ++i) {
+        const uint32_t voff = min(base + 8 * i + 2 * quad + (col >> 3), rlast) * kD + 16 * (col & 7);
+        st.v[i] = __builtin_nontemporal_load((const u32x4*)(vb + voff));
+      }
+    } else {
+      const uint32_t koff = min(base + col, rlast) * (kD * 2) + 16 * quad;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
         st.k[kk] = __builtin_bit_cast(bf16x8, __builtin_nontemporal_load((const u32x4*)(kb + koff + 64 * kk)));
-    }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t voff = min(base + 4 * i + quad, rlast) * (kD * kEs) + 8 * kEs * col;
-      if constexpr (kFp8)
-        st.v[i] = __builtin_nontemporal_load((const u32x2*)(vb + voff));
-      else
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t voff = min(base + 4 * i + quad, rlast) * (kD * 2) + 16 * col;
         st.v[i] = __builtin_bit_cast(bf16x8, __builtin_nontemporal_load((const u32x4*)(vb + voff)));
+      }
     }
   };
   auto kop = [&](const Stage& st, int kk) __attribute__((always_inline)) -> bf16x8 {
-    if constexpr (kFp8)
-      return e4m3x8_to_bf16(st.k[kk]);
-    else
+    if constexpr (kFp8) {
+      const u32x4 w = st.k[kk >> 1];
+      return e4m3x8_to_bf16((kk & 1) ? u32x2{w[2], w[3]} : u32x2{w[0], w[1]});
+    } else {
       return st.k[kk];
-  };
-  auto vrow = [&](const Stage& st, int i) __attribute__((always_inline)) -> bf16x8 {
-    if constexpr (kFp8)
-      return e4m3x8_to_bf16(st.v[i]);
-    else
-      return st.v[i];
+    }
   };
 
   f32x4 o[kD / 16];
@@ -587,10 +593,20 @@ __global__ __launch_bounds__(dec::kThreads, 2) void decode_mfma_kernel(DecodeArg
     lsum = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pa[2], pa[3]}, ones, lsum, false);
     const i16x4 pai = __builtin_bit_cast(i16x4, pa);
     // V tile: row r, 16-byte column c stored at c ^ 2 (r mod 8)
+    if constexpr (kFp8) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 4 * i + quad;
-      *(bf16x8*)(vt + r * 256 + ((col ^ (2 * (r & 7))) * 16)) = vrow(st, i);
+      for (int i = 0; i < 2; ++i) {
+        const int r = 8 * i + 2 * quad + (col >> 3), c0 = 2 * (col & 7);
+        const u32x4 w = st.v[i];
+        *(bf16x8*)(vt + r * 256 + ((c0 ^ (2 * (r & 7))) * 16)) = e4m3x8_to_bf16(u32x2{w[0], w[1]});
+        *(bf16x8*)(vt + r * 256 + (((c0 + 1) ^ (2 * (r & 7))) * 16)) = e4m3x8_to_bf16(u32x2{w[2], w[3]});
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * i + quad;
+        *(bf16x8*)(vt + r * 256 + ((col ^ (2 * (r & 7))) * 16)) = st.v[i];
+      }
     }
 #pragma unroll
     for (int blk = 0; blk < kD / 16; ++blk) {
