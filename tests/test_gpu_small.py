@@ -129,6 +129,9 @@ DECODE_CASES = [
     (2, 14, 2, 128, 100, 0, 500, 100),      # group 7
     (2, 6, 2, 64, 64, 0, 100, 64),          # plain kernel
     (2, 6, 6, 32, 4096, 1, 70, 100),
+    (2, 64, 64, 128, 256, 0, 700, 256),     # 64 heads: the decode prologue's 1,536 pair chunks
+    (3, 64, 8, 128, 4096, 1, 300, 301),     # group 8 with 64 query heads
+    (5, 1, 1, 128, 64, 0, 63, 64),          # a single head
 ]
 
 
