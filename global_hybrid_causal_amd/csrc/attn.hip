@@ -115,6 +115,14 @@ __device__ __forceinline__ float row16_sum(float x) {
   return x;
 }
 
+// Sum over the 8 lanes of each half of a 16-lane row.
+__device__ __forceinline__ float row8_sum(float x) {
+  x += dpp_operand<0xB1>(x);   // quad_perm [1, 0, 3, 2]
+  x += dpp_operand<0x4E>(x);   // quad_perm [2, 3, 0, 1]
+  x += dpp_operand<0x141>(x);  // row_half_mirror
+  return x;
+}
+
 __device__ __forceinline__ float dot2(bf16x2 a, bf16x2 b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(a, b, c, false);
 }
@@ -193,7 +201,85 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_eu<GRP, kFp8>()))) void deco
   const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
 
   const int64_t n_iter = r1 > r0 ? (r1 - r0 + kRowsPerIter - 1) / kRowsPerIter : 0;
-  if constexpr (kFp8) {
+  if constexpr (kFp8 && GRP == 1) {
+    // e4m3 codes, one query head: 16-byte loads (half the load instructions
+    // of 8-byte ones).  Each 16-lane group still reads rows row_of(i, u) for
+    // u = 0..3 of every iteration, as a pair of rows per step: lanes 8 h + c
+    // take codes 16 c .. 16 c + 15 of row row_of(i, 2 u2 + h), u2 = 0, 1.
+    // The two halves keep separate softmax states over their rows, merged
+    // after the loop, then spread to the 8-elements-per-lane layout below.
+    const int h = li >> 3, cc = li & 7;
+    float qf16[16];
+    {
+      const bf16* qp = (const bf16*)a.q + ((int64_t)b * a.H + g) * kD + 16 * cc;
+      const bf16x8 q0 = *(const bf16x8*)qp, q1 = *(const bf16x8*)(qp + 8);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        qf16[e] = (float)q0[e] * a.k_scale;
+        qf16[8 + e] = (float)q1[e] * a.k_scale;
+      }
+    }
+    float o16[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o16[e] = 0.f;
+    const uint8_t* kr8 = (const uint8_t*)a.k_cache + ((int64_t)b * a.G + g) * a.cap * kD + 16 * cc;
+    const uint8_t* vr8 = (const uint8_t*)a.v_cache + ((int64_t)b * a.G + g) * a.cap * kD + 16 * cc;
+    for (int64_t i = 0; i < n_iter; ++i) {
+      u32x4 kr[2], vr[2];
+      bool ok[2];
+#pragma unroll
+      for (int u2 = 0; u2 < 2; ++u2) {
+        const int64_t r = row_of(r0, i, 2 * u2 + h, grp);
+        ok[u2] = r < r1;
+        const int64_t rc = ok[u2] ? r : r0;
+        kr[u2] = __builtin_nontemporal_load((const u32x4*)(kr8 + rc * kD));
+        vr[u2] = __builtin_nontemporal_load((const u32x4*)(vr8 + rc * kD));
+      }
+      float sc[2];
+#pragma unroll
+      for (int u2 = 0; u2 < 2; ++u2) {
+        float kf[16];
+#pragma unroll
+        for (int w4 = 0; w4 < 4; ++w4) e4m3x4_to_f32(kr[u2][w4], kf + 4 * w4);
+        float acc = 0.f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc = fmaf(qf16[e], kf[e], acc);
+        const float t = row8_sum(acc) * c;  // every lane takes part in the sum
+        sc[u2] = ok[u2] ? t : -INFINITY;
+      }
+      const float mn = fmaxf(m[0], fmaxf(sc[0], sc[1]));
+      const float al = fast_exp2(m[0] - mn);
+      m[0] = mn;
+      const float p0 = fast_exp2(sc[0] - mn), p1 = fast_exp2(sc[1] - mn);
+      l[0] = l[0] * al + (p0 + p1);
+      float vf0[16], vf1[16];
+#pragma unroll
+      for (int w4 = 0; w4 < 4; ++w4) {
+        e4m3x4_to_f32(vr[0][w4], vf0 + 4 * w4);
+        e4m3x4_to_f32(vr[1][w4], vf1 + 4 * w4);
+      }
+#pragma unroll
+      for (int e = 0; e < 16; ++e) o16[e] = fmaf(p1, vf1[e], fmaf(p0, vf0[e], o16[e] * al));
+    }
+    // merge the halves (lanes l and l ^ 8 hold the same elements)
+    {
+      const float mo = __shfl_xor(m[0], 8, kWave), lo = __shfl_xor(l[0], 8, kWave);
+      const float mn = fmaxf(m[0], mo);
+      const float fa = fast_exp2(m[0] - mn), fb = fast_exp2(mo - mn);
+      l[0] = l[0] * fa + lo * fb;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) o16[e] = o16[e] * fa + __shfl_xor(o16[e], 8, kWave) * fb;
+      m[0] = mn;
+    }
+    // lane li of the group takes elements 8 li .. 8 li + 7: those of lane
+    // li / 2, first or second half
+    const int src = (lane & ~15) + (li >> 1);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float lo8 = __shfl(o16[e], src, kWave), hi8 = __shfl(o16[8 + e], src, kWave);
+      o[0][e] = (li & 1) ? hi8 : lo8;
+    }
+  } else if constexpr (kFp8) {
     // e4m3 codes: keys and values converted to fp32, exact running maximum
     // rescaled every iteration, every row masked against r1 (the loop shape
     // that measured fastest for these half-size rows)

@@ -184,6 +184,9 @@ DECODE = [
     (1, 12, 2, 4096, 1, 2046, 3000),      # group 6, several splits, ragged last stage
     (2, 14, 2, 100, 0, 500, 100),         # group 7, ring of 100 slots
     (3, 40, 8, 4096, 0, 5000, 4096),      # the 32B grouping on the 7B window
+    (1, 2, 2, 4096, 1, 9999, 10000),      # one query head per key/value head, 40 splits
+    (3, 4, 4, 100, 0, 250, 100),          # one query head per key/value head, ring of 100
+    (2, 3, 3, 4096, 1, 64, 200),          # 65 rows: one past a 64-row iteration
 ]
 
 
