@@ -28,7 +28,7 @@ decode of one token, which is the same computation with T = 1):
    section "The sliding-window mask"), softmax of q.k / sqrt(d), weighted sum
    of values.
 
-Readings taken where the pages are silent (each is listed in the design doc):
+Readings taken where the pages are silent:
 softmax scale 1/sqrt(d); the rotation direction x_i + i*x_{i+d/2} times
 exp(+i*angle); contiguous GQA grouping g(h) = h // (H/G); YaRN as the
 NTK-by-parts interpolation of Peng et al. (2023) with a ramp linear in the
