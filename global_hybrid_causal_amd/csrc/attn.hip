@@ -1,5 +1,7 @@
 // Causal attention kernels: a plain per-query kernel for other head sizes
-// and fp32, and split-KV decode (d = 128, bf16) with a log-sum-exp merge.
+// and fp32, and split-KV decode (d = 128, bf16 or e4m3 caches) with a
+// log-sum-exp merge across wavefronts and, when a key range is split, across
+// workgroups.
 // The MFMA prefill kernel lives in prefill.hip.
 //
 // Masking follows "OLMo 3's Sliding-Window Attention Pattern", "The
@@ -97,7 +99,8 @@ __global__ __launch_bounds__(64) void attn_generic_kernel(AttnArgs a) {
 // GRP query heads of its key/value head.  Scores are reduced across the 16
 // lanes, the softmax state is kept per lane group and merged, first across
 // the 4 groups of a wavefront with lane exchanges and then across
-// wavefronts in LDS, into one partial (m, l, o) per head and split.
+// wavefronts in LDS, into one partial (m, l, o) per head and split, or,
+// when the split is the whole key range, into the output row itself.
 // ---------------------------------------------------------------------------
 // Sum over the 16 lanes of a DPP row, returned in all of them: neighbours,
 // pairs of neighbours, the two quads of each half row (mirrored), then the

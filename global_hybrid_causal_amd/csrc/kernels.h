@@ -117,9 +117,11 @@ hipError_t launch_prefill_mfma(const AttnArgs& a, hipStream_t s);
 // Plain per-query kernel for the other head sizes and for fp32.
 hipError_t launch_attn_generic(const AttnArgs& a, int dtype, int d, hipStream_t s);
 
-// Split-KV decode, d = 128, bf16: one workgroup per (b, g, split) reads the
-// split's cache rows once for all H/G query heads and writes a partial
-// softmax state (m, l, o[d]) per head to part[((b*H + h)*splits + sp)*(d+2)].
+// Split-KV decode, d = 128, bf16 or e4m3 caches: one workgroup per
+// (b, g, split) reads the split's cache rows once for all H/G query heads and
+// writes a partial softmax state (m, l, o[d]) per head to
+// part[((b*H + h)*splits + sp)*(d+2)]; with splits == 1 it writes the output
+// rows out[(b*H + h)*d ..] instead and no merge is needed.
 struct DecodeArgs {
   const void* q;       // [B][H][d] rotated queries
   const void* k_cache; // [B][G][cap][d]
