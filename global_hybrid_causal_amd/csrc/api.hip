@@ -673,6 +673,32 @@ int olmo3_attn_decode_ragged(int B, int H, int G, int d, int window, int layer_t
                      (hipStream_t)stream);
 }
 
+int olmo3_attn_decode_ragged_e4m3(int B, int H, int G, int d, int window, int layer_type,
+                                  const olmo3_rope* rope, float eps, const int32_t* positions,
+                                  int64_t max_pos, const void* q_pre, const void* k_pre,
+                                  const void* v, const void* q_gain, const void* k_gain,
+                                  void* k_cache, void* v_cache, float k_scale, float v_scale,
+                                  int64_t cache_capacity, void* out, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  if (!positions || ((uintptr_t)positions & 3) || max_pos < 0 || max_pos > INT32_MAX)
+    return OLMO3_ERR_INVALID_ARG;
+  if (!valid_scale(k_scale) || !valid_scale(v_scale)) return OLMO3_ERR_INVALID_ARG;
+  const size_t need = (B > 0 && H > 0 && G > 0 && d > 0 && G <= H && cache_capacity > 0)
+                          ? decode_ws(B, H, G, d, layer_type, window, OLMO3_DTYPE_BF16_E4M3,
+                                      cache_capacity)
+                          : 0;
+  int st = validate_attn(B, 1, H, G, d, window, layer_type, rope, eps, max_pos, OLMO3_DTYPE_BF16,
+                         q_pre, k_pre, v, q_gain, k_gain, k_cache, v_cache, cache_capacity, out,
+                         workspace, workspace_bytes, need, B, max_pos, 1);
+  if (st) return st;
+  // the e4m3 cache is read by the split-KV kernels only
+  if (!decode_uses_split(OLMO3_DTYPE_BF16_E4M3, d, H, G)) return OLMO3_ERR_UNSUPPORTED;
+  return decode_impl(OLMO3_PHASE_PROLOGUE | OLMO3_PHASE_ATTENTION | OLMO3_PHASE_MERGE, B, H, G,
+                     d, window, layer_type, rope, eps, 0, positions, max_pos, OLMO3_DTYPE_BF16,
+                     q_pre, k_pre, v, q_gain, k_gain, k_cache, v_cache, cache_capacity, out,
+                     workspace, (hipStream_t)stream, CacheFormat{1, k_scale, v_scale});
+}
+
 int olmo3_attn_decode(int B, int H, int G, int d, int window, int layer_type,
                       const olmo3_rope* rope, float eps, int64_t pos, int dtype,
                       const void* q_pre, const void* k_pre, const void* v, const void* q_gain,

@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define OLMO3_ABI_VERSION 6
+#define OLMO3_ABI_VERSION 7
 
 typedef enum olmo3_status {
   OLMO3_OK = 0,
@@ -258,6 +258,19 @@ int olmo3_attn_decode_e4m3_phases(int phases, int B, int H, int G, int d, int wi
                                   const void* q_pre, const void* k_pre, const void* v,
                                   const void* q_gain, const void* k_gain, void* k_cache,
                                   void* v_cache, float k_scale, float v_scale,
+                                  int64_t cache_capacity, void* out, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
+/* Ragged decode against e4m3 caches: olmo3_attn_decode_ragged's positions
+ * (sequence b's new token at positions[b], each in [0, max_pos]) with
+ * olmo3_attn_decode_e4m3's cache format and scales.  workspace:
+ * olmo3_workspace_bytes(OLMO3_MODE_DECODE, ..., OLMO3_DTYPE_BF16_E4M3,
+ * cache_capacity).  Errors: as those two. */
+int olmo3_attn_decode_ragged_e4m3(int B, int H, int G, int d, int window, int layer_type,
+                                  const olmo3_rope* rope, float eps, const int32_t* positions,
+                                  int64_t max_pos, const void* q_pre, const void* k_pre,
+                                  const void* v, const void* q_gain, const void* k_gain,
+                                  void* k_cache, void* v_cache, float k_scale, float v_scale,
                                   int64_t cache_capacity, void* out, void* workspace,
                                   size_t workspace_bytes, void* stream);
 

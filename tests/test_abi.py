@@ -43,7 +43,7 @@ def test_header_binding_and_library_versions_agree():
 
 
 def test_abi_version():
-    assert A.olmo3_abi_version() == A.ABI_VERSION == 6
+    assert A.olmo3_abi_version() == A.ABI_VERSION == 7
 
 
 def test_layer_type_matches_oracle_bit_exact():
@@ -350,3 +350,28 @@ def test_e4m3_prefill_later_chunk_needs_the_copy(lt, rows):
     need = first + 2 * 2 * rows * 128 * 2
     cap = 64 if lt == 1 else 16
     assert e4m3_prefill_call(ws_bytes=need - 1, layer_type=lt, cap=cap) == A.ERR_WORKSPACE
+
+
+def ragged_e4m3_call(**kw):
+    a = dict(B=2, H=4, G=2, d=128, window=16, layer_type=0, eps=1e-6, pos=fake(10), max_pos=20,
+             cap=16, ks=0.5, vs=0.5)
+    a.update(kw)
+    p = [fake(i) for i in range(9)]
+    r = ctypes.byref(A.Rope(theta=1e4).to_c())
+    return A.lib().olmo3_attn_decode_ragged_e4m3(
+        a["B"], a["H"], a["G"], a["d"], a["window"], a["layer_type"], r, a["eps"], a["pos"],
+        a["max_pos"], *p[:7], a["ks"], a["vs"], a["cap"], p[7], p[8], 1 << 34, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(pos=0), A.ERR_INVALID_ARG),              # null positions
+    (dict(pos=fake(10) + 2), A.ERR_INVALID_ARG),   # misaligned positions
+    (dict(max_pos=-1), A.ERR_INVALID_ARG),
+    (dict(ks=0.0), A.ERR_INVALID_ARG),
+    (dict(vs=float("inf")), A.ERR_INVALID_ARG),
+    (dict(d=64), A.ERR_UNSUPPORTED),               # split kernels only
+    (dict(layer_type=1, cap=20), A.ERR_CAPACITY),  # needs max_pos + 1 slots
+    (dict(cap=15), A.ERR_CAPACITY),                # ring size != window
+])
+def test_ragged_decode_e4m3_rejects(kw, status):
+    assert ragged_e4m3_call(**kw) == status

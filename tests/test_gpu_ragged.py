@@ -190,3 +190,54 @@ def test_ragged_prefill_equal_lengths_is_uniform_prefill(lt):
         results.append((out, kc, vc))
     for a_, b_ in zip(*results):
         assert torch.equal(a_, b_)
+
+
+E4M3_DECODE_CASES = [
+    # H, G, window, layer_type, positions
+    (8, 8, 128, 0, [0, 1, 127, 128, 1000]),     # one query head per key/value head, ring
+    (10, 2, 4096, 1, [2999, 0, 1500]),           # group 5 (grouped MFMA kernel), linear
+    (16, 2, 300, 0, [4000, 10, 299, 300]),       # group 8, ring
+]
+
+
+@pytest.mark.parametrize("case", E4M3_DECODE_CASES, ids=[f"{c[3]}-g{c[0] // c[1]}-{len(c[4])}seq"
+                                                         for c in E4M3_DECODE_CASES])
+def test_ragged_decode_e4m3_vs_oracle(case):
+    """Per-sequence positions against e4m3 caches: each sequence matches the
+    oracle's e4m3 decode on its own cache, and its new codes land in its own
+    slot."""
+    H, G, w, lt, positions = case
+    B, d, ks, vs = len(positions), 128, 0.37, 1.9
+    _log("ragged e4m3 decode", case)
+    kind = KINDS[lt]
+    rope = A.Rope(theta=500000.0, yarn=True, factor=8.0, orig_ctx=512)
+    max_pos = max(positions)
+    cap = w if kind == O.SLIDING else max_pos + 1
+    kc, vc = synth.e4m3_cache_fill(53, lt, B, G, cap, d, device="cuda")
+    bk, bv = kc.cpu().numpy(), vc.cpu().numpy()  # codes, as uint8
+    table = O.e4m3_values()
+    x = inputs(53, 40 + lt, B, 1, H, G, d, BF16)
+    q, k, v = x["q_pre"][:, 0].contiguous(), x["k_pre"][:, 0].contiguous(), x["v"][:, 0].contiguous()
+    pos_t = torch.tensor(positions, dtype=torch.int32, device="cuda")
+    out = torch.empty_like(q)
+    ws = A.workspace(A.MODE_DECODE, B, 1, H, G, d, lt, A.DTYPE_BF16_E4M3, cap, "cuda")
+    A.olmo3_attn_decode_ragged_e4m3(q, k, v, x["q_gain"], x["k_gain"], kc, vc, out, ws, pos_t,
+                                    k_scale=ks, v_scale=vs, max_pos=max_pos, window=w,
+                                    layer_type=lt, rope=rope)
+    hx = host_inputs(x)
+    got_k, got_v = kc.cpu().numpy(), vc.cpu().numpy()
+    for b, p in enumerate(positions):
+        c = O.KvCacheRef(kind, w, cap, 1, G, d, e4m3_scales=(ks, vs))
+        c.k[:] = table[bk[b:b + 1]] * ks
+        c.v[:] = table[bv[b:b + 1]] * vs
+        c.pos[:] = O.ring_positions(kind, w, cap, int(p))
+        ref = O.decode_e4m3_ref(hx["q_pre"][b:b + 1, 0], hx["k_pre"][b:b + 1, 0],
+                                hx["v"][b:b + 1, 0], hx["q_gain"], hx["k_gain"], H=H, G=G, d=d,
+                                kind=kind, window=w, rope=oracle_rope(rope), pos=p, cache=c)
+        assert_close(host(out[b:b + 1]), ref, what=f"sequence {b} at {p}")
+        slot = p % w if kind == O.SLIDING else p
+        assert np.array_equal(got_v[b][:, slot], O.e4m3_store(hx["v"][b, 0].reshape(G, d), vs)), \
+            f"sequence {b}: value codes"
+        others = np.setdiff1d(np.arange(cap), [slot])
+        assert np.array_equal(got_k[b][:, others], bk[b][:, others]), f"sequence {b}: key slots"
+        assert np.array_equal(got_v[b][:, others], bv[b][:, others]), f"sequence {b}: value slots"
