@@ -18,7 +18,7 @@ from . import LAYER_FULL, LAYER_SLIDING  # noqa: F401  (re-exported)
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libolmo3attn.so")
 
-ABI_VERSION = 7  # OLMO3_ABI_VERSION of include/olmo3_attn.h
+ABI_VERSION = 8  # OLMO3_ABI_VERSION of include/olmo3_attn.h
 DTYPE_BF16, DTYPE_F32, DTYPE_BF16_E4M3 = 0, 1, 2
 MODE_PREFILL, MODE_DECODE = 0, 1
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_CAPACITY, ERR_HIP, ERR_WORKSPACE = range(6)
@@ -31,6 +31,7 @@ EXPORTS = (
     "olmo3_attn_decode_phases", "olmo3_attn_prefill_ragged", "olmo3_attn_decode_ragged",
     "olmo3_kv_append_e4m3", "olmo3_attn_prefill_e4m3", "olmo3_attn_decode_e4m3",
     "olmo3_attn_decode_e4m3_phases", "olmo3_attn_decode_ragged_e4m3",
+    "olmo3_attn_prefill_ragged_e4m3",
 )
 PHASE_PROLOGUE, PHASE_ATTENTION, PHASE_MERGE = 1, 2, 4
 PHASES_ALL = PHASE_PROLOGUE | PHASE_ATTENTION | PHASE_MERGE
@@ -126,6 +127,10 @@ def lib() -> ctypes.CDLL:
                                                     _p, _p, _p, _p, _p, _p, _f, _f, _i64, _p, _p,
                                                     _sz, _p]
         L.olmo3_attn_decode_ragged_e4m3.restype = _i
+        L.olmo3_attn_prefill_ragged_e4m3.argtypes = [_i, _i, _i, _i, _i, _i, _i, _i, R, _f, _p,
+                                                     _p, _p, _p, _p, _p, _p, _p, _f, _f, _i64, _p,
+                                                     _p, _sz, _p]
+        L.olmo3_attn_prefill_ragged_e4m3.restype = _i
         L.olmo3_status_string.argtypes = [_i]
         L.olmo3_status_string.restype = ctypes.c_char_p
         L.olmo3_abi_version.argtypes = []
@@ -366,6 +371,28 @@ def olmo3_attn_decode_e4m3(q_pre, k_pre, v, q_gain, k_gain, k_cache, v_cache, ou
         _check(lib().olmo3_attn_decode_e4m3(*args), "olmo3_attn_decode_e4m3")
     else:
         _check(lib().olmo3_attn_decode_e4m3_phases(phases, *args), "olmo3_attn_decode_e4m3_phases")
+
+
+def olmo3_attn_prefill_ragged_e4m3(q_pre, k_pre, v, q_gain, k_gain, k_cache, v_cache, out,
+                                   workspace, cu_seqlens, *, k_scale: float, v_scale: float,
+                                   max_len: int, window: int, layer_type: int, rope: Rope,
+                                   eps: float = 1e-6, stream=None) -> None:
+    """First chunks of B prompts packed row after row (q_pre [n_tokens, H*d],
+    k_pre/v [n_tokens, G*d], cu_seqlens int32 [B+1]) into e4m3 caches
+    [B, G, capacity, d] (uint8); out [n_tokens, H*d]."""
+    B, G, cap, d = _cache_dims(k_cache)
+    n_tokens = q_pre.shape[0]
+    H = q_pre.shape[-1] // d
+    dt = torch.bfloat16
+    kc, vc = _e4m3_caches(k_cache, v_cache)
+    r = rope.to_c()
+    st = lib().olmo3_attn_prefill_ragged_e4m3(
+        B, n_tokens, max_len, H, G, d, window, layer_type, ctypes.byref(r), eps,
+        _i32(cu_seqlens, "cu_seqlens", B + 1), _ptr(q_pre, "q_pre", dt), _ptr(k_pre, "k_pre", dt),
+        _ptr(v, "v", dt), _ptr(q_gain, "q_gain", dt), _ptr(k_gain, "k_gain", dt), kc, vc, k_scale,
+        v_scale, cap, _ptr(out, "out", dt), _ptr(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream(stream, q_pre.device))
+    _check(st, "olmo3_attn_prefill_ragged_e4m3")
 
 
 def olmo3_attn_decode_ragged_e4m3(q_pre, k_pre, v, q_gain, k_gain, k_cache, v_cache, out,

@@ -416,7 +416,8 @@ int prefill_impl(int phases, const PrefillShape& sh, int H, int G, int d, int wi
       a.p_sg = st_rows * d;
       a.p_sr = d;
       a.ring = st_rows;
-    } else if (ring_after) {
+    } else if (ring_after && !cf.e4m3) {
+      // (packed first chunks into e4m3 caches have no earlier positions)
       a.kp = k_cache;
       a.vp = v_cache;
       a.p_sb = (int64_t)G * cache_capacity * d;
@@ -708,6 +709,32 @@ int olmo3_attn_decode(int B, int H, int G, int d, int window, int layer_type,
                                   B, H, G, d, window, layer_type, rope, eps, pos, dtype, q_pre,
                                   k_pre, v, q_gain, k_gain, k_cache, v_cache, cache_capacity, out,
                                   workspace, workspace_bytes, stream);
+}
+
+int olmo3_attn_prefill_ragged_e4m3(int B, int n_tokens, int max_len, int H, int G, int d,
+                                   int window, int layer_type, const olmo3_rope* rope, float eps,
+                                   const int32_t* cu_seqlens, const void* q_pre,
+                                   const void* k_pre, const void* v, const void* q_gain,
+                                   const void* k_gain, void* k_cache, void* v_cache,
+                                   float k_scale, float v_scale, int64_t cache_capacity, void* out,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  if (B < 1 || n_tokens < 1 || max_len < 1 || max_len > n_tokens) return OLMO3_ERR_INVALID_ARG;
+  if (!cu_seqlens || ((uintptr_t)cu_seqlens & 3)) return OLMO3_ERR_INVALID_ARG;
+  if (!valid_scale(k_scale) || !valid_scale(v_scale)) return OLMO3_ERR_INVALID_ARG;
+  const size_t need = (H > 0 && G > 0 && d > 0)
+                          ? prefill_ws(1, n_tokens, H, G, d, layer_type, OLMO3_DTYPE_BF16_E4M3)
+                          : 0;
+  // the rows as one sequence for the input sizes; the caches hold B sequences
+  int st = validate_attn(1, n_tokens, H, G, d, window, layer_type, rope, eps, 0, OLMO3_DTYPE_BF16,
+                         q_pre, k_pre, v, q_gain, k_gain, k_cache, v_cache, cache_capacity, out,
+                         workspace, workspace_bytes, need, B, (int64_t)max_len - 1, 1);
+  if (st) return st;
+  if (max_len > kMaxPrefillPositions) return OLMO3_ERR_UNSUPPORTED;
+  const PrefillShape sh = {B, max_len, n_tokens, 0, cu_seqlens, nullptr};
+  return prefill_impl(OLMO3_PHASE_PROLOGUE | OLMO3_PHASE_ATTENTION, sh, H, G, d, window,
+                      layer_type, rope, eps, OLMO3_DTYPE_BF16, q_pre, k_pre, v, q_gain, k_gain,
+                      k_cache, v_cache, cache_capacity, out, workspace, (hipStream_t)stream,
+                      CacheFormat{1, k_scale, v_scale});
 }
 
 int olmo3_attn_prefill_e4m3(int B, int T, int H, int G, int d, int window, int layer_type,

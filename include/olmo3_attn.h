@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define OLMO3_ABI_VERSION 7
+#define OLMO3_ABI_VERSION 8
 
 typedef enum olmo3_status {
   OLMO3_OK = 0,
@@ -260,6 +260,22 @@ int olmo3_attn_decode_e4m3_phases(int phases, int B, int H, int G, int d, int wi
                                   void* v_cache, float k_scale, float v_scale,
                                   int64_t cache_capacity, void* out, void* workspace,
                                   size_t workspace_bytes, void* stream);
+
+/* Ragged first chunks into e4m3 caches: B prompts packed row after row
+ * (cu_seqlens as olmo3_attn_prefill_ragged, each sequence at positions
+ * 0 .. len_b - 1, no earlier positions), attended at bf16 precision as
+ * olmo3_attn_prefill_e4m3 does, their keys and values stored as codes.
+ * Later chunks of one sequence: olmo3_attn_prefill_e4m3 with its offset.
+ * workspace: olmo3_workspace_bytes(OLMO3_MODE_PREFILL, 1, n_tokens, ...,
+ * OLMO3_DTYPE_BF16_E4M3, 0).  Errors: as olmo3_attn_prefill_ragged with
+ * max_end = max_len, plus INVALID_ARG for scales as the e4m3 entry points. */
+int olmo3_attn_prefill_ragged_e4m3(int B, int n_tokens, int max_len, int H, int G, int d,
+                                   int window, int layer_type, const olmo3_rope* rope, float eps,
+                                   const int32_t* cu_seqlens, const void* q_pre,
+                                   const void* k_pre, const void* v, const void* q_gain,
+                                   const void* k_gain, void* k_cache, void* v_cache,
+                                   float k_scale, float v_scale, int64_t cache_capacity, void* out,
+                                   void* workspace, size_t workspace_bytes, void* stream);
 
 /* Ragged decode against e4m3 caches: olmo3_attn_decode_ragged's positions
  * (sequence b's new token at positions[b], each in [0, max_pos]) with

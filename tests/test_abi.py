@@ -43,7 +43,7 @@ def test_header_binding_and_library_versions_agree():
 
 
 def test_abi_version():
-    assert A.olmo3_abi_version() == A.ABI_VERSION == 7
+    assert A.olmo3_abi_version() == A.ABI_VERSION == 8
 
 
 def test_layer_type_matches_oracle_bit_exact():
@@ -375,3 +375,28 @@ def ragged_e4m3_call(**kw):
 ])
 def test_ragged_decode_e4m3_rejects(kw, status):
     assert ragged_e4m3_call(**kw) == status
+
+
+def ragged_prefill_e4m3_call(**kw):
+    a = dict(B=2, n=40, max_len=30, H=4, G=2, d=128, window=16, layer_type=0, eps=1e-6,
+             cu=fake(10), cap=16, ks=0.5, vs=0.5)
+    a.update(kw)
+    p = [fake(i) for i in range(9)]
+    r = ctypes.byref(A.Rope(theta=1e4).to_c())
+    return A.lib().olmo3_attn_prefill_ragged_e4m3(
+        a["B"], a["n"], a["max_len"], a["H"], a["G"], a["d"], a["window"], a["layer_type"], r,
+        a["eps"], a["cu"], *p[:7], a["ks"], a["vs"], a["cap"], p[7], p[8], 1 << 34, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(cu=0), A.ERR_INVALID_ARG),               # null cu_seqlens
+    (dict(cu=fake(10) + 2), A.ERR_INVALID_ARG),    # misaligned cu_seqlens
+    (dict(max_len=41), A.ERR_INVALID_ARG),         # longer than all rows
+    (dict(B=0), A.ERR_INVALID_ARG),
+    (dict(ks=-1.0), A.ERR_INVALID_ARG),
+    (dict(cap=15), A.ERR_CAPACITY),                # ring size != window
+    (dict(layer_type=1, cap=29), A.ERR_CAPACITY),  # a linear cache needs max_len slots
+    (dict(d=20), A.ERR_UNSUPPORTED),
+])
+def test_ragged_prefill_e4m3_rejects(kw, status):
+    assert ragged_prefill_e4m3_call(**kw) == status

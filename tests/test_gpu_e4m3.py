@@ -251,3 +251,59 @@ def test_e4m3_window_edge_planted_value(lt, w, pos, back):
     overwritten = p_star % cap == pos % cap  # the new token (value 0) took the slot
     want = 0.0 if overwritten else 2.0 * VS / n
     assert_close(got, np.full_like(got, want), 0.0, 2.0 ** -8, f"planted {lt} {pos} {back}")
+
+
+RAGGED_PREFILL = [
+    # H, G, window, layer_type, lengths
+    (8, 2, 64, 0, [100, 37, 200]),     # ring shorter than two of the prompts
+    (10, 2, 4096, 1, [129, 1, 300]),   # linear caches, group 5, a one-token prompt
+    (4, 4, 4096, 0, [64, 65]),         # one query head per key/value head
+]
+
+
+@pytest.mark.parametrize("case", RAGGED_PREFILL, ids=[str(c) for c in RAGGED_PREFILL])
+def test_e4m3_ragged_first_chunks_vs_oracle(case):
+    """Prompts of different lengths packed row after row into e4m3 caches:
+    each prompt matches the oracle's e4m3 prefill of that prompt alone, its
+    kept positions hold their codes, and no other slot changes."""
+    H, G, w, lt, lengths = case
+    B, d = len(lengths), 128
+    _log("e4m3 ragged first chunks", case)
+    kind = KINDS[lt]
+    rope = A.Rope(theta=500000.0, yarn=lt == 1, factor=8.0, orig_ctx=256)
+    n = sum(lengths)
+    max_len = max(lengths)
+    cap = w if kind == O.SLIDING else max_len + 3
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    x = inputs(89, lt, 1, n, H, G, d, BF16)
+    flat = {k: (t[0] if t.dim() == 3 else t) for k, t in x.items()}
+    kc, vc = synth.e4m3_cache_fill(89, lt, B, G, cap, d, device="cuda")
+    bk, bv = _codes(kc), _codes(vc)
+    out = torch.empty_like(flat["q_pre"])
+    ws = A.workspace(A.MODE_PREFILL, 1, n, H, G, d, lt, A.DTYPE_BF16_E4M3, 0, "cuda")
+    A.olmo3_attn_prefill_ragged_e4m3(flat["q_pre"], flat["k_pre"], flat["v"], flat["q_gain"],
+                                     flat["k_gain"], kc, vc, out, ws,
+                                     torch.tensor(cu, device="cuda"), k_scale=KS, v_scale=VS,
+                                     max_len=max_len, window=w, layer_type=lt, rope=rope)
+    hx = host_inputs(x)
+    got = host(out)
+    gk, gv = _codes(kc), _codes(vc)
+    for b in range(B):
+        r0, r1 = int(cu[b]), int(cu[b + 1])
+        T = r1 - r0
+        seq = {k: (v[:, r0:r1] if v.ndim == 3 else v) for k, v in hx.items()}
+        ref_cache = O.KvCacheRef(kind, w, cap, 1, G, d, e4m3_scales=(KS, VS))
+        ref = O.prefill_ref(**seq, H=H, G=G, d=d, kind=kind, window=w, rope=oracle_rope(rope),
+                            cache=ref_cache)
+        assert_close(got[r0:r1][None], ref, what=f"prompt {b} ({T} tokens)")
+        positions = np.arange(T)
+        keep = positions[-w:] if kind == O.SLIDING else positions
+        slots = keep % w if kind == O.SLIDING else keep
+        k_rot = _rotated_keys(seq, kind, rope, positions, G, d)[0, keep]          # [n_keep, G, d]
+        v_new = seq["v"][0].reshape(T, G, d)[keep]
+        assert np.array_equal(gv[b][:, slots].transpose(1, 0, 2), O.e4m3_store(v_new, VS)), \
+            f"prompt {b}: value codes"
+        _check_key_codes(gk[b][:, slots].transpose(1, 0, 2), _key_x32(k_rot, KS), f"prompt {b}")
+        rest = np.setdiff1d(np.arange(cap), slots)
+        assert np.array_equal(gk[b][:, rest], bk[b][:, rest]), f"prompt {b}: key slot overwritten"
+        assert np.array_equal(gv[b][:, rest], bv[b][:, rest]), f"prompt {b}: value slot overwritten"
