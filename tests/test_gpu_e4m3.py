@@ -307,3 +307,57 @@ def test_e4m3_ragged_first_chunks_vs_oracle(case):
         rest = np.setdiff1d(np.arange(cap), slots)
         assert np.array_equal(gk[b][:, rest], bk[b][:, rest]), f"prompt {b}: key slot overwritten"
         assert np.array_equal(gv[b][:, rest], bv[b][:, rest]), f"prompt {b}: value slot overwritten"
+
+
+@pytest.mark.parametrize("lt", [0, 1])
+def test_e4m3_ragged_serving_flow(lt):
+    """Prompts of different lengths ingested together, then four decode steps
+    in which every sequence advances from its own position: each sequence's
+    outputs follow the oracle's e4m3 cache flow (prefill, then one decode per
+    step, the cache holding codes throughout)."""
+    H, G, d, w = 8, 2, 128, 64
+    lengths = [70, 3, 40]
+    B = len(lengths)
+    kind = KINDS[lt]
+    rope = A.Rope(theta=500000.0, yarn=lt == 1, factor=8.0, orig_ctx=256)
+    steps = 4
+    cap = w if kind == O.SLIDING else max(lengths) + steps
+    n = sum(lengths)
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    x = inputs(97, lt, 1, n, H, G, d, BF16)
+    flat = {k: (t[0] if t.dim() == 3 else t) for k, t in x.items()}
+    kc = torch.zeros((B, G, cap, d), dtype=torch.uint8, device="cuda")
+    vc = torch.zeros_like(kc)
+    out = torch.empty_like(flat["q_pre"])
+    ws = A.workspace(A.MODE_PREFILL, 1, n, H, G, d, lt, A.DTYPE_BF16_E4M3, 0, "cuda")
+    A.olmo3_attn_prefill_ragged_e4m3(flat["q_pre"], flat["k_pre"], flat["v"], flat["q_gain"],
+                                     flat["k_gain"], kc, vc, out, ws,
+                                     torch.tensor(cu, device="cuda"), k_scale=KS, v_scale=VS,
+                                     max_len=max(lengths), window=w, layer_type=lt, rope=rope)
+    hx = host_inputs(x)
+    refs = []
+    for b in range(B):
+        seq = {k: (v[:, cu[b]:cu[b + 1]] if v.ndim == 3 else v) for k, v in hx.items()}
+        c = O.KvCacheRef(kind, w, cap, 1, G, d, e4m3_scales=(KS, VS))
+        ref = O.prefill_ref(**seq, H=H, G=G, d=d, kind=kind, window=w, rope=oracle_rope(rope),
+                            cache=c)
+        assert_close(host(out)[cu[b]:cu[b + 1]][None], ref, what=f"prefill of prompt {b}")
+        refs.append(c)
+    wsd = A.workspace(A.MODE_DECODE, B, 1, H, G, d, lt, A.DTYPE_BF16_E4M3, cap, "cuda")
+    for step in range(steps):
+        xs = inputs(97, 50 + step, B, 1, H, G, d, BF16)
+        q, k, v = (xs[key][:, 0].contiguous() for key in ("q_pre", "k_pre", "v"))
+        positions = [L + step for L in lengths]
+        dout = torch.empty_like(q)
+        A.olmo3_attn_decode_ragged_e4m3(q, k, v, flat["q_gain"], flat["k_gain"], kc, vc, dout, wsd,
+                                        torch.tensor(positions, dtype=torch.int32, device="cuda"),
+                                        k_scale=KS, v_scale=VS, max_pos=max(positions), window=w,
+                                        layer_type=lt, rope=rope)
+        hq = host_inputs(xs)
+        got = host(dout)
+        for b, p in enumerate(positions):
+            ref = O.decode_e4m3_ref(hq["q_pre"][b:b + 1, 0], hq["k_pre"][b:b + 1, 0],
+                                    hq["v"][b:b + 1, 0], hx["q_gain"], hx["k_gain"], H=H, G=G,
+                                    d=d, kind=kind, window=w, rope=oracle_rope(rope), pos=p,
+                                    cache=refs[b])
+            assert_close(got[b:b + 1], ref, what=f"step {step}, sequence {b} at {p}")
