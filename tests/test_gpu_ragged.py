@@ -241,3 +241,65 @@ def test_ragged_decode_e4m3_vs_oracle(case):
         others = np.setdiff1d(np.arange(cap), [slot])
         assert np.array_equal(got_k[b][:, others], bk[b][:, others]), f"sequence {b}: key slots"
         assert np.array_equal(got_v[b][:, others], bv[b][:, others]), f"sequence {b}: value slots"
+
+
+@pytest.mark.parametrize("lt", [0, 1])
+def test_ragged_serving_flow(lt):
+    """Prompts ingested together from empty caches, a second chunk of each at
+    its own offset (read over the cache the first one left), then three
+    decode steps at per-sequence positions: every output follows the
+    oracle's cache flow for that sequence alone."""
+    H, G, d, w = 8, 2, 128, 96
+    first, second, steps = [70, 3, 130], [40, 100, 1], 3
+    B = len(first)
+    kind = KINDS[lt]
+    rope = A.Rope(theta=500000.0, yarn=lt == 1, factor=8.0, orig_ctx=256)
+    ends = [a + b + steps for a, b in zip(first, second)]
+    cap = w if kind == O.SLIDING else max(ends)
+    kc = torch.zeros((B, G, cap, d), dtype=BF16, device="cuda")
+    vc = torch.zeros_like(kc)
+    refs = [O.KvCacheRef(kind, w, cap, 1, G, d) for _ in range(B)]
+
+    def chunk(lengths, offsets, seed):
+        per = [inputs(seed, b, 1, n, H, G, d, BF16) for b, n in enumerate(lengths)]
+        packed = {k: torch.cat([p[k][0] for p in per]).contiguous() for k in ("q_pre", "k_pre", "v")}
+        gains = {k: per[0][k] for k in ("q_gain", "k_gain")}
+        N = sum(lengths)
+        cu = torch.tensor(np.concatenate([[0], np.cumsum(lengths)]), dtype=torch.int32, device="cuda")
+        po = torch.tensor(offsets, dtype=torch.int32, device="cuda")
+        out = torch.empty_like(packed["q_pre"])
+        ws = A.workspace(A.MODE_PREFILL, 1, N, H, G, d, lt, BF16, cap, "cuda")
+        A.olmo3_attn_prefill_ragged(packed["q_pre"], packed["k_pre"], packed["v"], gains["q_gain"],
+                                    gains["k_gain"], kc, vc, out, ws, cu, po, max_len=max(lengths),
+                                    max_end=max(p + n for p, n in zip(offsets, lengths)), window=w,
+                                    layer_type=lt, rope=rope)
+        hq, hk_pre, hv_in = host(packed["q_pre"]), host(packed["k_pre"]), host(packed["v"])
+        hg = {k: host(t) for k, t in gains.items()}
+        got, row = host(out), 0
+        for b, (n, p) in enumerate(zip(lengths, offsets)):
+            ref = O.prefill_ref(hq[None, row:row + n], hk_pre[None, row:row + n],
+                                hv_in[None, row:row + n], hg["q_gain"], hg["k_gain"], H=H, G=G,
+                                d=d, kind=kind, window=w, rope=oracle_rope(rope), pos_offset=p,
+                                cache=refs[b])
+            assert_close(got[row:row + n][None], ref, what=f"chunk at {p} of sequence {b}")
+            row += n
+        return hg
+
+    hg = chunk(first, [0] * B, 101)
+    hg = chunk(second, first, 102)
+    ws = A.workspace(A.MODE_DECODE, B, 1, H, G, d, lt, BF16, cap, "cuda")
+    for step in range(steps):
+        xs = inputs(103, step, B, 1, H, G, d, BF16)
+        q, k, v = (xs[key][:, 0].contiguous() for key in ("q_pre", "k_pre", "v"))
+        positions = [a + b + step for a, b in zip(first, second)]
+        out = torch.empty_like(q)
+        A.olmo3_attn_decode_ragged(q, k, v, xs["q_gain"], xs["k_gain"], kc, vc, out, ws,
+                                   torch.tensor(positions, dtype=torch.int32, device="cuda"),
+                                   max_pos=max(positions), window=w, layer_type=lt, rope=rope)
+        hx = host_inputs(xs)
+        got = host(out)
+        for b, p in enumerate(positions):
+            ref = O.decode_ref(hx["q_pre"][b:b + 1, 0], hx["k_pre"][b:b + 1, 0],
+                               hx["v"][b:b + 1, 0], hx["q_gain"], hx["k_gain"], H=H, G=G, d=d,
+                               kind=kind, window=w, rope=oracle_rope(rope), pos=p, cache=refs[b])
+            assert_close(got[b:b + 1], ref, what=f"step {step}, sequence {b} at {p}")
