@@ -15,6 +15,8 @@ Workloads (synthetic, seeded, shaped like the OLMo 3 configurations):
   decode-stack  the same 32-layer stack decoding one token per sequence,
        B=16 at cache length 65,536: KV bytes read per step and per token of
        context (the per-layer-type cache of the page "Olmo 3 7B")
+  chunked  7B prefill of a 4,096-token chunk at position 61,440 onto a
+       filled cache (full layer: 61,440 cached positions; sliding: the ring)
   7b-e4m3  7B decode (B=32 at 65,536) against e4m3 caches (1-byte codes)
   decode-stack-e4m3  the decode stack against e4m3 caches
 
@@ -100,7 +102,18 @@ def prefill_pairs(T: int, window: int, sliding: bool) -> int:
     return window * (window + 1) // 2 + (T - window) * window
 
 
-def prefill_flops(T, H, d, window, sliding, B=1) -> int:
+def chunk_pairs(P: int, T: int, window: int, sliding: bool) -> int:
+    """Allowed pairs of queries at positions P .. P+T-1 over keys 0 .. P+T-1:
+    sum over t of min(t+1, window) (sliding) or t+1 (full)."""
+    if not sliding:
+        return T * P + T * (T + 1) // 2
+    grow = max(0, min(P + T, window) - P)  # queries with t + 1 <= window
+    return sum(P + j + 1 for j in range(grow)) + (T - grow) * window
+
+
+def prefill_flops(T, H, d, window, sliding, B=1, P=0) -> int:
+    if P:
+        return 4 * d * H * chunk_pairs(P, T, window, sliding) * B
     return 4 * d * H * prefill_pairs(T, window, sliding) * B
 
 
@@ -121,6 +134,8 @@ WORKLOADS = {
                  decode=None),
     "decode-stack": dict(name="olmo3-7b-decode-stack", prefill=None,
                          decode=dict(B=16, H=32, G=32, L=65536, layers=32)),
+    "chunked": dict(name="olmo3-7b-chunked-prefill",
+                    prefill=dict(B=1, T=4096, H=32, G=32, pos_offset=61440), decode=None),
     "7b-e4m3": dict(name="olmo3-7b-decode-e4m3", prefill=None,
                     decode=dict(B=32, H=32, G=32, L=65536, e4m3=True)),
     "decode-stack-e4m3": dict(name="olmo3-7b-decode-stack-e4m3", prefill=None,
@@ -203,20 +218,29 @@ def main():
             continue
         x = synth.layer_inputs(seed_base + (ell if n_layers else 0), ell, B, T, H, G, d,
                                device=dev, dtype=bf16)
-        cap = WINDOW if sliding else T
-        kc = torch.zeros((B, G, cap, d), dtype=bf16, device=dev)
-        vc = torch.zeros_like(kc)
+        P = pf.get("pos_offset", 0)
+        cap = WINDOW if sliding else P + T
+        if P:
+            # a cache already holding positions 0 .. P-1 (the ring: the last
+            # WINDOW of them); each call rewrites the chunk's slots (on the
+            # ring, the slots its later calls read as the prefix: the values
+            # change from the second call on, the work does not)
+            kc, vc = synth.cache_fill(7, ell, B, G, cap, d, device=dev, dtype=bf16)
+        else:
+            kc = torch.zeros((B, G, cap, d), dtype=bf16, device=dev)
+            vc = torch.zeros_like(kc)
         out = torch.empty_like(x["q_pre"])
         ws = A.workspace(A.MODE_PREFILL, B, T, H, G, d, lt, bf16, cap, dev)
         r = rope if not sliding else A.Rope(theta=THETA)
 
-        def run(phases, x=x, kc=kc, vc=vc, out=out, ws=ws, lt=lt, r=r):
+        def run(phases, x=x, kc=kc, vc=vc, out=out, ws=ws, lt=lt, r=r, P=P):
             A.olmo3_attn_prefill(x["q_pre"], x["k_pre"], x["v"], x["q_gain"], x["k_gain"], kc, vc,
-                                 out, ws, window=WINDOW, layer_type=lt, rope=r, phases=phases)
+                                 out, ws, window=WINDOW, layer_type=lt, rope=r, pos_offset=P,
+                                 phases=phases)
 
         segments.append(dict(name=f"prefill_{'sliding' if sliding else 'full'}_l{ell}", kind="prefill",
                              sliding=sliding, run=run, phases=[A.PHASE_PROLOGUE, A.PHASE_ATTENTION],
-                             work=prefill_flops(T, H, d, WINDOW, sliding, B)))
+                             work=prefill_flops(T, H, d, WINDOW, sliding, B, P)))
 
     # ---- decode layers
     dc = wl["decode"]
@@ -382,7 +406,7 @@ def main():
             "kv_bytes_per_token_of_context": kv_step // (dc["B"] * dc["L"]),
             "naive_bytes_per_token_of_context": NAIVE_BYTES_PER_TOKEN_7B // (2 if dc.get("e4m3") else 1),
         }
-    if args.cpu_seconds > 0 and (pre or dec):
+    if args.cpu_seconds > 0 and (pre or dec) and not (wl["prefill"] or {}).get("pos_offset"):
         print(f"[bench] timing the CPU oracle for ~{args.cpu_seconds:.0f} s", file=sys.stderr, flush=True)
         result["cpu_baseline"] = (cpu_baseline(args, wl, segments, dev) if pre else
                                   cpu_baseline_decode(args, wl))

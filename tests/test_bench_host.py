@@ -60,3 +60,16 @@ def test_decode_kernel_label():
     assert bench.decode_kernel(40, 8, False) == "decode_mfma_kernel"
     assert bench.decode_kernel(40, 8, True) == "decode_split_kernel"
     assert bench.decode_kernel(32, 32, True) == "decode_split_kernel"
+
+
+def test_chunk_pairs_brute_force():
+    """Allowed pairs of a chunk at an offset: the closed form against a count
+    over the chunk's queries."""
+    for P, T, w in [(0, 100, 64), (10, 100, 64), (60, 10, 64), (3, 5, 4), (61440, 4096, 4096),
+                    (4000, 200, 4096)]:
+        for sliding in (True, False):
+            want = sum(min(t + 1, w) if sliding else t + 1 for t in range(P, P + T))
+            assert bench.chunk_pairs(P, T, w, sliding) == want
+    # offset 0 agrees with the whole-prefill count
+    assert bench.chunk_pairs(0, 8192, 4096, True) == bench.prefill_pairs(8192, 4096, True)
+    assert bench.chunk_pairs(0, 8192, 4096, False) == bench.prefill_pairs(8192, 4096, False)
