@@ -82,6 +82,9 @@ PREFILL_CASES = [
     (1, 200, 4, 2, 64, 32, 0, False),      # d = 64 (plain kernel)
     (2, 150, 2, 1, 32, 4096, 1, True),     # d = 32, full, YaRN
     (1, 77, 3, 1, 16, 9, 0, False),        # d = 16 bf16
+    (1, 130, 64, 64, 128, 64, 0, False),   # 64 heads: the prologue's head limit
+    (1, 600, 64, 8, 128, 4096, 1, True),   # group 8 with 64 query heads, full
+    (3, 2100, 2, 1, 128, 256, 0, False),   # 6,300 rows: the one-wavefront-per-token prologue
 ]
 
 
