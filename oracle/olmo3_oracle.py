@@ -38,10 +38,15 @@ Parity unpinned by the pages: the rotation direction, the GQA grouping order,
 the YaRN ramp parameters and the softmax scale are shared conventions.
 
 No intermediate is rounded: inputs are taken exactly as given (bf16 values
-are exactly representable in fp64) and everything is computed in fp64.  The
-one exception is the optional e4m3 cache: a stored code is an integer that
+are exactly representable in fp64) and everything is computed in fp64.  Two
+exceptions: the optional e4m3 cache, whose stored code is an integer that
 floating point decides, so it is decided as the kernels decide it (the fp32
-product of the value and 1/scale, then the nearest code), see ``e4m3_encode``.
+product of the value and 1/scale, then the nearest code), see ``e4m3_encode``;
+and the opt-in ``round_rotated`` switch of ``prefill_ref`` / ``decode_ref``,
+which rounds the rotated queries and keys to bfloat16, the type every
+operand of a bfloat16 model's attention has (page "Olmo-3 End-to-End
+Implementation", "Technical Details": bfloat16 throughout), see
+``bf16_round``.
 """
 
 from __future__ import annotations
@@ -59,6 +64,7 @@ __all__ = [
     "kv_bytes_per_token", "attend", "prefill_ref", "decode_ref",
     "attention_rows_ref", "decode_rows_ref", "ring_positions",
     "E4M3_MAX", "e4m3_value", "e4m3_values", "e4m3_encode", "e4m3_store", "decode_e4m3_ref",
+    "BF16_MAX", "bf16_round",
 ]
 
 SLIDING = "sliding"
@@ -267,6 +273,33 @@ def rope_rotate(x: np.ndarray, positions: np.ndarray, inv_freq: np.ndarray,
 
 
 # --------------------------------------------------------------------------
+# bfloat16 rounding
+# --------------------------------------------------------------------------
+# bfloat16 is the upper half of an IEEE binary32: sign, 8 exponent bits (bias
+# 127), 7 stored mantissa bits.  A normal value of binade 2^e is a multiple
+# of 2^(e-7); below 2^-126 the values are the subnormal multiples of 2^-133.
+
+BF16_MAX = (2.0 - 2.0 ** -7) * 2.0 ** 127
+
+
+def bf16_round(x) -> np.ndarray:
+    """Nearest bfloat16 value to each fp64 value, returned as fp64: the
+    multiple of the binade's spacing nearest to x, halfway cases to the even
+    multiple (IEEE round to nearest even, taken once from the fp64 value);
+    magnitudes that round past BF16_MAX become infinities; signs, zeros and
+    NaNs are kept."""
+    x = np.asarray(x, dtype=np.float64)
+    mag = np.abs(x)
+    _, e2 = np.frexp(mag)                       # mag = f * 2^e2, f in [0.5, 1)
+    binade = np.maximum(e2 - 1, -126)           # floor(log2 |x|), normal range
+    step = np.ldexp(1.0, binade - 7)
+    with np.errstate(invalid="ignore", over="ignore"):
+        r = np.rint(mag / step) * step          # rint: halves to even
+        r = np.where(r > BF16_MAX, np.inf, r)
+    return np.copysign(r, x)
+
+
+# --------------------------------------------------------------------------
 # e4m3 cache codes
 # --------------------------------------------------------------------------
 # The pages name quantization only as a next step (page "Olmo-3 End-to-End
@@ -445,7 +478,8 @@ def _project_heads(q_pre, k_pre, v, q_gain, k_gain, H, G, d, eps):
 
 def prefill_ref(q_pre, k_pre, v, q_gain, k_gain, *, H: int, G: int, d: int,
                 kind: str, window: int, rope: RopeParams, eps: float = 1e-6,
-                pos_offset: int = 0, cache: KvCacheRef | None = None) -> np.ndarray:
+                pos_offset: int = 0, cache: KvCacheRef | None = None,
+                round_rotated: bool = False) -> np.ndarray:
     """One attention call over T new tokens at positions pos_offset .. +T-1.
 
     q_pre [B, T, H*d], k_pre and v [B, T, G*d] (projected, before QK-norm);
@@ -457,19 +491,26 @@ def prefill_ref(q_pre, k_pre, v, q_gain, k_gain, *, H: int, G: int, d: int,
     their absolute positions; attention runs under the mask; the new keys and
     values are then stored.  On a cache holding unrotated keys, each cached
     key is rotated by its own absolute position when it is read.
+
+    ``round_rotated``: every rotated query and key (cached keys rotated on
+    reading included) is rounded to bfloat16 before the scores, as a model
+    computing in bfloat16 holds them.  With large QK-norm gains the scores
+    grow with the gains and that rounding moves outputs by more than the
+    fp32 accumulation does; it is off by default.
     """
     q_pre = np.asarray(q_pre, dtype=np.float64)
     B, T = q_pre.shape[:2]
     qh, kh, vh = _project_heads(q_pre, k_pre, v, q_gain, k_gain, H, G, d, eps)
     w, m = layer_rope(rope, kind, d)
     positions = pos_offset + np.arange(T, dtype=np.int64)
-    q_rot = rope_rotate(qh, positions, w, m)
-    k_rot = rope_rotate(kh, positions, w, m)
+    rnd = bf16_round if round_rotated else (lambda t: t)
+    q_rot = rnd(rope_rotate(qh, positions, w, m))
+    k_rot = rnd(rope_rotate(kh, positions, w, m))
 
     if cache is not None:
         past_k, past_v, past_pos = cache.contents()
         if not cache.rotated and past_pos.size:
-            past_k = rope_rotate(past_k, past_pos, w, m)
+            past_k = rnd(rope_rotate(past_k, past_pos, w, m))
     else:
         past_k = np.zeros((B, 0, G, d))
         past_v = np.zeros((B, 0, G, d))
@@ -490,7 +531,7 @@ def prefill_ref(q_pre, k_pre, v, q_gain, k_gain, *, H: int, G: int, d: int,
 
 def decode_ref(q_pre, k_pre, v, q_gain, k_gain, *, H: int, G: int, d: int,
                kind: str, window: int, rope: RopeParams, eps: float = 1e-6,
-               pos: int, cache: KvCacheRef) -> np.ndarray:
+               pos: int, cache: KvCacheRef, round_rotated: bool = False) -> np.ndarray:
     """Single-token decode: the prefill computation with T = 1 at position
     ``pos`` against the cache (page "Olmo-3 End-to-End Implementation",
     "Inference Pipeline": generate one token at a time, reuse the cache).
@@ -499,7 +540,8 @@ def decode_ref(q_pre, k_pre, v, q_gain, k_gain, *, H: int, G: int, d: int,
     k_pre = np.asarray(k_pre, dtype=np.float64)[:, None, :]
     v = np.asarray(v, dtype=np.float64)[:, None, :]
     out = prefill_ref(q_pre, k_pre, v, q_gain, k_gain, H=H, G=G, d=d, kind=kind,
-                      window=window, rope=rope, eps=eps, pos_offset=pos, cache=cache)
+                      window=window, rope=rope, eps=eps, pos_offset=pos, cache=cache,
+                      round_rotated=round_rotated)
     return out[:, 0, :]
 
 

@@ -578,4 +578,114 @@ def check_decode_e4m3_equals_decode_on_the_grid():
         _close(a, b, 1e-12, f"e4m3 decode on the grid, {kind}")
 
 
+# ------------------------------------------------------------ bf16 rounding
+def _bf16_neighbours(rng, n):
+    """n random finite bfloat16 values b (normal and subnormal, both signs)
+    with the next value away from zero, as fp64 (exact: bf16 values are)."""
+    bits = rng.integers(0x0001, 0x7F7F, n).astype(np.uint32)
+    sign = rng.integers(0, 2, n).astype(np.uint32) << 15
+    lo = ((bits | sign) << 16).view(np.float32).astype(np.float64)
+    hi = (((bits + 1) | sign) << 16).view(np.float32).astype(np.float64)
+    return lo, hi
+
+
+def check_bf16_round_matches_torch():
+    """On values exactly representable in fp32, torch's fp32 -> bfloat16
+    conversion (round to nearest even) gives the same values, for random
+    magnitudes from fp32 subnormals to past the bfloat16 maximum, and for the
+    exact midpoints between neighbouring bfloat16 values."""
+    rng = _rng(91)
+    mant = rng.standard_normal(40000)
+    x = (mant * np.exp2(rng.integers(-140, 126, mant.size).astype(np.float64))).astype(np.float32)
+    lo, hi = _bf16_neighbours(rng, 20000)
+    mids = ((lo + hi) / 2).astype(np.float32)           # exact: 9 significant bits
+    near_max = np.float32(O.BF16_MAX) * np.array([1.0, 1.001, 1.0019, 1.002, 1.003], np.float32)
+    x = np.concatenate([x, mids, lo.astype(np.float32), near_max, -near_max,
+                        np.array([0.0, -0.0, 1e-45, -1e-45], np.float32)])
+    assert np.isfinite(x).all()
+    want = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    got = O.bf16_round(x.astype(np.float64))
+    assert np.array_equal(got, want), np.argwhere(got != want)[:5]
+    assert np.array_equal(np.signbit(got), np.signbit(want))
+    assert np.isinf(got).any() and (got[np.isinf(got)] == want[np.isinf(want)]).all()
+
+
+def check_bf16_round_closed_forms():
+    """Spacing 2^-7 at 1; halves go to the even neighbour; a value just past a
+    half goes up even when fp32 cannot hold it (rounded once, from fp64);
+    at most half a step from x (relative 2^-8 on normals); fixed points are
+    the bfloat16 values; signs, zeros and NaN kept."""
+    r = O.bf16_round
+    one = 1.0
+    assert list(r([one + 2.0 ** -8, one + 3 * 2.0 ** -8, one + 2.0 ** -8 + 2.0 ** -40,
+                   -(one + 2.0 ** -8), 2.0 ** -134, 3 * 2.0 ** -134])) == \
+        [1.0, one + 2.0 ** -6, one + 2.0 ** -7, -1.0, 0.0, 2.0 ** -132]
+    assert r(O.BF16_MAX) == O.BF16_MAX and r(-O.BF16_MAX) == -O.BF16_MAX
+    assert r(O.BF16_MAX + 2.0 ** 119) == np.inf and r(O.BF16_MAX + 2.0 ** 118) == O.BF16_MAX
+    assert np.signbit(r(-0.0)) and r(0.0) == 0.0 and np.isnan(r(np.nan))
+    rng = _rng(92)
+    x = rng.standard_normal(20000) * np.exp2(rng.integers(-100, 100, 20000).astype(np.float64))
+    y = r(x)
+    assert (np.abs(y - x) <= 2.0 ** -8 * np.abs(x)).all()
+    assert np.array_equal(r(y), y)
+    lo, hi = _bf16_neighbours(rng, 5000)
+    assert np.array_equal(r(lo), lo) and np.array_equal(r(hi), hi)
+    t = 0.25 * lo + 0.75 * hi                            # strictly nearer hi
+    assert np.array_equal(r(t), hi) and np.array_equal(r(0.75 * lo + 0.25 * hi), lo)
+
+
+def check_round_rotated_matches_sdpa_on_rounded_operands():
+    """With round_rotated, prefill equals torch's SDPA over the rotated
+    queries and keys rounded by torch's bfloat16 conversion (both of them,
+    the values untouched).  torch converts fp64 through fp32, which can only
+    differ from one rounding when an fp64 value lies within an fp32 half
+    step of a bfloat16 midpoint; the test asserts that no operand does."""
+    rng = _rng(93)
+    B, T, H, G, d, w = 1, 23, 4, 2, 16, 7
+    x = _inputs(rng, B, T, H, G, d)
+    x["q_gain"] = x["q_gain"] * 3.0
+    x["k_gain"] = x["k_gain"] * 3.0
+    for kind, yarn in ((O.SLIDING, False), (O.FULL, True)):
+        rope = O.RopeParams(theta=10000.0, yarn=yarn, factor=4.0, orig_ctx=8)
+        wr, m = O.layer_rope(rope, kind, d)
+        p = np.arange(T)
+        q = O.rope_rotate(O.rms_norm(x["q_pre"], x["q_gain"], 1e-6).reshape(T, H, d), p, wr, m)
+        k = O.rope_rotate(O.rms_norm(x["k_pre"], x["k_gain"], 1e-6).reshape(T, G, d), p, wr, m)
+        for t in (q, k):
+            _, e2 = np.frexp(np.abs(t))
+            frac = np.abs(t) / np.ldexp(1.0, np.maximum(e2 - 1, -126) - 7) % 1.0
+            assert (np.abs(frac - 0.5) > 2.0 ** -15).all(), "operand next to a bf16 midpoint"
+        def tb(t):
+            return torch.from_numpy(t).to(torch.bfloat16).to(torch.float64).numpy()
+        want = _sdpa(tb(q), tb(k), x["v"].reshape(T, G, d), O.mask_at_positions(p, p, kind, w))
+        got = O.prefill_ref(**x, H=H, G=G, d=d, kind=kind, window=w, rope=rope,
+                            round_rotated=True).reshape(T, H, d)
+        _close(got, want, 1e-12, f"round_rotated vs sdpa {kind}")
+        plain = O.prefill_ref(**x, H=H, G=G, d=d, kind=kind, window=w, rope=rope)
+        assert np.abs(plain.reshape(T, H, d) - want).max() > 1e-4, "rounding had no effect"
+
+
+def check_round_rotated_cache_flow():
+    """With round_rotated, prefill(T0) then decodes reproduce prefill(T) on
+    the ring and the linear cache, with rotated and unrotated key storage:
+    cached keys are rounded once, as the new ones are."""
+    rng = _rng(94)
+    B, T, T0, H, G, d, w = 1, 19, 7, 2, 1, 8, 5
+    x = _inputs(rng, B, T, H, G, d)
+    rope = O.RopeParams(theta=10000.0, yarn=True, factor=4.0, orig_ctx=8)
+    for kind, cap in ((O.SLIDING, w), (O.FULL, T)):
+        full = O.prefill_ref(**x, H=H, G=G, d=d, kind=kind, window=w, rope=rope,
+                             round_rotated=True)
+        for rotated in (True, False):
+            c = O.KvCacheRef(kind, w, cap, B, G, d, rotated=rotated)
+            head = {k: (v[:, :T0] if v.ndim == 3 else v) for k, v in x.items()}
+            O.prefill_ref(**head, H=H, G=G, d=d, kind=kind, window=w, rope=rope, cache=c,
+                          round_rotated=True)
+            for p in range(T0, T):
+                o = O.decode_ref(x["q_pre"][:, p], x["k_pre"][:, p], x["v"][:, p],
+                                 x["q_gain"], x["k_gain"], H=H, G=G, d=d, kind=kind,
+                                 window=w, rope=rope, pos=p, cache=c, round_rotated=True)
+                _close(o, full[:, p], 1e-12, f"rounded decode {kind} rotated={rotated} p={p}")
+
+
 ALL_CHECKS = [v for k, v in sorted(globals().items()) if k.startswith("check_") and callable(v)]

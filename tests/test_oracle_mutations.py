@@ -2,6 +2,7 @@
 pin in ``oracle_pins`` fails for each: evidence that the pins would notice a
 dropped term, a wrong sign or index, or a transposed operand."""
 
+import inspect
 import math
 
 import numpy as np
@@ -198,6 +199,33 @@ def _decode_e4m3_drops_new_token(q_pre, k_pre, v, q_gain, k_gain, *, H, G, d, ki
                      for b in range(B)]).reshape(B, H * d)
 
 
+def _bf16_factory(mode):
+    def rnd(x):
+        x = np.asarray(x, dtype=np.float64)
+        mag = np.abs(x)
+        _, e2 = np.frexp(mag)
+        bits = 8 if mode == "8 bits" else 7
+        step = np.ldexp(1.0, np.maximum(e2 - 1, -126) - bits)
+        q = mag / step
+        if mode == "truncate":
+            r = np.floor(q)
+        elif mode == "away":
+            r = np.floor(q + 0.5)
+        else:
+            r = np.rint(q)
+        return np.copysign(r * step, x)
+    return rnd
+
+
+def _prefill_edited(old, new):
+    """prefill_ref with one source line replaced (same module globals)."""
+    src = inspect.getsource(_orig["prefill_ref"])
+    assert old in src, old
+    ns = dict(vars(O))
+    exec(compile(src.replace(old, new), O.__file__, "exec"), ns)
+    return ns["prefill_ref"]
+
+
 MUTANTS = {
     "mask t-s <= window": dict(sliding_window_mask=_mask_le_window, mask_at_positions=_mask_at_le_window),
     "mask not causal": dict(mask_at_positions=_mask_at_noncausal),
@@ -226,6 +254,15 @@ MUTANTS = {
     "e4m3 ties away from zero": dict(e4m3_encode=_e4m3_encode_factory("away")),
     "e4m3 scale applied twice": dict(e4m3_store=_e4m3_store_twice),
     "e4m3 decode drops the new token": dict(decode_e4m3_ref=_decode_e4m3_drops_new_token),
+    "bf16 truncates": dict(bf16_round=_bf16_factory("truncate")),
+    "bf16 ties away from zero": dict(bf16_round=_bf16_factory("away")),
+    "bf16 keeps 8 mantissa bits": dict(bf16_round=_bf16_factory("8 bits")),
+    "round_rotated skips keys": dict(prefill_ref=_prefill_edited(
+        "k_rot = rnd(rope_rotate(kh,", "k_rot = (rope_rotate(kh,")),
+    "round_rotated skips queries": dict(prefill_ref=_prefill_edited(
+        "q_rot = rnd(rope_rotate(qh,", "q_rot = (rope_rotate(qh,")),
+    "round_rotated skips cached keys": dict(prefill_ref=_prefill_edited(
+        "past_k = rnd(rope_rotate(", "past_k = (rope_rotate(")),
 }
 
 
