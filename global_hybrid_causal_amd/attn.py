@@ -427,8 +427,9 @@ def workspace(mode: int, B: int, T: int, H: int, G: int, d: int, layer_type: int
 
 def olmo3_probe_prefill_visits(T: int, window: int, layer_type: int, pos_offset: int = 0,
                                device="cuda") -> torch.Tensor:
-    """[T, pos_offset + T] uint8 table of the (query, key position) pairs the
-    prefill kernel accumulates for queries at pos_offset .. pos_offset + T - 1."""
+    """[T, pos_offset + T] uint8 table: how many times the prefill kernel
+    accumulates each (query, key position) pair, for queries at pos_offset ..
+    pos_offset + T - 1."""
     visit = torch.empty((T, pos_offset + T), dtype=torch.uint8, device=device)
     st = lib().olmo3_probe_prefill_visits(T, pos_offset, window, layer_type, _ptr(visit, "visit"),
                                           _stream(None, visit.device))

@@ -369,7 +369,7 @@ __global__ __launch_bounds__(256, 2) void prefill_d128_kernel(AttnArgs a) {
   }
 }
 
-// Records every (query, key) pair the kernel above accumulates: the same
+// Counts every (query, key) pair the kernel above accumulates: the same
 // work mapping, tile runs, lane -> (query, key) map and predicate.
 // visit[(t - pos_offset) * (pos_offset + T) + s] for query position t and key
 // position s.
@@ -392,7 +392,8 @@ __global__ __launch_bounds__(256) void probe_prefill_kernel(int T, int pos_offse
       for (int r = 0; r < 16; ++r) {
         const int s = lane_key(k0, kb, r, lane);
         const bool acc = interior || visible(tq, s, window, sliding);
-        if (acc && tq < q1 && s < n_keys) visit[(int64_t)(tq - pos_offset) * n_keys + s] = 1;
+        // one lane owns each (query, key) pair, so the count has no race
+        if (acc && tq < q1 && s < n_keys) ++visit[(int64_t)(tq - pos_offset) * n_keys + s];
       }
   }
 }

@@ -335,10 +335,10 @@ int olmo3_abi_version(void);
  * the decode kernel's own split / row enumeration, and record what those
  * visit, so that indexing can be compared bit for bit with the oracle.  */
 
-/* visit [T][pos_offset + T] uint8 (device): entry (t, s) is set to 1 for
- * every pair of query position pos_offset + t and key position s that the
- * d = 128 bf16 prefill kernel would accumulate, 0 elsewhere (the probe
- * clears it first).  T <= 4096, pos_offset + T <= 8192.
+/* visit [T][pos_offset + T] uint8 (device): entry (t, s) counts how many
+ * times the d = 128 bf16 prefill kernel would accumulate the pair of query
+ * position pos_offset + t and key position s (1 for every visible pair when
+ * each is taken once; the probe clears the table first).  T <= 4096, pos_offset + T <= 8192.
  * Errors: INVALID_ARG, UNSUPPORTED. */
 int olmo3_probe_prefill_visits(int T, int64_t pos_offset, int window, int layer_type,
                                uint8_t* visit, void* stream);
