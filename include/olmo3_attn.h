@@ -63,7 +63,7 @@ extern "C" {
 typedef enum olmo3_status {
   OLMO3_OK = 0,
   OLMO3_ERR_INVALID_ARG = 1, /* bad size, null or overlapping pointer, bad enum   */
-  OLMO3_ERR_UNSUPPORTED = 2, /* valid request this build does not implement       */
+  OLMO3_ERR_UNSUPPORTED = 2, /* valid request the library does not implement      */
   OLMO3_ERR_CAPACITY = 3,    /* cache too small, or ring size != window            */
   OLMO3_ERR_HIP = 4,         /* a HIP call or kernel launch failed                 */
   OLMO3_ERR_WORKSPACE = 5    /* workspace null or smaller than olmo3_workspace_bytes */
