@@ -57,6 +57,14 @@ int check_common(int B, int T, int H, int G, int d, int window, int layer_type, 
   return OLMO3_OK;
 }
 
+// A cache of more than 2^50 bytes cannot be allocated on any device; larger
+// claimed capacities are refused before their byte sizes could overflow.
+bool cache_size_ok(int64_t n_rows_blocks, int64_t cap, int d, size_t es) {
+  const unsigned __int128 bytes = (unsigned __int128)n_rows_blocks * (unsigned __int128)cap *
+                                  (unsigned __int128)d * es;
+  return bytes <= ((unsigned __int128)1 << 50);
+}
+
 int check_capacity(int layer_type, int window, int64_t cap, int64_t last_pos) {
   if (cap < 1) return OLMO3_ERR_CAPACITY;
   if (layer_type == OLMO3_LAYER_SLIDING) return cap == window ? OLMO3_OK : OLMO3_ERR_CAPACITY;
@@ -164,6 +172,7 @@ int kv_append_impl(int B, int T, int G, int d, int window, int layer_type,
   st = check_capacity(layer_type, window, cache_capacity, pos_offset + T - 1);
   if (st) return st;
   const size_t es = elem_size(dtype), ces = cf.e4m3 ? 1 : es;
+  if (!cache_size_ok((int64_t)B * G, cache_capacity, d, ces)) return OLMO3_ERR_UNSUPPORTED;
   const Span kc = span(k_cache, (size_t)B * G * cache_capacity * d * ces);
   const Span vc = span(v_cache, (size_t)B * G * cache_capacity * d * ces);
   const Span in[] = {span(k_pre, (size_t)B * T * G * d * es), span(v, (size_t)B * T * G * d * es),
@@ -276,6 +285,7 @@ static int validate_attn(int B, int T, int H, int G, int d, int window, int laye
   const size_t es = elem_size(dtype);
   if (cache_B < 1 || (int64_t)cache_B * G > 65535 * 64) return OLMO3_ERR_INVALID_ARG;
   const size_t ces = cache_es ? cache_es : es;
+  if (!cache_size_ok((int64_t)cache_B * G, cache_capacity, d, ces)) return OLMO3_ERR_UNSUPPORTED;
   const Span kc = span(k_cache, (size_t)cache_B * G * cache_capacity * d * ces);
   const Span vc = span(v_cache, (size_t)cache_B * G * cache_capacity * d * ces);
   const Span o = span(out, (size_t)B * T * H * d * es);
@@ -815,6 +825,7 @@ int olmo3_probe_decode_reads(int B, int H, int G, int d, int window, int layer_t
   if (layer_type != OLMO3_LAYER_SLIDING && layer_type != OLMO3_LAYER_FULL) return OLMO3_ERR_INVALID_ARG;
   int st = check_capacity(layer_type, window, cache_capacity, pos);
   if (st) return st;
+  if (!cache_size_ok(1, cache_capacity, 1, sizeof(int32_t))) return OLMO3_ERR_UNSUPPORTED;
   const bool sliding = layer_type == OLMO3_LAYER_SLIDING;
   DecodeArgs a = {};
   a.cap = cache_capacity;

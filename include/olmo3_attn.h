@@ -120,7 +120,8 @@ size_t olmo3_workspace_bytes(int mode, int B, int T, int H, int G, int d,
  * [B][T][G*d].  Errors: INVALID_ARG (sizes <= 0, odd d, pos_offset < 0, bad
  * enum, null pointer, k_cache/v_cache overlapping each other or an input),
  * CAPACITY (ring size != window, or a linear cache shorter than
- * pos_offset + T), UNSUPPORTED (d not in {16, 32, 64, 128}). */
+ * pos_offset + T), UNSUPPORTED (d not in {16, 32, 64, 128}, or a
+ * cache_capacity that makes a cache larger than 2^50 bytes). */
 int olmo3_kv_append(int B, int T, int G, int d, int window, int layer_type,
                     const olmo3_rope* rope, float eps, int64_t pos_offset,
                     int dtype, const void* k_pre, const void* v,

@@ -139,6 +139,8 @@ def prefill_call(**kw):
     (dict(layer_type=1, cap=100, pos_offset=40), A.ERR_CAPACITY),  # chunk past a linear cache
     (dict(pos_offset=(1 << 30) - 63), A.ERR_UNSUPPORTED),  # positions past 2^30
     (dict(H=40 * 8, G=8), A.ERR_UNSUPPORTED),  # too many heads for one wavefront's norm
+    (dict(layer_type=1, cap=1 << 45), A.ERR_UNSUPPORTED),  # cache past 2^50 bytes
+    (dict(layer_type=1, cap=(1 << 62) + 1), A.ERR_UNSUPPORTED),  # byte size would wrap 64 bits
 ])
 def test_prefill_rejects(kw, status):
     assert prefill_call(**kw) == status
@@ -161,6 +163,7 @@ def decode_call(**kw):
     (dict(layer_type=1, cap=100), A.ERR_CAPACITY),  # needs pos + 1 slots
     (dict(ws_bytes=16), A.ERR_WORKSPACE),
     (dict(H=5, G=2), A.ERR_INVALID_ARG),
+    (dict(layer_type=1, cap=(1 << 62) + 1), A.ERR_UNSUPPORTED),  # byte size would wrap 64 bits
 ])
 def test_decode_rejects(kw, status):
     assert decode_call(**kw) == status
@@ -183,6 +186,7 @@ def append_call(**kw):
     (dict(layer_type=0, cap=8), A.ERR_CAPACITY),
     (dict(k_cache=fake(0)), A.ERR_INVALID_ARG),  # cache overlaps an input
     (dict(d=24), A.ERR_UNSUPPORTED),
+    (dict(cap=(1 << 62) + 1), A.ERR_UNSUPPORTED),  # byte size would wrap 64 bits
 ])
 def test_append_rejects(kw, status):
     assert append_call(**kw) == status
@@ -197,6 +201,8 @@ def test_probe_rejects():
     assert L.olmo3_probe_decode_reads(1, 1, 1, 64, 4, 0, 0, 3, 4, fake(0), None) == A.ERR_INVALID_ARG
     assert L.olmo3_probe_decode_reads(1, 3, 2, 128, 4, 0, 0, 3, 4, fake(0), None) == A.ERR_INVALID_ARG
     assert L.olmo3_probe_decode_reads(1, 2, 1, 128, 4, 0, 1, 3, 4, fake(0), None) == A.ERR_INVALID_ARG
+    assert L.olmo3_probe_decode_reads(1, 1, 1, 128, 4, 1, 0, 3, (1 << 62) + 1, fake(0),
+                                      None) == A.ERR_UNSUPPORTED
     assert L.olmo3_probe_decode_reads(1, 1, 1, 128, 4, 0, 0, 3, 5, fake(0), None) == A.ERR_CAPACITY
 
 
