@@ -140,6 +140,15 @@ WORKLOADS = {
                     decode=dict(B=32, H=32, G=32, L=65536, e4m3=True)),
     "decode-stack-e4m3": dict(name="olmo3-7b-decode-stack-e4m3", prefill=None,
                               decode=dict(B=16, H=32, G=32, L=65536, layers=32, e4m3=True)),
+    # one GPU's share when a layer's heads are spread over 8 GPUs (4 of the
+    # 7B's 32 key/value heads; 1 of the 32B's 8 with its 5 query heads); the
+    # QK-norm statistic then covers the local heads only, where a sharded
+    # model would add the other GPUs' sums of squares (an all-reduce of one
+    # value per token), so these time the kernels, not the whole layer
+    "7b-shard": dict(name="olmo3-7b-head-shard-of-8", prefill=dict(B=1, T=8192, H=4, G=4),
+                     decode=dict(B=32, H=4, G=4, L=65536)),
+    "32b-shard": dict(name="olmo3-32b-head-shard-of-8", prefill=dict(B=1, T=8192, H=5, G=1),
+                      decode=dict(B=64, H=5, G=1, L=32768)),
 }
 E4M3_SCALES = (1.0 / 16, 1.0 / 16)  # k_scale, v_scale of the e4m3 workload
 N_LAYERS_7B = 32
