@@ -18,7 +18,7 @@ from . import LAYER_FULL, LAYER_SLIDING  # noqa: F401  (re-exported)
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libolmo3attn.so")
 
-ABI_VERSION = 8  # OLMO3_ABI_VERSION of include/olmo3_attn.h
+ABI_VERSION = 9  # OLMO3_ABI_VERSION of include/olmo3_attn.h
 DTYPE_BF16, DTYPE_F32, DTYPE_BF16_E4M3 = 0, 1, 2
 MODE_PREFILL, MODE_DECODE = 0, 1
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_CAPACITY, ERR_HIP, ERR_WORKSPACE = range(6)
@@ -135,7 +135,7 @@ def lib() -> ctypes.CDLL:
         L.olmo3_status_string.restype = ctypes.c_char_p
         L.olmo3_abi_version.argtypes = []
         L.olmo3_abi_version.restype = _i
-        L.olmo3_probe_prefill_visits.argtypes = [_i, _i64, _i, _i, _p, _p]
+        L.olmo3_probe_prefill_visits.argtypes = [_i, _i64, _i, _i, _i, _p, _p]
         L.olmo3_probe_prefill_visits.restype = _i
         L.olmo3_probe_decode_reads.argtypes = [_i, _i, _i, _i, _i, _i, _i, _i64, _i64, _p, _p]
         L.olmo3_probe_decode_reads.restype = _i
@@ -426,13 +426,13 @@ def workspace(mode: int, B: int, T: int, H: int, G: int, d: int, layer_type: int
 
 
 def olmo3_probe_prefill_visits(T: int, window: int, layer_type: int, pos_offset: int = 0,
-                               device="cuda") -> torch.Tensor:
+                               kv_splits: int = 1, device="cuda") -> torch.Tensor:
     """[T, pos_offset + T] uint8 table: how many times the prefill kernel
-    accumulates each (query, key position) pair, for queries at pos_offset ..
-    pos_offset + T - 1."""
+    (with kv_splits workgroups per query block) accumulates each (query, key
+    position) pair, for queries at pos_offset .. pos_offset + T - 1."""
     visit = torch.empty((T, pos_offset + T), dtype=torch.uint8, device=device)
-    st = lib().olmo3_probe_prefill_visits(T, pos_offset, window, layer_type, _ptr(visit, "visit"),
-                                          _stream(None, visit.device))
+    st = lib().olmo3_probe_prefill_visits(T, pos_offset, window, layer_type, kv_splits,
+                                          _ptr(visit, "visit"), _stream(None, visit.device))
     _check(st, "olmo3_probe_prefill_visits")
     return visit
 

@@ -108,11 +108,31 @@ bool decode_uses_split(int dtype, int d, int H, int G) {
 
 // Rotated queries, plus rotated keys where the attention cannot read them
 // from the cache: a ring shorter than the call, or an e4m3 cache.
-size_t prefill_ws(int B, int T, int H, int G, int d, int layer_type, int dtype) {
+size_t prefill_ws_base(int B, int T, int H, int G, int d, int layer_type, int dtype) {
   const size_t es = elem_size(dtype);
   size_t bytes = align_up((size_t)B * T * H * d * es);
   if (layer_type == OLMO3_LAYER_SLIDING || dtype == OLMO3_DTYPE_BF16_E4M3)
     bytes += align_up((size_t)B * G * T * d * es);
+  return bytes;
+}
+
+// Key splits of a uniform prefill without a prefix: two when the grid of
+// query blocks x heads x sequences would not give every CU two workgroups.
+// A sliding layer's blocks carry equal work, so there the split pays only
+// while the doubled grid still runs in one round; a full layer's blocks
+// differ in length, and halving the longest ones shortens the last round.
+int prefill_kv_splits(int B, int T, int H, int d, int dtype, int layer_type) {
+  const int64_t blocks = (int64_t)((T + pf::kBQ - 1) / pf::kBQ) * H * B;
+  if (!use_mfma(dtype, d) || blocks >= pf::kSplitBelowBlocks) return 1;
+  if (layer_type == OLMO3_LAYER_SLIDING && blocks * pf::kKvSplits > pf::kSplitBelowBlocks) return 1;
+  return pf::kKvSplits;
+}
+
+// ... plus, for such grids, the partial states of the splits (after the rest).
+size_t prefill_ws(int B, int T, int H, int G, int d, int layer_type, int dtype) {
+  size_t bytes = prefill_ws_base(B, T, H, G, d, layer_type, dtype);
+  const int splits = prefill_kv_splits(B, T, H, d, dtype, layer_type);
+  if (splits > 1) bytes += align_up((size_t)B * T * H * splits * (d + 2) * sizeof(float));
   return bytes;
 }
 
@@ -459,8 +479,26 @@ int prefill_impl(int phases, const PrefillShape& sh, int H, int G, int d, int wi
   a.seq_pos = sh.pos_offsets;
   a.n_rows = N;
   a.key_limit = sliding ? kMaxPrefillPositions : cache_capacity;
+  // split key ranges for small uniform grids; not with a prefix source or
+  // packed rows (their instances keep one workgroup per query block)
+  a.kv_splits = packed || a.kp ? 1 : prefill_kv_splits(B, T, H, d, dtype, layer_type);
+  // partial states after the rotated queries and (if there) keys; calls that
+  // split have neither a prefix nor packed rows, so no staged copy follows
+  if (a.kv_splits > 1)
+    a.part = (float*)(ws + align_up((size_t)N * H * d * es) +
+                      (kv_from_ws ? align_up((size_t)B * G * T * d * es) : 0));
   st = hip_status(use_mfma(dtype, d) ? launch_prefill_mfma(a, s)
                                      : launch_attn_generic(a, dtype, d, s));
+  if (!st && a.kv_splits > 1) {
+    // one merge row per (query row, head)
+    DecodeArgs m = {};
+    m.part = a.part;
+    m.out = out;
+    m.B = (int)N;
+    m.H = H;
+    m.splits = a.kv_splits;
+    st = hip_status(launch_decode_merge(m, s));
+  }
   if (st || !ring_after) return st;
   // store the chunk's kept positions in the ring (keys normalised and rotated
   // again from k_pre: the same arithmetic, so the same bits)
@@ -809,12 +847,13 @@ int olmo3_attn_decode_e4m3(int B, int H, int G, int d, int window, int layer_typ
 }
 
 int olmo3_probe_prefill_visits(int T, int64_t pos_offset, int window, int layer_type,
-                               uint8_t* visit, void* stream) {
+                               int kv_splits, uint8_t* visit, void* stream) {
   if (T < 1 || pos_offset < 0 || window < 1 || !visit) return OLMO3_ERR_INVALID_ARG;
+  if (kv_splits != 1 && kv_splits != pf::kKvSplits) return OLMO3_ERR_INVALID_ARG;
   if (T > 4096 || pos_offset + T > 8192) return OLMO3_ERR_UNSUPPORTED;
   if (layer_type != OLMO3_LAYER_SLIDING && layer_type != OLMO3_LAYER_FULL) return OLMO3_ERR_INVALID_ARG;
-  return hip_status(launch_probe_prefill(T, pos_offset, window, layer_type == OLMO3_LAYER_SLIDING, visit,
-                                         (hipStream_t)stream));
+  return hip_status(launch_probe_prefill(T, pos_offset, window, layer_type == OLMO3_LAYER_SLIDING,
+                                         kv_splits, visit, (hipStream_t)stream));
 }
 
 int olmo3_probe_decode_reads(int B, int H, int G, int d, int window, int layer_type, int dtype,

@@ -109,6 +109,12 @@ struct AttnArgs {
   int64_t key_limit;
   int main_packed;  // packed batch: main rows are the sequence's packed rows
                     // (main_pos0 = its first position) instead of b*k_sb rows
+  // kv_splits > 1 (uniform batches without a prefix only): each query block's
+  // key tiles are split over kv_splits workgroups, which write unnormalised
+  // partial states part[((row*H + h)*kv_splits + split)*(d+2) ..] = (m, l,
+  // o[d]) instead of out; the decode merge kernel then combines them.
+  float* part;
+  int kv_splits;
 };
 
 // Flash-style prefill, d = 128, bf16, MFMA.  Requires n_keys == q_pos0 + Tq
@@ -149,7 +155,7 @@ hipError_t launch_decode_split(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t s);
 
 // Probes: the prefill kernel's tile walk and the decode kernel's row walk.
-hipError_t launch_probe_prefill(int T, int64_t pos_offset, int window, int sliding,
+hipError_t launch_probe_prefill(int T, int64_t pos_offset, int window, int sliding, int kv_splits,
                                 uint8_t* visit, hipStream_t s);
 hipError_t launch_probe_decode(const DecodeArgs& a, int32_t* count, hipStream_t s);
 

@@ -83,7 +83,9 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const char* p) {
 // sliding layer); without it every key is a main row (main_pos0 == 0).
 // kPacked: sequences of different lengths and offsets packed row after row
 // (cu_seqlens, seq_pos); a workgroup past its sequence's end exits.
-template <bool kPrefix, bool kPacked>
+// kSplit (neither of the others): kKvSplits workgroups per query block, each
+// taking a contiguous share of its key tiles and writing a partial state.
+template <bool kPrefix, bool kPacked, bool kSplit = false>
 __global__ __launch_bounds__(256, 2) void prefill_d128_kernel(AttnArgs a) {
   using namespace pf;
   __shared__ __attribute__((aligned(16))) char smem[4 * kTileBytes];
@@ -91,7 +93,9 @@ __global__ __launch_bounds__(256, 2) void prefill_d128_kernel(AttnArgs a) {
   char* const sV = smem + 2 * kTileBytes;  // V ring: 2 x 16 KiB
 
   const int n_qblk = (a.Tq + kBQ - 1) / kBQ;
-  const Work w = work_of(blockIdx.x, gridDim.x, n_qblk, a.H);
+  int split = 0;
+  const Work w = kSplit ? work_of_split(blockIdx.x, gridDim.x, n_qblk, a.H, split)
+                        : work_of(blockIdx.x, gridDim.x, n_qblk, a.H);
   const int g = w.h / (a.H / a.G);
   // this sequence: query rows row0 .. row0 + len - 1 at positions qpos0 ..,
   // keys at positions 0 .. n_keys - 1
@@ -124,6 +128,9 @@ __global__ __launch_bounds__(256, 2) void prefill_d128_kernel(AttnArgs a) {
   int kt0, kt1, i0, i1;
   key_tiles(q0, q1, a.window, a.sliding, kt0, kt1);
   interior_tiles(q0, q1, a.window, a.sliding, kt0, kt1, i0, i1);
+  // this workgroup's tiles [kta, ktb): all of them, or its split's share
+  int kta = kt0, ktb = kt1;
+  if constexpr (kSplit) split_tiles(kt0, kt1, split, kta, ktb);
 
   // Direct loads: instruction i of wavefront w fills tile rows 16 i + 4 w ..
   // +3; lane l takes row 16 i + 4 w + l/16, stored column l mod 16, i.e.
@@ -230,7 +237,7 @@ __global__ __launch_bounds__(256, 2) void prefill_d128_kernel(AttnArgs a) {
   f32x16 s0, s1;  // scores of the current tile
 
   // Step of tile kt.  kMask: apply the visibility predicate per element.
-  // kBuf: buffers holding K_kt and V_kt ((kt - kt0) mod 2, known at compile
+  // kBuf: buffers holding K_kt and V_kt ((kt - kta) mod 2, known at compile
   // time so that every LDS offset is an immediate).
   auto step = [&](int kt, auto mask_tag, auto buf_tag) __attribute__((always_inline)) {
     constexpr bool kMask = decltype(mask_tag)::value;
@@ -238,8 +245,8 @@ __global__ __launch_bounds__(256, 2) void prefill_d128_kernel(AttnArgs a) {
     const int k0 = kt * kBK;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (kt + 2 < kt1) load_k(k0 + 2 * kBK, jb);
-    if (kt + 1 < kt1) load_v(k0 + kBK, jb ^ 1);
+    if (kt + 2 < ktb) load_k(k0 + 2 * kBK, jb);
+    if (kt + 1 < ktb) load_v(k0 + kBK, jb ^ 1);
 
     if constexpr (kMask) {
       // key of register r of block kb = k0 + 4*half + kb*32 + 8*(r/4) + r%4,
@@ -333,28 +340,53 @@ __global__ __launch_bounds__(256, 2) void prefill_d128_kernel(AttnArgs a) {
     s1 = n1;
   };
 
-  load_k(kt0 * kBK, 0);
-  load_v(kt0 * kBK, 0);
-  if (kt0 + 1 < kt1) load_k((kt0 + 1) * kBK, 1);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  qk(0, s0, s1);
-  using B0 = std::integral_constant<int, 0>;
-  using B1 = std::integral_constant<int, 1>;
-  auto run = [&](int& kt, int end, auto mask_tag) __attribute__((always_inline)) {
-    if (kt < end && ((kt - kt0) & 1)) step(kt++, mask_tag, B1{});
-    for (; kt + 1 < end; kt += 2) {
-      step(kt, mask_tag, B0{});
-      step(kt + 1, mask_tag, B1{});
-    }
-    if (kt < end) step(kt++, mask_tag, B0{});
-  };
-  int kt = kt0;
-  run(kt, i0, std::true_type{});
-  run(kt, i1, std::false_type{});
-  run(kt, kt1, std::true_type{});
+  // (a split with no tiles skips to its empty partial state)
+  if (!kSplit || kta < ktb) {
+    load_k(kta * kBK, 0);
+    load_v(kta * kBK, 0);
+    if (kta + 1 < ktb) load_k((kta + 1) * kBK, 1);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    qk(0, s0, s1);
+    using B0 = std::integral_constant<int, 0>;
+    using B1 = std::integral_constant<int, 1>;
+    auto run = [&](int& kt, int end, auto mask_tag) __attribute__((always_inline)) {
+      if (kt < end && ((kt - kta) & 1)) step(kt++, mask_tag, B1{});
+      for (; kt + 1 < end; kt += 2) {
+        step(kt, mask_tag, B0{});
+        step(kt + 1, mask_tag, B1{});
+      }
+      if (kt < end) step(kt++, mask_tag, B0{});
+    };
+    int kt = kta;
+    run(kt, kSplit ? min(i0, ktb) : i0, std::true_type{});
+    run(kt, kSplit ? min(i1, ktb) : i1, std::false_type{});
+    run(kt, ktb, std::true_type{});
+  }
 
   lsum += __shfl_xor(lsum, 32, kWave);
+  if constexpr (kSplit) {
+    // partial state (m, l, o[d]) of this query, head and split; lanes l and
+    // l + 32 hold the same m and l and different halves of o
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    if (tq < q1) {
+      float* pp = a.part +
+                  (((row0 + (tq - qpos0)) * a.H + w.h) * kKvSplits + split) * (int64_t)(kD + 2);
+      if (half == 0) {
+        pp[0] = m;
+        pp[1] = lsum;
+      }
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          float* po = pp + 2 + db * 32 + 8 * r4 + 4 * half;
+          *(f32x2*)po = f32x2{o[db][4 * r4], o[db][4 * r4 + 1]};
+          *(f32x2*)(po + 2) = f32x2{o[db][4 * r4 + 2], o[db][4 * r4 + 3]};
+        }
+    }
+    return;
+  }
   const float inv = 1.0f / lsum;
   if (tq < q1) {
     bf16* orow = (bf16*)a.out + ((row0 + (tq - qpos0)) * a.H + w.h) * kD;
@@ -374,18 +406,23 @@ __global__ __launch_bounds__(256, 2) void prefill_d128_kernel(AttnArgs a) {
 // visit[(t - pos_offset) * (pos_offset + T) + s] for query position t and key
 // position s.
 __global__ __launch_bounds__(256) void probe_prefill_kernel(int T, int pos_offset, int window,
-                                                            int sliding, uint8_t* visit) {
+                                                            int sliding, int kv_splits,
+                                                            uint8_t* visit) {
   using namespace pf;
   const int n_qblk = (T + kBQ - 1) / kBQ;
   const int n_keys = pos_offset + T;
-  const Work w = work_of(blockIdx.x, gridDim.x, n_qblk, 1);
+  int split = 0;
+  const Work w = kv_splits > 1 ? work_of_split(blockIdx.x, gridDim.x, n_qblk, 1, split)
+                               : work_of(blockIdx.x, gridDim.x, n_qblk, 1);
   const int q0 = pos_offset + w.qb * kBQ, q1 = min(q0 + kBQ, n_keys);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int tq = lane_query(q0, wave, lane);
   int kt0, kt1, i0, i1;
   key_tiles(q0, q1, window, sliding, kt0, kt1);
   interior_tiles(q0, q1, window, sliding, kt0, kt1, i0, i1);
-  for (int kt = kt0; kt < kt1; ++kt) {
+  int kta = kt0, ktb = kt1;
+  if (kv_splits > 1) split_tiles(kt0, kt1, split, kta, ktb);
+  for (int kt = kta; kt < ktb; ++kt) {
     const int k0 = kt * kBK;
     const bool interior = kt >= i0 && kt < i1;
     for (int kb = 0; kb < 2; ++kb)
@@ -410,18 +447,21 @@ hipError_t launch_prefill_mfma(const AttnArgs& a, hipStream_t s) {
       prefill_d128_kernel<false, true><<<blocks, 256, 0, s>>>(a);
   } else if (a.kp) {
     prefill_d128_kernel<true, false><<<blocks, 256, 0, s>>>(a);
+  } else if (a.kv_splits == pf::kKvSplits) {
+    prefill_d128_kernel<false, false, true><<<blocks * pf::kKvSplits, 256, 0, s>>>(a);
   } else {
     prefill_d128_kernel<false, false><<<blocks, 256, 0, s>>>(a);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_probe_prefill(int T, int64_t pos_offset, int window, int sliding,
+hipError_t launch_probe_prefill(int T, int64_t pos_offset, int window, int sliding, int kv_splits,
                                 uint8_t* visit, hipStream_t s) {
   hipError_t e = hipMemsetAsync(visit, 0, (size_t)T * (size_t)(pos_offset + T), s);
   if (e != hipSuccess) return e;
   const int n_qblk = (T + pf::kBQ - 1) / pf::kBQ;
-  probe_prefill_kernel<<<n_qblk, 256, 0, s>>>(T, (int)pos_offset, window, sliding, visit);
+  probe_prefill_kernel<<<n_qblk * kv_splits, 256, 0, s>>>(T, (int)pos_offset, window, sliding,
+                                                          kv_splits, visit);
   return hipGetLastError();
 }
 

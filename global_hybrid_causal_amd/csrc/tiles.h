@@ -55,17 +55,44 @@ __host__ __device__ __forceinline__ void interior_tiles(int q0, int q1, int wind
   if (i0 > i1) i0 = i1;
 }
 
+// Grids of fewer workgroups than this (two per CU) may split each query
+// block's key tiles over kKvSplits workgroups, whose partial softmax states
+// are then merged, so that the chip holds two workgroups per CU.
+constexpr int kSplitBelowBlocks = 512;
+constexpr int kKvSplits = 2;
+
 struct Work {
   int b, h, qb;
 };
 
-// Workgroup -> (batch, head, query block).  Query blocks of one head sit on
-// one XCD (shared K/V in its L2) and start with the longest causal rows.
-__device__ __forceinline__ Work work_of(int bid, int nblk, int n_qblk, int H) {
-  const int L = xcd_remap(bid, nblk);
+// Query block L of the remapped order -> (batch, head, query block).
+__device__ __forceinline__ Work work_at(int L, int n_qblk, int H) {
   const int qi = L % n_qblk;
   const int bh = L / n_qblk;
   return Work{bh / H, bh % H, n_qblk - 1 - qi};
+}
+
+// Workgroup -> (batch, head, query block).  Query blocks of one head sit on
+// one XCD (shared K/V in its L2) and start with the longest causal rows.
+__device__ __forceinline__ Work work_of(int bid, int nblk, int n_qblk, int H) {
+  return work_at(xcd_remap(bid, nblk), n_qblk, H);
+}
+
+// With kKvSplits workgroups per query block: workgroup -> block and split
+// (the splits of a block are neighbours in the remapped order, so they share
+// an XCD).
+__device__ __forceinline__ Work work_of_split(int bid, int nblk, int n_qblk, int H, int& split) {
+  const int L = xcd_remap(bid, nblk);
+  split = L % kKvSplits;
+  return work_at(L / kKvSplits, n_qblk, H);
+}
+
+// Key tiles [kta, ktb) of split `split` of the block's tiles [kt0, kt1).
+__host__ __device__ __forceinline__ void split_tiles(int kt0, int kt1, int split, int& kta,
+                                                     int& ktb) {
+  const int n = kt1 - kt0;
+  kta = kt0 + n * split / kKvSplits;
+  ktb = kt0 + n * (split + 1) / kKvSplits;
 }
 
 // Query of a lane: wavefront w owns 32 consecutive queries; lanes l and

@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define OLMO3_ABI_VERSION 8
+#define OLMO3_ABI_VERSION 9
 
 typedef enum olmo3_status {
   OLMO3_OK = 0,
@@ -110,7 +110,11 @@ int olmo3_layer_type(int layer, int n_layers);
  * figure covers every position that fits `cache_capacity`.  With e4m3 caches
  * (dtype OLMO3_DTYPE_BF16_E4M3) the prefill figure includes a bf16 copy of
  * `cache_capacity` cache rows, which chunks at pos_offset > 0 need; a first
- * chunk may pass cache_capacity = 0.  Returns 0 for invalid sizes. */
+ * chunk may pass cache_capacity = 0.  For d = 128 bf16 calls whose query
+ * blocks of 128 rows times H times B number fewer than 512 (full layers) or
+ * at most 256 (sliding layers), the prefill figure also holds the partial
+ * softmax states of a two-way split of every block's keys (B*T*H*2*(d+2)
+ * floats), which such calls use.  Returns 0 for invalid sizes. */
 size_t olmo3_workspace_bytes(int mode, int B, int T, int H, int G, int d,
                              int layer_type, int dtype, int64_t cache_capacity);
 
@@ -339,10 +343,12 @@ int olmo3_abi_version(void);
 /* visit [T][pos_offset + T] uint8 (device): entry (t, s) counts how many
  * times the d = 128 bf16 prefill kernel would accumulate the pair of query
  * position pos_offset + t and key position s (1 for every visible pair when
- * each is taken once; the probe clears the table first).  T <= 4096, pos_offset + T <= 8192.
+ * each is taken once; the probe clears the table first).  kv_splits 1: one
+ * workgroup per query block; 2: the key-split instance (both workgroups of
+ * a block counted together).  Any other kv_splits: INVALID_ARG.  T <= 4096, pos_offset + T <= 8192.
  * Errors: INVALID_ARG, UNSUPPORTED. */
 int olmo3_probe_prefill_visits(int T, int64_t pos_offset, int window, int layer_type,
-                               uint8_t* visit, void* stream);
+                               int kv_splits, uint8_t* visit, void* stream);
 
 /* count [cache_capacity] int32 (device): number of times the decode kernel
  * at position `pos` reads each cache slot of one (sequence, KV head) into

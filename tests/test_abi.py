@@ -43,7 +43,7 @@ def test_header_binding_and_library_versions_agree():
 
 
 def test_abi_version():
-    assert A.olmo3_abi_version() == A.ABI_VERSION == 8
+    assert A.olmo3_abi_version() == A.ABI_VERSION == 9
 
 
 def test_layer_type_matches_oracle_bit_exact():
@@ -59,6 +59,23 @@ def test_status_strings():
     for s in range(6):
         assert A.status_string(s)
     assert A.status_string(99) == "unknown status"
+
+
+def test_workspace_bytes_split_partials():
+    """Full layers with fewer than 512 query blocks x heads x sequences, and
+    sliding layers with at most 256, reserve two partial states (d + 2
+    floats) per query row and head; larger grids none."""
+    ws = A.olmo3_workspace_bytes
+    q = 8192 * 4 * 128 * 2  # rotated queries, H = 4
+    assert ws(A.MODE_PREFILL, 1, 8192, 4, 4, 128, 1, 0, 8192) >= q + 8192 * 4 * 2 * 130 * 4
+    assert ws(A.MODE_PREFILL, 1, 8192, 8, 8, 128, 1, 0, 8192) < 2 * (2 * q)   # 512 blocks: none
+    assert ws(A.MODE_PREFILL, 1, 8192, 8, 8, 128, 1, 0, 8192) >= 2 * q
+    assert ws(A.MODE_PREFILL, 1, 64, 2, 1, 16, 1, 1, 64) == 64 * 2 * 16 * 4  # fp32 path: none
+    # sliding layers split only while the doubled grid fits one round (<= 256 blocks)
+    q5, k1 = 8192 * 5 * 128 * 2, 8192 * 1 * 128 * 2
+    assert ws(A.MODE_PREFILL, 1, 8192, 5, 1, 128, 0, 0, 4096) == q5 + k1   # 320 blocks
+    assert ws(A.MODE_PREFILL, 1, 8192, 5, 1, 128, 1, 0, 8192) > q5          # full layer splits
+    assert ws(A.MODE_PREFILL, 1, 8192, 4, 4, 128, 0, 0, 4096) > 2 * q       # 256 blocks: splits
 
 
 def test_workspace_bytes():
@@ -194,10 +211,12 @@ def test_append_rejects(kw, status):
 
 def test_probe_rejects():
     L = A.lib()
-    assert L.olmo3_probe_prefill_visits(0, 0, 4, 0, fake(0), None) == A.ERR_INVALID_ARG
-    assert L.olmo3_probe_prefill_visits(5, -1, 4, 0, fake(0), None) == A.ERR_INVALID_ARG
-    assert L.olmo3_probe_prefill_visits(5000, 0, 4, 0, fake(0), None) == A.ERR_UNSUPPORTED
-    assert L.olmo3_probe_prefill_visits(100, 8100, 4, 0, fake(0), None) == A.ERR_UNSUPPORTED
+    assert L.olmo3_probe_prefill_visits(0, 0, 4, 0, 1, fake(0), None) == A.ERR_INVALID_ARG
+    assert L.olmo3_probe_prefill_visits(5, -1, 4, 0, 1, fake(0), None) == A.ERR_INVALID_ARG
+    assert L.olmo3_probe_prefill_visits(5000, 0, 4, 0, 1, fake(0), None) == A.ERR_UNSUPPORTED
+    assert L.olmo3_probe_prefill_visits(100, 8100, 4, 0, 1, fake(0), None) == A.ERR_UNSUPPORTED
+    for bad in (0, 3, 4):
+        assert L.olmo3_probe_prefill_visits(5, 0, 4, 0, bad, fake(0), None) == A.ERR_INVALID_ARG
     assert L.olmo3_probe_decode_reads(1, 1, 1, 64, 4, 0, 0, 3, 4, fake(0), None) == A.ERR_INVALID_ARG
     assert L.olmo3_probe_decode_reads(1, 3, 2, 128, 4, 0, 0, 3, 4, fake(0), None) == A.ERR_INVALID_ARG
     assert L.olmo3_probe_decode_reads(1, 2, 1, 128, 4, 0, 1, 3, 4, fake(0), None) == A.ERR_INVALID_ARG

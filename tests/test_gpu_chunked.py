@@ -111,8 +111,10 @@ def test_chunks_equal_one_prefill(lt, chunks):
 @pytest.mark.parametrize("T,P", [(1, 1), (5, 64), (64, 64), (127, 300), (300, 129), (1000, 4096),
                                  (200, 4000), (4096, 4096)])
 @pytest.mark.parametrize("window", [1, 63, 100, 128, 4096])
-def test_probe_prefill_visits_with_offset(T, P, window):
+@pytest.mark.parametrize("splits", [1, 2])
+def test_probe_prefill_visits_with_offset(T, P, window, splits):
     for lt in (0, 1):
-        got = A.olmo3_probe_prefill_visits(T, window, lt, pos_offset=P).cpu().numpy()
+        got = A.olmo3_probe_prefill_visits(T, window, lt, pos_offset=P,
+                                           kv_splits=splits).cpu().numpy()
         want = O.mask_at_positions(P + np.arange(T), np.arange(P + T), KINDS[lt], window)
         assert np.array_equal(got, want), (T, P, window, lt, np.argwhere(got != want)[:5])

@@ -167,7 +167,11 @@ def test_ragged_prefill_vs_oracle(case):
 
 @pytest.mark.parametrize("lt", [0, 1])
 def test_ragged_prefill_equal_lengths_is_uniform_prefill(lt):
-    B, T, H, G, d, w = 3, 200, 8, 4, 128, 64
+    """32 sequences of 200 rows x 8 heads are 512 query blocks x heads, so
+    the uniform call keeps one workgroup per block (smaller grids split the
+    keys and merge, which sums in another order) like the packed one: the
+    two must agree bit for bit."""
+    B, T, H, G, d, w = 32, 200, 8, 4, 128, 64
     rope = A.Rope(theta=500000.0, yarn=True)
     cap = w if lt == 0 else T
     x = inputs(59, lt, B, T, H, G, d, BF16)

@@ -220,13 +220,15 @@ def test_kv_append(lt, T, pos_offset, cap):
 
 
 # ----------------------------------------------------------------- probes
+@pytest.mark.parametrize("splits", [1, 2])
 @pytest.mark.parametrize("T", [1, 5, 64, 127, 128, 129, 300, 1000, 4096])
 @pytest.mark.parametrize("window", [1, 2, 63, 64, 100, 128, 4096])
-def test_probe_prefill_visits_bit_exact(T, window):
+def test_probe_prefill_visits_bit_exact(T, window, splits):
     """Every visible pair is accumulated exactly once (counts, not flags:
-    a tile taken twice reads 2), and no other pair."""
+    a tile taken twice, or by both workgroups of a split block, reads 2),
+    and no other pair."""
     for lt in (0, 1):
-        got = A.olmo3_probe_prefill_visits(T, window, lt).cpu().numpy()
+        got = A.olmo3_probe_prefill_visits(T, window, lt, kv_splits=splits).cpu().numpy()
         want = O.sliding_window_mask(T, window) if lt == 0 else O.causal_mask(T)
         assert np.array_equal(got, want), (T, window, lt, np.argwhere(got != want)[:5])
 
