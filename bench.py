@@ -68,14 +68,14 @@ def decode_kernel(H: int, G: int, e4m3: bool) -> str:
 
 
 MEASURED_TRAFFIC = {
-    ("olmo3-7b-layer", "prefill_sliding_l0"): dict(bytes=700297143, sources="3bc9cbd506cb2b68"),
-    ("olmo3-7b-layer", "prefill_full_l3"): dict(bytes=283572083, sources="3bc9cbd506cb2b68"),
-    ("olmo3-7b-layer", "decode_sliding"): dict(bytes=2148099723, sources="1bb78d08d293ba50"),
-    ("olmo3-7b-layer", "decode_full"): dict(bytes=34359461924, sources="1bb78d08d293ba50"),
-    ("olmo3-32b-layer", "prefill_sliding_l0"): dict(bytes=320268918, sources="3bc9cbd506cb2b68"),
-    ("olmo3-32b-layer", "prefill_full_l3"): dict(bytes=310592412, sources="3bc9cbd506cb2b68"),
-    ("olmo3-32b-layer", "decode_sliding"): dict(bytes=1079251942, sources="1bb78d08d293ba50"),
-    ("olmo3-32b-layer", "decode_full"): dict(bytes=8621789250, sources="1bb78d08d293ba50"),
+    ("olmo3-7b-layer", "prefill_sliding_l0"): dict(bytes=695532543, sources="3bc9cbd506cb2b68"),
+    ("olmo3-7b-layer", "prefill_full_l3"): dict(bytes=301389061, sources="3bc9cbd506cb2b68"),
+    ("olmo3-7b-layer", "decode_sliding"): dict(bytes=2148100278, sources="1bb78d08d293ba50"),
+    ("olmo3-7b-layer", "decode_full"): dict(bytes=34359469838, sources="1bb78d08d293ba50"),
+    ("olmo3-32b-layer", "prefill_sliding_l0"): dict(bytes=321227602, sources="3bc9cbd506cb2b68"),
+    ("olmo3-32b-layer", "prefill_full_l3"): dict(bytes=320242780, sources="3bc9cbd506cb2b68"),
+    ("olmo3-32b-layer", "decode_sliding"): dict(bytes=1079199164, sources="1bb78d08d293ba50"),
+    ("olmo3-32b-layer", "decode_full"): dict(bytes=8621331768, sources="1bb78d08d293ba50"),
 }
 
 
