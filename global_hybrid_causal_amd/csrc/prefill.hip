@@ -249,17 +249,9 @@ __global__ __launch_bounds__(256, 2) void prefill_d128_kernel(AttnArgs a) {
     if (kt + 1 < ktb) load_v(k0 + kBK, jb ^ 1);
 
     if constexpr (kMask) {
-      // key of register r of block kb = k0 + 4*half + kb*32 + 8*(r/4) + r%4,
-      // visible iff rel - window < offset <= rel (the lower bound only on
-      // sliding layers)
-      const int rel = tq - k0 - 4 * half;
-      const int lo = a.sliding ? rel - a.window : INT_MIN;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int c0 = 8 * (r >> 2) + (r & 3), c1 = 32 + c0;
-        s0[r] = ((c0 <= rel) & (c0 > lo)) ? s0[r] : -INFINITY;
-        s1[r] = ((c1 <= rel) & (c1 > lo)) ? s1[r] : -INFINITY;
-      }
+      // the two 32-key blocks of the tile start at k0 and k0 + 32
+      mask_block(s0, tq, k0, lane, a.window, a.sliding);
+      mask_block(s1, tq, k0 + 32, lane, a.window, a.sliding);
     }
     // tile maximum: a max3 tree (depth 4), then the partner lane (l ^ 32)
     float t1[12];
@@ -402,7 +394,7 @@ __global__ __launch_bounds__(256, 2) void prefill_d128_kernel(AttnArgs a) {
 }
 
 // Counts every (query, key) pair the kernel above accumulates: the same
-// work mapping, tile runs, lane -> (query, key) map and predicate.
+// work mapping, tile runs, lane -> (query, key) map and mask function.
 // visit[(t - pos_offset) * (pos_offset + T) + s] for query position t and key
 // position s.
 __global__ __launch_bounds__(256) void probe_prefill_kernel(int T, int pos_offset, int window,
@@ -425,13 +417,17 @@ __global__ __launch_bounds__(256) void probe_prefill_kernel(int T, int pos_offse
   for (int kt = kta; kt < ktb; ++kt) {
     const int k0 = kt * kBK;
     const bool interior = kt >= i0 && kt < i1;
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 2; ++kb) {
+      // the kernel's own masking of this block (interior tiles unmasked)
+      f32x16 sc;
+      for (int r = 0; r < 16; ++r) sc[r] = 0.f;
+      if (!interior) mask_block(sc, tq, k0 + 32 * kb, lane, window, sliding);
       for (int r = 0; r < 16; ++r) {
         const int s = lane_key(k0, kb, r, lane);
-        const bool acc = interior || visible(tq, s, window, sliding);
         // one lane owns each (query, key) pair, so the count has no race
-        if (acc && tq < q1 && s < n_keys) ++visit[(int64_t)(tq - pos_offset) * n_keys + s];
+        if (sc[r] == 0.f && tq < q1 && s < n_keys) ++visit[(int64_t)(tq - pos_offset) * n_keys + s];
       }
+    }
   }
 }
 

@@ -3,6 +3,9 @@
 // visit.
 #pragma once
 
+#include <limits.h>
+#include <math.h>
+
 #include "common.h"
 
 namespace olmo3 {
@@ -19,6 +22,27 @@ constexpr int kQW = 32;     // queries per wavefront
 // sliding layers.
 __host__ __device__ __forceinline__ bool visible(int t, int s, int window, int sliding) {
   return s <= t && (!sliding || t - s < window);
+}
+
+// Applies the visibility predicate to one 32x32 block of scores in the
+// v_mfma_f32_32x32x16 output layout (row = key, column = query): register r
+// of a lane holds key kb0 + 8*(r/4) + 4*(lane/32) + r%4 for the lane's query
+// tq, and is set to -inf unless visible(tq, key).  With rel = tq - kb0 -
+// 4*(lane/32) and the key offset c = 8*(r/4) + r%4, tq - key = rel - c, so
+// the key is visible iff 0 <= rel - c (and rel - c < window on sliding
+// layers).  The prefill kernel and its probe both mask through this function.
+__host__ __device__ __forceinline__ void mask_block(f32x16& s, int tq, int kb0, int lane,
+                                                    int window, int sliding) {
+  const int rel = tq - kb0 - 4 * (lane >> 5);
+  // positions stay below 2^30: a window at least that wide is a full one;
+  // then rel - c < w is the visibility test as one unsigned comparison
+  // (negative differences wrap past every window)
+  const unsigned w = sliding && window < (1 << 30) ? (unsigned)window : (1u << 31);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int c = 8 * (r >> 2) + (r & 3);
+    s[r] = (unsigned)(rel - c) < w ? s[r] : -INFINITY;
+  }
 }
 
 // Key tiles [kt0, kt1) that hold any key visible from queries [q0, q1):
