@@ -18,7 +18,7 @@ from . import LAYER_FULL, LAYER_SLIDING  # noqa: F401  (re-exported)
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libolmo3attn.so")
 
-ABI_VERSION = 9  # OLMO3_ABI_VERSION of include/olmo3_attn.h
+ABI_VERSION = 10  # OLMO3_ABI_VERSION of include/olmo3_attn.h
 DTYPE_BF16, DTYPE_F32, DTYPE_BF16_E4M3 = 0, 1, 2
 MODE_PREFILL, MODE_DECODE = 0, 1
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_CAPACITY, ERR_HIP, ERR_WORKSPACE = range(6)
@@ -31,8 +31,11 @@ EXPORTS = (
     "olmo3_attn_decode_phases", "olmo3_attn_prefill_ragged", "olmo3_attn_decode_ragged",
     "olmo3_kv_append_e4m3", "olmo3_attn_prefill_e4m3", "olmo3_attn_decode_e4m3",
     "olmo3_attn_decode_e4m3_phases", "olmo3_attn_decode_ragged_e4m3",
-    "olmo3_attn_prefill_ragged_e4m3",
+    "olmo3_attn_prefill_ragged_e4m3", "olmo3_attn_decode_noalloc",
 )
+# Size of the library's per-device scratch array that olmo3_attn_decode_noalloc
+# uses in place of a workspace (OLMO3_NOALLOC_SCRATCH_BYTES).
+NOALLOC_SCRATCH_BYTES = 16 << 20
 PHASE_PROLOGUE, PHASE_ATTENTION, PHASE_MERGE = 1, 2, 4
 PHASES_ALL = PHASE_PROLOGUE | PHASE_ATTENTION | PHASE_MERGE
 
@@ -99,6 +102,8 @@ def lib() -> ctypes.CDLL:
         L.olmo3_attn_decode.argtypes = [_i, _i, _i, _i, _i, _i, ctypes.POINTER(RopeStruct), _f, _i64,
                                         _i, _p, _p, _p, _p, _p, _p, _p, _i64, _p, _p, _sz, _p]
         L.olmo3_attn_decode.restype = _i
+        L.olmo3_attn_decode_noalloc.argtypes = L.olmo3_attn_decode.argtypes[:19] + [_p]
+        L.olmo3_attn_decode_noalloc.restype = _i
         L.olmo3_attn_prefill_phases.argtypes = [_i] + L.olmo3_attn_prefill.argtypes
         L.olmo3_attn_prefill_phases.restype = _i
         L.olmo3_attn_decode_phases.argtypes = [_i] + L.olmo3_attn_decode.argtypes
@@ -255,6 +260,24 @@ def olmo3_attn_decode(q_pre, k_pre, v, q_gain, k_gain, k_cache, v_cache, out, wo
         _check(lib().olmo3_attn_decode(*args), "olmo3_attn_decode")
     else:
         _check(lib().olmo3_attn_decode_phases(phases, *args), "olmo3_attn_decode_phases")
+
+
+def olmo3_attn_decode_noalloc(q_pre, k_pre, v, q_gain, k_gain, k_cache, v_cache, out, *,
+                              window: int, layer_type: int, rope: Rope, pos: int,
+                              eps: float = 1e-6, stream=None) -> None:
+    """olmo3_attn_decode without a workspace: the library's per-device
+    scratch array (NOALLOC_SCRATCH_BYTES) stands in for it, and the call
+    allocates nothing.  Calls on one device must not overlap in time."""
+    B, G, cap, d = _cache_dims(k_cache)
+    H = q_pre.shape[-1] // d
+    dt = q_pre.dtype
+    r = rope.to_c()
+    _check(lib().olmo3_attn_decode_noalloc(
+        B, H, G, d, window, layer_type, ctypes.byref(r), eps, pos, _dtype_code(q_pre),
+        _ptr(q_pre, "q_pre", dt), _ptr(k_pre, "k_pre", dt), _ptr(v, "v", dt),
+        _ptr(q_gain, "q_gain", dt), _ptr(k_gain, "k_gain", dt), _ptr(k_cache, "k_cache", dt),
+        _ptr(v_cache, "v_cache", dt), cap, _ptr(out, "out", dt), _stream(stream, q_pre.device)),
+        "olmo3_attn_decode_noalloc")
 
 
 def _i32(t: torch.Tensor | None, name: str, n: int) -> int:

@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "../../include/olmo3_attn.h"
 #include "kernels.h"
@@ -877,6 +878,66 @@ int olmo3_probe_decode_reads(int B, int H, int G, int d, int window, int layer_t
   a.G = G;
   a.fp8 = dtype == OLMO3_DTYPE_BF16_E4M3;
   return hip_status(launch_probe_decode(a, count, (hipStream_t)stream));
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- decode
+// without allocation.  One scratch array per device, in the library's own
+// device memory, stands in for the workspace argument.
+namespace {
+
+constexpr size_t kNoAllocScratchBytes = OLMO3_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+
+// Held by every device the library runs on until the process ends.  Host
+// code never passes this name to a kernel or copy: it stands for a host-side
+// shadow there.  The device address comes from hipGetSymbolAddress.
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// Address of the current device's scratch array, looked up once per device
+// (with that device current) and kept; nullptr when the lookup fails.
+void* device_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+int olmo3_attn_decode_noalloc(int B, int H, int G, int d, int window, int layer_type,
+                              const olmo3_rope* rope, float eps, int64_t pos, int dtype,
+                              const void* q_pre, const void* k_pre, const void* v,
+                              const void* q_gain, const void* k_gain, void* k_cache,
+                              void* v_cache, int64_t cache_capacity, void* out, void* stream) {
+  // argument errors first, before anything touches the device
+  int st = check_common(B, 1, H, G, d, window, layer_type, dtype, rope, eps, pos);
+  if (st) return st;
+  const void* ptrs[] = {q_pre, k_pre, v, q_gain, k_gain, k_cache, v_cache, out};
+  for (const void* p : ptrs)
+    if (!p || !aligned16(p)) return OLMO3_ERR_INVALID_ARG;
+  st = check_capacity(layer_type, window, cache_capacity, pos);
+  if (st) return st;
+  // the scratch takes the workspace's place, so the call must fit in it
+  if (decode_ws(B, H, G, d, layer_type, window, dtype, cache_capacity) > kNoAllocScratchBytes)
+    return OLMO3_ERR_WORKSPACE;
+  // the rest (overlaps, cache size) as olmo3_attn_decode checks it
+  void* ws = device_scratch();
+  if (!ws) return OLMO3_ERR_HIP;
+  return olmo3_attn_decode(B, H, G, d, window, layer_type, rope, eps, pos, dtype, q_pre, k_pre, v,
+                           q_gain, k_gain, k_cache, v_cache, cache_capacity, out, ws,
+                           kNoAllocScratchBytes, stream);
 }
 
 }  // extern "C"

@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define OLMO3_ABI_VERSION 9
+#define OLMO3_ABI_VERSION 10
 
 typedef enum olmo3_status {
   OLMO3_OK = 0,
@@ -170,6 +170,27 @@ int olmo3_attn_decode(int B, int H, int G, int d, int window, int layer_type,
                       void* k_cache, void* v_cache, int64_t cache_capacity,
                       void* out, void* workspace, size_t workspace_bytes,
                       void* stream);
+
+/* For callers that cannot allocate device memory (code under graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): olmo3_attn_decode
+ * with the workspace replaced by a scratch array of
+ * OLMO3_NOALLOC_SCRATCH_BYTES that the library holds in each device's memory
+ * from load until the process ends.  Same arguments, layouts, results (bit
+ * for bit) and errors as olmo3_attn_decode, without workspace and
+ * workspace_bytes; the call makes no allocation.  A call whose
+ * olmo3_workspace_bytes(OLMO3_MODE_DECODE, ...) exceeds
+ * OLMO3_NOALLOC_SCRATCH_BYTES returns OLMO3_ERR_WORKSPACE and does nothing;
+ * OLMO3_ERR_HIP if the scratch address of the current device cannot be
+ * found.  Every call on one device uses that device's one array, and no
+ * state carries from one call to the next: calls on one device that can
+ * overlap in time (two streams, two host threads without ordering) race on
+ * it and must be serialised by the caller. */
+#define OLMO3_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+int olmo3_attn_decode_noalloc(int B, int H, int G, int d, int window, int layer_type,
+                              const olmo3_rope* rope, float eps, int64_t pos, int dtype,
+                              const void* q_pre, const void* k_pre, const void* v,
+                              const void* q_gain, const void* k_gain, void* k_cache,
+                              void* v_cache, int64_t cache_capacity, void* out, void* stream);
 
 /* Ragged batches: several prompts served together ("Olmo-3 End-to-End
  * Implementation", "Next Steps": batch processing), whose sequences differ in

@@ -43,7 +43,7 @@ def test_header_binding_and_library_versions_agree():
 
 
 def test_abi_version():
-    assert A.olmo3_abi_version() == A.ABI_VERSION == 9
+    assert A.olmo3_abi_version() == A.ABI_VERSION == 10
 
 
 def test_layer_type_matches_oracle_bit_exact():
@@ -184,6 +184,51 @@ def decode_call(**kw):
 ])
 def test_decode_rejects(kw, status):
     assert decode_call(**kw) == status
+
+
+def decode_noalloc_call(**kw):
+    a = dict(GOOD, pos=100)
+    a.pop("T")
+    a.update(kw)
+    ptrs = [fake(i) for i in range(8)]
+    for i, n in enumerate(["q_pre", "k_pre", "v", "q_gain", "k_gain", "k_cache", "v_cache", "out"]):
+        if n in kw:
+            ptrs[i] = kw[n]
+    r = ctypes.byref(A.Rope(theta=500000.0).to_c())
+    return A.lib().olmo3_attn_decode_noalloc(
+        a["B"], a["H"], a["G"], a["d"], a["window"], a["layer_type"], r, a["eps"], a["pos"],
+        a["dtype"], *ptrs[:7], a["cap"], ptrs[7], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(pos=-1), A.ERR_INVALID_ARG),
+    (dict(H=5, G=2), A.ERR_INVALID_ARG),
+    (dict(dtype=2), A.ERR_INVALID_ARG),             # e4m3 caches have their own entry points
+    (dict(q_pre=0), A.ERR_INVALID_ARG),
+    (dict(out=fake(7) + 8), A.ERR_INVALID_ARG),     # misaligned
+    (dict(cap=15), A.ERR_CAPACITY),
+    (dict(layer_type=1, cap=100), A.ERR_CAPACITY),  # needs pos + 1 slots
+    # more scratch than the library holds: 1024 sequences x 64 heads of a
+    # 2^17-slot linear cache need about 51 MiB of partial states
+    (dict(B=1024, H=64, G=8, layer_type=1, cap=1 << 17, pos=(1 << 17) - 1), A.ERR_WORKSPACE),
+])
+def test_decode_noalloc_rejects_before_the_device(kw, status):
+    """Every argument error, and a call needing more than the scratch array,
+    returns its status before the device is touched (no GPU here)."""
+    assert decode_noalloc_call(**kw) == status
+
+
+def test_decode_noalloc_scratch_bound_matches_the_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define OLMO3_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == A.NOALLOC_SCRATCH_BYTES
+    B, H, G, d, cap = 1024, 64, 8, 128, 1 << 17
+    assert A.olmo3_workspace_bytes(A.MODE_DECODE, B, 1, H, G, d, 1, A.DTYPE_BF16, cap) > \
+        A.NOALLOC_SCRATCH_BYTES
+    # the 7B and 32B decode batches fit
+    for H, G in ((32, 32), (40, 8)):
+        assert A.olmo3_workspace_bytes(A.MODE_DECODE, 32, 1, H, G, d, 1, A.DTYPE_BF16, 65536) <= \
+            A.NOALLOC_SCRATCH_BYTES
 
 
 def append_call(**kw):
