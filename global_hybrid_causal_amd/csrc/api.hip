@@ -46,7 +46,9 @@ int check_common(int B, int T, int H, int G, int d, int window, int layer_type, 
   if (dtype != OLMO3_DTYPE_BF16 && dtype != OLMO3_DTYPE_F32) return OLMO3_ERR_INVALID_ARG;
   if (!rope || !(rope->theta > 0.0) || !isfinite(rope->theta)) return OLMO3_ERR_INVALID_ARG;
   if (rope->yarn && (!(rope->factor >= 1.0) || rope->orig_ctx < 1 ||
-                     !(rope->beta_fast > rope->beta_slow)))
+                     !(rope->beta_fast > rope->beta_slow) || !(rope->beta_slow > 0.0) ||
+                     !isfinite(rope->beta_fast) || !isfinite(rope->factor) ||
+                     (rope->factor > 1.0 && !(rope->theta > 1.0))))
     return OLMO3_ERR_INVALID_ARG;
   if (!(eps >= 0.0f) || !isfinite(eps)) return OLMO3_ERR_INVALID_ARG;
   if (pos_offset < 0) return OLMO3_ERR_INVALID_ARG;
@@ -78,16 +80,30 @@ int check_capacity(int layer_type, int window, int64_t cap, int64_t last_pos) {
 void rope_table(const olmo3_rope* rope, int layer_type, int d, RopeTable* t) {
   memset(t, 0, sizeof(*t));
   const bool yarn = rope->yarn && layer_type == OLMO3_LAYER_FULL && rope->factor > 1.0;
+  // YaRN in the form its authors' code computes it: pair i turns
+  // orig_ctx * w_i / (2 pi) times over the original context, a count that
+  // equals beta at the pair index c(beta) = d ln(orig_ctx / (2 pi beta)) /
+  // (2 ln theta); the weight u of the interpolated rate w_i / factor ramps
+  // linearly over the pair index from floor(c(beta_fast)) to
+  // ceil(c(beta_slow)) (kept within [0, d - 1]).
+  double lo = 0.0, hi = 1.0;
+  if (yarn) {
+    auto pair_index = [&](double beta) {
+      return d * log((double)rope->orig_ctx / (2.0 * M_PI * beta)) / (2.0 * log(rope->theta));
+    };
+    lo = std::max(floor(pair_index(rope->beta_fast)), 0.0);
+    hi = std::min(ceil(pair_index(rope->beta_slow)), (double)(d - 1));
+    if (lo == hi) hi += 0.001;
+  }
   for (int i = 0; i < d / 2; ++i) {
     const double w = pow(rope->theta, -2.0 * i / d);
     if (!yarn) {
       t->inv_freq[i] = w;
       continue;
     }
-    const double r = (double)rope->orig_ctx * w / (2.0 * M_PI);
-    double gamma = (r - rope->beta_slow) / (rope->beta_fast - rope->beta_slow);
-    gamma = gamma < 0.0 ? 0.0 : (gamma > 1.0 ? 1.0 : gamma);
-    t->inv_freq[i] = (1.0 - gamma) * (w / rope->factor) + gamma * w;
+    double u = (i - lo) / (hi - lo);
+    u = u < 0.0 ? 0.0 : (u > 1.0 ? 1.0 : u);
+    t->inv_freq[i] = (1.0 - u) * w + u * (w / rope->factor);
   }
   double m = 1.0;
   if (rope->yarn && layer_type == OLMO3_LAYER_FULL) {

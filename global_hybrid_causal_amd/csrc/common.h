@@ -63,14 +63,21 @@ template <> struct Io<float> {
 // infinities, largest finite value 448), converted in hardware on gfx950.
 // The hardware rounds to nearest even but turns values past the largest
 // finite one into NaN, so inputs are clamped to +-448 first (saturation).
+// A NaN is passed through unclamped (min/max would replace it by a bound),
+// so it is stored as a NaN code.
 constexpr float kE4m3Max = 448.f;
+
+__device__ __forceinline__ float e4m3_saturate(float x) {
+  const float c = fminf(fmaxf(x, -kE4m3Max), kE4m3Max);
+  return __builtin_isnan(x) ? x : c;
+}
 
 // Four fp32 values -> four e4m3 codes, first value in the low byte.
 __device__ __forceinline__ uint32_t f32x4_to_e4m3(float a, float b, float c, float d) {
-  a = fminf(fmaxf(a, -kE4m3Max), kE4m3Max);
-  b = fminf(fmaxf(b, -kE4m3Max), kE4m3Max);
-  c = fminf(fmaxf(c, -kE4m3Max), kE4m3Max);
-  d = fminf(fmaxf(d, -kE4m3Max), kE4m3Max);
+  a = e4m3_saturate(a);
+  b = e4m3_saturate(b);
+  c = e4m3_saturate(c);
+  d = e4m3_saturate(d);
   int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
   w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
   return (uint32_t)w;

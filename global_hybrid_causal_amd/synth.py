@@ -70,11 +70,16 @@ def layer_inputs(seed: int, layer: int, B: int, T: int, H: int, G: int, d: int,
 
 
 def e4m3_codes(shape, seed: int, *keys: int, device="cpu", exp_lo: int = 5,
-               exp_hi: int = 8) -> torch.Tensor:
+               exp_hi: int = 8, all_codes: bool = False) -> torch.Tensor:
     """Random e4m3 bytes (uint8): uniform sign bit, exponent field uniform in
     [exp_lo, exp_hi], uniform 3-bit mantissa.  The default fields give
-    magnitudes 0.25 .. 3.75; no NaN code is drawn."""
+    magnitudes 0.25 .. 3.75; no NaN code is drawn.  all_codes: every one of
+    the 254 non-NaN codes equally likely instead (zeros, subnormals and the
+    largest magnitude 448 included)."""
     g = _generator(device, seed, keys)
+    if all_codes:
+        k = torch.randint(0, 254, shape, generator=g, device=device, dtype=torch.int32)
+        return (k + (k >= 0x7F).to(torch.int32)).to(torch.uint8)  # skip 0x7F; 0xFF is past the range
     sign = torch.randint(0, 2, shape, generator=g, device=device, dtype=torch.int32)
     exp = torch.randint(exp_lo, exp_hi + 1, shape, generator=g, device=device, dtype=torch.int32)
     man = torch.randint(0, 8, shape, generator=g, device=device, dtype=torch.int32)
@@ -82,10 +87,11 @@ def e4m3_codes(shape, seed: int, *keys: int, device="cpu", exp_lo: int = 5,
 
 
 def e4m3_cache_fill(seed: int, layer: int, B: int, G: int, capacity: int, d: int,
-                    device="cpu") -> tuple[torch.Tensor, torch.Tensor]:
-    """Pre-filled e4m3 K and V caches [B, G, capacity, d] of random codes."""
-    return (e4m3_codes((B, G, capacity, d), seed, layer, CACHE_K, device=device),
-            e4m3_codes((B, G, capacity, d), seed, layer, CACHE_V, device=device))
+                    device="cpu", all_codes: bool = False) -> tuple[torch.Tensor, torch.Tensor]:
+    """Pre-filled e4m3 K and V caches [B, G, capacity, d] of random codes
+    (``e4m3_codes``; all_codes draws every non-NaN code)."""
+    return (e4m3_codes((B, G, capacity, d), seed, layer, CACHE_K, device=device, all_codes=all_codes),
+            e4m3_codes((B, G, capacity, d), seed, layer, CACHE_V, device=device, all_codes=all_codes))
 
 
 def cache_fill(seed: int, layer: int, B: int, G: int, capacity: int, d: int,

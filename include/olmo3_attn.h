@@ -77,18 +77,23 @@ enum { OLMO3_DTYPE_BF16 = 0, OLMO3_DTYPE_F32 = 1, OLMO3_DTYPE_BF16_E4M3 = 2 };
 enum { OLMO3_MODE_PREFILL = 0, OLMO3_MODE_DECODE = 1 };
 
 /* RoPE / YaRN settings ("Case Study: OLMo 3", items 3 and 7).
- *   theta        RoPE base; rate of pair i is theta^(-2i/d).
+ *   theta        RoPE base; rate of pair i is omega_i = theta^(-2i/d).
  *   yarn         nonzero: full layers use YaRN rates and temperature;
  *                sliding layers always use plain RoPE.
  *   factor       YaRN scale s (>= 1), e.g. 8 for 8192 -> 65536 positions.
  *   orig_ctx     original training context L, e.g. 8192.
- *   beta_fast    ramp end in rotations over L (rates with more are kept), e.g. 32.
- *   beta_slow    ramp start (rates with fewer are divided by s), e.g. 1.
+ *   beta_fast    rotations over L above which rates are kept, e.g. 32.
+ *   beta_slow    rotations over L below which rates are divided by s, e.g. 1.
  *   attn_factor  multiplier applied to rotated q and k; <= 0 selects
  *                0.1*ln(s) + 1 (Peng et al., 2023).  Logits scale by its square.
- * YaRN rate of pair i: with r = L*omega_i/(2*pi) and
- * gamma = clamp((r - beta_slow)/(beta_fast - beta_slow), 0, 1):
- * omega'_i = (1 - gamma)*omega_i/s + gamma*omega_i. */
+ * YaRN rate of pair i (Peng et al., 2023, as its authors' code and model
+ * configurations compute it): pair i turns L*omega_i/(2*pi) times over L,
+ * which equals beta at the pair index c(beta) = d*ln(L/(2*pi*beta)) /
+ * (2*ln(theta)); with lo = max(floor(c(beta_fast)), 0), hi =
+ * min(ceil(c(beta_slow)), d - 1) (hi = lo + 0.001 if they meet) and
+ * u = clamp((i - lo)/(hi - lo), 0, 1): omega'_i = (1 - u)*omega_i + u*omega_i/s.
+ * With yarn set: factor >= 1 and finite, orig_ctx >= 1, beta_fast >
+ * beta_slow > 0, and theta > 1 when factor > 1; otherwise INVALID_ARG. */
 typedef struct olmo3_rope {
   double theta;
   int32_t yarn;
@@ -241,9 +246,11 @@ int olmo3_attn_decode_ragged(int B, int H, int G, int d, int window, int layer_t
  * mishandled).  A cache element is one byte, an OCP e4m3 code c (sign, 4
  * exponent bits with bias 7, 3 mantissa bits, largest finite 448, no
  * infinities); it stands for c * k_scale in k_cache and c * v_scale in
- * v_cache.  A key or value x is stored as the code nearest to
- * x * (1/scale) (fp32 product, ties to even, saturated to +-448), keys taken
- * after QK-norm and RoPE in fp32.  Activations are bf16.  Layouts, slots and
+ * v_cache.  A key or value x is stored as the code nearest to the fp32
+ * product x * fp32(1/scale) (ties to the even mantissa; magnitudes past 448,
+ * infinities included, saturate to the code of +-448; a NaN is stored as a
+ * NaN code, 0x7F or 0xFF), keys taken after QK-norm and RoPE in fp32.
+ * Activations are bf16.  Layouts, slots and
  * errors as the bf16 entry points, with 1-byte cache elements; scales must
  * be finite and > 0 (INVALID_ARG). */
 

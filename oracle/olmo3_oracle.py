@@ -31,17 +31,21 @@ decode of one token, which is the same computation with T = 1):
 Readings taken where the pages are silent:
 softmax scale 1/sqrt(d); the rotation direction x_i + i*x_{i+d/2} times
 exp(+i*angle); contiguous GQA grouping g(h) = h // (H/G); YaRN as the
-NTK-by-parts interpolation of Peng et al. (2023) with a ramp linear in the
-number of rotations r, alpha = beta_slow = 1, beta = beta_fast = 32, and an
-attention temperature m = 0.1*ln(s) + 1 multiplied into both q and k.
-Parity unpinned by the pages: the rotation direction, the GQA grouping order,
-the YaRN ramp parameters and the softmax scale are shared conventions.
+NTK-by-parts interpolation of Peng et al. (2023) in the form its authors'
+code computes it (a ramp over the pair index between the floor and ceiling
+of the indices where beta_fast = 32 and beta_slow = 1 rotations fit in the
+original context; see ``yarn_inv_freq``), and an attention temperature
+m = 0.1*ln(s) + 1 multiplied into both q and k.  The pages pin none of
+these; the tests pin them to an independent implementation of the model's
+attention (the transformers library's OLMo 3 attention and its YaRN rates).
 
 No intermediate is rounded: inputs are taken exactly as given (bf16 values
 are exactly representable in fp64) and everything is computed in fp64.  Two
 exceptions: the optional e4m3 cache, whose stored code is an integer that
-floating point decides, so it is decided as the kernels decide it (the fp32
-product of the value and 1/scale, then the nearest code), see ``e4m3_encode``;
+floating point decides; the library's interface fixes that decision (the
+code nearest to the fp32 product of the value and fp32(1/scale), ties to the
+even mantissa, saturated at +-448, NaN kept as a NaN code), and the oracle
+implements that contract, see ``e4m3_store``;
 and the opt-in ``round_rotated`` switch of ``prefill_ref`` / ``decode_ref``,
 which rounds the rotated queries and keys to bfloat16, the type every
 operand of a bfloat16 model's attention has (page "Olmo-3 End-to-End
@@ -195,20 +199,31 @@ def yarn_inv_freq(theta: float, d: int, factor: float, orig_ctx: int,
     """YaRN rates (Peng et al., 2023, "NTK-by-parts" interpolation).
 
     Page "Case Study: OLMo 3", item 7: full layers are rescaled with YaRN from
-    8,192 to 65,536 positions (factor 8); the pages give no formula, so the
-    paper's definition is taken: with wavelength lambda_i = 2*pi/omega_i and
-    r_i = orig_ctx / lambda_i rotations over the original context, the ramp
-    gamma_i = clip((r_i - beta_slow)/(beta_fast - beta_slow), 0, 1) mixes the
-    interpolated rate omega_i/factor (gamma = 0, long wavelengths) with the
-    original rate (gamma = 1, short wavelengths).
+    8,192 to 65,536 positions (factor 8); page "Olmo 3 7B" says the scaling
+    comes from the model's configuration.  The pages give no formula, so the
+    method's published definition in the form its authors' code computes it
+    (the form model configurations are run with) is taken:
+    - pair i turns r_i = orig_ctx * omega_i / (2 pi) times over the original
+      context; r_i = beta falls at the (fractional) pair index
+      c(beta) = d * ln(orig_ctx / (2 pi beta)) / (2 ln theta);
+    - the ramp runs over the pair index between lo = floor(c(beta_fast)) and
+      hi = ceil(c(beta_slow)) (clipped to [0, d - 1]; hi moved 0.001 past lo
+      if they meet): u_i = clip((i - lo) / (hi - lo), 0, 1);
+    - omega'_i = (1 - u_i) * omega_i + u_i * omega_i / factor: pairs below
+      lo (many turns) keep their rate, pairs from hi on (under one turn) are
+      interpolated by the factor.
     """
     w = rope_inv_freq(theta, d)
     if factor == 1.0:
         return w
-    wavelength = 2.0 * math.pi / w
-    r = orig_ctx / wavelength
-    gamma = np.clip((r - beta_slow) / (beta_fast - beta_slow), 0.0, 1.0)
-    return (1.0 - gamma) * (w / factor) + gamma * w
+    def pair_index(beta):
+        return d * math.log(orig_ctx / (2.0 * math.pi * beta)) / (2.0 * math.log(theta))
+    lo = max(math.floor(pair_index(beta_fast)), 0)
+    hi = min(math.ceil(pair_index(beta_slow)), d - 1)
+    if lo == hi:
+        hi += 0.001
+    u = np.clip((np.arange(d // 2, dtype=np.float64) - lo) / (hi - lo), 0.0, 1.0)
+    return (1.0 - u) * w + u * (w / factor)
 
 
 def yarn_mscale(factor: float) -> float:
@@ -336,9 +351,12 @@ def e4m3_encode(x) -> np.ndarray:
     """Nearest code to each value, as uint8.  Magnitudes above 448 saturate to
     448; a value halfway between two codes takes the one whose mantissa is
     even (consecutive non-negative codes differ by one in their low bit); the
-    sign bit is the value's sign (so -0.0 and small negatives give 0x80).
+    sign bit is the value's sign (so -0.0 and small negatives give 0x80); a
+    NaN gives the NaN code 0x7F (0xFF with the sign bit set).
     Brute force: compare against all 127 finite non-negative codes."""
     x = np.asarray(x, dtype=np.float64)
+    nan = np.isnan(x)
+    x = np.where(nan, np.copysign(0.0, x), x)    # keeps a NaN's sign bit
     mag = np.minimum(np.abs(x), E4M3_MAX)
     codes = np.arange(0x7F)                      # 0x00 .. 0x7E, increasing values
     vals = np.array([e4m3_value(c) for c in codes])
@@ -348,12 +366,15 @@ def e4m3_encode(x) -> np.ndarray:
     even = cand & (codes % 2 == 0)
     pick = np.where(even.any(axis=-1), np.argmax(even, axis=-1), np.argmax(cand, axis=-1))
     out = codes[pick].astype(np.uint8)
+    out = np.where(nan, np.uint8(0x7F), out)
     return np.where(np.signbit(x), out | 0x80, out).astype(np.uint8)
 
 
 def e4m3_store(x, scale: float) -> np.ndarray:
-    """Code stored for value x with cache scale `scale`: the kernels form the
-    fp32 product x * fp32(1/scale) and take its nearest code."""
+    """Code stored for value x with cache scale `scale`, as the library's
+    interface defines it for every e4m3 entry point: the fp32 product
+    x * fp32(1/scale), then its nearest code (``e4m3_encode``: ties to the
+    even mantissa, saturated at +-448, NaN to a NaN code)."""
     inv = np.float32(1.0 / np.float64(scale))
     return e4m3_encode(np.asarray(x, dtype=np.float32) * inv)
 
@@ -547,11 +568,14 @@ def decode_ref(q_pre, k_pre, v, q_gain, k_gain, *, H: int, G: int, d: int,
 
 def decode_e4m3_ref(q_pre, k_pre, v, q_gain, k_gain, *, H: int, G: int, d: int,
                     kind: str, window: int, rope: RopeParams, eps: float = 1e-6,
-                    pos: int, cache: KvCacheRef) -> np.ndarray:
+                    pos: int, cache: KvCacheRef, round_rotated: bool = False) -> np.ndarray:
     """Single-token decode against an e4m3 cache: the token's rotated key and
     its value are stored as codes at the slot of ``pos`` first, and the query
     then attends to the cache as stored, the new token's dequantized key and
-    value included.  q_pre [B, H*d], k_pre and v [B, G*d]; returns [B, H*d]."""
+    value included.  q_pre [B, H*d], k_pre and v [B, G*d]; returns [B, H*d].
+    ``round_rotated``: the rotated query is rounded to bfloat16 before the
+    scores, as in ``prefill_ref`` (the keys are the codes' values, which
+    bfloat16 holds exactly)."""
     if cache.e4m3_scales is None:
         raise ValueError("decode_e4m3_ref needs a cache with e4m3 storage")
     q_pre = np.asarray(q_pre, dtype=np.float64)[:, None, :]
@@ -562,6 +586,8 @@ def decode_e4m3_ref(q_pre, k_pre, v, q_gain, k_gain, *, H: int, G: int, d: int,
     w, m = layer_rope(rope, kind, d)
     p = np.array([pos], dtype=np.int64)
     q_rot = rope_rotate(qh, p, w, m)
+    if round_rotated:
+        q_rot = bf16_round(q_rot)
     cache.append(rope_rotate(kh, p, w, m), vh, p)
     keys, vals, key_pos = cache.contents()
     out = np.zeros((B, 1, H, d))

@@ -8,6 +8,7 @@ plants plausible mistakes in the oracle and requires some check to fail.
 
 from __future__ import annotations
 
+import copy
 import math
 import os
 
@@ -258,6 +259,78 @@ def _sdpa(q, k, v, mask):
     vt = torch.from_numpy(np.repeat(v, H // G, axis=1)).permute(1, 0, 2)[None]
     o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=torch.from_numpy(mask))
     return o[0].permute(1, 0, 2).numpy()
+
+
+def _hf_olmo3_config(H, G, d, theta, factor, orig_ctx, window=4096, n_layers=4):
+    """transformers' OLMo 3 configuration with the given attention shapes:
+    plain RoPE on sliding layers, YaRN on full layers (factor, original
+    context, beta_fast 32, beta_slow 1), hidden size H*d."""
+    from transformers import Olmo3Config
+    rope = {"sliding_attention": {"rope_type": "default", "rope_theta": theta},
+            "full_attention": {"rope_type": "yarn", "rope_theta": theta, "factor": factor,
+                               "original_max_position_embeddings": orig_ctx,
+                               "beta_fast": 32.0, "beta_slow": 1.0}}
+    return Olmo3Config(hidden_size=H * d, intermediate_size=8, num_hidden_layers=n_layers,
+                       num_attention_heads=H, num_key_value_heads=G, head_dim=d,
+                       max_position_embeddings=int(orig_ctx * factor), rope_parameters=rope,
+                       sliding_window=window, rms_norm_eps=1e-6, attention_bias=False)
+
+
+def check_yarn_matches_transformers():
+    """YaRN rates and temperature equal those of an independent
+    implementation, the transformers library's (the code model
+    configurations with rope_type "yarn" run), interior of the ramp
+    included; it computes in fp32, hence the 1e-6 relative bound."""
+    from transformers.modeling_rope_utils import ROPE_INIT_FUNCTIONS
+    for theta, d, s, L in [(500000.0, 128, 8.0, 8192), (10000.0, 64, 4.0, 2048),
+                           (1e6, 128, 16.0, 4096), (500000.0, 128, 8.0, 256)]:
+        cfg = _hf_olmo3_config(2, 1, d, theta, s, L)
+        inv, att = ROPE_INIT_FUNCTIONS["yarn"](cfg, None, layer_type="full_attention")
+        inv = inv.double().numpy()
+        ours = O.yarn_inv_freq(theta, d, s, L)
+        w = O.rope_inv_freq(theta, d)
+        interior = (ours < w * (1 - 1e-9)) & (ours > w / s * (1 + 1e-9))
+        assert interior.sum() >= 3, (theta, d, s, L)
+        _close(ours / inv, np.ones(d // 2), 1e-6, f"YaRN rates {theta, d, s, L}")
+        assert abs(att - O.yarn_mscale(s)) < 1e-12
+
+
+def check_attention_layer_matches_transformers():
+    """A whole attention call (QK-norm over H*d / G*d, RoPE or YaRN at
+    absolute positions, GQA grouping, 1/sqrt(d) scale, softmax, weighted
+    values) equals the transformers library's OLMo 3 attention module run in
+    fp64 (its norm, rotation angles and softmax in fp32: 1e-5 relative) on
+    the same projections, with its output projection set to the identity
+    and the oracle's mask passed in: this pins the rotation direction, the
+    grouping order, the scale and the YaRN temperature."""
+    from transformers.models.olmo3.modeling_olmo3 import Olmo3Attention, Olmo3RotaryEmbedding
+    H, G, d, T, w, theta, s, L, p0 = 4, 2, 32, 48, 10, 10000.0, 8.0, 64, 100
+    cfg = _hf_olmo3_config(H, G, d, theta, s, L, window=w)
+    gen = torch.Generator().manual_seed(11)
+    rope = O.RopeParams(theta=theta, yarn=True, factor=s, orig_ctx=L)
+    for layer_idx, kind in ((0, O.SLIDING), (3, O.FULL)):
+        assert cfg.layer_types[layer_idx] == ("sliding_attention" if kind == O.SLIDING else "full_attention")
+        att = Olmo3Attention(cfg, layer_idx).double().eval()
+        with torch.no_grad():
+            for lin in (att.q_proj, att.k_proj, att.v_proj):
+                lin.weight.copy_(torch.randn(lin.weight.shape, generator=gen, dtype=torch.float64) / 8)
+            att.o_proj.weight.copy_(torch.eye(H * d, dtype=torch.float64))
+            for nrm in (att.q_norm, att.k_norm):
+                nrm.weight.copy_(0.5 + torch.rand(nrm.weight.shape, generator=gen, dtype=torch.float64))
+            x = torch.randn((1, T, H * d), generator=gen, dtype=torch.float64)
+            pos = p0 + np.arange(T)
+            rot = Olmo3RotaryEmbedding(cfg)
+            cos, sin = rot(x, torch.as_tensor(pos)[None], cfg.layer_types[layer_idx])
+            allowed = O.mask_at_positions(pos, pos, kind, w)
+            mask = torch.where(torch.as_tensor(allowed), 0.0, -torch.inf).double()[None, None]
+            got, _ = att(x, (cos.double(), sin.double()), mask)
+            xn = x[0].numpy()
+            ref = O.prefill_ref(xn[None] @ att.q_proj.weight.numpy().T, xn[None] @ att.k_proj.weight.numpy().T,
+                                xn[None] @ att.v_proj.weight.numpy().T, att.q_norm.weight.numpy(),
+                                att.k_norm.weight.numpy(), H=H, G=G, d=d, kind=kind, window=w,
+                                rope=rope, pos_offset=p0)
+        scale = float(np.abs(ref).max())
+        _close(got.numpy(), ref, 1e-5 * scale, f"attention layer {kind}")
 
 
 def check_attend_matches_sdpa():
@@ -511,6 +584,11 @@ def check_e4m3_closed_forms():
     assert len(set(table[~np.isnan(table)].tolist())) == 253   # 254 finite codes, +-0 equal
     enc = O.e4m3_encode
     assert list(enc([1e6, -1e6, 449.0, 463.9, 464.0, 1e30])) == [0x7E, 0xFE, 0x7E, 0x7E, 0x7E, 0x7E]
+    # infinities saturate like any magnitude past 448; a NaN stays a NaN
+    # (the code torch's float8_e4m3fn conversion gives it)
+    assert list(enc([math.inf, -math.inf])) == [0x7E, 0xFE]
+    nan_code = int(torch.tensor([math.nan]).to(torch.float8_e4m3fn).view(torch.uint8)[0])
+    assert nan_code == 0x7F and list(enc([math.nan, -math.nan])) == [0x7F, 0xFF]
     # ties go to the even mantissa: 1 + 1/16 -> 1.0, 1 + 3/16 -> 1.25, 2^-10 -> 0
     assert list(enc([1.0625, 1.1875, 2.0 ** -10, 3 * 2.0 ** -10])) == [0x38, 0x3A, 0x00, 0x02]
     # half-ulp error: relative 2^-4 on normals, absolute 2^-10 on subnormals
@@ -571,11 +649,17 @@ def check_decode_e4m3_equals_decode_on_the_grid():
         k0 = np.zeros((B, G * d))
         v_new = table[rng.integers(0x20, 0x48, (B, G * d))] * vs
         qg, kg = rng.uniform(0.5, 1.5, H * d), rng.uniform(0.5, 1.5, G * d)
-        a = O.decode_ref(q, k0, v_new, qg, kg, H=H, G=G, d=d, kind=kind, window=w, rope=rope,
-                         pos=pos, cache=caches[0])
-        b = O.decode_e4m3_ref(q, k0, v_new, qg, kg, H=H, G=G, d=d, kind=kind, window=w,
-                              rope=rope, pos=pos, cache=caches[1])
-        _close(a, b, 1e-12, f"e4m3 decode on the grid, {kind}")
+        # with and without bf16 rounding of the rotated query (the cached
+        # values are e4m3 multiples, which bf16 holds exactly)
+        for rr in (False, True):
+            cs = [copy.deepcopy(c) for c in caches]
+            a = O.decode_ref(q, k0, v_new, qg, kg, H=H, G=G, d=d, kind=kind, window=w, rope=rope,
+                             pos=pos, cache=cs[0], round_rotated=rr)
+            b = O.decode_e4m3_ref(q, k0, v_new, qg, kg, H=H, G=G, d=d, kind=kind, window=w,
+                                  rope=rope, pos=pos, cache=cs[1], round_rotated=rr)
+            _close(a, b, 1e-12, f"e4m3 decode on the grid, {kind}, round_rotated {rr}")
+        assert np.abs(a - O.decode_ref(q, k0, v_new, qg, kg, H=H, G=G, d=d, kind=kind, window=w,
+                                       rope=rope, pos=pos, cache=copy.deepcopy(caches[0]))).max() > 0
 
 
 # ------------------------------------------------------------ bf16 rounding

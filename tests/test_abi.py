@@ -143,6 +143,9 @@ def prefill_call(**kw):
     (dict(rope=A.Rope(theta=0.0)), A.ERR_INVALID_ARG),
     (dict(rope=A.Rope(theta=1e4, yarn=True, factor=0.5)), A.ERR_INVALID_ARG),
     (dict(rope=A.Rope(theta=1e4, yarn=True, beta_fast=1.0, beta_slow=32.0)), A.ERR_INVALID_ARG),
+    (dict(rope=A.Rope(theta=1e4, yarn=True, beta_fast=32.0, beta_slow=0.0)), A.ERR_INVALID_ARG),
+    (dict(rope=A.Rope(theta=1.0, yarn=True, factor=8.0)), A.ERR_INVALID_ARG),
+    (dict(rope=A.Rope(theta=1e4, yarn=True, factor=float("inf"))), A.ERR_INVALID_ARG),
     (dict(q_pre=0), A.ERR_INVALID_ARG),
     (dict(out=0), A.ERR_INVALID_ARG),
     (dict(q_pre=fake(0) + 8), A.ERR_INVALID_ARG),   # misaligned

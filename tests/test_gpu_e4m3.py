@@ -220,6 +220,96 @@ def test_e4m3_decode_vs_oracle(case):
     _check_slots(kc, vc, bk, bv, [slot], k_rot, hx["v"].reshape(B, 1, G, d), f"e4m3 decode {case}")
 
 
+ALL_CODES_DECODE = [
+    # B, H, G, window, layer_type, pos, cap
+    (3, 8, 8, 128, 0, 1000, 128),         # one query head per key/value head (per-row kernel)
+    (2, 10, 2, 4096, 1, 2999, 3000),      # group 5 (grouped MFMA kernel), several splits
+    (4, 16, 2, 300, 0, 299, 300),         # group 8, ring just filled
+]
+
+
+@pytest.mark.parametrize("case", ALL_CODES_DECODE, ids=[str(c) for c in ALL_CODES_DECODE])
+def test_e4m3_decode_every_code(case):
+    """Caches holding every non-NaN code equally often (zeros, subnormals down
+    to 2^-9 and the largest magnitudes 0x7E / 0xFE = +-448 included): every
+    code's value reaches the scores and the weighted sum as the oracle's
+    table gives it.  Scales 1/64 (keys: scores stay moderate with keys up to
+    7) and 1/16 (values)."""
+    B, H, G, w, lt, pos, cap = case
+    d, ks, vs = 128, 1.0 / 64, 1.0 / 16
+    _log("e4m3 decode, every code", case)
+    kind = KINDS[lt]
+    rope = A.Rope(theta=500000.0, yarn=True, factor=8.0, orig_ctx=512)
+    kc, vc = synth.e4m3_cache_fill(75, lt, B, G, cap, d, device="cuda", all_codes=True)
+    bk, bv = _codes(kc), _codes(vc)
+    for c in (0x00, 0x01, 0x07, 0x08, 0x7E, 0x80, 0x81, 0xFE):
+        assert (bk == c).any() and (bv == c).any(), hex(c)
+    assert not ((bk & 0x7F) == 0x7F).any() and not ((bv & 0x7F) == 0x7F).any()
+    x = inputs(75, 10 + lt, B, 1, H, G, d, BF16)
+    q, k, v = x["q_pre"][:, 0].contiguous(), x["k_pre"][:, 0].contiguous(), x["v"][:, 0].contiguous()
+    out = torch.empty_like(q)
+    ws = A.workspace(A.MODE_DECODE, B, 1, H, G, d, lt, A.DTYPE_BF16_E4M3, cap, "cuda")
+    A.olmo3_attn_decode_e4m3(q, k, v, x["q_gain"], x["k_gain"], kc, vc, out, ws, k_scale=ks,
+                             v_scale=vs, window=w, layer_type=lt, rope=rope, pos=pos)
+    hx = host_inputs(x)
+    ref_cache = O.KvCacheRef(kind, w, cap, B, G, d, e4m3_scales=(ks, vs))
+    ref_cache.k[:] = TABLE[bk] * ks
+    ref_cache.v[:] = TABLE[bv] * vs
+    ref_cache.pos[:] = O.ring_positions(kind, w, cap, pos)
+    # with keys up to 7 the scores' error from holding the rotated query in
+    # bf16 grows with |k|, and values up to 28 carry it into the outputs: the
+    # oracle rounds the rotated query as the kernel holds it
+    ref = O.decode_e4m3_ref(hx["q_pre"][:, 0], hx["k_pre"][:, 0], hx["v"][:, 0], hx["q_gain"],
+                            hx["k_gain"], H=H, G=G, d=d, kind=kind, window=w,
+                            rope=oracle_rope(rope), pos=pos, cache=ref_cache, round_rotated=True)
+    err = assert_close(host(out), ref, what=f"e4m3 decode every code {case}")
+    _log("  max abs / rel err", err)
+
+
+@pytest.mark.parametrize("lt", [0, 1])
+def test_e4m3_append_saturates_and_keeps_nan(lt):
+    """Scales so small (keys 1/512, values 1/1024) that most |x / scale|
+    exceed 448: those store the saturated codes 0x7E / 0xFE, bit for bit as
+    the interface's rule (``e4m3_store``) gives them; a NaN planted in one
+    value element and in one token's projected key (whose norm then makes
+    that token's whole key row NaN) is stored as a NaN code."""
+    B, T, G, d, w, cap = 2, 40, 2, 128, 16, 48
+    ks, vs = 1.0 / 512, 1.0 / 1024
+    kind = KINDS[lt]
+    cap = w if lt == 0 else cap
+    rope = A.Rope(theta=500000.0, yarn=True, factor=4.0, orig_ctx=64)
+    x = inputs(77, lt, B, T, G, G, d, BF16)
+    t_nan_v, t_nan_k = T - 3, T - 5
+    x["v"][1, t_nan_v, 7] = float("nan")
+    x["k_pre"][0, t_nan_k, 130] = float("nan")
+    kc, vc = synth.e4m3_cache_fill(77, lt, B, G, cap, d, device="cuda")
+    bk, bv = _codes(kc), _codes(vc)
+    A.olmo3_kv_append_e4m3(x["k_pre"], x["v"], x["k_gain"], kc, vc, k_scale=ks, v_scale=vs,
+                           window=w, layer_type=lt, rope=rope)
+    hx = host_inputs(x)
+    positions = np.arange(T)
+    keep = positions[-w:] if kind == O.SLIDING else positions
+    slots = keep % w if kind == O.SLIDING else keep
+    gk, gv = _codes(kc), _codes(vc)
+    got_v = gv[:, :, slots].transpose(0, 2, 1, 3)
+    want_v = O.e4m3_store(hx["v"].reshape(B, T, G, d)[:, keep], vs)
+    nan_v = (want_v & 0x7F) == 0x7F
+    assert nan_v.sum() == 1 and ((got_v[nan_v] & 0x7F) == 0x7F).all(), "value NaN code"
+    assert np.array_equal(got_v[~nan_v], want_v[~nan_v]), "value codes"
+    sat = (want_v[~nan_v] & 0x7F) == 0x7E
+    assert sat.mean() > 0.5, sat.mean()
+    k_rot = _rotated_keys(hx, kind, rope, positions, G, d)[:, keep]
+    got_k = gk[:, :, slots].transpose(0, 2, 1, 3)
+    x32 = _key_x32(k_rot, ks)
+    nan_k = np.isnan(x32)
+    assert nan_k.sum() == G * d and ((got_k[nan_k] & 0x7F) == 0x7F).all(), "key NaN codes"
+    want_k = O.e4m3_encode(x32[~nan_k])
+    assert ((want_k & 0x7F) == 0x7E).mean() > 0.25
+    _check_key_codes(got_k[~nan_k], x32[~nan_k], f"saturating append {lt}")
+    rest = np.setdiff1d(np.arange(cap), slots)
+    assert np.array_equal(gk[:, :, rest], bk[:, :, rest]) and np.array_equal(gv[:, :, rest], bv[:, :, rest])
+
+
 @pytest.mark.parametrize("lt,w,pos,back", [
     (0, 128, 127, 127), (0, 128, 128, 127), (0, 128, 129, 127), (0, 128, 401, 127),
     (0, 128, 128, 128), (0, 128, 401, 128),      # the evicted position: its slot holds the new token

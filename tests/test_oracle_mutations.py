@@ -96,13 +96,36 @@ def _inv_freq_i_over_d(theta, d):
     return np.float64(theta) ** (-1.0 * i / d)
 
 
+def _yarn_ramp(theta, d, factor, orig_ctx, beta_fast, beta_slow, truncate=True, swap=False):
+    w = O.rope_inv_freq(theta, d)
+    if factor == 1.0:
+        return w
+    c = [d * math.log(orig_ctx / (2 * math.pi * b)) / (2 * math.log(theta)) for b in (beta_fast, beta_slow)]
+    lo, hi = (math.floor(c[0]), math.ceil(c[1])) if truncate else (c[0], c[1])
+    lo, hi = max(lo, 0), min(hi, d - 1)
+    u = np.clip((np.arange(d // 2) - lo) / (hi - lo), 0.0, 1.0)
+    if swap:
+        u = 1.0 - u
+    return (1.0 - u) * w + u * w / factor
+
+
 def _yarn_swapped(theta, d, factor, orig_ctx, beta_fast=32.0, beta_slow=1.0):
+    return _yarn_ramp(theta, d, factor, orig_ctx, beta_fast, beta_slow, swap=True)
+
+
+def _yarn_untruncated(theta, d, factor, orig_ctx, beta_fast=32.0, beta_slow=1.0):
+    return _yarn_ramp(theta, d, factor, orig_ctx, beta_fast, beta_slow, truncate=False)
+
+
+def _yarn_ramp_in_rotations(theta, d, factor, orig_ctx, beta_fast=32.0, beta_slow=1.0):
+    """The ramp written linear in the number of rotations r instead of the
+    pair index."""
     w = O.rope_inv_freq(theta, d)
     if factor == 1.0:
         return w
     r = orig_ctx * w / (2 * math.pi)
     gamma = np.clip((r - beta_slow) / (beta_fast - beta_slow), 0.0, 1.0)
-    return gamma * (w / factor) + (1.0 - gamma) * w
+    return (1.0 - gamma) * (w / factor) + gamma * w
 
 
 def _yarn_mscale_log2(factor):
@@ -181,13 +204,18 @@ def _e4m3_encode_factory(mode):
     return enc
 
 
+def _e4m3_encode_nan_saturates(x):
+    x = np.asarray(x, dtype=np.float64)
+    return _orig["e4m3_encode"](np.where(np.isnan(x), -448.0, x))
+
+
 def _e4m3_store_twice(x, scale):
     inv = np.float32(1.0 / np.float64(scale))
     return _orig["e4m3_encode"](np.asarray(x, dtype=np.float32) * inv * inv)
 
 
 def _decode_e4m3_drops_new_token(q_pre, k_pre, v, q_gain, k_gain, *, H, G, d, kind, window, rope,
-                                 eps=1e-6, pos, cache):
+                                 eps=1e-6, pos, cache, round_rotated=False):
     keys, vals, key_pos = cache.contents()
     q_pre = np.asarray(q_pre, dtype=np.float64)[:, None, :]
     B = q_pre.shape[0]
@@ -195,6 +223,8 @@ def _decode_e4m3_drops_new_token(q_pre, k_pre, v, q_gain, k_gain, *, H, G, d, ki
     w, m = O.layer_rope(rope, kind, d)
     p = np.array([pos])
     q_rot = O.rope_rotate(qh, p, w, m)
+    if round_rotated:
+        q_rot = O.bf16_round(q_rot)
     return np.stack([O.attend(q_rot[b], p, keys[b], vals[b], key_pos, kind, window)
                      for b in range(B)]).reshape(B, H * d)
 
@@ -226,6 +256,15 @@ def _prefill_edited(old, new):
     return ns["prefill_ref"]
 
 
+def _decode_e4m3_edited(old, new):
+    """decode_e4m3_ref with one source line replaced (same module globals)."""
+    src = inspect.getsource(_orig["decode_e4m3_ref"])
+    assert old in src, old
+    ns = dict(vars(O))
+    exec(compile(src.replace(old, new), O.__file__, "exec"), ns)
+    return ns["decode_e4m3_ref"]
+
+
 MUTANTS = {
     "mask t-s <= window": dict(sliding_window_mask=_mask_le_window, mask_at_positions=_mask_at_le_window),
     "mask not causal": dict(mask_at_positions=_mask_at_noncausal),
@@ -240,6 +279,8 @@ MUTANTS = {
     "rope drops mscale": dict(rope_rotate=_rope_no_mscale),
     "rope exponent i/d": dict(rope_inv_freq=_inv_freq_i_over_d),
     "yarn ramp swapped": dict(yarn_inv_freq=_yarn_swapped),
+    "yarn ramp bounds not rounded": dict(yarn_inv_freq=_yarn_untruncated),
+    "yarn ramp linear in rotations": dict(yarn_inv_freq=_yarn_ramp_in_rotations),
     "yarn mscale log2": dict(yarn_mscale=_yarn_mscale_log2),
     "yarn on sliding layers": dict(layer_rope=_layer_rope_yarn_everywhere),
     "scale 1/d": dict(attend=_attend_factory(scale_fn=lambda d: 1.0 / d)),
@@ -253,7 +294,10 @@ MUTANTS = {
     "e4m3 truncates": dict(e4m3_encode=_e4m3_encode_factory("truncate")),
     "e4m3 ties away from zero": dict(e4m3_encode=_e4m3_encode_factory("away")),
     "e4m3 scale applied twice": dict(e4m3_store=_e4m3_store_twice),
+    "e4m3 NaN saturates": dict(e4m3_encode=_e4m3_encode_nan_saturates),
     "e4m3 decode drops the new token": dict(decode_e4m3_ref=_decode_e4m3_drops_new_token),
+    "e4m3 round_rotated skips queries": dict(decode_e4m3_ref=_decode_e4m3_edited(
+        "q_rot = bf16_round(q_rot)", "q_rot = q_rot")),
     "bf16 truncates": dict(bf16_round=_bf16_factory("truncate")),
     "bf16 ties away from zero": dict(bf16_round=_bf16_factory("away")),
     "bf16 keeps 8 mantissa bits": dict(bf16_round=_bf16_factory("8 bits")),
