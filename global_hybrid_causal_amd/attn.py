@@ -16,7 +16,10 @@ import torch
 
 from . import LAYER_FULL, LAYER_SLIDING  # noqa: F401  (re-exported)
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libolmo3attn.so")
+# OLMO3_ATTN_LIB selects another build of the library (the host-sanitized
+# one that the ABI tests run under AddressSanitizer and UBSan).
+LIB_PATH = os.environ.get("OLMO3_ATTN_LIB") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libolmo3attn.so")
 
 ABI_VERSION = 10  # OLMO3_ABI_VERSION of include/olmo3_attn.h
 DTYPE_BF16, DTYPE_F32, DTYPE_BF16_E4M3 = 0, 1, 2

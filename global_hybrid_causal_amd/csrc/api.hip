@@ -146,9 +146,14 @@ int prefill_kv_splits(int B, int T, int H, int d, int dtype, int layer_type) {
 }
 
 // ... plus, for such grids, the partial states of the splits (after the rest).
-size_t prefill_ws(int B, int T, int H, int G, int d, int layer_type, int dtype) {
+// Workspace of a prefill call.  may_split: the call can split each query
+// block's keys (uniform rows without a prefix source: not packed, not a
+// sliding chunk after a ring prefix, not an e4m3 chunk after a staged
+// prefix); only then are the split partial states reserved.
+size_t prefill_ws(int B, int T, int H, int G, int d, int layer_type, int dtype,
+                  bool may_split = true) {
   size_t bytes = prefill_ws_base(B, T, H, G, d, layer_type, dtype);
-  const int splits = prefill_kv_splits(B, T, H, d, dtype, layer_type);
+  const int splits = may_split ? prefill_kv_splits(B, T, H, d, dtype, layer_type) : 1;
   if (splits > 1) bytes += align_up((size_t)B * T * H * splits * (d + 2) * sizeof(float));
   return bytes;
 }
@@ -539,8 +544,10 @@ int olmo3_attn_prefill_phases(int phases, int B, int T, int H, int G, int d, int
                               void* workspace, size_t workspace_bytes, void* stream) {
   if (phases <= 0 || (phases & ~(OLMO3_PHASE_PROLOGUE | OLMO3_PHASE_ATTENTION | OLMO3_PHASE_MERGE)))
     return OLMO3_ERR_INVALID_ARG;
+  // a sliding chunk after a ring prefix keeps one workgroup per query block
+  const bool may_split = !(layer_type == OLMO3_LAYER_SLIDING && pos_offset > 0);
   const size_t need = (B > 0 && T > 0 && H > 0 && G > 0 && d > 0)
-                          ? prefill_ws(B, T, H, G, d, layer_type, dtype)
+                          ? prefill_ws(B, T, H, G, d, layer_type, dtype, may_split)
                           : 0;
   int st = validate_attn(B, T, H, G, d, window, layer_type, rope, eps, pos_offset, dtype, q_pre,
                          k_pre, v, q_gain, k_gain, k_cache, v_cache, cache_capacity, out,
@@ -565,7 +572,8 @@ int olmo3_attn_prefill_ragged(int B, int n_tokens, int max_len, int64_t max_end,
     return OLMO3_ERR_INVALID_ARG;
   if (!cu_seqlens || ((uintptr_t)cu_seqlens & 3) || ((uintptr_t)pos_offsets & 3))
     return OLMO3_ERR_INVALID_ARG;
-  const size_t need = (H > 0 && G > 0 && d > 0) ? prefill_ws(1, n_tokens, H, G, d, layer_type, dtype)
+  const size_t need = (H > 0 && G > 0 && d > 0) ? prefill_ws(1, n_tokens, H, G, d, layer_type, dtype,
+                                                             false)
                                                 : 0;
   // the rows as one sequence for the input sizes; the caches hold B sequences
   int st = validate_attn(1, n_tokens, H, G, d, window, layer_type, rope, eps, 0, dtype, q_pre,
@@ -787,7 +795,8 @@ int olmo3_attn_prefill_ragged_e4m3(int B, int n_tokens, int max_len, int H, int 
   if (!cu_seqlens || ((uintptr_t)cu_seqlens & 3)) return OLMO3_ERR_INVALID_ARG;
   if (!valid_scale(k_scale) || !valid_scale(v_scale)) return OLMO3_ERR_INVALID_ARG;
   const size_t need = (H > 0 && G > 0 && d > 0)
-                          ? prefill_ws(1, n_tokens, H, G, d, layer_type, OLMO3_DTYPE_BF16_E4M3)
+                          ? prefill_ws(1, n_tokens, H, G, d, layer_type, OLMO3_DTYPE_BF16_E4M3,
+                                       false)
                           : 0;
   // the rows as one sequence for the input sizes; the caches hold B sequences
   int st = validate_attn(1, n_tokens, H, G, d, window, layer_type, rope, eps, 0, OLMO3_DTYPE_BF16,
@@ -810,7 +819,10 @@ int olmo3_attn_prefill_e4m3(int B, int T, int H, int G, int d, int window, int l
                             void* out, void* workspace, size_t workspace_bytes, void* stream) {
   if (!valid_scale(k_scale) || !valid_scale(v_scale)) return OLMO3_ERR_INVALID_ARG;
   const bool sizes_ok = B > 0 && T > 0 && H > 0 && G > 0 && d > 0 && window > 0 && pos_offset >= 0;
-  size_t need = sizes_ok ? prefill_ws(B, T, H, G, d, layer_type, OLMO3_DTYPE_BF16_E4M3) : 0;
+  // a later chunk reads its prefix from a staged copy and does not split
+  size_t need = sizes_ok ? prefill_ws(B, T, H, G, d, layer_type, OLMO3_DTYPE_BF16_E4M3,
+                                      pos_offset == 0)
+                         : 0;
   if (sizes_ok && pos_offset > 0) need += stage_ws(B, G, d, stage_rows(layer_type, window, pos_offset));
   int st = validate_attn(B, T, H, G, d, window, layer_type, rope, eps, pos_offset,
                          OLMO3_DTYPE_BF16, q_pre, k_pre, v, q_gain, k_gain, k_cache, v_cache,

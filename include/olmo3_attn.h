@@ -119,7 +119,13 @@ int olmo3_layer_type(int layer, int n_layers);
  * blocks of 128 rows times H times B number fewer than 512 (full layers) or
  * at most 256 (sliding layers), the prefill figure also holds the partial
  * softmax states of a two-way split of every block's keys (B*T*H*2*(d+2)
- * floats), which such calls use.  Returns 0 for invalid sizes. */
+ * floats), which such calls use unless they read a prefix (a sliding-layer
+ * chunk at pos_offset > 0, an e4m3 chunk at pos_offset > 0) or come packed
+ * (the ragged entry points); those calls accept the smaller workspace
+ * without the split states.  The figure is therefore not monotone in T: a
+ * workspace sized for the largest chunk of a prompt may be too small for a
+ * shorter one that splits; size it per call, or for the largest figure over
+ * the lengths used.  Returns 0 for invalid sizes. */
 size_t olmo3_workspace_bytes(int mode, int B, int T, int H, int G, int d,
                              int layer_type, int dtype, int64_t cache_capacity);
 

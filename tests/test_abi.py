@@ -416,11 +416,14 @@ def test_e4m3_prefill_rejects(kw, status):
 
 @pytest.mark.parametrize("lt,rows", [(1, 40), (0, 16)])
 def test_e4m3_prefill_later_chunk_needs_the_copy(lt, rows):
-    # a chunk at pos_offset 40 needs the first-chunk workspace plus a bf16
-    # copy of 40 linear rows, or of the 16-slot ring
+    # a chunk at pos_offset 40 reads its prefix from a bf16 copy and never
+    # splits its keys: it needs its rotated queries (8 x 4 x 128 bf16) and
+    # keys (8 x 2 x 128), each region 256-byte aligned, plus the copy of 40
+    # linear rows, or of the 16-slot ring, of keys and of values
     L = A.lib()
     first = L.olmo3_workspace_bytes(0, 1, 8, 4, 2, 128, lt, A.DTYPE_BF16_E4M3, 0)
-    need = first + 2 * 2 * rows * 128 * 2
+    need = 8 * 4 * 128 * 2 + 8 * 2 * 128 * 2 + 2 * 2 * rows * 128 * 2
+    assert first > 8 * 4 * 128 * 2 + 8 * 2 * 128 * 2   # the first chunk may split: its states
     cap = 64 if lt == 1 else 16
     assert e4m3_prefill_call(ws_bytes=need - 1, layer_type=lt, cap=cap) == A.ERR_WORKSPACE
 

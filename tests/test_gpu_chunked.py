@@ -108,6 +108,33 @@ def test_chunks_equal_one_prefill(lt, chunks):
     assert_close(host(kc)[:, :, held], ref_cache.k[:, :, held], what="cache keys")
 
 
+def test_ring_chunk_takes_the_workspace_without_split_states():
+    """A sliding-layer chunk after a ring prefix never splits its keys, so it
+    runs with the workspace of its rotated queries and keys alone, smaller
+    than olmo3_workspace_bytes gives for a small grid (which holds split
+    states for the call without a prefix), and matches the oracle."""
+    B, T, H, G, d, w, P = 1, 300, 4, 2, 128, 256, 1000
+    rope = A.Rope(theta=500000.0)
+    x = inputs(43, 0, B, T, H, G, d, BF16)
+    align = lambda n: (n + 255) // 256 * 256
+    small = align(B * T * H * d * 2) + align(B * G * T * d * 2)
+    full = A.olmo3_workspace_bytes(A.MODE_PREFILL, B, T, H, G, d, 0, A.DTYPE_BF16, w)
+    assert full > small
+    kc, vc = synth.cache_fill(43, 5, B, G, w, d, device="cuda", dtype=BF16)
+    hk, hv = host(kc), host(vc)
+    ws = torch.empty(small, dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(x["q_pre"])
+    A.olmo3_attn_prefill(x["q_pre"], x["k_pre"], x["v"], x["q_gain"], x["k_gain"], kc, vc, out, ws,
+                         window=w, layer_type=0, rope=rope, pos_offset=P)
+    ref_cache = O.KvCacheRef(O.SLIDING, w, w, B, G, d)
+    ref_cache.k[:] = hk
+    ref_cache.v[:] = hv
+    ref_cache.pos[:] = O.ring_positions(O.SLIDING, w, w, P)
+    ref = O.prefill_ref(**host_inputs(x), H=H, G=G, d=d, kind=O.SLIDING, window=w,
+                        rope=oracle_rope(rope), pos_offset=P, cache=ref_cache)
+    assert_close(host(out), ref, what="ring chunk, small workspace")
+
+
 @pytest.mark.parametrize("T,P", [(1, 1), (5, 64), (64, 64), (127, 300), (300, 129), (1000, 4096),
                                  (200, 4000), (4096, 4096)])
 @pytest.mark.parametrize("window", [1, 63, 100, 128, 4096])
