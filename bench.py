@@ -1,32 +1,35 @@
 #!/usr/bin/env python3
 """Throughput of the OLMo 3 per-layer attention path on one MI355X.
 
-One step runs the whole path once per layer kind:
-  prefill of T new tokens (QK-norm + RoPE + cache append, then attention), on
-  a sliding layer and on a full (YaRN) layer, and
-  decode of one token per sequence against a pre-filled cache (append, then
-  split-KV attention and merge), on a sliding (ring) and a full layer.
-Workloads (synthetic, seeded, shaped like the OLMo 3 configurations):
-  7b   (default) prefill B=1, T=8192, H=G=32, d=128, window 4096;
-       decode B=32 at cache length 65,536 (new token at position 65,535)
-  32b  prefill B=1, T=8192, H=40, G=8; decode B=64 at cache length 32,768
+One step runs every workload named by --workload once, each call stage by
+stage (prologue: QK-norm + RoPE + cache append; then attention):
+  7b   prefill B=1, T=8192, H=G=32, d=128 on a sliding layer (window 4096)
+       and on a full (YaRN) layer; decode B=32 at cache length 65,536 (new
+       token at position 65,535) on a sliding (ring) and a full layer
+  32b  the same with H=40, G=8; decode B=64 at cache length 32,768
   long 32-layer attention-only stack (24 sliding, 8 full YaRN), B=1,
        T=65,536, 7B head shapes, prefill only
-  decode-stack  the same 32-layer stack decoding one token per sequence,
-       B=16 at cache length 65,536: KV bytes read per step and per token of
-       context (the per-layer-type cache of the page "Olmo 3 7B")
+The default is all three ("7b,32b,long").  Other workloads, one at a time or
+in a list:
+  decode-stack  the 32-layer stack decoding one token per sequence, B=16 at
+       cache length 65,536: KV bytes read per step and per token of context
+       (the per-layer-type cache of the page "Olmo 3 7B")
   chunked  7B prefill of a 4,096-token chunk at position 61,440 onto a
        filled cache (full layer: 61,440 cached positions; sliding: the ring)
   7b-e4m3  7B decode (B=32 at 65,536) against e4m3 caches (1-byte codes)
   decode-stack-e4m3  the decode stack against e4m3 caches
+  7b-shard, 32b-shard  one GPU's share of an 8-way head split of a layer
 
 Printed: one JSON line.  `value` is prefill TFLOP/s (algorithmic FLOPs of the
-allowed query/key pairs over the whole prefill call time); decode KV GB/s is
-in "decode" (and is `value` for the decode-only stack workload).  Each kernel is bracketed by HIP events on the stream it is
-launched on (the stage-by-stage entry points), giving the per-kernel
-rooflines; a decode call's merge stage shares its attention stage's events
-(at these batch sizes each (sequence, key/value head) is one workgroup of the
-split kernel, which writes the output itself, and no merge kernel runs).  The CPU oracle is timed on a bounded sample of the same workload.
+allowed query/key pairs over the whole call time, prologue included) over the
+prefill calls of the 7B and 32B layers when either is run (else over every
+prefill call, else decode KV GB/s); per-workload blocks give each call.  Each
+kernel is bracketed by HIP events on the stream it is launched on (the
+stage-by-stage entry points), giving the per-kernel rooflines; a decode
+call's merge stage shares its attention stage's events (at these batch sizes
+each (sequence, key/value head) is one workgroup of the split kernel, which
+writes the output itself, and no merge kernel runs).  The CPU oracle is timed
+on a bounded sample of the 7B layer shape.
 """
 
 from __future__ import annotations
@@ -48,16 +51,19 @@ WINDOW = 4096
 THETA = 500000.0
 
 
-# HBM bytes per launch of the timed kernels (7B and 32B layer workloads), from
-# two rocprofv3 --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE, KiB per
-# dispatch), each scaled by what the same counter reads for a 1 GiB
-# device-to-device copy on the same GPU (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0).
-# An entry holds only while the kernel's sources hash to `sources`; otherwise
-# the figure is reported null.
+# HBM bytes per launch of the timed kernels, from two rocprofv3 --pmc runs of
+# this script (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled by
+# what the same counter reads for a 1 GiB device-to-device copy on the same
+# GPU.  Keyed by (roofline group, kernel); a group of several launches (the
+# long stack's layers of one kind) holds the mean per launch.  An entry holds
+# only while the kernel's sources hash to `sources`; otherwise the figure is
+# reported null.
 KERNEL_SOURCES = {
     "prefill_d128_kernel": ["prefill.hip", "tiles.h", "common.h", "kernels.h"],
     "decode_split_kernel": ["attn.hip", "tiles.h", "common.h", "kernels.h"],
     "decode_mfma_kernel": ["attn.hip", "tiles.h", "common.h", "kernels.h"],
+    "qknorm_rope_append_kernel": ["prologue.hip", "common.h", "kernels.h"],
+    "decode_prologue_kernel": ["prologue.hip", "common.h", "kernels.h"],
 }
 
 
@@ -67,16 +73,7 @@ def decode_kernel(H: int, G: int, e4m3: bool) -> str:
     return "decode_mfma_kernel" if not e4m3 and H // G >= 2 else "decode_split_kernel"
 
 
-MEASURED_TRAFFIC = {
-    ("olmo3-7b-layer", "prefill_sliding_l0"): dict(bytes=695532543, sources="3bc9cbd506cb2b68"),
-    ("olmo3-7b-layer", "prefill_full_l3"): dict(bytes=301389061, sources="3bc9cbd506cb2b68"),
-    ("olmo3-7b-layer", "decode_sliding"): dict(bytes=2148100278, sources="1bb78d08d293ba50"),
-    ("olmo3-7b-layer", "decode_full"): dict(bytes=34359469838, sources="1bb78d08d293ba50"),
-    ("olmo3-32b-layer", "prefill_sliding_l0"): dict(bytes=321227602, sources="3bc9cbd506cb2b68"),
-    ("olmo3-32b-layer", "prefill_full_l3"): dict(bytes=320242780, sources="3bc9cbd506cb2b68"),
-    ("olmo3-32b-layer", "decode_sliding"): dict(bytes=1079199164, sources="1bb78d08d293ba50"),
-    ("olmo3-32b-layer", "decode_full"): dict(bytes=8621331768, sources="1bb78d08d293ba50"),
-}
+MEASURED_TRAFFIC = {}
 
 
 def sources_digest(kernel: str) -> str:
@@ -88,8 +85,8 @@ def sources_digest(kernel: str) -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str, segment: str, kernel: str):
-    entry = MEASURED_TRAFFIC.get((workload, segment))
+def measured_traffic(group: str, kernel: str):
+    entry = MEASURED_TRAFFIC.get((group, kernel))
     if entry is None or kernel not in KERNEL_SOURCES or sources_digest(kernel) != entry["sources"]:
         return None
     return entry["bytes"]
@@ -125,6 +122,22 @@ def decode_kv_bytes(B, G, d, n, elem=2) -> int:
     return B * G * n * d * 2 * elem
 
 
+def prefill_prologue_bytes(B, T, H, G, d, sliding, window=4096, es=2) -> int:
+    """Algorithmic HBM bytes of the prefill prologue at position 0: it reads
+    the projected q, k and v rows and writes the rotated queries, the cache
+    rows it keeps (the last `window` positions on a ring) and, on a sliding
+    layer, a rotated copy of every key for the attention."""
+    kept = min(T, window) if sliding else T
+    return (B * T * (H + 2 * G) * d * es + B * T * H * d * es + B * kept * 2 * G * d * es
+            + (B * T * G * d * es if sliding else 0))
+
+
+def decode_prologue_bytes(B, H, G, d, cache_elem=2, es=2) -> int:
+    """Reads one token's q, k, v per sequence; writes its rotated query and
+    its key and value to one cache slot."""
+    return B * (H + 2 * G) * d * es + B * H * d * es + B * 2 * G * d * cache_elem
+
+
 WORKLOADS = {
     "7b": dict(name="olmo3-7b-layer", prefill=dict(B=1, T=8192, H=32, G=32),
                decode=dict(B=32, H=32, G=32, L=65536)),
@@ -155,13 +168,17 @@ N_LAYERS_7B = 32
 NAIVE_BYTES_PER_TOKEN_7B = N_LAYERS_7B * 32 * 128 * 2 * 2  # every layer full: 524,288
 
 
+HEADLINE = ("7b", "32b")  # `value` and `roofline` cover these workloads' prefill calls
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", choices=sorted(WORKLOADS), default="7b")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+    ap.add_argument("--workload", default="7b,32b,long",
+                    help="comma-separated list of " + ", ".join(sorted(WORKLOADS)))
+    ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="CPU time budget of the oracle baseline (0 disables it)")
     ap.add_argument("--segments", default="",
                     help="comma-separated subset of prefill_sliding, prefill_full, decode_sliding, "
@@ -169,7 +186,12 @@ def parse():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes three times "
                          "(reference for HBM byte counters) and exit")
-    return ap.parse_args()
+    args = ap.parse_args()
+    args.workloads = [w for w in args.workload.split(",") if w]
+    bad = [w for w in args.workloads if w not in WORKLOADS]
+    if bad or not args.workloads:
+        ap.error(f"unknown workload(s) {bad}; choose from {sorted(WORKLOADS)}")
+    return args
 
 
 def copy_calibration(nbytes: int) -> None:
@@ -183,75 +205,65 @@ def copy_calibration(nbytes: int) -> None:
     print(json.dumps({"copy_calibration_bytes": nbytes, "launches": 3}), flush=True)
 
 
-def main():
-    args = parse()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: the library has no multi-GPU path "
-              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
-        sys.exit(2)
-
-    import torch
-
-    from global_hybrid_causal_amd import attn as A
-    from global_hybrid_causal_amd import synth
-
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    if args.copy_calibration:
-        copy_calibration(args.copy_calibration)
-        return
-    wanted = set(filter(None, args.segments.split(",")))
-
-    def keep(kind, sliding):
-        return not wanted or f"{kind}_{'sliding' if sliding else 'full'}" in wanted
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    A.lib()  # fail loudly if the HIP library is missing
-    wl = WORKLOADS[args.workload]
+def build_segments(key, wanted, dev, A, synth, torch):
+    """The calls of workload `key`, in step order: dicts with the workload,
+    the call's name, its roofline group, a run(phases) closure, the stages
+    timed separately and, per stage, the kernel and its algorithmic work."""
+    wl = WORKLOADS[key]
     d = 128
     bf16 = torch.bfloat16
     rope = A.Rope(theta=THETA, yarn=True, factor=8.0, orig_ctx=8192)
-    segments = []  # (name, kind, callable(phases), phase list, work, work unit)
+    segments = []
 
-    # ---- prefill layers
-    pf = wl["prefill"] or dict(B=0, T=0, H=0, G=0)
-    B, T, H, G = pf["B"], pf["T"], pf["H"], pf["G"]
-    n_layers = pf.get("layers", 0)
-    layer_list = ([(ell, A.olmo3_layer_type(ell, n_layers)) for ell in range(n_layers)]
-                  if n_layers else [(0, 0), (3, 1)]) if wl["prefill"] else []
-    print(f"[bench] workload {wl['name']}: preparing {len(layer_list)} prefill layer(s)", file=sys.stderr,
-          flush=True)
-    seed_base = 5 if n_layers else (2 if args.workload == "7b" else 4)
-    for ell, lt in layer_list:
-        sliding = lt == 0
-        if not keep("prefill", sliding):
-            continue
-        x = synth.layer_inputs(seed_base + (ell if n_layers else 0), ell, B, T, H, G, d,
-                               device=dev, dtype=bf16)
-        P = pf.get("pos_offset", 0)
-        cap = WINDOW if sliding else P + T
-        if P:
-            # a cache already holding positions 0 .. P-1 (the ring: the last
-            # WINDOW of them); each call rewrites the chunk's slots (on the
-            # ring, the slots its later calls read as the prefix: the values
-            # change from the second call on, the work does not)
-            kc, vc = synth.cache_fill(7, ell, B, G, cap, d, device=dev, dtype=bf16)
-        else:
-            kc = torch.zeros((B, G, cap, d), dtype=bf16, device=dev)
-            vc = torch.zeros_like(kc)
-        out = torch.empty_like(x["q_pre"])
-        ws = A.workspace(A.MODE_PREFILL, B, T, H, G, d, lt, bf16, cap, dev)
-        r = rope if not sliding else A.Rope(theta=THETA)
+    def keep(kind, sliding):
+        return not wanted or f"{kind}_{'sliding' if sliding else 'full'}" in wanted
 
-        def run(phases, x=x, kc=kc, vc=vc, out=out, ws=ws, lt=lt, r=r, P=P):
-            A.olmo3_attn_prefill(x["q_pre"], x["k_pre"], x["v"], x["q_gain"], x["k_gain"], kc, vc,
-                                 out, ws, window=WINDOW, layer_type=lt, rope=r, pos_offset=P,
-                                 phases=phases)
+    pf = wl["prefill"]
+    if pf:
+        B, T, H, G = pf["B"], pf["T"], pf["H"], pf["G"]
+        n_layers = pf.get("layers", 0)
+        layer_list = ([(ell, A.olmo3_layer_type(ell, n_layers)) for ell in range(n_layers)]
+                      if n_layers else [(0, 0), (3, 1)])
+        print(f"[bench] {wl['name']}: preparing {len(layer_list)} prefill layer(s)", file=sys.stderr,
+              flush=True)
+        seed_base = 5 if n_layers else (2 if key == "7b" else 4)
+        for ell, lt in layer_list:
+            sliding = lt == 0
+            if not keep("prefill", sliding):
+                continue
+            x = synth.layer_inputs(seed_base + (ell if n_layers else 0), ell, B, T, H, G, d,
+                                   device=dev, dtype=bf16)
+            P = pf.get("pos_offset", 0)
+            cap = WINDOW if sliding else P + T
+            if P:
+                # a cache already holding positions 0 .. P-1 (the ring: the last
+                # WINDOW of them); each call rewrites the chunk's slots (on the
+                # ring, the slots its later calls read as the prefix: the values
+                # change from the second call on, the work does not)
+                kc, vc = synth.cache_fill(7, ell, B, G, cap, d, device=dev, dtype=bf16)
+            else:
+                kc = torch.zeros((B, G, cap, d), dtype=bf16, device=dev)
+                vc = torch.zeros_like(kc)
+            out = torch.empty_like(x["q_pre"])
+            ws = A.workspace(A.MODE_PREFILL, B, T, H, G, d, lt, bf16, cap, dev)
+            r = rope if not sliding else A.Rope(theta=THETA)
 
-        segments.append(dict(name=f"prefill_{'sliding' if sliding else 'full'}_l{ell}", kind="prefill",
-                             sliding=sliding, run=run, phases=[A.PHASE_PROLOGUE, A.PHASE_ATTENTION],
-                             work=prefill_flops(T, H, d, WINDOW, sliding, B, P)))
+            def run(phases, x=x, kc=kc, vc=vc, out=out, ws=ws, lt=lt, r=r, P=P):
+                A.olmo3_attn_prefill(x["q_pre"], x["k_pre"], x["v"], x["q_gain"], x["k_gain"], kc,
+                                     vc, out, ws, window=WINDOW, layer_type=lt, rope=r,
+                                     pos_offset=P, phases=phases)
 
-    # ---- decode layers
+            kind = "sliding" if sliding else "full"
+            flops = prefill_flops(T, H, d, WINDOW, sliding, B, P)
+            segments.append(dict(
+                wl=key, wl_name=wl["name"], name=f"prefill_{kind}_l{ell}", kind="prefill",
+                group=f"{key}/prefill_{kind}" + ("" if n_layers else f"_l{ell}"), sliding=sliding,
+                run=run, phases=[A.PHASE_PROLOGUE, A.PHASE_ATTENTION],
+                kernels=["qknorm_rope_append_kernel", "prefill_d128_kernel"],
+                # the prologue's bytes are stated for calls at position 0 only
+                stage_work=[prefill_prologue_bytes(B, T, H, G, d, sliding) if not P else None, flops],
+                stage_bound=["hbm", "mfma"], work=flops))
+
     dc = wl["decode"]
     if dc:
         Bd, Hd, Gd, L = dc["B"], dc["H"], dc["G"], dc["L"]
@@ -259,23 +271,23 @@ def main():
         n_dec_layers = dc.get("layers", 0)
         dec_layers = ([(ell, A.olmo3_layer_type(ell, n_dec_layers)) for ell in range(n_dec_layers)]
                       if n_dec_layers else [(0, 0), (3, 1)])
-        dseed = 6 if n_dec_layers else (3 if args.workload == "7b" else 4)
+        dseed = 6 if n_dec_layers else (3 if key == "7b" else 4)
+        e4m3 = dc.get("e4m3", False)
         for ell, lt in dec_layers:
             sliding = lt == 0
             if not keep("decode", sliding):
                 continue
             cap = WINDOW if sliding else L
-            print(f"[bench] filling {'ring' if sliding else 'linear'} decode cache of layer {ell} "
-                  f"[{Bd}, {Gd}, {cap}, {d}] x2", file=sys.stderr, flush=True)
-            e4m3 = dc.get("e4m3", False)
+            print(f"[bench] {wl['name']}: filling {'ring' if sliding else 'linear'} decode cache of "
+                  f"layer {ell} [{Bd}, {Gd}, {cap}, {d}] x2", file=sys.stderr, flush=True)
             if e4m3:
                 kc, vc = synth.e4m3_cache_fill(dseed, (ell if n_dec_layers else 100 + lt), Bd, Gd,
                                                cap, d, device=dev)
             else:
-                kc, vc = synth.cache_fill(dseed, (ell if n_dec_layers else 100 + lt), Bd, Gd, cap, d,
-                                          device=dev, dtype=bf16)
-            x = synth.layer_inputs(dseed, (100 + ell if n_dec_layers else 200 + lt), Bd, 1, Hd, Gd, d,
-                                   device=dev, dtype=bf16)
+                kc, vc = synth.cache_fill(dseed, (ell if n_dec_layers else 100 + lt), Bd, Gd, cap,
+                                          d, device=dev, dtype=bf16)
+            x = synth.layer_inputs(dseed, (100 + ell if n_dec_layers else 200 + lt), Bd, 1, Hd, Gd,
+                                   d, device=dev, dtype=bf16)
             q = x["q_pre"][:, 0].contiguous()
             k = x["k_pre"][:, 0].contiguous()
             v = x["v"][:, 0].contiguous()
@@ -296,16 +308,46 @@ def main():
                                         window=WINDOW, layer_type=lt, rope=r, pos=pos, phases=phases)
 
             n = decode_rows(pos, WINDOW, sliding)
-            name = f"decode_{'sliding' if sliding else 'full'}" + (f"_l{ell}" if n_dec_layers else "")
-            segments.append(dict(name=name, kind="decode", sliding=sliding, run=run,
-                                 # the merge (a kernel only when a key range is split,
-                                 # which these batch sizes never need) shares the
-                                 # attention stage's events: one event pair fewer
-                                 phases=[A.PHASE_PROLOGUE, A.PHASE_ATTENTION | A.PHASE_MERGE],
-                                 work=decode_kv_bytes(Bd, Gd, d, n, elem=1 if e4m3 else 2),
-                                 rows=n))
-    torch.cuda.synchronize()
+            kind = "sliding" if sliding else "full"
+            name = f"decode_{kind}" + (f"_l{ell}" if n_dec_layers else "")
+            kv = decode_kv_bytes(Bd, Gd, d, n, elem=1 if e4m3 else 2)
+            segments.append(dict(
+                wl=key, wl_name=wl["name"], name=name, kind="decode",
+                group=f"{key}/decode_{kind}", sliding=sliding, run=run,
+                # the merge (a kernel only when a key range is split, which
+                # these batch sizes never need) shares the attention stage's
+                # events: one event pair fewer
+                phases=[A.PHASE_PROLOGUE, A.PHASE_ATTENTION | A.PHASE_MERGE],
+                kernels=["decode_prologue_kernel", decode_kernel(Hd, Gd, e4m3)],
+                stage_work=[decode_prologue_bytes(Bd, Hd, Gd, d, 1 if e4m3 else 2), kv],
+                stage_bound=["hbm", "hbm"], work=kv, rows=n))
+    return segments
 
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from global_hybrid_causal_amd import attn as A
+    from global_hybrid_causal_amd import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
+    wanted = set(filter(None, args.segments.split(",")))
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    A.lib()  # fail loudly if the HIP library is missing
+    segments = []
+    for key in args.workloads:
+        segments += build_segments(key, wanted, dev, A, synth, torch)
+    torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
 
     def step(record):
@@ -332,12 +374,7 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    # ---- per-kernel and per-call times (ms), averaged over the timed steps
-    dcfg = wl["decode"] or {}
-    kernel_names = {("prefill", 0): "qknorm_rope_append_kernel", ("prefill", 1): "prefill_d128_kernel",
-                    ("decode", 0): "decode_prologue_kernel",
-                    ("decode", 1): decode_kernel(dcfg.get("H", 1), dcfg.get("G", 1),
-                                                 bool(dcfg.get("e4m3")))}
+    # ---- per-stage and per-call times (ms), averaged over the timed steps
     for seg in segments:
         per_phase = [[evs[i].elapsed_time(evs[i + 1]) for evs in seg["events"]]
                      for i in range(len(seg["phases"]))]
@@ -345,36 +382,96 @@ def main():
         seg["call_ms"] = sum(seg["phase_ms"])
     ms_per_step = wall * 1e3 / args.steps
 
+    def tflops(segs):
+        return sum(s["work"] for s in segs) / (sum(s["call_ms"] for s in segs) * 1e-3) / 1e12
+
+    def gbs(segs):
+        return sum(s["work"] for s in segs) / (sum(s["call_ms"] for s in segs) * 1e-3) / 1e9
+
+    def roof(segs, stage, label):
+        """Roofline of one kernel over the launches of `segs` at `stage`:
+        algorithmic work per launch / mean launch time."""
+        ms = sum(s["phase_ms"][stage] for s in segs) / len(segs)
+        work = sum(s["stage_work"][stage] for s in segs) / len(segs)
+        kernel, bound = segs[0]["kernels"][stage], segs[0]["stage_bound"][stage]
+        mfma = bound == "mfma"
+        ach = work / (ms * 1e-3) / (1e12 if mfma else 1e9)
+        peak = PEAK_BF16_TFLOPS if mfma else PEAK_HBM_GBS
+        return dict(kernel=kernel, segment=label, launches_per_step=len(segs), bound=bound,
+                    achieved=round(ach, 2), peak=peak, unit="TFLOP/s" if mfma else "GB/s",
+                    frac=round(ach / peak, 4), traffic=measured_traffic(label, kernel),
+                    avg_ms=round(ms, 4))
+
+    groups = {}
+    for seg in segments:
+        groups.setdefault(seg["group"], []).append(seg)
+    rooflines = []
+    for label, segs in groups.items():
+        for stage in (1, 0):
+            if all(s["stage_work"][stage] for s in segs):
+                rooflines.append(roof(segs, stage, label))
+
     pre = [s for s in segments if s["kind"] == "prefill"]
     dec = [s for s in segments if s["kind"] == "decode"]
-    prefill_tflops = (sum(s["work"] for s in pre) / (sum(s["call_ms"] for s in pre) * 1e-3) / 1e12
-                      if pre else 0.0)
+    head = [s for s in pre if s["wl"] in HEADLINE] or pre
+    if head:
+        dominant = roof(head, 1, "+".join(sorted({s["wl"] for s in head})) + " prefill calls")
+        value, unit = tflops(head), "TFLOP/s"
+    else:
+        dominant = max(rooflines, key=lambda r: r["avg_ms"] * r["launches_per_step"])
+        value, unit = gbs(dec), "GB/s"
 
-    def roof(seg, phase_idx):
-        ms = seg["phase_ms"][phase_idx]
-        if seg["kind"] == "prefill":
-            ach = seg["work"] / (ms * 1e-3) / 1e12
-            kernel = kernel_names[("prefill", phase_idx)]
-            return dict(kernel=kernel, segment=seg["name"], bound="mfma",
-                        achieved=round(ach, 2), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
-                        frac=round(ach / PEAK_BF16_TFLOPS, 4),
-                        traffic=measured_traffic(wl["name"], seg["name"], kernel), avg_ms=round(ms, 4))
-        ach = seg["work"] / (ms * 1e-3) / 1e9
-        kernel = kernel_names[("decode", phase_idx)]
-        return dict(kernel=kernel, segment=seg["name"], bound="hbm",
-                    achieved=round(ach, 1), peak=PEAK_HBM_GBS, unit="GB/s",
-                    frac=round(ach / PEAK_HBM_GBS, 4),
-                    traffic=measured_traffic(wl["name"], seg["name"], kernel), avg_ms=round(ms, 4))
+    by_wl = {}
+    for key in args.workloads:
+        wl = WORKLOADS[key]
+        wp = [s for s in pre if s["wl"] == key]
+        wd = [s for s in dec if s["wl"] == key]
+        block = {"name": wl["name"]}
+        if wp:
+            pf = wl["prefill"]
+            block["prefill"] = {
+                "config": dict(pf, d=128, window=WINDOW, theta=THETA, yarn_full="factor 8, orig 8192"),
+                "tflops": round(tflops(wp), 2), "frac_of_peak": round(tflops(wp) / PEAK_BF16_TFLOPS, 4),
+                "attention_tflops": round(sum(s["work"] for s in wp) /
+                                          (sum(s["phase_ms"][1] for s in wp) * 1e-3) / 1e12, 2),
+                "calls_ms": round(sum(s["call_ms"] for s in wp), 4)}
+            if not pf.get("layers"):
+                block["prefill"]["calls"] = {
+                    s["name"]: {"call_ms": round(s["call_ms"], 4),
+                                "tflops": round(s["work"] / (s["call_ms"] * 1e-3) / 1e12, 2),
+                                "flop": s["work"]} for s in wp}
+            else:
+                block["prefill"]["layers"] = pf["layers"]
+                block["prefill"]["sliding_layers"] = sum(s["sliding"] for s in wp)
+        if wd:
+            dc = wl["decode"]
+            block["decode"] = {
+                "config": dict(dc, d=128, window=WINDOW, pos=dc["L"] - 1),
+                "gbs": round(gbs(wd), 1), "frac_of_peak": round(gbs(wd) / PEAK_HBM_GBS, 4),
+                "tokens_per_s": round(dc["B"] / (sum(s["call_ms"] for s in wd) * 1e-3), 1),
+                "cache_dtype": "e4m3" if dc.get("e4m3") else "bf16"}
+            if not dc.get("layers"):
+                block["decode"]["calls"] = {
+                    s["name"]: {"call_ms": round(s["call_ms"], 4),
+                                "gbs": round(s["work"] / (s["call_ms"] * 1e-3) / 1e9, 1),
+                                "kv_bytes": s["work"], "rows": s["rows"]} for s in wd}
+            elif len(wd) == dc["layers"]:
+                # per decode step of the stack: every layer reads its whole cache once
+                kv_step = sum(s["work"] for s in wd)
+                step_ms = sum(s["call_ms"] for s in wd)
+                block["decode"]["stack"] = {
+                    "layers": dc["layers"], "sliding": sum(s["sliding"] for s in wd),
+                    "kv_bytes_per_step": kv_step, "step_ms": round(step_ms, 4),
+                    "kv_bytes_per_token_of_context": kv_step // (dc["B"] * dc["L"]),
+                    "naive_bytes_per_token_of_context":
+                        NAIVE_BYTES_PER_TOKEN_7B // (2 if dc.get("e4m3") else 1)}
+        by_wl[key] = block
 
-    rooflines = [roof(s, 1) for s in segments]
-    dominant = max(zip(segments, rooflines), key=lambda sr: sr[0]["phase_ms"][1])[1]
-
-    dec_gbs = (sum(s["work"] for s in dec) / (sum(s["call_ms"] for s in dec) * 1e-3) / 1e9
-               if dec else 0.0)
+    names = [WORKLOADS[k]["name"] for k in args.workloads]
     result = {
         "metric": METRIC,
-        "value": round(prefill_tflops, 2) if pre else round(dec_gbs, 1),
-        "unit": "TFLOP/s" if pre else "GB/s",
+        "value": round(value, 2),
+        "unit": unit,
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -384,89 +481,93 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": wl["name"],
-                   "prefill": (dict(pf, d=d, window=WINDOW, theta=THETA, yarn_full="factor 8, orig 8192")
-                               if pre else None),
-                   "decode": (dict(dc, d=d, window=WINDOW, pos=dc["L"] - 1) if dc else None),
+        "config": {"workload": " + ".join(names), "workloads": args.workloads,
+                   "value_covers": ("prefill calls (prologue + attention) of " +
+                                    " and ".join(sorted({s["wl_name"] for s in head}))
+                                    if head else "decode calls"),
                    "parallelism": "single GPU"},
-        "prefill": {"tflops": round(prefill_tflops, 2),
-                    "frac_of_peak": round(prefill_tflops / PEAK_BF16_TFLOPS, 4),
-                    "calls": {s["name"]: {"call_ms": round(s["call_ms"], 4),
-                                          "tflops": round(s["work"] / (s["call_ms"] * 1e-3) / 1e12, 2),
-                                          "flop": s["work"]} for s in pre}},
+        "workloads": by_wl,
         "roofline": dominant,
         "rooflines": rooflines,
     }
-    if dec:
-        gbs = dec_gbs
-        result["decode"] = {"gbs": round(gbs, 1), "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4),
-                            "calls": {s["name"]: {"call_ms": round(s["call_ms"], 4),
-                                                  "gbs": round(s["work"] / (s["call_ms"] * 1e-3) / 1e9, 1),
-                                                  "kv_bytes": s["work"], "rows": s["rows"]}
-                                      for s in dec}}
-    if dc and dc.get("layers") and len(dec) == dc["layers"]:
-        # per decode step of the stack: every layer reads its whole cache once
-        kv_step = sum(s["work"] for s in dec)
-        step_ms = sum(s["call_ms"] for s in dec)
-        result["stack"] = {
-            "layers": dc["layers"], "sliding": sum(s["sliding"] for s in dec),
-            "kv_bytes_per_step": kv_step, "step_ms": round(step_ms, 4),
-            "tokens_per_s": round(dc["B"] / (step_ms * 1e-3), 1),
-            "kv_bytes_per_token_of_context": kv_step // (dc["B"] * dc["L"]),
-            "naive_bytes_per_token_of_context": NAIVE_BYTES_PER_TOKEN_7B // (2 if dc.get("e4m3") else 1),
-        }
-    if args.cpu_seconds > 0 and (pre or dec) and not (wl["prefill"] or {}).get("pos_offset"):
-        print(f"[bench] timing the CPU oracle for ~{args.cpu_seconds:.0f} s", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = (cpu_baseline(args, wl, segments, dev) if pre else
-                                  cpu_baseline_decode(args, wl))
-    if dc and dec:
-        result["decode"]["tokens_per_s"] = round(
-            dc["B"] / (sum(s["call_ms"] for s in dec) * 1e-3), 1)
-        result["decode"]["cache_dtype"] = "e4m3" if dc.get("e4m3") else "bf16"
+    plain = [k for k in args.workloads if WORKLOADS[k]["prefill"] and
+             not WORKLOADS[k]["prefill"].get("pos_offset")]
+    if args.cpu_seconds > 0 and plain:
+        print(f"[bench] timing the CPU oracle for ~{args.cpu_seconds:.0f} s", file=sys.stderr,
+              flush=True)
+        result["cpu_baseline"] = cpu_baseline(args, dev, args.cpu_seconds)
+    elif args.cpu_seconds > 0 and dec:
+        result["cpu_baseline"] = cpu_baseline_decode(args, WORKLOADS[dec[0]["wl"]])
     print(json.dumps(result), flush=True)
 
 
-def cpu_baseline(args, wl, segments, dev):
-    """The oracle, as it stands, on a bounded sample of the prefill workload:
-    blocks of 32 query rows of the sliding layer (all heads, the keys those
-    rows can see), spread over the sequence, until the time budget is spent.
-    FLOPs are counted like the GPU's (allowed pairs only)."""
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover - informational only
+        pass
+    return "unknown"
+
+
+def cpu_baseline(args, dev, seconds):
+    """The oracle, as it stands (fp64 NumPy), on a bounded sample of the 7B
+    layer prefill: blocks of 32 query rows (all heads, the keys those rows
+    can see) at random places of the sequence, half the budget on a sliding
+    and half on a full layer.  FLOPs are counted like the GPU's (allowed
+    pairs only).  The rates extrapolate to whole calls and to the long stack
+    (24 sliding + 8 full layers at T = 65,536), labelled as extrapolated."""
     import numpy as np
     import torch
 
     import oracle as O
-
-    threads = _blas_threads()
     from global_hybrid_causal_amd import synth
 
-    pf = wl["prefill"]
-    B, T, H, G, d = 1, pf["T"], pf["H"], pf["G"], 128
-    seed = 5 if pf.get("layers") else (2 if args.workload == "7b" else 4)
-    x = synth.layer_inputs(seed, 0, B, T, H, G, d, device=dev, dtype=torch.bfloat16)
+    threads = _blas_threads()
+    B, T, H, G, d = 1, 8192, 32, 32, 128
+    x = synth.layer_inputs(2, 0, B, T, H, G, d, device=dev, dtype=torch.bfloat16)
     hx = {k: v.detach().to("cpu", torch.float64).numpy() for k, v in x.items()}
-    rope = O.RopeParams(theta=THETA)
     rng = np.random.default_rng(0)
     rows_per_block = 32
-    flops = 0
-    blocks = 0
-    t0 = time.perf_counter()
-    while time.perf_counter() - t0 < args.cpu_seconds:
-        t_start = int(rng.integers(0, T - rows_per_block + 1))
-        rows = np.arange(t_start, t_start + rows_per_block)
-        k_lo = max(0, t_start - WINDOW + 1)
-        keys = np.arange(k_lo, t_start + rows_per_block)
-        O.attention_rows_ref(hx["q_pre"][0, rows], rows, hx["k_pre"][0, keys],
-                             hx["v"][0, keys].reshape(len(keys), G, d), keys, hx["q_gain"],
-                             hx["k_gain"], H=H, G=G, d=d, kv_heads=range(G), kind=O.SLIDING,
-                             window=WINDOW, rope=rope)
-        flops += 4 * d * H * int(np.minimum(rows + 1, WINDOW).sum())
-        blocks += 1
-    elapsed = time.perf_counter() - t0
-    return {"value": round(flops / elapsed / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"{blocks} blocks of {rows_per_block} query rows x {H} heads of the "
-                      f"{wl['name']} sliding prefill (T={T}, window {WINDOW}), fp64 NumPy, "
-                      f"{elapsed:.1f} s"}
+    rates, blocks, spent, done = {}, {}, 0.0, 0
+    for kind, rope in ((O.SLIDING, O.RopeParams(theta=THETA)),
+                       (O.FULL, O.RopeParams(theta=THETA, yarn=True, factor=8.0, orig_ctx=8192))):
+        flops, n, t0 = 0, 0, time.perf_counter()
+        while time.perf_counter() - t0 < seconds / 2:
+            t_start = int(rng.integers(0, T - rows_per_block + 1))
+            rows = np.arange(t_start, t_start + rows_per_block)
+            k_lo = max(0, t_start - WINDOW + 1) if kind == O.SLIDING else 0
+            keys = np.arange(k_lo, t_start + rows_per_block)
+            O.attention_rows_ref(hx["q_pre"][0, rows], rows, hx["k_pre"][0, keys],
+                                 hx["v"][0, keys].reshape(len(keys), G, d), keys, hx["q_gain"],
+                                 hx["k_gain"], H=H, G=G, d=d, kv_heads=range(G), kind=kind,
+                                 window=WINDOW, rope=rope)
+            allowed = np.minimum(rows + 1, WINDOW) if kind == O.SLIDING else rows + 1
+            flops += 4 * d * H * int(allowed.sum())
+            n += 1
+        elapsed = time.perf_counter() - t0
+        rates[kind] = flops / elapsed
+        blocks[kind] = n
+        spent += elapsed
+        done += flops
+    total = sum(blocks.values())
+    value = done / spent
+    f_s, f_f = prefill_flops(T, H, d, WINDOW, True), prefill_flops(T, H, d, WINDOW, False)
+    long_T = WORKLOADS["long"]["prefill"]["T"]
+    long_s = (24 * prefill_flops(long_T, H, d, WINDOW, True) / rates[O.SLIDING] +
+              8 * prefill_flops(long_T, H, d, WINDOW, False) / rates[O.FULL])
+    return {"value": round(value / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "cpu_model": _cpu_model(), "precision": "fp64 (NumPy, BLAS matmuls)", "kind": "oracle",
+            "sample": f"{total} blocks of {rows_per_block} query rows x {H} heads of the 7B layer "
+                      f"prefill (T={T}, window {WINDOW}): {blocks[O.SLIDING]} sliding, "
+                      f"{blocks[O.FULL]} full (YaRN), {spent:.1f} s in all",
+            "tflops_sliding": round(rates[O.SLIDING] / 1e12, 6),
+            "tflops_full": round(rates[O.FULL] / 1e12, 6),
+            "extrapolated_s": {"7b_prefill_sliding_call": round(f_s / rates[O.SLIDING], 1),
+                               "7b_prefill_full_call": round(f_f / rates[O.FULL], 1),
+                               "long_stack_prefill_32_layers": round(long_s, 1)}}
 
 
 def cpu_baseline_decode(args, wl):
@@ -506,7 +607,7 @@ def cpu_baseline_decode(args, wl):
     elapsed = time.perf_counter() - t0
     nbytes = calls * L * d * 2 * (1 if e4m3 else 2)
     return {"value": round(nbytes / elapsed / 1e9, 3), "unit": "GB/s", "cores": int(threads),
-            "kind": "oracle",
+            "cpu_model": _cpu_model(), "precision": "fp64 (NumPy)", "kind": "oracle",
             "sample": f"{calls} decode calls of one sequence x one key/value head ({group} query "
                       f"head{'s' if group > 1 else ''}) of a full layer at cache length {L}, fp64 "
                       f"NumPy, {elapsed:.1f} s"}

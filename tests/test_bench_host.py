@@ -45,14 +45,40 @@ def test_more_than_one_gpu_is_refused():
 
 
 def test_recorded_traffic_needs_unchanged_sources(monkeypatch):
-    key = ("olmo3-7b-layer", "decode_full")
-    entry = dict(bench.MEASURED_TRAFFIC[key])
-    monkeypatch.setitem(bench.MEASURED_TRAFFIC, key, dict(entry, sources="0" * 16))
-    assert bench.measured_traffic(*key, "decode_split_kernel") is None
+    key = ("7b/decode_full", "decode_split_kernel")
+    monkeypatch.setitem(bench.MEASURED_TRAFFIC, key, dict(bytes=123, sources="0" * 16))
+    assert bench.measured_traffic(*key) is None
     monkeypatch.setitem(bench.MEASURED_TRAFFIC, key,
-                        dict(entry, sources=bench.sources_digest("decode_split_kernel")))
-    assert bench.measured_traffic(*key, "decode_split_kernel") == entry["bytes"]
-    assert bench.measured_traffic("olmo3-7b-layer", "no such segment", "decode_split_kernel") is None
+                        dict(bytes=123, sources=bench.sources_digest("decode_split_kernel")))
+    assert bench.measured_traffic(*key) == 123
+    assert bench.measured_traffic("7b/no such group", "decode_split_kernel") is None
+
+
+def test_every_recorded_traffic_figure_is_current():
+    """A figure whose kernel's sources changed since it was measured is
+    reported null; the table keeps only current ones."""
+    for (group, kernel), entry in bench.MEASURED_TRAFFIC.items():
+        assert bench.sources_digest(kernel) == entry["sources"], (group, kernel)
+
+
+def test_prologue_bytes():
+    # 7B sliding prefill at T = 8192: read q, k, v (3 x 64 MiB), write rotated q
+    # (64 MiB), the ring's 4096 kept rows of k and v (2 x 32 MiB) and the
+    # rotated-key copy (64 MiB)
+    mib = 1 << 20
+    assert bench.prefill_prologue_bytes(1, 8192, 32, 32, 128, True) == (3 * 64 + 64 + 64 + 64) * mib
+    assert bench.prefill_prologue_bytes(1, 8192, 32, 32, 128, False) == (3 * 64 + 64 + 128) * mib
+    assert bench.decode_prologue_bytes(32, 32, 32, 128) == 32 * (96 + 32 + 64) * 128 * 2
+
+
+def test_workload_list_is_parsed(monkeypatch):
+    monkeypatch.setattr(sys, "argv", ["bench.py", "--workload", "7b,32b"])
+    assert bench.parse().workloads == ["7b", "32b"]
+    monkeypatch.setattr(sys, "argv", ["bench.py"])
+    assert bench.parse().workloads == ["7b", "32b", "long"]
+    monkeypatch.setattr(sys, "argv", ["bench.py", "--workload", "7b,nope"])
+    with pytest.raises(SystemExit):
+        bench.parse()
 
 
 def test_decode_kernel_label():
