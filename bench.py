@@ -52,9 +52,9 @@ THETA = 500000.0
 
 
 # HBM bytes per launch of the timed kernels, from two rocprofv3 --pmc runs of
-# this script (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled by
-# what the same counter reads for a 1 GiB device-to-device copy on the same
-# GPU.  Keyed by (roofline group, kernel); a group of several launches (the
+# this script's default step (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch),
+# each scaled by what the same counter reads for a 1 GiB device-to-device
+# copy on the same GPU (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0).  Keyed by (roofline group, kernel); a group of several launches (the
 # long stack's layers of one kind) holds the mean per launch.  An entry holds
 # only while the kernel's sources hash to `sources`; otherwise the figure is
 # reported null.
@@ -73,7 +73,30 @@ def decode_kernel(H: int, G: int, e4m3: bool) -> str:
     return "decode_mfma_kernel" if not e4m3 and H // G >= 2 else "decode_split_kernel"
 
 
-MEASURED_TRAFFIC = {}
+MEASURED_TRAFFIC = {
+    ("7b/prefill_sliding_l0", "qknorm_rope_append_kernel"): dict(bytes=369845772, sources="2fb156025c4a8ef3"),
+    ("7b/prefill_sliding_l0", "prefill_d128_kernel"): dict(bytes=691577792, sources="93fd7ea55a1002ac"),
+    ("7b/prefill_full_l3", "qknorm_rope_append_kernel"): dict(bytes=403390241, sources="2fb156025c4a8ef3"),
+    ("7b/prefill_full_l3", "prefill_d128_kernel"): dict(bytes=291699924, sources="93fd7ea55a1002ac"),
+    ("7b/decode_sliding", "decode_prologue_kernel"): dict(bytes=1897629, sources="2fb156025c4a8ef3"),
+    ("7b/decode_sliding", "decode_split_kernel"): dict(bytes=2148090805, sources="62153bad07e099ab"),
+    ("7b/decode_full", "decode_prologue_kernel"): dict(bytes=1914076, sources="2fb156025c4a8ef3"),
+    ("7b/decode_full", "decode_split_kernel"): dict(bytes=34359324310, sources="62153bad07e099ab"),
+    ("32b/prefill_sliding_l0", "qknorm_rope_append_kernel"): dict(bytes=227168987, sources="2fb156025c4a8ef3"),
+    ("32b/prefill_sliding_l0", "prefill_d128_kernel"): dict(bytes=321982807, sources="93fd7ea55a1002ac"),
+    ("32b/prefill_full_l3", "qknorm_rope_append_kernel"): dict(bytes=235557136, sources="2fb156025c4a8ef3"),
+    ("32b/prefill_full_l3", "prefill_d128_kernel"): dict(bytes=311770651, sources="93fd7ea55a1002ac"),
+    ("32b/decode_sliding", "decode_prologue_kernel"): dict(bytes=2117146, sources="2fb156025c4a8ef3"),
+    ("32b/decode_sliding", "decode_mfma_kernel"): dict(bytes=1079630169, sources="62153bad07e099ab"),
+    ("32b/decode_full", "decode_prologue_kernel"): dict(bytes=2120858, sources="2fb156025c4a8ef3"),
+    ("32b/decode_full", "decode_mfma_kernel"): dict(bytes=8623216498, sources="62153bad07e099ab"),
+    ("long/prefill_sliding", "qknorm_rope_append_kernel"): dict(bytes=2249094398, sources="2fb156025c4a8ef3"),
+    ("long/prefill_sliding", "prefill_d128_kernel"): dict(bytes=22647474972, sources="93fd7ea55a1002ac"),
+    ("long/prefill_full", "qknorm_rope_append_kernel"): dict(bytes=3222459761, sources="2fb156025c4a8ef3"),
+    ("long/prefill_full", "prefill_d128_kernel"): dict(bytes=10502534280, sources="93fd7ea55a1002ac"),
+    # mean per launch over the four 7B and 32B layer launches (the `roofline` group)
+    ("32b+7b prefill calls", "prefill_d128_kernel"): dict(bytes=404257793, sources="93fd7ea55a1002ac"),
+}
 
 
 def sources_digest(kernel: str) -> str:
