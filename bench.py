@@ -23,12 +23,14 @@ in a list:
 Printed: one JSON line.  `value` is prefill TFLOP/s (algorithmic FLOPs of the
 allowed query/key pairs over the whole call time, prologue included) over the
 prefill calls of the 7B and 32B layers when either is run (else over every
-prefill call, else decode KV GB/s); per-workload blocks give each call.  Each
-kernel is bracketed by HIP events on the stream it is launched on (the
-stage-by-stage entry points), giving the per-kernel rooflines; a decode
-call's merge stage shares its attention stage's events (at these batch sizes
-each (sequence, key/value head) is one workgroup of the split kernel, which
-writes the output itself, and no merge kernel runs).  The CPU oracle is timed
+prefill call, else decode KV GB/s); per-workload blocks give each call.  The
+timed steps run twice.  First stage by stage: each kernel is bracketed by HIP
+events on the stream it is launched on (the stage-by-stage entry points),
+giving the per-kernel rooflines; a decode call's merge stage shares its
+attention stage's events (at these batch sizes each (sequence, key/value
+head) is one workgroup of the split kernel, which writes the output itself,
+and no merge kernel runs).  Then call by call, one pair of events around each
+whole call: the call times, `value` and ms_per_step.  The CPU oracle is timed
 on a bounded sample of the 7B layer shape.
 """
 
@@ -373,27 +375,43 @@ def main():
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
 
-    def step(record):
+    whole = {"prefill": A.PHASE_PROLOGUE | A.PHASE_ATTENTION, "decode": A.PHASES_ALL}
+
+    def step(mode):
+        """mode None: untimed; "stages": every stage of every call between its
+        own events; "calls": every call whole, between one pair of events."""
         for seg in segments:
-            if record:
+            if mode == "stages":
                 evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(seg["phases"]) + 1)]
                 evs[0].record(stream)
                 for i, ph in enumerate(seg["phases"]):
                     seg["run"](ph)
                     evs[i + 1].record(stream)
                 seg.setdefault("events", []).append(evs)
+            elif mode == "calls":
+                evs = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+                evs[0].record(stream)
+                seg["run"](whole[seg["kind"]])
+                evs[1].record(stream)
+                seg.setdefault("call_events", []).append(evs)
             else:
-                seg["run"](A.PHASES_ALL if seg["kind"] == "decode" else
-                           A.PHASE_PROLOGUE | A.PHASE_ATTENTION)
+                seg["run"](whole[seg["kind"]])
 
     print(f"[bench] warmup {args.warmup} step(s)", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
-        step(False)
+        step(None)
     torch.cuda.synchronize()
-    print(f"[bench] timing {args.steps} step(s)", file=sys.stderr, flush=True)
+    # the timed steps, twice: stage by stage for the per-kernel figures, then
+    # call by call (no events between a call's kernels) for the call times,
+    # `value` and ms_per_step
+    print(f"[bench] timing {args.steps} step(s), stage by stage", file=sys.stderr, flush=True)
+    for _ in range(args.steps):
+        step("stages")
+    torch.cuda.synchronize()
+    print(f"[bench] timing {args.steps} step(s), call by call", file=sys.stderr, flush=True)
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        step(True)
+        step("calls")
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
@@ -402,7 +420,8 @@ def main():
         per_phase = [[evs[i].elapsed_time(evs[i + 1]) for evs in seg["events"]]
                      for i in range(len(seg["phases"]))]
         seg["phase_ms"] = [sum(p) / len(p) for p in per_phase]
-        seg["call_ms"] = sum(seg["phase_ms"])
+        calls = [e0.elapsed_time(e1) for e0, e1 in seg["call_events"]]
+        seg["call_ms"] = sum(calls) / len(calls)
     ms_per_step = wall * 1e3 / args.steps
 
     def tflops(segs):
