@@ -41,6 +41,9 @@ CHUNK_CASES = [
     (2, 33, 2, 1, 16, 4096, 1, 20, True, BF16),      # plain kernel, linear
     (1, 8, 2, 1, 16, 16, 0, 64, False, F32),         # fp32, ring
     (1, 8, 2, 1, 16, 16, 1, 64, False, F32),         # fp32, linear
+    # the last positions a prefill takes (pos_offset + T = 2^30), on rings
+    (1, 700, 4, 2, 128, 4096, 0, (1 << 30) - 700, False, BF16),
+    (2, 300, 8, 2, 128, 256, 0, (1 << 30) - 300, False, BF16),
 ]
 
 

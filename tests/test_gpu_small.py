@@ -135,6 +135,9 @@ DECODE_CASES = [
     (2, 64, 64, 128, 256, 0, 700, 256),     # 64 heads: the decode prologue's 1,536 pair chunks
     (3, 64, 8, 128, 4096, 1, 300, 301),     # group 8 with 64 query heads
     (5, 1, 1, 128, 64, 0, 63, 64),          # a single head
+    # the last position a decode takes (2^40 - 1), on rings
+    (3, 8, 8, 128, 4096, 0, (1 << 40) - 1, 4096),
+    (2, 10, 2, 128, 256, 0, (1 << 40) - 1, 256),
 ]
 
 
