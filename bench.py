@@ -76,28 +76,28 @@ def decode_kernel(H: int, G: int, e4m3: bool) -> str:
 
 
 MEASURED_TRAFFIC = {
-    ("7b/prefill_sliding_l0", "qknorm_rope_append_kernel"): dict(bytes=369845772, sources="2fb156025c4a8ef3"),
-    ("7b/prefill_sliding_l0", "prefill_d128_kernel"): dict(bytes=691577792, sources="93fd7ea55a1002ac"),
-    ("7b/prefill_full_l3", "qknorm_rope_append_kernel"): dict(bytes=403390241, sources="2fb156025c4a8ef3"),
-    ("7b/prefill_full_l3", "prefill_d128_kernel"): dict(bytes=291699924, sources="93fd7ea55a1002ac"),
-    ("7b/decode_sliding", "decode_prologue_kernel"): dict(bytes=1897629, sources="2fb156025c4a8ef3"),
-    ("7b/decode_sliding", "decode_split_kernel"): dict(bytes=2148090805, sources="62153bad07e099ab"),
-    ("7b/decode_full", "decode_prologue_kernel"): dict(bytes=1914076, sources="2fb156025c4a8ef3"),
-    ("7b/decode_full", "decode_split_kernel"): dict(bytes=34359324310, sources="62153bad07e099ab"),
-    ("32b/prefill_sliding_l0", "qknorm_rope_append_kernel"): dict(bytes=227168987, sources="2fb156025c4a8ef3"),
-    ("32b/prefill_sliding_l0", "prefill_d128_kernel"): dict(bytes=321982807, sources="93fd7ea55a1002ac"),
-    ("32b/prefill_full_l3", "qknorm_rope_append_kernel"): dict(bytes=235557136, sources="2fb156025c4a8ef3"),
-    ("32b/prefill_full_l3", "prefill_d128_kernel"): dict(bytes=311770651, sources="93fd7ea55a1002ac"),
-    ("32b/decode_sliding", "decode_prologue_kernel"): dict(bytes=2117146, sources="2fb156025c4a8ef3"),
-    ("32b/decode_sliding", "decode_mfma_kernel"): dict(bytes=1079630169, sources="62153bad07e099ab"),
-    ("32b/decode_full", "decode_prologue_kernel"): dict(bytes=2120858, sources="2fb156025c4a8ef3"),
-    ("32b/decode_full", "decode_mfma_kernel"): dict(bytes=8623216498, sources="62153bad07e099ab"),
-    ("long/prefill_sliding", "qknorm_rope_append_kernel"): dict(bytes=2249094398, sources="2fb156025c4a8ef3"),
-    ("long/prefill_sliding", "prefill_d128_kernel"): dict(bytes=22647474972, sources="93fd7ea55a1002ac"),
-    ("long/prefill_full", "qknorm_rope_append_kernel"): dict(bytes=3222459761, sources="2fb156025c4a8ef3"),
-    ("long/prefill_full", "prefill_d128_kernel"): dict(bytes=10502534280, sources="93fd7ea55a1002ac"),
+    ("7b/prefill_sliding_l0", "qknorm_rope_append_kernel"): dict(bytes=369838441, sources="2fb156025c4a8ef3"),
+    ("7b/prefill_sliding_l0", "prefill_d128_kernel"): dict(bytes=693459909, sources="93d82eb0e87feae3"),
+    ("7b/prefill_full_l3", "qknorm_rope_append_kernel"): dict(bytes=403387324, sources="2fb156025c4a8ef3"),
+    ("7b/prefill_full_l3", "prefill_d128_kernel"): dict(bytes=299191039, sources="93d82eb0e87feae3"),
+    ("7b/decode_sliding", "decode_prologue_kernel"): dict(bytes=1895042, sources="2fb156025c4a8ef3"),
+    ("7b/decode_sliding", "decode_split_kernel"): dict(bytes=2148069154, sources="62153bad07e099ab"),
+    ("7b/decode_full", "decode_prologue_kernel"): dict(bytes=1910722, sources="2fb156025c4a8ef3"),
+    ("7b/decode_full", "decode_split_kernel"): dict(bytes=34359465561, sources="62153bad07e099ab"),
+    ("32b/prefill_sliding_l0", "qknorm_rope_append_kernel"): dict(bytes=227168162, sources="2fb156025c4a8ef3"),
+    ("32b/prefill_sliding_l0", "prefill_d128_kernel"): dict(bytes=325430664, sources="93d82eb0e87feae3"),
+    ("32b/prefill_full_l3", "qknorm_rope_append_kernel"): dict(bytes=235556799, sources="2fb156025c4a8ef3"),
+    ("32b/prefill_full_l3", "prefill_d128_kernel"): dict(bytes=321993268, sources="93d82eb0e87feae3"),
+    ("32b/decode_sliding", "decode_prologue_kernel"): dict(bytes=2113824, sources="2fb156025c4a8ef3"),
+    ("32b/decode_sliding", "decode_mfma_kernel"): dict(bytes=1079471916, sources="62153bad07e099ab"),
+    ("32b/decode_full", "decode_prologue_kernel"): dict(bytes=2116767, sources="2fb156025c4a8ef3"),
+    ("32b/decode_full", "decode_mfma_kernel"): dict(bytes=8622425676, sources="62153bad07e099ab"),
+    ("long/prefill_sliding", "qknorm_rope_append_kernel"): dict(bytes=2249098936, sources="2fb156025c4a8ef3"),
+    ("long/prefill_sliding", "prefill_d128_kernel"): dict(bytes=20774993678, sources="93d82eb0e87feae3"),
+    ("long/prefill_full", "qknorm_rope_append_kernel"): dict(bytes=3222471686, sources="2fb156025c4a8ef3"),
+    ("long/prefill_full", "prefill_d128_kernel"): dict(bytes=11960036002, sources="93d82eb0e87feae3"),
     # mean per launch over the four 7B and 32B layer launches (the `roofline` group)
-    ("32b+7b prefill calls", "prefill_d128_kernel"): dict(bytes=404257793, sources="93fd7ea55a1002ac"),
+    ("32b+7b prefill calls", "prefill_d128_kernel"): dict(bytes=410018720, sources="93d82eb0e87feae3"),
 }
 
 

@@ -30,8 +30,8 @@ __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const
 // the S accumulators (converted to bf16) as the B operand.
 //
 // K and V tiles go from global memory straight into LDS
-// (global_load_lds_dwordx4: lane l of a wavefront fills bytes 16 l .. 16 l + 15
-// after the wavefront's base), row-major, 256-byte rows, with XOR-swizzled
+// (buffer_load_dwordx4 ... lds: lane l of a wavefront fills bytes 16 l ..
+// 16 l + 15 after the wavefront's base), row-major, 256-byte rows, with XOR-swizzled
 // 16-byte columns: column c of K row r sits at c ^ (r mod 16), of V row r at
 // c ^ 4 (r mod 4).  The V^T operand is read with ds_read_b64_tr_b16: within a
 // group of 16 lanes, lane i receives element i mod 4 of the 8-byte pieces
@@ -47,6 +47,19 @@ __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const
 // step of tile j loads K_{j+2} and V_{j+1} into the buffers that held K_j and
 // V_{j-1}, which every wavefront was done with before that step's barrier.
 //
+// The step's instruction order is fixed by hand (scheduling fences between
+// MFMA slots): each of the 16 S MFMAs is followed by the LDS read of the K
+// operand three MFMAs ahead and one pair of this tile's weights (two exp2, a
+// bf16 pack, a dot2 into the row sum); each of the 16 O MFMAs by the
+// transposed reads of the V operand two MFMAs ahead, and the O MFMAs also
+// cover the next tile's maximum.  Two choices keep the compiler's wait
+// counters precise: the tile loads are MUBUF (buffer_load ... lds) rather
+// than global_load_lds, whose outstanding loads make every LDS read wait for
+// all of them (lgkmcnt(0)); and each LDS buffer is its own __shared__ array,
+// so the transposed reads of one V buffer are known not to alias the loads
+// still landing in the other buffers (one array makes the first transposed
+// read of a step wait for every load issued at the step's start).
+//
 // The tiles of a query block split into three runs: far window edge, interior
 // (every pair visible: no mask code at all) and diagonal.  The running maximum
 // is rescaled lazily: O and the row sum are rescaled only when a tile's
@@ -60,8 +73,16 @@ constexpr float kRescaleSlack = 8.0f;             // log2 units
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
-__device__ __forceinline__ void load_to_lds(const bf16* src, char* dst) {
-  __builtin_amdgcn_global_load_lds((const void*)src, (lds_ptr)dst, 16, 0, 0);
+// Buffer resource for a run of rows starting at p: raw (stride 0), range
+// 2^31 - 1 bytes (the per-lane offsets of one tile stay far below), dword 3
+// as gfx950 takes it for untyped loads.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* p) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, 0x7fffffff, 0x00020000);
+}
+
+// 16 bytes per lane from rs + off into LDS at dst + 16 * lane (dst uniform).
+__device__ __forceinline__ void load_to_lds(__amdgpu_buffer_rsrc_t rs, uint32_t off, char* dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr)dst, 16, off, 0, 0, 0);
 }
 
 // max(x[l], x[l ^ 32]) in every lane: v_permlane32_swap exchanges the upper
@@ -88,9 +109,11 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const char* p) {
 template <bool kPrefix, bool kPacked, bool kSplit = false>
 __global__ __launch_bounds__(256, 2) void prefill_d128_kernel(AttnArgs a) {
   using namespace pf;
-  __shared__ __attribute__((aligned(16))) char smem[4 * kTileBytes];
-  char* const sK = smem;                   // K ring: 2 x 16 KiB
-  char* const sV = smem + 2 * kTileBytes;  // V ring: 2 x 16 KiB
+  // K ring and V ring, two 16 KiB buffers each, one array per buffer
+  __shared__ __attribute__((aligned(512))) char sK0[kTileBytes], sK1[kTileBytes];
+  __shared__ __attribute__((aligned(512))) char sV0[kTileBytes], sV1[kTileBytes];
+  auto kbuf_of = [&](int b) __attribute__((always_inline)) { return b ? sK1 : sK0; };
+  auto vbuf_of = [&](int b) __attribute__((always_inline)) { return b ? sV1 : sV0; };
 
   const int n_qblk = (a.Tq + kBQ - 1) / kBQ;
   int split = 0;
@@ -139,10 +162,11 @@ __global__ __launch_bounds__(256, 2) void prefill_d128_kernel(AttnArgs a) {
   const int lrow = 4 * wave + (lane >> 4);  // row within each 16-row slab
   const int kcol = (lane & 15) ^ (lrow & 15);
   const int vcol = (lane & 15) ^ (4 * (lrow & 3));
-  // Uniform per-head bases plus 32-bit per-lane byte offsets.  Tiles
-  // whose 64 rows are consecutive rows of one source take the fast path;
-  // the last tile (positions past n_keys) and, with a prefix, tiles that
-  // cross the prefix/main boundary or the ring's wrap go row by row.
+  // A tile's loads use a buffer resource based at its first row plus 32-bit
+  // per-lane byte offsets.  Tiles whose 64 rows are consecutive rows of one
+  // source take that fast path; the last tile (positions past n_keys) and,
+  // with a prefix, tiles that cross the prefix/main boundary or the ring's
+  // wrap go row by row.
   const bool packed_main = kPacked && a.main_packed;
   const bf16* kbase = (const bf16*)a.k + (packed_main ? row0 * a.k_sr : w.b * a.k_sb) + g * a.k_sg;
   const bf16* vbase = (const bf16*)a.v + (packed_main ? row0 * a.v_sr : w.b * a.v_sb) + g * a.v_sg;
@@ -168,35 +192,34 @@ __global__ __launch_bounds__(256, 2) void prefill_d128_kernel(AttnArgs a) {
                        const uint32_t* poff, int col8, int k0, char* dst) __attribute__((always_inline)) {
     if (!kPrefix || k0 >= main0) {
       if (k0 + kBK <= n_keys) {
-        const char* tb = (const char*)(base + (int64_t)(k0 - main0) * sr);
+        const auto rs = rows_rsrc(base + (int64_t)(k0 - main0) * sr);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) load_to_lds((const bf16*)(tb + off[i]), dst + 16 * i * 256);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = min(k0 + 16 * i + lrow, n_keys - 1) - main0;
-          load_to_lds(base + (int64_t)row * sr + col8, dst + 16 * i * 256);
-        }
+        for (int i = 0; i < 4; ++i) load_to_lds(rs, off[i], dst + 16 * i * 256);
+        return;
       }
     } else if (k0 + kBK <= main0 && k0 % ring + kBK <= ring) {
-      const char* tb = (const char*)(pbase + (int64_t)(k0 % ring) * p_sr);
+      const auto rs = rows_rsrc(pbase + (int64_t)(k0 % ring) * p_sr);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) load_to_lds((const bf16*)(tb + poff[i]), dst + 16 * i * 256);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int p = min(k0 + 16 * i + lrow, n_keys - 1);
-        const bf16* src = p >= main0 ? base + (int64_t)(p - main0) * sr + col8
-                                     : pbase + (int64_t)(p % ring) * p_sr + col8;
-        load_to_lds(src, dst + 16 * i * 256);
-      }
+      for (int i = 0; i < 4; ++i) load_to_lds(rs, poff[i], dst + 16 * i * 256);
+      return;
     }
+    // row by row: each load covers four rows of 16 lanes; the lanes of each
+    // row load it from a resource based at that row (uniform per row)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int p = min(k0 + 16 * i + 4 * wave + r, n_keys - 1);
+        const bf16* row = (!kPrefix || p >= main0) ? base + (int64_t)(p - main0) * sr
+                                                   : pbase + (int64_t)(p % ring) * p_sr;
+        if ((lane >> 4) == r) load_to_lds(rows_rsrc(row), (uint32_t)(col8 * 2), dst + 16 * i * 256);
+      }
   };
   auto load_k = [&](int k0, int buf) __attribute__((always_inline)) {
-    load_rows(kbase, a.k_sr, k_off, kpbase, kp_off, kcol * 8, k0, sK + buf * kTileBytes + slab);
+    load_rows(kbase, a.k_sr, k_off, kpbase, kp_off, kcol * 8, k0, kbuf_of(buf) + slab);
   };
   auto load_v = [&](int k0, int buf) __attribute__((always_inline)) {
-    load_rows(vbase, a.v_sr, v_off, vpbase, vp_off, vcol * 8, k0, sV + buf * kTileBytes + slab);
+    load_rows(vbase, a.v_sr, v_off, vpbase, vp_off, vcol * 8, k0, vbuf_of(buf) + slab);
   };
 
   // LDS read offsets.  K (A operand of S^T): row 32 kb + col, column
@@ -215,7 +238,7 @@ __global__ __launch_bounds__(256, 2) void prefill_d128_kernel(AttnArgs a) {
   }
 
   auto qk = [&](int buf, f32x16& s0, f32x16& s1) __attribute__((always_inline)) {
-    const char* k = sK + buf * kTileBytes;
+    const char* k = kbuf_of(buf);
 #pragma unroll
     for (int r = 0; r < 16; ++r) s0[r] = s1[r] = 0.f;
 #pragma unroll
@@ -235,10 +258,32 @@ __global__ __launch_bounds__(256, 2) void prefill_d128_kernel(AttnArgs a) {
   float m = -1e30f, lsum = 0.f;
   const float c = a.scale_log2;
   f32x16 s0, s1;  // scores of the current tile
+  // c times the unmasked maximum of the current tile's scores, taken during
+  // the previous step (a masked tile recomputes it after masking)
+  float mt_next = 0.f;
+  const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
+
+  // c times the maximum of a tile's 64 scores of this lane's query: a max3
+  // tree (depth 4), then the partner lane (l ^ 32)
+  auto tile_max = [&](const f32x16& x0, const f32x16& x1) __attribute__((always_inline)) {
+    float t1[12];
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+      t1[i] = fmaxf(fmaxf(x0[3 * i], x0[3 * i + 1]), x0[3 * i + 2]);
+      t1[5 + i] = fmaxf(fmaxf(x1[3 * i], x1[3 * i + 1]), x1[3 * i + 2]);
+    }
+    t1[10] = x0[15];
+    t1[11] = x1[15];
+    const float t2a = fmaxf(fmaxf(t1[0], t1[1]), t1[2]), t2b = fmaxf(fmaxf(t1[3], t1[4]), t1[5]);
+    const float t2c = fmaxf(fmaxf(t1[6], t1[7]), t1[8]), t2d = fmaxf(fmaxf(t1[9], t1[10]), t1[11]);
+    return pair_max(fmaxf(fmaxf(t2a, t2b), fmaxf(t2c, t2d))) * c;
+  };
 
   // Step of tile kt.  kMask: apply the visibility predicate per element.
   // kBuf: buffers holding K_kt and V_kt ((kt - kta) mod 2, known at compile
-  // time so that every LDS offset is an immediate).
+  // time so that every LDS address is a constant offset).  Operand rings:
+  // K reads run kKA MFMAs ahead of their use, V reads kVA.
+  constexpr int kKA = 3, kVA = 2;
   auto step = [&](int kt, auto mask_tag, auto buf_tag) __attribute__((always_inline)) {
     constexpr bool kMask = decltype(mask_tag)::value;
     constexpr int jb = decltype(buf_tag)::value;
@@ -248,25 +293,32 @@ __global__ __launch_bounds__(256, 2) void prefill_d128_kernel(AttnArgs a) {
     if (kt + 2 < ktb) load_k(k0 + 2 * kBK, jb);
     if (kt + 1 < ktb) load_v(k0 + kBK, jb ^ 1);
 
+    const char* kbuf = kbuf_of(jb ^ 1);  // K of tile kt + 1
+    const char* vbuf = vbuf_of(jb);      // V of tile kt
+    // K operand of S MFMA i (i = 0..15): 16-dim chunk i / 2, keys 32 (i mod 2) ..
+    auto kread = [&](int i) __attribute__((always_inline)) {
+      return *(const bf16x8*)(kbuf + koff[i >> 1] + (i & 1) * 32 * 256);
+    };
+    // V^T operand of O MFMA i: keys 16 (i / 4) .., dims 32 (i mod 4) ..
+    auto vread = [&](int i) __attribute__((always_inline)) {
+      const int kk = i >> 2, db = i & 3;
+      const bf16x4 lo4 = lds_read_tr(vbuf + voff[db] + (16 * kk) * 256);
+      const bf16x4 hi4 = lds_read_tr(vbuf + voff[db] + (16 * kk + 8) * 256);
+      return bf16x8{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+    };
+    // the first K reads overlap the mask, maximum and rescale test
+    bf16x8 ka[kKA + 1];
+#pragma unroll
+    for (int i = 0; i < kKA; ++i) ka[i] = kread(i);
+    __builtin_amdgcn_sched_barrier(0);
+
+    float mt = mt_next;
     if constexpr (kMask) {
       // the two 32-key blocks of the tile start at k0 and k0 + 32
       mask_block(s0, tq, k0, lane, a.window, a.sliding);
       mask_block(s1, tq, k0 + 32, lane, a.window, a.sliding);
+      mt = tile_max(s0, s1);
     }
-    // tile maximum: a max3 tree (depth 4), then the partner lane (l ^ 32)
-    float t1[12];
-#pragma unroll
-    for (int i = 0; i < 5; ++i) {
-      t1[i] = fmaxf(fmaxf(s0[3 * i], s0[3 * i + 1]), s0[3 * i + 2]);
-      t1[5 + i] = fmaxf(fmaxf(s1[3 * i], s1[3 * i + 1]), s1[3 * i + 2]);
-    }
-    t1[10] = s0[15];
-    t1[11] = s1[15];
-    const float t2a = fmaxf(fmaxf(t1[0], t1[1]), t1[2]), t2b = fmaxf(fmaxf(t1[3], t1[4]), t1[5]);
-    const float t2c = fmaxf(fmaxf(t1[6], t1[7]), t1[8]), t2d = fmaxf(fmaxf(t1[9], t1[10]), t1[11]);
-    float mx = fmaxf(fmaxf(t2a, t2b), fmaxf(t2c, t2d));
-    mx = pair_max(mx);
-    const float mt = mx * c;
     if (__ballot(mt > m + kRescaleSlack)) {
       const float mn = fmaxf(m, mt);
       float alpha = fast_exp2(m - mn);
@@ -280,57 +332,70 @@ __global__ __launch_bounds__(256, 2) void prefill_d128_kernel(AttnArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
     }
-
-    // S of the next tile (on the last tile the result is discarded)
-    f32x16 n0, n1;
-    qk(jb ^ 1, n0, n1);
-
     const float nm = -m;
+
     bf16x8 pk[4];
+    // weights of key pair p of the tile (p = 0..15: 16-key chunk p / 4, pair
+    // p mod 4), packed to bf16 and added to the row sum
+    auto pair = [&](int p) __attribute__((always_inline)) {
+      const int kk = p >> 2, e = 2 * (p & 3), r = (kk & 1) * 8 + e;
+      const float x0 = (kk < 2 ? s0 : s1)[r], x1 = (kk < 2 ? s0 : s1)[r + 1];
+      pk[kk][e] = (bf16)fast_exp2(fmaf(x0, c, nm));
+      pk[kk][e + 1] = (bf16)fast_exp2(fmaf(x1, c, nm));
+      const bf16x2 pr = {pk[kk][e], pk[kk][e + 1]};
+      lsum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lsum, false);
+    };
+
+    // S of the next tile (on the last tile the result is discarded): MFMA i,
+    // then the K read for MFMA i + kKA, then weight pair i of this tile
+    f32x16 n0, n1;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      pk[0][e] = (bf16)fast_exp2(fmaf(s0[e], c, nm));
-      pk[1][e] = (bf16)fast_exp2(fmaf(s0[8 + e], c, nm));
-      pk[2][e] = (bf16)fast_exp2(fmaf(s1[e], c, nm));
-      pk[3][e] = (bf16)fast_exp2(fmaf(s1[8 + e], c, nm));
-    }
-    const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        const bf16x2 pr = {pk[kk][e], pk[kk][e + 1]};
-        lsum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lsum, false);
-      }
-    const char* v = sV + jb * kTileBytes;
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const bf16x4 lo4 = lds_read_tr(v + voff[db] + (16 * kk) * 256);
-        const bf16x4 hi4 = lds_read_tr(v + voff[db] + (16 * kk + 8) * 256);
-        const bf16x8 va = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
-        o[db] = mfma32(va, pk[kk], o[db]);
-      }
-    // Scheduling shape of the step: each QK MFMA followed by one LDS read
-    // and four softmax VALU instructions, each PV MFMA by two transposed
-    // reads and two VALU instructions, so that the MFMA pipe is fed evenly
-    // (the default schedule bunches the exponentials).
+    for (int r = 0; r < 16; ++r) n0[r] = n1[r] = 0.f;
+    bf16x8 va[kVA + 1];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
-      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
+      if (i & 1)
+        n1 = mfma32(ka[i % (kKA + 1)], qop[i >> 1], n1);
+      else
+        n0 = mfma32(ka[i % (kKA + 1)], qop[i >> 1], n0);
+      if (i + kKA < 16) ka[(i + kKA) % (kKA + 1)] = kread(i + kKA);
+      if (i == 15) {
+#pragma unroll
+        for (int u = 0; u < kVA; ++u) va[u] = vread(u);
+      }
+      pair(i);
+      __builtin_amdgcn_sched_barrier(0);
     }
+    // O += P V: MFMA i, then the V reads for MFMA i + kVA; slots 8-12 also
+    // take the next tile's maximum (its S MFMAs are done by then)
+    float t1[12], t2[4], mx = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+      o[i & 3] = mfma32(va[i % (kVA + 1)], pk[i >> 2], o[i & 3]);
+      if (i + kVA < 16) va[(i + kVA) % (kVA + 1)] = vread(i + kVA);
+      if (i == 8 || i == 9) {
+#pragma unroll
+        for (int u = 5 * (i - 8); u < 5 * (i - 7); ++u) {
+          t1[u] = fmaxf(fmaxf(n0[3 * u], n0[3 * u + 1]), n0[3 * u + 2]);
+          t1[5 + u] = fmaxf(fmaxf(n1[3 * u], n1[3 * u + 1]), n1[3 * u + 2]);
+        }
+      }
+      if (i == 10) {
+        t1[10] = n0[15];
+        t1[11] = n1[15];
+        t2[0] = fmaxf(fmaxf(t1[0], t1[1]), t1[2]);
+        t2[1] = fmaxf(fmaxf(t1[3], t1[4]), t1[5]);
+        t2[2] = fmaxf(fmaxf(t1[6], t1[7]), t1[8]);
+        t2[3] = fmaxf(fmaxf(t1[9], t1[10]), t1[11]);
+      }
+      if (i == 11) mx = fmaxf(fmaxf(t2[0], t2[1]), fmaxf(t2[2], t2[3]));
+      if (i == 12) mt_next = pair_max(mx) * c;
+      __builtin_amdgcn_sched_barrier(0);
     }
     s0 = n0;
     s1 = n1;
   };
+
 
   // (a split with no tiles skips to its empty partial state)
   if (!kSplit || kta < ktb) {
@@ -340,6 +405,7 @@ __global__ __launch_bounds__(256, 2) void prefill_d128_kernel(AttnArgs a) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     qk(0, s0, s1);
+    mt_next = tile_max(s0, s1);
     using B0 = std::integral_constant<int, 0>;
     using B1 = std::integral_constant<int, 1>;
     auto run = [&](int& kt, int end, auto mask_tag) __attribute__((always_inline)) {
