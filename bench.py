@@ -76,28 +76,28 @@ def decode_kernel(H: int, G: int, e4m3: bool) -> str:
 
 
 MEASURED_TRAFFIC = {
-    ("7b/prefill_sliding_l0", "qknorm_rope_append_kernel"): dict(bytes=369838441, sources="2fb156025c4a8ef3"),
-    ("7b/prefill_sliding_l0", "prefill_d128_kernel"): dict(bytes=693459909, sources="93d82eb0e87feae3"),
-    ("7b/prefill_full_l3", "qknorm_rope_append_kernel"): dict(bytes=403387324, sources="2fb156025c4a8ef3"),
-    ("7b/prefill_full_l3", "prefill_d128_kernel"): dict(bytes=299191039, sources="93d82eb0e87feae3"),
-    ("7b/decode_sliding", "decode_prologue_kernel"): dict(bytes=1895042, sources="2fb156025c4a8ef3"),
-    ("7b/decode_sliding", "decode_split_kernel"): dict(bytes=2148069154, sources="62153bad07e099ab"),
-    ("7b/decode_full", "decode_prologue_kernel"): dict(bytes=1910722, sources="2fb156025c4a8ef3"),
-    ("7b/decode_full", "decode_split_kernel"): dict(bytes=34359465561, sources="62153bad07e099ab"),
-    ("32b/prefill_sliding_l0", "qknorm_rope_append_kernel"): dict(bytes=227168162, sources="2fb156025c4a8ef3"),
-    ("32b/prefill_sliding_l0", "prefill_d128_kernel"): dict(bytes=325430664, sources="93d82eb0e87feae3"),
-    ("32b/prefill_full_l3", "qknorm_rope_append_kernel"): dict(bytes=235556799, sources="2fb156025c4a8ef3"),
-    ("32b/prefill_full_l3", "prefill_d128_kernel"): dict(bytes=321993268, sources="93d82eb0e87feae3"),
-    ("32b/decode_sliding", "decode_prologue_kernel"): dict(bytes=2113824, sources="2fb156025c4a8ef3"),
-    ("32b/decode_sliding", "decode_mfma_kernel"): dict(bytes=1079471916, sources="62153bad07e099ab"),
-    ("32b/decode_full", "decode_prologue_kernel"): dict(bytes=2116767, sources="2fb156025c4a8ef3"),
-    ("32b/decode_full", "decode_mfma_kernel"): dict(bytes=8622425676, sources="62153bad07e099ab"),
-    ("long/prefill_sliding", "qknorm_rope_append_kernel"): dict(bytes=2249098936, sources="2fb156025c4a8ef3"),
-    ("long/prefill_sliding", "prefill_d128_kernel"): dict(bytes=20774993678, sources="93d82eb0e87feae3"),
-    ("long/prefill_full", "qknorm_rope_append_kernel"): dict(bytes=3222471686, sources="2fb156025c4a8ef3"),
-    ("long/prefill_full", "prefill_d128_kernel"): dict(bytes=11960036002, sources="93d82eb0e87feae3"),
+    ("7b/prefill_sliding_l0", "qknorm_rope_append_kernel"): dict(bytes=369838378, sources="2fb156025c4a8ef3"),
+    ("7b/prefill_sliding_l0", "prefill_d128_kernel"): dict(bytes=693630079, sources="fe866b84af21260b"),
+    ("7b/prefill_full_l3", "qknorm_rope_append_kernel"): dict(bytes=403388247, sources="2fb156025c4a8ef3"),
+    ("7b/prefill_full_l3", "prefill_d128_kernel"): dict(bytes=298092002, sources="fe866b84af21260b"),
+    ("7b/decode_sliding", "decode_prologue_kernel"): dict(bytes=1894970, sources="2fb156025c4a8ef3"),
+    ("7b/decode_sliding", "decode_split_kernel"): dict(bytes=2148054539, sources="62153bad07e099ab"),
+    ("7b/decode_full", "decode_prologue_kernel"): dict(bytes=1911386, sources="2fb156025c4a8ef3"),
+    ("7b/decode_full", "decode_split_kernel"): dict(bytes=34359229839, sources="62153bad07e099ab"),
+    ("32b/prefill_sliding_l0", "qknorm_rope_append_kernel"): dict(bytes=227167348, sources="2fb156025c4a8ef3"),
+    ("32b/prefill_sliding_l0", "prefill_d128_kernel"): dict(bytes=325318690, sources="fe866b84af21260b"),
+    ("32b/prefill_full_l3", "qknorm_rope_append_kernel"): dict(bytes=235556216, sources="2fb156025c4a8ef3"),
+    ("32b/prefill_full_l3", "prefill_d128_kernel"): dict(bytes=320026827, sources="fe866b84af21260b"),
+    ("32b/decode_sliding", "decode_prologue_kernel"): dict(bytes=2112343, sources="2fb156025c4a8ef3"),
+    ("32b/decode_sliding", "decode_mfma_kernel"): dict(bytes=1079287429, sources="62153bad07e099ab"),
+    ("32b/decode_full", "decode_prologue_kernel"): dict(bytes=2116599, sources="2fb156025c4a8ef3"),
+    ("32b/decode_full", "decode_mfma_kernel"): dict(bytes=8622692820, sources="62153bad07e099ab"),
+    ("long/prefill_sliding", "qknorm_rope_append_kernel"): dict(bytes=2249099889, sources="2fb156025c4a8ef3"),
+    ("long/prefill_sliding", "prefill_d128_kernel"): dict(bytes=20752918606, sources="fe866b84af21260b"),
+    ("long/prefill_full", "qknorm_rope_append_kernel"): dict(bytes=3222448399, sources="2fb156025c4a8ef3"),
+    ("long/prefill_full", "prefill_d128_kernel"): dict(bytes=11963824156, sources="fe866b84af21260b"),
     # mean per launch over the four 7B and 32B layer launches (the `roofline` group)
-    ("32b+7b prefill calls", "prefill_d128_kernel"): dict(bytes=410018720, sources="93d82eb0e87feae3"),
+    ("32b+7b prefill calls", "prefill_d128_kernel"): dict(bytes=409266900, sources="fe866b84af21260b"),
 }
 
 

@@ -188,8 +188,11 @@ __global__ __launch_bounds__(256, 2) void prefill_d128_kernel(AttnArgs a) {
     vp_off[i] = kPrefix ? (uint32_t)(((16 * i + lrow) * (int)p_sr + vcol * 8) * 2) : 0u;
   }
   const int slab = 4 * wave * 256;  // this wavefront's byte offset in a slab
+  // slot0 = k0 mod ring (kept up to date by the caller: an integer division
+  // per tile costs about as much VALU work as a tenth of the step's softmax)
   auto load_rows = [&](const bf16* base, int64_t sr, const uint32_t* off, const bf16* pbase,
-                       const uint32_t* poff, int col8, int k0, char* dst) __attribute__((always_inline)) {
+                       const uint32_t* poff, int col8, int k0, int slot0,
+                       char* dst) __attribute__((always_inline)) {
     if (!kPrefix || k0 >= main0) {
       if (k0 + kBK <= n_keys) {
         const auto rs = rows_rsrc(base + (int64_t)(k0 - main0) * sr);
@@ -197,8 +200,8 @@ __global__ __launch_bounds__(256, 2) void prefill_d128_kernel(AttnArgs a) {
         for (int i = 0; i < 4; ++i) load_to_lds(rs, off[i], dst + 16 * i * 256);
         return;
       }
-    } else if (k0 + kBK <= main0 && k0 % ring + kBK <= ring) {
-      const auto rs = rows_rsrc(pbase + (int64_t)(k0 % ring) * p_sr);
+    } else if (k0 + kBK <= main0 && slot0 + kBK <= ring) {
+      const auto rs = rows_rsrc(pbase + (int64_t)slot0 * p_sr);
 #pragma unroll
       for (int i = 0; i < 4; ++i) load_to_lds(rs, poff[i], dst + 16 * i * 256);
       return;
@@ -215,11 +218,17 @@ __global__ __launch_bounds__(256, 2) void prefill_d128_kernel(AttnArgs a) {
         if ((lane >> 4) == r) load_to_lds(rows_rsrc(row), (uint32_t)(col8 * 2), dst + 16 * i * 256);
       }
   };
-  auto load_k = [&](int k0, int buf) __attribute__((always_inline)) {
-    load_rows(kbase, a.k_sr, k_off, kpbase, kp_off, kcol * 8, k0, kbuf_of(buf) + slab);
+  auto load_k = [&](int k0, int slot0, int buf) __attribute__((always_inline)) {
+    load_rows(kbase, a.k_sr, k_off, kpbase, kp_off, kcol * 8, k0, slot0, kbuf_of(buf) + slab);
   };
-  auto load_v = [&](int k0, int buf) __attribute__((always_inline)) {
-    load_rows(vbase, a.v_sr, v_off, vpbase, vp_off, vcol * 8, k0, vbuf_of(buf) + slab);
+  auto load_v = [&](int k0, int slot0, int buf) __attribute__((always_inline)) {
+    load_rows(vbase, a.v_sr, v_off, vpbase, vp_off, vcol * 8, k0, slot0, vbuf_of(buf) + slab);
+  };
+  // ring slots of the next K and V tiles a step loads (prefix only)
+  int kslot = 0, vslot = 0;
+  auto advance_slot = [&](int& s) __attribute__((always_inline)) {
+    s += kBK;
+    if (s >= ring) s = ring >= kBK ? s - ring : s % ring;
   };
 
   // LDS read offsets.  K (A operand of S^T): row 32 kb + col, column
@@ -290,8 +299,12 @@ __global__ __launch_bounds__(256, 2) void prefill_d128_kernel(AttnArgs a) {
     const int k0 = kt * kBK;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (kt + 2 < ktb) load_k(k0 + 2 * kBK, jb);
-    if (kt + 1 < ktb) load_v(k0 + kBK, jb ^ 1);
+    if (kt + 2 < ktb) load_k(k0 + 2 * kBK, kslot, jb);
+    if (kt + 1 < ktb) load_v(k0 + kBK, vslot, jb ^ 1);
+    if constexpr (kPrefix) {
+      advance_slot(kslot);
+      advance_slot(vslot);
+    }
 
     const char* kbuf = kbuf_of(jb ^ 1);  // K of tile kt + 1
     const char* vbuf = vbuf_of(jb);      // V of tile kt
@@ -399,9 +412,16 @@ __global__ __launch_bounds__(256, 2) void prefill_d128_kernel(AttnArgs a) {
 
   // (a split with no tiles skips to its empty partial state)
   if (!kSplit || kta < ktb) {
-    load_k(kta * kBK, 0);
-    load_v(kta * kBK, 0);
-    if (kta + 1 < ktb) load_k((kta + 1) * kBK, 1);
+    const int slot_a = kPrefix ? (kta * kBK) % ring : 0;
+    load_k(kta * kBK, slot_a, 0);
+    load_v(kta * kBK, slot_a, 0);
+    if constexpr (kPrefix) {
+      vslot = slot_a;
+      advance_slot(vslot);  // tile kta + 1
+      kslot = vslot;
+      advance_slot(kslot);  // tile kta + 2
+    }
+    if (kta + 1 < ktb) load_k((kta + 1) * kBK, vslot, 1);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     qk(0, s0, s1);
