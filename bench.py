@@ -17,6 +17,7 @@ in a list:
   chunked  7B prefill of a 4,096-token chunk at position 61,440 onto a
        filled cache (full layer: 61,440 cached positions; sliding: the ring)
   7b-e4m3  7B decode (B=32 at 65,536) against e4m3 caches (1-byte codes)
+  32b-e4m3  32B decode (B=64 at 32,768) against e4m3 caches
   decode-stack-e4m3  the decode stack against e4m3 caches
   7b-shard, 32b-shard  one GPU's share of an 8-way head split of a layer
 
@@ -176,6 +177,8 @@ WORKLOADS = {
                     prefill=dict(B=1, T=4096, H=32, G=32, pos_offset=61440), decode=None),
     "7b-e4m3": dict(name="olmo3-7b-decode-e4m3", prefill=None,
                     decode=dict(B=32, H=32, G=32, L=65536, e4m3=True)),
+    "32b-e4m3": dict(name="olmo3-32b-decode-e4m3", prefill=None,
+                     decode=dict(B=64, H=40, G=8, L=32768, e4m3=True)),
     "decode-stack-e4m3": dict(name="olmo3-7b-decode-stack-e4m3", prefill=None,
                               decode=dict(B=16, H=32, G=32, L=65536, layers=32, e4m3=True)),
     # one GPU's share when a layer's heads are spread over 8 GPUs (4 of the
