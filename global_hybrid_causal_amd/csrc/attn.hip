@@ -537,15 +537,14 @@ struct DecStage8 {
 };
 
 // Eight e4m3 codes -> their values as bf16 (exact: every e4m3 value is a
-// bf16 value).
+// bf16 value), two per v_cvt_scalef32_pk_bf16_fp8 (scale 1: the cache scales
+// are applied to the softmax scale and the output instead).
 __device__ __forceinline__ bf16x8 e4m3x8_to_bf16(u32x2 w) {
-  float f[8];
-  e4m3x4_to_f32(w[0], f);
-  e4m3x4_to_f32(w[1], f + 4);
-  bf16x8 r;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) r[e] = (bf16)f[e];
-  return r;
+  const bf16x2 a0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w[0], 1.0f, false);
+  const bf16x2 a1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w[0], 1.0f, true);
+  const bf16x2 a2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w[1], 1.0f, false);
+  const bf16x2 a3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w[1], 1.0f, true);
+  return bf16x8{a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
 }
 
 // Two wavefronts per SIMD: the three stages in registers (96 VGPRs of K and V)

@@ -266,6 +266,48 @@ def test_e4m3_decode_every_code(case):
     _log("  max abs / rel err", err)
 
 
+VALUE_CODES_DECODE = [
+    # B, H, G, layer_type: one query head per key/value head (per-row kernel)
+    # and groups of 5 (grouped MFMA kernel), ring and linear caches
+    (2, 2, 2, 0), (2, 2, 2, 1), (2, 10, 2, 0), (2, 10, 2, 1),
+]
+
+
+@pytest.mark.parametrize("case", VALUE_CODES_DECODE, ids=[str(c) for c in VALUE_CODES_DECODE])
+def test_e4m3_decode_returns_value_codes_exactly(case):
+    """Decode at position 0: the new row is the only visible key, so its
+    weight is exactly 1 and each query head's output is the value row as the
+    kernel decodes it from its codes, times v_scale.  The values are every
+    non-NaN code's value times v_scale = 1/16 (a power of two, so the codes
+    and every product are exact): the output must equal them bit for bit,
+    which pins the kernel's code -> value conversion for every code (an
+    output compared within tolerance cannot see one code decoded wrongly)."""
+    B, H, G, lt = case
+    d, cap, w, vs = 128, 128, 128, 1.0 / 16
+    _log("e4m3 decode, value codes exact", case)
+    kind = KINDS[lt]
+    rope = A.Rope(theta=500000.0, yarn=True, factor=8.0, orig_ctx=512)
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.int64)
+    rng = np.random.default_rng(77 + lt)
+    picks = np.concatenate([rng.permutation(codes) for _ in range((B * G * d) // len(codes) + 1)])
+    vrow = (TABLE[picks[: B * G * d]] * vs).reshape(B, G, d)
+    x = inputs(77, 10 + lt, B, 1, H, G, d, BF16)
+    v = torch.tensor(vrow, dtype=torch.float32).to(BF16).cuda()
+    assert np.array_equal(host(v).astype(np.float64), vrow), "values not exact in bf16"
+    kc, vc = synth.e4m3_cache_fill(77, lt, B, G, cap, d, device="cuda")
+    q, k = x["q_pre"][:, 0].contiguous(), x["k_pre"][:, 0].contiguous()
+    out = torch.empty_like(q)
+    ws = A.workspace(A.MODE_DECODE, B, 1, H, G, d, lt, A.DTYPE_BF16_E4M3, cap, "cuda")
+    A.olmo3_attn_decode_e4m3(q, k, v.reshape(B, G * d), x["q_gain"], x["k_gain"], kc, vc, out, ws,
+                             k_scale=KS, v_scale=vs, window=w, layer_type=lt, rope=rope, pos=0)
+    got = host(out).astype(np.float64).reshape(B, H, d)
+    want = vrow[:, np.arange(H) // (H // G), :]
+    bad = got != want
+    assert not bad.any(), (f"{int(bad.sum())} outputs differ; first codes "
+                           f"{[hex(int(c)) for c in picks[: B * G * d].reshape(B, G, d)[:, np.arange(H) // (H // G), :][bad][:8]]}")
+    assert np.array_equal(_codes(vc)[:, :, 0, :], picks[: B * G * d].reshape(B, G, d)), "stored value codes"
+
+
 @pytest.mark.parametrize("lt", [0, 1])
 def test_e4m3_append_saturates_and_keeps_nan(lt):
     """Scales so small (keys 1/512, values 1/1024) that most |x / scale|
