@@ -77,28 +77,28 @@ def decode_kernel(H: int, G: int, e4m3: bool) -> str:
 
 
 MEASURED_TRAFFIC = {
-    ("7b/prefill_sliding_l0", "qknorm_rope_append_kernel"): dict(bytes=369836169, sources="2fb156025c4a8ef3"),
-    ("7b/prefill_sliding_l0", "prefill_d128_kernel"): dict(bytes=703906940, sources="fe866b84af21260b"),
-    ("7b/prefill_full_l3", "qknorm_rope_append_kernel"): dict(bytes=403413493, sources="2fb156025c4a8ef3"),
-    ("7b/prefill_full_l3", "prefill_d128_kernel"): dict(bytes=299714445, sources="fe866b84af21260b"),
-    ("7b/decode_sliding", "decode_prologue_kernel"): dict(bytes=1895033, sources="2fb156025c4a8ef3"),
-    ("7b/decode_sliding", "decode_split_kernel"): dict(bytes=2148032107, sources="f1cff64b4e393216"),
-    ("7b/decode_full", "decode_prologue_kernel"): dict(bytes=1911449, sources="2fb156025c4a8ef3"),
-    ("7b/decode_full", "decode_split_kernel"): dict(bytes=34359176882, sources="f1cff64b4e393216"),
-    ("32b/prefill_sliding_l0", "qknorm_rope_append_kernel"): dict(bytes=227167916, sources="2fb156025c4a8ef3"),
-    ("32b/prefill_sliding_l0", "prefill_d128_kernel"): dict(bytes=326456108, sources="fe866b84af21260b"),
-    ("32b/prefill_full_l3", "qknorm_rope_append_kernel"): dict(bytes=235555495, sources="2fb156025c4a8ef3"),
-    ("32b/prefill_full_l3", "prefill_d128_kernel"): dict(bytes=320912347, sources="fe866b84af21260b"),
-    ("32b/decode_sliding", "decode_prologue_kernel"): dict(bytes=2113142, sources="2fb156025c4a8ef3"),
-    ("32b/decode_sliding", "decode_mfma_kernel"): dict(bytes=1079329535, sources="f1cff64b4e393216"),
-    ("32b/decode_full", "decode_prologue_kernel"): dict(bytes=2116438, sources="2fb156025c4a8ef3"),
-    ("32b/decode_full", "decode_mfma_kernel"): dict(bytes=8623522232, sources="f1cff64b4e393216"),
-    ("long/prefill_sliding", "qknorm_rope_append_kernel"): dict(bytes=2249097182, sources="2fb156025c4a8ef3"),
-    ("long/prefill_sliding", "prefill_d128_kernel"): dict(bytes=20722862475, sources="fe866b84af21260b"),
-    ("long/prefill_full", "qknorm_rope_append_kernel"): dict(bytes=3222444269, sources="2fb156025c4a8ef3"),
-    ("long/prefill_full", "prefill_d128_kernel"): dict(bytes=11931464029, sources="fe866b84af21260b"),
+    ("7b/prefill_sliding_l0", "qknorm_rope_append_kernel"): dict(bytes=369835303, sources="2fb156025c4a8ef3"),
+    ("7b/prefill_sliding_l0", "prefill_d128_kernel"): dict(bytes=656574702, sources="2d26a6f93fab2dce"),
+    ("7b/prefill_full_l3", "qknorm_rope_append_kernel"): dict(bytes=403389217, sources="2fb156025c4a8ef3"),
+    ("7b/prefill_full_l3", "prefill_d128_kernel"): dict(bytes=291485302, sources="2d26a6f93fab2dce"),
+    ("7b/decode_sliding", "decode_prologue_kernel"): dict(bytes=1895069, sources="2fb156025c4a8ef3"),
+    ("7b/decode_sliding", "decode_split_kernel"): dict(bytes=2148038796, sources="f1cff64b4e393216"),
+    ("7b/decode_full", "decode_prologue_kernel"): dict(bytes=1911260, sources="2fb156025c4a8ef3"),
+    ("7b/decode_full", "decode_split_kernel"): dict(bytes=34359286444, sources="f1cff64b4e393216"),
+    ("32b/prefill_sliding_l0", "qknorm_rope_append_kernel"): dict(bytes=227167725, sources="2fb156025c4a8ef3"),
+    ("32b/prefill_sliding_l0", "prefill_d128_kernel"): dict(bytes=329188313, sources="2d26a6f93fab2dce"),
+    ("32b/prefill_full_l3", "qknorm_rope_append_kernel"): dict(bytes=235556067, sources="2fb156025c4a8ef3"),
+    ("32b/prefill_full_l3", "prefill_d128_kernel"): dict(bytes=315704564, sources="2d26a6f93fab2dce"),
+    ("32b/decode_sliding", "decode_prologue_kernel"): dict(bytes=2113722, sources="2fb156025c4a8ef3"),
+    ("32b/decode_sliding", "decode_mfma_kernel"): dict(bytes=1079389197, sources="f1cff64b4e393216"),
+    ("32b/decode_full", "decode_prologue_kernel"): dict(bytes=2116730, sources="2fb156025c4a8ef3"),
+    ("32b/decode_full", "decode_mfma_kernel"): dict(bytes=8622852024, sources="f1cff64b4e393216"),
+    ("long/prefill_sliding", "qknorm_rope_append_kernel"): dict(bytes=2249102838, sources="2fb156025c4a8ef3"),
+    ("long/prefill_sliding", "prefill_d128_kernel"): dict(bytes=21042436778, sources="2d26a6f93fab2dce"),
+    ("long/prefill_full", "qknorm_rope_append_kernel"): dict(bytes=3222448017, sources="2fb156025c4a8ef3"),
+    ("long/prefill_full", "prefill_d128_kernel"): dict(bytes=6052077017, sources="2d26a6f93fab2dce"),
     # mean per launch over the four 7B and 32B layer launches (the `roofline` group)
-    ("32b+7b prefill calls", "prefill_d128_kernel"): dict(bytes=412747460, sources="fe866b84af21260b"),
+    ("32b+7b prefill calls", "prefill_d128_kernel"): dict(bytes=398238220, sources="2d26a6f93fab2dce"),
 }
 
 

@@ -359,6 +359,11 @@ __global__ __launch_bounds__(256, 2) void prefill_d128_kernel(AttnArgs a) {
       lsum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lsum, false);
     };
 
+    // The S MFMAs carry this tile's exponentials between them: a wavefront
+    // in that half of its step issues ahead of the other wavefront on its
+    // SIMD (wave priority 1), whose O MFMAs then fill the MFMA pipe while
+    // the first one's VALU work runs (+2-5 % against equal priorities).
+    __builtin_amdgcn_s_setprio(1);
     // S of the next tile (on the last tile the result is discarded): MFMA i,
     // then the K read for MFMA i + kKA, then weight pair i of this tile
     f32x16 n0, n1;
@@ -379,6 +384,7 @@ __global__ __launch_bounds__(256, 2) void prefill_d128_kernel(AttnArgs a) {
       pair(i);
       __builtin_amdgcn_sched_barrier(0);
     }
+    __builtin_amdgcn_s_setprio(0);
     // O += P V: MFMA i, then the V reads for MFMA i + kVA; slots 8-12 also
     // take the next tile's maximum (its S MFMAs are done by then)
     float t1[12], t2[4], mx = 0.f;
@@ -405,6 +411,7 @@ __global__ __launch_bounds__(256, 2) void prefill_d128_kernel(AttnArgs a) {
       if (i == 12) mt_next = pair_max(mx) * c;
       __builtin_amdgcn_sched_barrier(0);
     }
+    __builtin_amdgcn_s_setprio(0);
     s0 = n0;
     s1 = n1;
   };
