@@ -77,28 +77,28 @@ def decode_kernel(H: int, G: int, e4m3: bool) -> str:
 
 
 MEASURED_TRAFFIC = {
-    ("7b/prefill_sliding_l0", "qknorm_rope_append_kernel"): dict(bytes=369835303, sources="2fb156025c4a8ef3"),
-    ("7b/prefill_sliding_l0", "prefill_d128_kernel"): dict(bytes=656574702, sources="2d26a6f93fab2dce"),
-    ("7b/prefill_full_l3", "qknorm_rope_append_kernel"): dict(bytes=403389217, sources="2fb156025c4a8ef3"),
-    ("7b/prefill_full_l3", "prefill_d128_kernel"): dict(bytes=291485302, sources="2d26a6f93fab2dce"),
-    ("7b/decode_sliding", "decode_prologue_kernel"): dict(bytes=1895069, sources="2fb156025c4a8ef3"),
-    ("7b/decode_sliding", "decode_split_kernel"): dict(bytes=2148038796, sources="f1cff64b4e393216"),
-    ("7b/decode_full", "decode_prologue_kernel"): dict(bytes=1911260, sources="2fb156025c4a8ef3"),
-    ("7b/decode_full", "decode_split_kernel"): dict(bytes=34359286444, sources="f1cff64b4e393216"),
-    ("32b/prefill_sliding_l0", "qknorm_rope_append_kernel"): dict(bytes=227167725, sources="2fb156025c4a8ef3"),
-    ("32b/prefill_sliding_l0", "prefill_d128_kernel"): dict(bytes=329188313, sources="2d26a6f93fab2dce"),
-    ("32b/prefill_full_l3", "qknorm_rope_append_kernel"): dict(bytes=235556067, sources="2fb156025c4a8ef3"),
-    ("32b/prefill_full_l3", "prefill_d128_kernel"): dict(bytes=315704564, sources="2d26a6f93fab2dce"),
-    ("32b/decode_sliding", "decode_prologue_kernel"): dict(bytes=2113722, sources="2fb156025c4a8ef3"),
-    ("32b/decode_sliding", "decode_mfma_kernel"): dict(bytes=1079389197, sources="f1cff64b4e393216"),
-    ("32b/decode_full", "decode_prologue_kernel"): dict(bytes=2116730, sources="2fb156025c4a8ef3"),
-    ("32b/decode_full", "decode_mfma_kernel"): dict(bytes=8622852024, sources="f1cff64b4e393216"),
-    ("long/prefill_sliding", "qknorm_rope_append_kernel"): dict(bytes=2249102838, sources="2fb156025c4a8ef3"),
-    ("long/prefill_sliding", "prefill_d128_kernel"): dict(bytes=21042436778, sources="2d26a6f93fab2dce"),
-    ("long/prefill_full", "qknorm_rope_append_kernel"): dict(bytes=3222448017, sources="2fb156025c4a8ef3"),
-    ("long/prefill_full", "prefill_d128_kernel"): dict(bytes=6052077017, sources="2d26a6f93fab2dce"),
+    ("7b/prefill_sliding_l0", "qknorm_rope_append_kernel"): dict(bytes=369833898, sources="2fb156025c4a8ef3"),
+    ("7b/prefill_sliding_l0", "prefill_d128_kernel"): dict(bytes=651497290, sources="044386b0d9f5dc25"),
+    ("7b/prefill_full_l3", "qknorm_rope_append_kernel"): dict(bytes=403417615, sources="2fb156025c4a8ef3"),
+    ("7b/prefill_full_l3", "prefill_d128_kernel"): dict(bytes=297621508, sources="044386b0d9f5dc25"),
+    ("7b/decode_sliding", "decode_prologue_kernel"): dict(bytes=1894908, sources="2fb156025c4a8ef3"),
+    ("7b/decode_sliding", "decode_split_kernel"): dict(bytes=2148037665, sources="f1cff64b4e393216"),
+    ("7b/decode_full", "decode_prologue_kernel"): dict(bytes=1910524, sources="2fb156025c4a8ef3"),
+    ("7b/decode_full", "decode_split_kernel"): dict(bytes=34359270210, sources="f1cff64b4e393216"),
+    ("32b/prefill_sliding_l0", "qknorm_rope_append_kernel"): dict(bytes=227167856, sources="2fb156025c4a8ef3"),
+    ("32b/prefill_sliding_l0", "prefill_d128_kernel"): dict(bytes=329244766, sources="044386b0d9f5dc25"),
+    ("32b/prefill_full_l3", "qknorm_rope_append_kernel"): dict(bytes=235556162, sources="2fb156025c4a8ef3"),
+    ("32b/prefill_full_l3", "prefill_d128_kernel"): dict(bytes=315081704, sources="044386b0d9f5dc25"),
+    ("32b/decode_sliding", "decode_prologue_kernel"): dict(bytes=2113081, sources="2fb156025c4a8ef3"),
+    ("32b/decode_sliding", "decode_mfma_kernel"): dict(bytes=1079359157, sources="f1cff64b4e393216"),
+    ("32b/decode_full", "decode_prologue_kernel"): dict(bytes=2116825, sources="2fb156025c4a8ef3"),
+    ("32b/decode_full", "decode_mfma_kernel"): dict(bytes=8624676992, sources="f1cff64b4e393216"),
+    ("long/prefill_sliding", "qknorm_rope_append_kernel"): dict(bytes=2249093211, sources="2fb156025c4a8ef3"),
+    ("long/prefill_sliding", "prefill_d128_kernel"): dict(bytes=20689043944, sources="044386b0d9f5dc25"),
+    ("long/prefill_full", "qknorm_rope_append_kernel"): dict(bytes=3222473468, sources="2fb156025c4a8ef3"),
+    ("long/prefill_full", "prefill_d128_kernel"): dict(bytes=6017203264, sources="044386b0d9f5dc25"),
     # mean per launch over the four 7B and 32B layer launches (the `roofline` group)
-    ("32b+7b prefill calls", "prefill_d128_kernel"): dict(bytes=398238220, sources="2d26a6f93fab2dce"),
+    ("32b+7b prefill calls", "prefill_d128_kernel"): dict(bytes=398361317, sources="044386b0d9f5dc25"),
 }
 
 

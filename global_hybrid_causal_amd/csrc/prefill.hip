@@ -49,9 +49,9 @@ __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const
 //
 // The step's instruction order is fixed by hand (scheduling fences between
 // MFMA slots): each of the 16 S MFMAs is followed by the LDS read of the K
-// operand three MFMAs ahead and one pair of this tile's weights (two exp2, a
+// operand four MFMAs ahead and one pair of this tile's weights (two exp2, a
 // bf16 pack, a dot2 into the row sum); each of the 16 O MFMAs by the
-// transposed reads of the V operand two MFMAs ahead, and the O MFMAs also
+// transposed reads of the V operand three MFMAs ahead, and the O MFMAs also
 // cover the next tile's maximum.  Two choices keep the compiler's wait
 // counters precise: the tile loads are MUBUF (buffer_load ... lds) rather
 // than global_load_lds, whose outstanding loads make every LDS read wait for
@@ -292,7 +292,7 @@ __global__ __launch_bounds__(256, 2) void prefill_d128_kernel(AttnArgs a) {
   // kBuf: buffers holding K_kt and V_kt ((kt - kta) mod 2, known at compile
   // time so that every LDS address is a constant offset).  Operand rings:
   // K reads run kKA MFMAs ahead of their use, V reads kVA.
-  constexpr int kKA = 3, kVA = 2;
+  constexpr int kKA = 4, kVA = 3;
   auto step = [&](int kt, auto mask_tag, auto buf_tag) __attribute__((always_inline)) {
     constexpr bool kMask = decltype(mask_tag)::value;
     constexpr int jb = decltype(buf_tag)::value;
