@@ -77,28 +77,28 @@ def decode_kernel(H: int, G: int, e4m3: bool) -> str:
 
 
 MEASURED_TRAFFIC = {
-    ("7b/prefill_sliding_l0", "qknorm_rope_append_kernel"): dict(bytes=369833898, sources="2fb156025c4a8ef3"),
-    ("7b/prefill_sliding_l0", "prefill_d128_kernel"): dict(bytes=651497290, sources="044386b0d9f5dc25"),
-    ("7b/prefill_full_l3", "qknorm_rope_append_kernel"): dict(bytes=403417615, sources="2fb156025c4a8ef3"),
-    ("7b/prefill_full_l3", "prefill_d128_kernel"): dict(bytes=297621508, sources="044386b0d9f5dc25"),
-    ("7b/decode_sliding", "decode_prologue_kernel"): dict(bytes=1894908, sources="2fb156025c4a8ef3"),
-    ("7b/decode_sliding", "decode_split_kernel"): dict(bytes=2148037665, sources="f1cff64b4e393216"),
-    ("7b/decode_full", "decode_prologue_kernel"): dict(bytes=1910524, sources="2fb156025c4a8ef3"),
-    ("7b/decode_full", "decode_split_kernel"): dict(bytes=34359270210, sources="f1cff64b4e393216"),
-    ("32b/prefill_sliding_l0", "qknorm_rope_append_kernel"): dict(bytes=227167856, sources="2fb156025c4a8ef3"),
-    ("32b/prefill_sliding_l0", "prefill_d128_kernel"): dict(bytes=329244766, sources="044386b0d9f5dc25"),
-    ("32b/prefill_full_l3", "qknorm_rope_append_kernel"): dict(bytes=235556162, sources="2fb156025c4a8ef3"),
-    ("32b/prefill_full_l3", "prefill_d128_kernel"): dict(bytes=315081704, sources="044386b0d9f5dc25"),
-    ("32b/decode_sliding", "decode_prologue_kernel"): dict(bytes=2113081, sources="2fb156025c4a8ef3"),
-    ("32b/decode_sliding", "decode_mfma_kernel"): dict(bytes=1079359157, sources="f1cff64b4e393216"),
-    ("32b/decode_full", "decode_prologue_kernel"): dict(bytes=2116825, sources="2fb156025c4a8ef3"),
-    ("32b/decode_full", "decode_mfma_kernel"): dict(bytes=8624676992, sources="f1cff64b4e393216"),
-    ("long/prefill_sliding", "qknorm_rope_append_kernel"): dict(bytes=2249093211, sources="2fb156025c4a8ef3"),
-    ("long/prefill_sliding", "prefill_d128_kernel"): dict(bytes=20689043944, sources="044386b0d9f5dc25"),
-    ("long/prefill_full", "qknorm_rope_append_kernel"): dict(bytes=3222473468, sources="2fb156025c4a8ef3"),
-    ("long/prefill_full", "prefill_d128_kernel"): dict(bytes=6017203264, sources="044386b0d9f5dc25"),
+    ("7b/prefill_sliding_l0", "qknorm_rope_append_kernel"): dict(bytes=369837753, sources="fb3a6d46b16fbca7"),
+    ("7b/prefill_sliding_l0", "prefill_d128_kernel"): dict(bytes=663888064, sources="80a32a71e329155c"),
+    ("7b/prefill_full_l3", "qknorm_rope_append_kernel"): dict(bytes=403416315, sources="fb3a6d46b16fbca7"),
+    ("7b/prefill_full_l3", "prefill_d128_kernel"): dict(bytes=286878947, sources="80a32a71e329155c"),
+    ("7b/decode_sliding", "decode_prologue_kernel"): dict(bytes=1894977, sources="fb3a6d46b16fbca7"),
+    ("7b/decode_sliding", "decode_split_kernel"): dict(bytes=2148047554, sources="fce1ec309f4677d1"),
+    ("7b/decode_full", "decode_prologue_kernel"): dict(bytes=1910753, sources="fb3a6d46b16fbca7"),
+    ("7b/decode_full", "decode_split_kernel"): dict(bytes=34359428602, sources="fce1ec309f4677d1"),
+    ("32b/prefill_sliding_l0", "qknorm_rope_append_kernel"): dict(bytes=227166222, sources="fb3a6d46b16fbca7"),
+    ("32b/prefill_sliding_l0", "prefill_d128_kernel"): dict(bytes=331957273, sources="80a32a71e329155c"),
+    ("32b/prefill_full_l3", "qknorm_rope_append_kernel"): dict(bytes=235554663, sources="fb3a6d46b16fbca7"),
+    ("32b/prefill_full_l3", "prefill_d128_kernel"): dict(bytes=316898192, sources="80a32a71e329155c"),
+    ("32b/decode_sliding", "decode_prologue_kernel"): dict(bytes=2112735, sources="fb3a6d46b16fbca7"),
+    ("32b/decode_sliding", "decode_mfma_kernel"): dict(bytes=1079649700, sources="fce1ec309f4677d1"),
+    ("32b/decode_full", "decode_prologue_kernel"): dict(bytes=2117087, sources="fb3a6d46b16fbca7"),
+    ("32b/decode_full", "decode_mfma_kernel"): dict(bytes=8626261779, sources="fce1ec309f4677d1"),
+    ("long/prefill_sliding", "qknorm_rope_append_kernel"): dict(bytes=2249085043, sources="fb3a6d46b16fbca7"),
+    ("long/prefill_sliding", "prefill_d128_kernel"): dict(bytes=19823154172, sources="80a32a71e329155c"),
+    ("long/prefill_full", "qknorm_rope_append_kernel"): dict(bytes=3222450134, sources="fb3a6d46b16fbca7"),
+    ("long/prefill_full", "prefill_d128_kernel"): dict(bytes=6185615903, sources="80a32a71e329155c"),
     # mean per launch over the four 7B and 32B layer launches (the `roofline` group)
-    ("32b+7b prefill calls", "prefill_d128_kernel"): dict(bytes=398361317, sources="044386b0d9f5dc25"),
+    ("32b+7b prefill calls", "prefill_d128_kernel"): dict(bytes=399905619, sources="80a32a71e329155c"),
 }
 
 

@@ -408,6 +408,8 @@ int prefill_impl(int phases, const PrefillShape& sh, int H, int G, int d, int wi
   p.pos_offset = sh.pos_offset;
   p.keep_last = sliding ? window : INT64_MAX;  // a ring keeps the last `window`
   p.store = !ring_after;
+  // the MFMA kernel takes its queries times its base-2 softmax scale
+  p.q_scale = use_mfma(dtype, d) ? scale_log2(d) : 1.0f;
   p.seq_pos = sh.pos_offsets;
   p.cu_seqlens = sh.cu_seqlens;
   p.n_rows = N;

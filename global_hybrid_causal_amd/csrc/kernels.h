@@ -43,6 +43,10 @@ struct PrologueArgs {
   // e4m3 caches (bf16 rows only): code = e4m3(value * inv_scale)
   int cache_fp8;
   float k_inv_scale, v_inv_scale;
+  // the rotated queries are written times this factor: the MFMA prefill
+  // kernel takes them times its base-2 softmax scale, so that its scores
+  // leave the MFMAs scaled; 1 everywhere else (a product by 1 is exact)
+  float q_scale = 1.0f;
 };
 
 hipError_t launch_prologue(const PrologueArgs& a, const RopeTable& rope, int dtype, int d,

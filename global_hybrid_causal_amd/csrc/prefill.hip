@@ -29,6 +29,11 @@ __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const
 // query column, and accumulates O^T += V^T P^T with P^T taken straight from
 // the S accumulators (converted to bf16) as the B operand.
 //
+// The queries arrive times c = log2(e)/sqrt(d) (the prologue rounds c q to
+// bf16 once), and each tile's first two S MFMAs start from -m, the running
+// maximum, instead of 0: the scores leave the MFMAs as c s - m, ready for
+// exp2, with no per-score multiply-add.
+//
 // K and V tiles go from global memory straight into LDS
 // (buffer_load_dwordx4 ... lds: lane l of a wavefront fills bytes 16 l ..
 // 16 l + 15 after the wavefront's base), row-major, 256-byte rows, with XOR-swizzled
@@ -264,16 +269,24 @@ __global__ __launch_bounds__(256, 2) void prefill_d128_kernel(AttnArgs a) {
   for (int db = 0; db < 4; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
+  // running maximum m of c s (the -1e30 sentinel until a score is seen)
   float m = -1e30f, lsum = 0.f;
-  const float c = a.scale_log2;
+  // the current tile's scores hold c s - sb: sb = m once the lane has seen a
+  // score, 0 before; negm holds -sb in all 16 entries, the accumulator input
+  // of the next tile's first S MFMAs (a sentinel base would swamp the scores
+  // in fp32)
+  float sb = 0.f;
+  f32x16 negm;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) negm[r] = 0.f;
   f32x16 s0, s1;  // scores of the current tile
-  // c times the unmasked maximum of the current tile's scores, taken during
-  // the previous step (a masked tile recomputes it after masking)
+  // the unmasked maximum of the current tile's scores, taken during the
+  // previous step (a masked tile recomputes it after masking)
   float mt_next = 0.f;
   const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
 
-  // c times the maximum of a tile's 64 scores of this lane's query: a max3
-  // tree (depth 4), then the partner lane (l ^ 32)
+  // the maximum of a tile's 64 scores of this lane's query: a max3 tree
+  // (depth 4), then the partner lane (l ^ 32)
   auto tile_max = [&](const f32x16& x0, const f32x16& x1) __attribute__((always_inline)) {
     float t1[12];
 #pragma unroll
@@ -285,7 +298,7 @@ __global__ __launch_bounds__(256, 2) void prefill_d128_kernel(AttnArgs a) {
     t1[11] = x1[15];
     const float t2a = fmaxf(fmaxf(t1[0], t1[1]), t1[2]), t2b = fmaxf(fmaxf(t1[3], t1[4]), t1[5]);
     const float t2c = fmaxf(fmaxf(t1[6], t1[7]), t1[8]), t2d = fmaxf(fmaxf(t1[9], t1[10]), t1[11]);
-    return pair_max(fmaxf(fmaxf(t2a, t2b), fmaxf(t2c, t2d))) * c;
+    return pair_max(fmaxf(fmaxf(t2a, t2b), fmaxf(t2c, t2d)));
   };
 
   // Step of tile kt.  kMask: apply the visibility predicate per element.
@@ -332,8 +345,8 @@ __global__ __launch_bounds__(256, 2) void prefill_d128_kernel(AttnArgs a) {
       mask_block(s1, tq, k0 + 32, lane, a.window, a.sliding);
       mt = tile_max(s0, s1);
     }
-    if (__ballot(mt > m + kRescaleSlack)) {
-      const float mn = fmaxf(m, mt);
+    if (__ballot(mt + sb > m + kRescaleSlack)) {
+      const float mn = fmaxf(m, mt + sb);
       float alpha = fast_exp2(m - mn);
       // keep this a real (uniform) branch: without the barrier the compiler
       // folds the condition into the multiplier and rescales every tile
@@ -344,8 +357,17 @@ __global__ __launch_bounds__(256, 2) void prefill_d128_kernel(AttnArgs a) {
       for (int db = 0; db < 4; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+      // the tile's scores and the next tile's start move to the new base
+      const float nb = mn > -1e29f ? mn : 0.f;
+      const float sh = sb - nb;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s0[r] += sh;
+        s1[r] += sh;
+        negm[r] = -nb;
+      }
+      sb = nb;
     }
-    const float nm = -m;
 
     bf16x8 pk[4];
     // weights of key pair p of the tile (p = 0..15: 16-key chunk p / 4, pair
@@ -353,8 +375,8 @@ __global__ __launch_bounds__(256, 2) void prefill_d128_kernel(AttnArgs a) {
     auto pair = [&](int p) __attribute__((always_inline)) {
       const int kk = p >> 2, e = 2 * (p & 3), r = (kk & 1) * 8 + e;
       const float x0 = (kk < 2 ? s0 : s1)[r], x1 = (kk < 2 ? s0 : s1)[r + 1];
-      pk[kk][e] = (bf16)fast_exp2(fmaf(x0, c, nm));
-      pk[kk][e + 1] = (bf16)fast_exp2(fmaf(x1, c, nm));
+      pk[kk][e] = (bf16)fast_exp2(x0);
+      pk[kk][e + 1] = (bf16)fast_exp2(x1);
       const bf16x2 pr = {pk[kk][e], pk[kk][e + 1]};
       lsum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lsum, false);
     };
@@ -364,18 +386,17 @@ __global__ __launch_bounds__(256, 2) void prefill_d128_kernel(AttnArgs a) {
     // SIMD (wave priority 1), whose O MFMAs then fill the MFMA pipe while
     // the first one's VALU work runs (+2-5 % against equal priorities).
     __builtin_amdgcn_s_setprio(1);
-    // S of the next tile (on the last tile the result is discarded): MFMA i,
-    // then the K read for MFMA i + kKA, then weight pair i of this tile
+    // S of the next tile (on the last tile the result is discarded), started
+    // from -sb: MFMA i, then the K read for MFMA i + kKA, then weight pair i
+    // of this tile
     f32x16 n0, n1;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) n0[r] = n1[r] = 0.f;
     bf16x8 va[kVA + 1];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       if (i & 1)
-        n1 = mfma32(ka[i % (kKA + 1)], qop[i >> 1], n1);
+        n1 = mfma32(ka[i % (kKA + 1)], qop[i >> 1], i == 1 ? negm : n1);
       else
-        n0 = mfma32(ka[i % (kKA + 1)], qop[i >> 1], n0);
+        n0 = mfma32(ka[i % (kKA + 1)], qop[i >> 1], i == 0 ? negm : n0);
       if (i + kKA < 16) ka[(i + kKA) % (kKA + 1)] = kread(i + kKA);
       if (i == 15) {
 #pragma unroll
@@ -408,7 +429,7 @@ __global__ __launch_bounds__(256, 2) void prefill_d128_kernel(AttnArgs a) {
         t2[3] = fmaxf(fmaxf(t1[9], t1[10]), t1[11]);
       }
       if (i == 11) mx = fmaxf(fmaxf(t2[0], t2[1]), fmaxf(t2[2], t2[3]));
-      if (i == 12) mt_next = pair_max(mx) * c;
+      if (i == 12) mt_next = pair_max(mx);
       __builtin_amdgcn_sched_barrier(0);
     }
     __builtin_amdgcn_s_setprio(0);

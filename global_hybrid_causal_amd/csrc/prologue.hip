@@ -215,7 +215,7 @@ __global__ __launch_bounds__(kWave * kTokensPerBlock) void qknorm_rope_append_ke
     const T* src = (const T*)a.q_pre + row * a.H * D;
     T* qo = (T*)a.q_out + row * a.H * D;
     norm_rope_row<T, D, kEarly, kStream>(src, (const T*)a.q_gain, a.H, a.eps, lane, cs, sn,
-                                         rope.mscale, angles,
+                                         rope.mscale * a.q_scale, angles,
                                          [&](int h, int j, const float* y0, const float* y1) {
                                   store_chunk(qo + h * D + j * kVec, y0);
                                   store_chunk(qo + h * D + D / 2 + j * kVec, y1);
@@ -425,6 +425,7 @@ __global__ __launch_bounds__(kDecProThreads) void decode_prologue_kernel(Prologu
 // sequence with d = 128, queries present, no rotated-key copy.
 bool decode_prologue_fits(const PrologueArgs& a, int dtype, int d) {
   return dtype == 0 && d == 128 && a.T == 1 && !a.cu_seqlens && a.q_pre && !a.k_out &&
+         a.q_scale == 1.0f &&
          8 * (a.H + 2 * a.G) <= kDecProThreads * kDecProItems;
 }
 

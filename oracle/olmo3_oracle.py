@@ -500,7 +500,7 @@ def _project_heads(q_pre, k_pre, v, q_gain, k_gain, H, G, d, eps):
 def prefill_ref(q_pre, k_pre, v, q_gain, k_gain, *, H: int, G: int, d: int,
                 kind: str, window: int, rope: RopeParams, eps: float = 1e-6,
                 pos_offset: int = 0, cache: KvCacheRef | None = None,
-                round_rotated: bool = False) -> np.ndarray:
+                round_rotated: bool = False, q_scale: float = 1.0) -> np.ndarray:
     """One attention call over T new tokens at positions pos_offset .. +T-1.
 
     q_pre [B, T, H*d], k_pre and v [B, T, G*d] (projected, before QK-norm);
@@ -517,7 +517,10 @@ def prefill_ref(q_pre, k_pre, v, q_gain, k_gain, *, H: int, G: int, d: int,
     reading included) is rounded to bfloat16 before the scores, as a model
     computing in bfloat16 holds them.  With large QK-norm gains the scores
     grow with the gains and that rounding moves outputs by more than the
-    fp32 accumulation does; it is off by default.
+    fp32 accumulation does; it is off by default.  ``q_scale`` (with
+    ``round_rotated``): the queries are rounded as q_scale times their value
+    and divided by q_scale after, as a model that holds its queries times
+    its softmax scale in bfloat16 does; 1 rounds the queries themselves.
     """
     q_pre = np.asarray(q_pre, dtype=np.float64)
     B, T = q_pre.shape[:2]
@@ -525,7 +528,9 @@ def prefill_ref(q_pre, k_pre, v, q_gain, k_gain, *, H: int, G: int, d: int,
     w, m = layer_rope(rope, kind, d)
     positions = pos_offset + np.arange(T, dtype=np.int64)
     rnd = bf16_round if round_rotated else (lambda t: t)
-    q_rot = rnd(rope_rotate(qh, positions, w, m))
+    q_rot = rope_rotate(qh, positions, w, m)
+    if round_rotated:
+        q_rot = bf16_round(q_rot * q_scale) / q_scale
     k_rot = rnd(rope_rotate(kh, positions, w, m))
 
     if cache is not None:

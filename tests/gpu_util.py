@@ -19,6 +19,16 @@ ATOL_F32, RTOL_F32 = 1e-4, 1e-4
 KINDS = {0: O.SLIDING, 1: O.FULL}
 
 
+def prefill_q_scale(d: int, dtype=torch.bfloat16) -> float:
+    """Factor the library's prefill holds its rotated queries times: the MFMA
+    kernel (d = 128, bfloat16 operands) takes them times its base-2 softmax
+    scale, fp32(log2(e) / sqrt(d)), rounded to bfloat16 once; other paths
+    hold the queries themselves.  The rounded oracle's ``q_scale``."""
+    if d == 128 and dtype != torch.float32:
+        return float(np.float32(np.log2(np.e) / np.sqrt(np.float64(d))))
+    return 1.0
+
+
 def host(t: torch.Tensor) -> np.ndarray:
     return t.detach().to("cpu", torch.float64).numpy()
 

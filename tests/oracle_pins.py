@@ -735,18 +735,27 @@ def check_round_rotated_matches_sdpa_on_rounded_operands():
         p = np.arange(T)
         q = O.rope_rotate(O.rms_norm(x["q_pre"], x["q_gain"], 1e-6).reshape(T, H, d), p, wr, m)
         k = O.rope_rotate(O.rms_norm(x["k_pre"], x["k_gain"], 1e-6).reshape(T, G, d), p, wr, m)
-        for t in (q, k):
+        # a query scale as a kernel's base-2 softmax scale (fp32 log2(e)/sqrt(d))
+        qs = float(np.float32(math.log2(math.e) / math.sqrt(d)))
+        for t in (q, k, q * qs):
             _, e2 = np.frexp(np.abs(t))
             frac = np.abs(t) / np.ldexp(1.0, np.maximum(e2 - 1, -126) - 7) % 1.0
             assert (np.abs(frac - 0.5) > 2.0 ** -15).all(), "operand next to a bf16 midpoint"
         def tb(t):
             return torch.from_numpy(t).to(torch.bfloat16).to(torch.float64).numpy()
-        want = _sdpa(tb(q), tb(k), x["v"].reshape(T, G, d), O.mask_at_positions(p, p, kind, w))
+        mask = O.mask_at_positions(p, p, kind, w)
+        want = _sdpa(tb(q), tb(k), x["v"].reshape(T, G, d), mask)
         got = O.prefill_ref(**x, H=H, G=G, d=d, kind=kind, window=w, rope=rope,
                             round_rotated=True).reshape(T, H, d)
         _close(got, want, 1e-12, f"round_rotated vs sdpa {kind}")
         plain = O.prefill_ref(**x, H=H, G=G, d=d, kind=kind, window=w, rope=rope)
         assert np.abs(plain.reshape(T, H, d) - want).max() > 1e-4, "rounding had no effect"
+        # queries held as bf16 of qs times their value, divided by qs after
+        want_s = _sdpa(tb(q * qs) / qs, tb(k), x["v"].reshape(T, G, d), mask)
+        got_s = O.prefill_ref(**x, H=H, G=G, d=d, kind=kind, window=w, rope=rope,
+                              round_rotated=True, q_scale=qs).reshape(T, H, d)
+        _close(got_s, want_s, 1e-12, f"round_rotated with a query scale vs sdpa {kind}")
+        assert np.abs(got_s - want).max() > 1e-4, "the query scale had no effect"
 
 
 def check_round_rotated_cache_flow():

@@ -25,7 +25,7 @@ import torch
 import oracle as O
 from global_hybrid_causal_amd import attn as A
 from global_hybrid_causal_amd import synth
-from gpu_util import KINDS, assert_close, gpu_prefill, host, inputs, oracle_rope
+from gpu_util import KINDS, assert_close, gpu_prefill, host, inputs, oracle_rope, prefill_q_scale
 
 pytestmark = pytest.mark.gpu
 
@@ -226,8 +226,9 @@ PROLOGUE_CASES = [
 @pytest.mark.parametrize("case", PROLOGUE_CASES, ids=[str(c) for c in PROLOGUE_CASES])
 def test_prologue_stage_rotated_rows(case):
     """The prologue alone (phase 1): rotated queries read back from the
-    workspace's first region ([rows][H][d] bfloat16); then the rest of the
-    call, and the rotated keys read from the cache slots the call wrote."""
+    workspace's first region ([rows][H][d] bfloat16, times the MFMA
+    kernel's base-2 softmax scale); then the rest of the call, and the
+    rotated keys read from the cache slots the call wrote."""
     B, T, H, G, w, lt, yarn, P = case
     d, eps = 128, 1e-6
     kind = KINDS[lt]
@@ -259,7 +260,8 @@ def test_prologue_stage_rotated_rows(case):
     total = 0
     for b in range(B):
         e, m = _rotated_ref(hq[b], qg, H, d, eps, positions, inv_freq, mscale)
-        total += _assert_bf16_of(q_rot[b], e, m, f"queries of sequence {b}")
+        qs = prefill_q_scale(d)
+        total += _assert_bf16_of(q_rot[b], e * qs, m * qs, f"queries of sequence {b}")
         e, m = _rotated_ref(hk[b], kg, G, d, eps, positions, inv_freq, mscale)
         sel = kept - P
         got = np.transpose(hkc[b][:, slots], (1, 0, 2))

@@ -15,7 +15,7 @@ import torch
 import oracle as O
 from global_hybrid_causal_amd import attn as A
 from gpu_util import (KINDS, assert_close, gpu_decode, gpu_prefill, host, host_inputs, inputs,
-                      oracle_rope)
+                      oracle_rope, prefill_q_scale)
 
 pytestmark = pytest.mark.gpu
 
@@ -50,7 +50,8 @@ def test_sharp_scores_prefill_then_decode(H, G, lt, chunks):
         out = gpu_prefill(pre, kc, vc, window=w, layer_type=lt, rope=rope, H=H, pos_offset=p0)
         hpre = {k: (v[:, p0:p0 + n] if v.ndim == 3 else v) for k, v in hx.items()}
         ref = O.prefill_ref(**hpre, H=H, G=G, d=d, kind=kind, window=w, rope=oracle_rope(rope),
-                            pos_offset=p0, cache=c, round_rotated=True)
+                            pos_offset=p0, cache=c, round_rotated=True,
+                            q_scale=prefill_q_scale(d))
         err = assert_close(host(out), ref, what=f"sharp prefill {kind} at {p0}")
         print(f"  prefill at {p0} max err", err, flush=True)
         p0 += n

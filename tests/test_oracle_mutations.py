@@ -304,7 +304,11 @@ MUTANTS = {
     "round_rotated skips keys": dict(prefill_ref=_prefill_edited(
         "k_rot = rnd(rope_rotate(kh,", "k_rot = (rope_rotate(kh,")),
     "round_rotated skips queries": dict(prefill_ref=_prefill_edited(
-        "q_rot = rnd(rope_rotate(qh,", "q_rot = (rope_rotate(qh,")),
+        "q_rot = bf16_round(q_rot * q_scale) / q_scale", "q_rot = q_rot")),
+    "round_rotated rounds queries without their scale": dict(prefill_ref=_prefill_edited(
+        "q_rot = bf16_round(q_rot * q_scale) / q_scale", "q_rot = bf16_round(q_rot)")),
+    "round_rotated keeps the query scale": dict(prefill_ref=_prefill_edited(
+        "q_rot = bf16_round(q_rot * q_scale) / q_scale", "q_rot = bf16_round(q_rot * q_scale)")),
     "round_rotated skips cached keys": dict(prefill_ref=_prefill_edited(
         "past_k = rnd(rope_rotate(", "past_k = (rope_rotate(")),
 }
