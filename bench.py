@@ -77,28 +77,28 @@ def decode_kernel(H: int, G: int, e4m3: bool) -> str:
 
 
 MEASURED_TRAFFIC = {
-    ("7b/prefill_sliding_l0", "qknorm_rope_append_kernel"): dict(bytes=369837753, sources="fb3a6d46b16fbca7"),
-    ("7b/prefill_sliding_l0", "prefill_d128_kernel"): dict(bytes=663888064, sources="80a32a71e329155c"),
-    ("7b/prefill_full_l3", "qknorm_rope_append_kernel"): dict(bytes=403416315, sources="fb3a6d46b16fbca7"),
-    ("7b/prefill_full_l3", "prefill_d128_kernel"): dict(bytes=286878947, sources="80a32a71e329155c"),
-    ("7b/decode_sliding", "decode_prologue_kernel"): dict(bytes=1894977, sources="fb3a6d46b16fbca7"),
-    ("7b/decode_sliding", "decode_split_kernel"): dict(bytes=2148047554, sources="fce1ec309f4677d1"),
-    ("7b/decode_full", "decode_prologue_kernel"): dict(bytes=1910753, sources="fb3a6d46b16fbca7"),
-    ("7b/decode_full", "decode_split_kernel"): dict(bytes=34359428602, sources="fce1ec309f4677d1"),
-    ("32b/prefill_sliding_l0", "qknorm_rope_append_kernel"): dict(bytes=227166222, sources="fb3a6d46b16fbca7"),
-    ("32b/prefill_sliding_l0", "prefill_d128_kernel"): dict(bytes=331957273, sources="80a32a71e329155c"),
-    ("32b/prefill_full_l3", "qknorm_rope_append_kernel"): dict(bytes=235554663, sources="fb3a6d46b16fbca7"),
-    ("32b/prefill_full_l3", "prefill_d128_kernel"): dict(bytes=316898192, sources="80a32a71e329155c"),
-    ("32b/decode_sliding", "decode_prologue_kernel"): dict(bytes=2112735, sources="fb3a6d46b16fbca7"),
-    ("32b/decode_sliding", "decode_mfma_kernel"): dict(bytes=1079649700, sources="fce1ec309f4677d1"),
-    ("32b/decode_full", "decode_prologue_kernel"): dict(bytes=2117087, sources="fb3a6d46b16fbca7"),
-    ("32b/decode_full", "decode_mfma_kernel"): dict(bytes=8626261779, sources="fce1ec309f4677d1"),
-    ("long/prefill_sliding", "qknorm_rope_append_kernel"): dict(bytes=2249085043, sources="fb3a6d46b16fbca7"),
-    ("long/prefill_sliding", "prefill_d128_kernel"): dict(bytes=19823154172, sources="80a32a71e329155c"),
-    ("long/prefill_full", "qknorm_rope_append_kernel"): dict(bytes=3222450134, sources="fb3a6d46b16fbca7"),
-    ("long/prefill_full", "prefill_d128_kernel"): dict(bytes=6185615903, sources="80a32a71e329155c"),
+    ("7b/prefill_sliding_l0", "qknorm_rope_append_kernel"): dict(bytes=369835060, sources="fb3a6d46b16fbca7"),
+    ("7b/prefill_sliding_l0", "prefill_d128_kernel"): dict(bytes=1011203123, sources="2a28372811d951b9"),
+    ("7b/prefill_full_l3", "qknorm_rope_append_kernel"): dict(bytes=403418427, sources="fb3a6d46b16fbca7"),
+    ("7b/prefill_full_l3", "prefill_d128_kernel"): dict(bytes=565135980, sources="2a28372811d951b9"),
+    ("7b/decode_sliding", "decode_prologue_kernel"): dict(bytes=1894978, sources="fb3a6d46b16fbca7"),
+    ("7b/decode_sliding", "decode_split_kernel"): dict(bytes=2148048568, sources="ec3ae74d19fe5624"),
+    ("7b/decode_full", "decode_prologue_kernel"): dict(bytes=1910721, sources="fb3a6d46b16fbca7"),
+    ("7b/decode_full", "decode_split_kernel"): dict(bytes=34359435279, sources="ec3ae74d19fe5624"),
+    ("32b/prefill_sliding_l0", "qknorm_rope_append_kernel"): dict(bytes=227165984, sources="fb3a6d46b16fbca7"),
+    ("32b/prefill_sliding_l0", "prefill_d128_kernel"): dict(bytes=253344603, sources="2a28372811d951b9"),
+    ("32b/prefill_full_l3", "qknorm_rope_append_kernel"): dict(bytes=235555322, sources="fb3a6d46b16fbca7"),
+    ("32b/prefill_full_l3", "prefill_d128_kernel"): dict(bytes=266845809, sources="2a28372811d951b9"),
+    ("32b/decode_sliding", "decode_prologue_kernel"): dict(bytes=2113151, sources="fb3a6d46b16fbca7"),
+    ("32b/decode_sliding", "decode_mfma_kernel"): dict(bytes=1079555187, sources="ec3ae74d19fe5624"),
+    ("32b/decode_full", "decode_prologue_kernel"): dict(bytes=2116671, sources="fb3a6d46b16fbca7"),
+    ("32b/decode_full", "decode_mfma_kernel"): dict(bytes=8625947511, sources="ec3ae74d19fe5624"),
+    ("long/prefill_sliding", "qknorm_rope_append_kernel"): dict(bytes=2249112100, sources="fb3a6d46b16fbca7"),
+    ("long/prefill_sliding", "prefill_d128_kernel"): dict(bytes=20240468130, sources="2a28372811d951b9"),
+    ("long/prefill_full", "qknorm_rope_append_kernel"): dict(bytes=3222480146, sources="fb3a6d46b16fbca7"),
+    ("long/prefill_full", "prefill_d128_kernel"): dict(bytes=6414968898, sources="2a28372811d951b9"),
     # mean per launch over the four 7B and 32B layer launches (the `roofline` group)
-    ("32b+7b prefill calls", "prefill_d128_kernel"): dict(bytes=399905619, sources="80a32a71e329155c"),
+    ("32b+7b prefill calls", "prefill_d128_kernel"): dict(bytes=524132379, sources="2a28372811d951b9"),
 }
 
 

@@ -89,17 +89,37 @@ struct Work {
   int b, h, qb;
 };
 
-// Query block L of the remapped order -> (batch, head, query block).
-__device__ __forceinline__ Work work_at(int L, int n_qblk, int H) {
+// Grids of up to this many query blocks (16 rounds of the 512 workgroups
+// the GPU holds at once) take the interleaved order of work_at: with few
+// rounds the last one's imbalance shows.  Longer grids keep each (batch,
+// head)'s blocks together, which keeps its keys and values in the caches.
+constexpr int kInterleaveMaxBlocks = 8192;
+
+// Query block L of the remapped order -> (batch, head, query block); BH =
+// B*H pairs.  The XCD remap hands each XCD a contiguous range of L.  When
+// the pairs split evenly over the 8 XCDs, XCD x takes pairs x*k .. x*k+k-1
+// (k = BH/8: with grouped heads, the query heads of one key/value head) and,
+// in a small grid, walks their blocks longest causal rows first with the
+// pairs interleaved (query block outer, pair inner), so that every long
+// block starts in the first rounds; otherwise pair after pair, each longest
+// rows first.
+__device__ __forceinline__ Work work_at(int L, int n_qblk, int BH, int H) {
+  if (BH % 8 == 0 && n_qblk * BH <= kInterleaveMaxBlocks) {
+    const int k = BH / 8;
+    const int per = k * n_qblk;
+    const int x = L / per, j = L % per;
+    const int bh = x * k + j % k;
+    return Work{bh / H, bh % H, n_qblk - 1 - j / k};
+  }
   const int qi = L % n_qblk;
   const int bh = L / n_qblk;
   return Work{bh / H, bh % H, n_qblk - 1 - qi};
 }
 
-// Workgroup -> (batch, head, query block).  Query blocks of one head sit on
-// one XCD (shared K/V in its L2) and start with the longest causal rows.
+// Workgroup -> (batch, head, query block): the query blocks of a (batch,
+// head) sit on one XCD (shared K/V in its L2).
 __device__ __forceinline__ Work work_of(int bid, int nblk, int n_qblk, int H) {
-  return work_at(xcd_remap(bid, nblk), n_qblk, H);
+  return work_at(xcd_remap(bid, nblk), n_qblk, nblk / n_qblk, H);
 }
 
 // With kKvSplits workgroups per query block: workgroup -> block and split
@@ -108,7 +128,7 @@ __device__ __forceinline__ Work work_of(int bid, int nblk, int n_qblk, int H) {
 __device__ __forceinline__ Work work_of_split(int bid, int nblk, int n_qblk, int H, int& split) {
   const int L = xcd_remap(bid, nblk);
   split = L % kKvSplits;
-  return work_at(L / kKvSplits, n_qblk, H);
+  return work_at(L / kKvSplits, n_qblk, nblk / (kKvSplits * n_qblk), H);
 }
 
 // Key tiles [kta, ktb) of split `split` of the block's tiles [kt0, kt1).

@@ -85,6 +85,10 @@ PREFILL_CASES = [
     (1, 130, 64, 64, 128, 64, 0, False),   # 64 heads: the prologue's head limit
     (1, 600, 64, 8, 128, 4096, 1, True),   # group 8 with 64 query heads, full
     (3, 2100, 2, 1, 128, 256, 0, False),   # 6,300 rows: the one-wavefront-per-token prologue
+    # 16 query blocks x 32 heads = 512 workgroups: the unsplit instance, with
+    # the query blocks of 4 heads per XCD interleaved (the 7B / 32B order)
+    (1, 2048, 32, 8, 128, 700, 0, False),
+    (1, 2048, 32, 8, 128, 4096, 1, True),
 ]
 
 
