@@ -77,28 +77,28 @@ def decode_kernel(H: int, G: int, e4m3: bool) -> str:
 
 
 MEASURED_TRAFFIC = {
-    ("7b/prefill_sliding_l0", "qknorm_rope_append_kernel"): dict(bytes=369835060, sources="fb3a6d46b16fbca7"),
-    ("7b/prefill_sliding_l0", "prefill_d128_kernel"): dict(bytes=1011203123, sources="2a28372811d951b9"),
-    ("7b/prefill_full_l3", "qknorm_rope_append_kernel"): dict(bytes=403418427, sources="fb3a6d46b16fbca7"),
-    ("7b/prefill_full_l3", "prefill_d128_kernel"): dict(bytes=565135980, sources="2a28372811d951b9"),
-    ("7b/decode_sliding", "decode_prologue_kernel"): dict(bytes=1894978, sources="fb3a6d46b16fbca7"),
-    ("7b/decode_sliding", "decode_split_kernel"): dict(bytes=2148048568, sources="ec3ae74d19fe5624"),
-    ("7b/decode_full", "decode_prologue_kernel"): dict(bytes=1910721, sources="fb3a6d46b16fbca7"),
-    ("7b/decode_full", "decode_split_kernel"): dict(bytes=34359435279, sources="ec3ae74d19fe5624"),
-    ("32b/prefill_sliding_l0", "qknorm_rope_append_kernel"): dict(bytes=227165984, sources="fb3a6d46b16fbca7"),
-    ("32b/prefill_sliding_l0", "prefill_d128_kernel"): dict(bytes=253344603, sources="2a28372811d951b9"),
-    ("32b/prefill_full_l3", "qknorm_rope_append_kernel"): dict(bytes=235555322, sources="fb3a6d46b16fbca7"),
-    ("32b/prefill_full_l3", "prefill_d128_kernel"): dict(bytes=266845809, sources="2a28372811d951b9"),
-    ("32b/decode_sliding", "decode_prologue_kernel"): dict(bytes=2113151, sources="fb3a6d46b16fbca7"),
-    ("32b/decode_sliding", "decode_mfma_kernel"): dict(bytes=1079555187, sources="ec3ae74d19fe5624"),
-    ("32b/decode_full", "decode_prologue_kernel"): dict(bytes=2116671, sources="fb3a6d46b16fbca7"),
-    ("32b/decode_full", "decode_mfma_kernel"): dict(bytes=8625947511, sources="ec3ae74d19fe5624"),
-    ("long/prefill_sliding", "qknorm_rope_append_kernel"): dict(bytes=2249112100, sources="fb3a6d46b16fbca7"),
-    ("long/prefill_sliding", "prefill_d128_kernel"): dict(bytes=20240468130, sources="2a28372811d951b9"),
-    ("long/prefill_full", "qknorm_rope_append_kernel"): dict(bytes=3222480146, sources="fb3a6d46b16fbca7"),
-    ("long/prefill_full", "prefill_d128_kernel"): dict(bytes=6414968898, sources="2a28372811d951b9"),
+    ("7b/prefill_sliding_l0", "qknorm_rope_append_kernel"): dict(bytes=369837429, sources="fb3a6d46b16fbca7"),
+    ("7b/prefill_sliding_l0", "prefill_d128_kernel"): dict(bytes=534840329, sources="409255db9a69aba4"),
+    ("7b/prefill_full_l3", "qknorm_rope_append_kernel"): dict(bytes=403385162, sources="fb3a6d46b16fbca7"),
+    ("7b/prefill_full_l3", "prefill_d128_kernel"): dict(bytes=499154469, sources="409255db9a69aba4"),
+    ("7b/decode_sliding", "decode_prologue_kernel"): dict(bytes=1894943, sources="fb3a6d46b16fbca7"),
+    ("7b/decode_sliding", "decode_split_kernel"): dict(bytes=2148042860, sources="b4d3143a9d70430c"),
+    ("7b/decode_full", "decode_prologue_kernel"): dict(bytes=1910814, sources="fb3a6d46b16fbca7"),
+    ("7b/decode_full", "decode_split_kernel"): dict(bytes=34359347113, sources="b4d3143a9d70430c"),
+    ("32b/prefill_sliding_l0", "qknorm_rope_append_kernel"): dict(bytes=227166129, sources="fb3a6d46b16fbca7"),
+    ("32b/prefill_sliding_l0", "prefill_d128_kernel"): dict(bytes=253315514, sources="409255db9a69aba4"),
+    ("32b/prefill_full_l3", "qknorm_rope_append_kernel"): dict(bytes=235554167, sources="fb3a6d46b16fbca7"),
+    ("32b/prefill_full_l3", "prefill_d128_kernel"): dict(bytes=266702179, sources="409255db9a69aba4"),
+    ("32b/decode_sliding", "decode_prologue_kernel"): dict(bytes=2113532, sources="fb3a6d46b16fbca7"),
+    ("32b/decode_sliding", "decode_mfma_kernel"): dict(bytes=1079198971, sources="b4d3143a9d70430c"),
+    ("32b/decode_full", "decode_prologue_kernel"): dict(bytes=2116284, sources="fb3a6d46b16fbca7"),
+    ("32b/decode_full", "decode_mfma_kernel"): dict(bytes=8622524827, sources="b4d3143a9d70430c"),
+    ("long/prefill_sliding", "qknorm_rope_append_kernel"): dict(bytes=2249108787, sources="fb3a6d46b16fbca7"),
+    ("long/prefill_sliding", "prefill_d128_kernel"): dict(bytes=20318600774, sources="409255db9a69aba4"),
+    ("long/prefill_full", "qknorm_rope_append_kernel"): dict(bytes=3222453515, sources="fb3a6d46b16fbca7"),
+    ("long/prefill_full", "prefill_d128_kernel"): dict(bytes=6505109549, sources="409255db9a69aba4"),
     # mean per launch over the four 7B and 32B layer launches (the `roofline` group)
-    ("32b+7b prefill calls", "prefill_d128_kernel"): dict(bytes=524132379, sources="2a28372811d951b9"),
+    ("32b+7b prefill calls", "prefill_d128_kernel"): dict(bytes=388503123, sources="409255db9a69aba4"),
 }
 
 

@@ -122,8 +122,11 @@ __global__ __launch_bounds__(256, 2) void prefill_d128_kernel(AttnArgs a) {
 
   const int n_qblk = (a.Tq + kBQ - 1) / kBQ;
   int split = 0;
-  const Work w = kSplit ? work_of_split(blockIdx.x, gridDim.x, n_qblk, a.H, split)
-                        : work_of(blockIdx.x, gridDim.x, n_qblk, a.H);
+  // (packed sequences start at their own positions: all interleaved)
+  const int n_even =
+      kPacked ? 0 : even_blocks(n_qblk, a.H, a.G, a.sliding, a.window, (int)a.q_pos0);
+  const Work w = kSplit ? work_of_split(blockIdx.x, gridDim.x, n_qblk, a.H, n_even, split)
+                        : work_of(blockIdx.x, gridDim.x, n_qblk, a.H, n_even);
   const int g = w.h / (a.H / a.G);
   // this sequence: query rows row0 .. row0 + len - 1 at positions qpos0 ..,
   // keys at positions 0 .. n_keys - 1
@@ -518,8 +521,8 @@ __global__ __launch_bounds__(256) void probe_prefill_kernel(int T, int pos_offse
   const int n_qblk = (T + kBQ - 1) / kBQ;
   const int n_keys = pos_offset + T;
   int split = 0;
-  const Work w = kv_splits > 1 ? work_of_split(blockIdx.x, gridDim.x, n_qblk, 1, split)
-                               : work_of(blockIdx.x, gridDim.x, n_qblk, 1);
+  const Work w = kv_splits > 1 ? work_of_split(blockIdx.x, gridDim.x, n_qblk, 1, 0, split)
+                               : work_of(blockIdx.x, gridDim.x, n_qblk, 1, 0);
   const int q0 = pos_offset + w.qb * kBQ, q1 = min(q0 + kBQ, n_keys);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int tq = lane_query(q0, wave, lane);

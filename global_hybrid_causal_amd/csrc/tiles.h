@@ -98,37 +98,65 @@ constexpr int kInterleaveMaxBlocks = 8192;
 // Query block L of the remapped order -> (batch, head, query block); BH =
 // B*H pairs.  The XCD remap hands each XCD a contiguous range of L.  When
 // the pairs split evenly over the 8 XCDs, XCD x takes pairs x*k .. x*k+k-1
-// (k = BH/8: with grouped heads, the query heads of one key/value head) and,
-// in a small grid, walks their blocks longest causal rows first with the
-// pairs interleaved (query block outer, pair inner), so that every long
-// block starts in the first rounds; otherwise pair after pair, each longest
-// rows first.
-__device__ __forceinline__ Work work_at(int L, int n_qblk, int BH, int H) {
+// (k = BH/8: with grouped heads, the query heads of one key/value head).
+// In a small grid it first walks the last n_even blocks of each pair (blocks
+// of equal work, e.g. full sliding windows) pair after pair, then the rest
+// longest causal rows first with the pairs interleaved (query block outer,
+// pair inner), so that every long block starts in the first rounds while
+// blocks of one pair keep their keys and values together where order does
+// not matter.  Otherwise (and with n_even = n_qblk) pair after pair, each
+// longest rows first.
+__device__ __forceinline__ Work work_at(int L, int n_qblk, int BH, int H, int n_even) {
   if (BH % 8 == 0 && n_qblk * BH <= kInterleaveMaxBlocks) {
     const int k = BH / 8;
     const int per = k * n_qblk;
-    const int x = L / per, j = L % per;
-    const int bh = x * k + j % k;
-    return Work{bh / H, bh % H, n_qblk - 1 - j / k};
+    const int x = L / per;
+    int j = L % per, p, qb;
+    if (j < k * n_even) {
+      p = j / n_even;
+      qb = n_qblk - 1 - j % n_even;
+    } else {
+      j -= k * n_even;
+      p = j % k;
+      qb = n_qblk - n_even - 1 - j / k;
+    }
+    const int bh = x * k + p;
+    return Work{bh / H, bh % H, qb};
   }
   const int qi = L % n_qblk;
   const int bh = L / n_qblk;
   return Work{bh / H, bh % H, n_qblk - 1 - qi};
 }
 
+// Blocks a uniform prefill keeps pair after pair (work_at's n_even): on a
+// sliding layer with one query head per key/value head, the blocks whose
+// windows are full (equal work, the last ones); everywhere else none.
+// Grouped query heads read the same keys and values, so they gain from
+// running side by side; full layers measured faster interleaved.
+__device__ __forceinline__ int even_blocks(int n_qblk, int H, int G, int sliding, int window,
+                                           int q_pos0) {
+  if (H != G || !sliding) return 0;
+  // block qb starts at q_pos0 + qb kBQ; its window is full from q0 >= window - 1
+  const int64_t d = (int64_t)window - 1 - q_pos0;
+  if (d <= 0) return n_qblk;
+  const int64_t first = (d + kBQ - 1) / kBQ;
+  return first >= n_qblk ? 0 : n_qblk - (int)first;
+}
+
 // Workgroup -> (batch, head, query block): the query blocks of a (batch,
 // head) sit on one XCD (shared K/V in its L2).
-__device__ __forceinline__ Work work_of(int bid, int nblk, int n_qblk, int H) {
-  return work_at(xcd_remap(bid, nblk), n_qblk, nblk / n_qblk, H);
+__device__ __forceinline__ Work work_of(int bid, int nblk, int n_qblk, int H, int n_even) {
+  return work_at(xcd_remap(bid, nblk), n_qblk, nblk / n_qblk, H, n_even);
 }
 
 // With kKvSplits workgroups per query block: workgroup -> block and split
 // (the splits of a block are neighbours in the remapped order, so they share
 // an XCD).
-__device__ __forceinline__ Work work_of_split(int bid, int nblk, int n_qblk, int H, int& split) {
+__device__ __forceinline__ Work work_of_split(int bid, int nblk, int n_qblk, int H, int n_even,
+                                              int& split) {
   const int L = xcd_remap(bid, nblk);
   split = L % kKvSplits;
-  return work_at(L / kKvSplits, n_qblk, nblk / (kKvSplits * n_qblk), H);
+  return work_at(L / kKvSplits, n_qblk, nblk / (kKvSplits * n_qblk), H, n_even);
 }
 
 // Key tiles [kta, ktb) of split `split` of the block's tiles [kt0, kt1).

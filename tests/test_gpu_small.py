@@ -86,9 +86,13 @@ PREFILL_CASES = [
     (1, 600, 64, 8, 128, 4096, 1, True),   # group 8 with 64 query heads, full
     (3, 2100, 2, 1, 128, 256, 0, False),   # 6,300 rows: the one-wavefront-per-token prologue
     # 16 query blocks x 32 heads = 512 workgroups: the unsplit instance, with
-    # the query blocks of 4 heads per XCD interleaved (the 7B / 32B order)
+    # the query blocks of 4 heads per XCD interleaved (grouped heads; full
+    # layers), or the 10 full-window blocks of each head first, head after
+    # head, and the rest interleaved (one query head per key/value head,
+    # sliding)
     (1, 2048, 32, 8, 128, 700, 0, False),
     (1, 2048, 32, 8, 128, 4096, 1, True),
+    (1, 2048, 32, 32, 128, 700, 0, False),
 ]
 
 
