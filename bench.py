@@ -77,28 +77,28 @@ def decode_kernel(H: int, G: int, e4m3: bool) -> str:
 
 
 MEASURED_TRAFFIC = {
-    ("7b/prefill_sliding_l0", "qknorm_rope_append_kernel"): dict(bytes=369837429, sources="fb3a6d46b16fbca7"),
-    ("7b/prefill_sliding_l0", "prefill_d128_kernel"): dict(bytes=534840329, sources="409255db9a69aba4"),
-    ("7b/prefill_full_l3", "qknorm_rope_append_kernel"): dict(bytes=403385162, sources="fb3a6d46b16fbca7"),
-    ("7b/prefill_full_l3", "prefill_d128_kernel"): dict(bytes=499154469, sources="409255db9a69aba4"),
-    ("7b/decode_sliding", "decode_prologue_kernel"): dict(bytes=1894943, sources="fb3a6d46b16fbca7"),
-    ("7b/decode_sliding", "decode_split_kernel"): dict(bytes=2148042860, sources="b4d3143a9d70430c"),
-    ("7b/decode_full", "decode_prologue_kernel"): dict(bytes=1910814, sources="fb3a6d46b16fbca7"),
-    ("7b/decode_full", "decode_split_kernel"): dict(bytes=34359347113, sources="b4d3143a9d70430c"),
-    ("32b/prefill_sliding_l0", "qknorm_rope_append_kernel"): dict(bytes=227166129, sources="fb3a6d46b16fbca7"),
-    ("32b/prefill_sliding_l0", "prefill_d128_kernel"): dict(bytes=253315514, sources="409255db9a69aba4"),
-    ("32b/prefill_full_l3", "qknorm_rope_append_kernel"): dict(bytes=235554167, sources="fb3a6d46b16fbca7"),
-    ("32b/prefill_full_l3", "prefill_d128_kernel"): dict(bytes=266702179, sources="409255db9a69aba4"),
-    ("32b/decode_sliding", "decode_prologue_kernel"): dict(bytes=2113532, sources="fb3a6d46b16fbca7"),
-    ("32b/decode_sliding", "decode_mfma_kernel"): dict(bytes=1079198971, sources="b4d3143a9d70430c"),
-    ("32b/decode_full", "decode_prologue_kernel"): dict(bytes=2116284, sources="fb3a6d46b16fbca7"),
-    ("32b/decode_full", "decode_mfma_kernel"): dict(bytes=8622524827, sources="b4d3143a9d70430c"),
-    ("long/prefill_sliding", "qknorm_rope_append_kernel"): dict(bytes=2249108787, sources="fb3a6d46b16fbca7"),
-    ("long/prefill_sliding", "prefill_d128_kernel"): dict(bytes=20318600774, sources="409255db9a69aba4"),
-    ("long/prefill_full", "qknorm_rope_append_kernel"): dict(bytes=3222453515, sources="fb3a6d46b16fbca7"),
-    ("long/prefill_full", "prefill_d128_kernel"): dict(bytes=6505109549, sources="409255db9a69aba4"),
+    ("7b/prefill_sliding_l0", "qknorm_rope_append_kernel"): dict(bytes=369829721, sources="698d00bb50ad00da"),
+    ("7b/prefill_sliding_l0", "prefill_d128_kernel"): dict(bytes=550013977, sources="ca4d3856a3738d99"),
+    ("7b/prefill_full_l3", "qknorm_rope_append_kernel"): dict(bytes=403382729, sources="698d00bb50ad00da"),
+    ("7b/prefill_full_l3", "prefill_d128_kernel"): dict(bytes=568240730, sources="ca4d3856a3738d99"),
+    ("7b/decode_sliding", "decode_prologue_kernel"): dict(bytes=1895197, sources="698d00bb50ad00da"),
+    ("7b/decode_sliding", "decode_split_kernel"): dict(bytes=2148037911, sources="4b67bc8a681e176b"),
+    ("7b/decode_full", "decode_prologue_kernel"): dict(bytes=1910972, sources="698d00bb50ad00da"),
+    ("7b/decode_full", "decode_split_kernel"): dict(bytes=34359278327, sources="4b67bc8a681e176b"),
+    ("32b/prefill_sliding_l0", "qknorm_rope_append_kernel"): dict(bytes=227165550, sources="698d00bb50ad00da"),
+    ("32b/prefill_sliding_l0", "prefill_d128_kernel"): dict(bytes=253362563, sources="ca4d3856a3738d99"),
+    ("32b/prefill_full_l3", "qknorm_rope_append_kernel"): dict(bytes=235553795, sources="698d00bb50ad00da"),
+    ("32b/prefill_full_l3", "prefill_d128_kernel"): dict(bytes=266877244, sources="ca4d3856a3738d99"),
+    ("32b/decode_sliding", "decode_prologue_kernel"): dict(bytes=2113562, sources="698d00bb50ad00da"),
+    ("32b/decode_sliding", "decode_mfma_kernel"): dict(bytes=1079346818, sources="4b67bc8a681e176b"),
+    ("32b/decode_full", "decode_prologue_kernel"): dict(bytes=2116858, sources="698d00bb50ad00da"),
+    ("32b/decode_full", "decode_mfma_kernel"): dict(bytes=8624507172, sources="4b67bc8a681e176b"),
+    ("long/prefill_sliding", "qknorm_rope_append_kernel"): dict(bytes=2249100419, sources="698d00bb50ad00da"),
+    ("long/prefill_sliding", "prefill_d128_kernel"): dict(bytes=20187753857, sources="ca4d3856a3738d99"),
+    ("long/prefill_full", "qknorm_rope_append_kernel"): dict(bytes=3222470100, sources="698d00bb50ad00da"),
+    ("long/prefill_full", "prefill_d128_kernel"): dict(bytes=6537490627, sources="ca4d3856a3738d99"),
     # mean per launch over the four 7B and 32B layer launches (the `roofline` group)
-    ("32b+7b prefill calls", "prefill_d128_kernel"): dict(bytes=388503123, sources="409255db9a69aba4"),
+    ("32b+7b prefill calls", "prefill_d128_kernel"): dict(bytes=409623628, sources="ca4d3856a3738d99"),
 }
 
 

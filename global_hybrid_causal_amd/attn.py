@@ -21,7 +21,7 @@ from . import LAYER_FULL, LAYER_SLIDING  # noqa: F401  (re-exported)
 LIB_PATH = os.environ.get("OLMO3_ATTN_LIB") or os.path.join(
     os.path.dirname(os.path.abspath(__file__)), "libolmo3attn.so")
 
-ABI_VERSION = 10  # OLMO3_ABI_VERSION of include/olmo3_attn.h
+ABI_VERSION = 11  # OLMO3_ABI_VERSION of include/olmo3_attn.h
 DTYPE_BF16, DTYPE_F32, DTYPE_BF16_E4M3 = 0, 1, 2
 MODE_PREFILL, MODE_DECODE = 0, 1
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_CAPACITY, ERR_HIP, ERR_WORKSPACE = range(6)
@@ -30,7 +30,8 @@ OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_CAPACITY, ERR_HIP, ERR_WORKSPACE = ran
 EXPORTS = (
     "olmo3_layer_type", "olmo3_workspace_bytes", "olmo3_kv_append", "olmo3_attn_prefill",
     "olmo3_attn_decode", "olmo3_status_string", "olmo3_abi_version",
-    "olmo3_probe_prefill_visits", "olmo3_probe_decode_reads", "olmo3_attn_prefill_phases",
+    "olmo3_probe_prefill_visits", "olmo3_probe_prefill_order", "olmo3_probe_decode_reads",
+    "olmo3_attn_prefill_phases",
     "olmo3_attn_decode_phases", "olmo3_attn_prefill_ragged", "olmo3_attn_decode_ragged",
     "olmo3_kv_append_e4m3", "olmo3_attn_prefill_e4m3", "olmo3_attn_decode_e4m3",
     "olmo3_attn_decode_e4m3_phases", "olmo3_attn_decode_ragged_e4m3",
@@ -145,6 +146,8 @@ def lib() -> ctypes.CDLL:
         L.olmo3_abi_version.restype = _i
         L.olmo3_probe_prefill_visits.argtypes = [_i, _i64, _i, _i, _i, _p, _p]
         L.olmo3_probe_prefill_visits.restype = _i
+        L.olmo3_probe_prefill_order.argtypes = [_i, _i, _i, _i, _i, _i, _i64, _i, _p, _i64]
+        L.olmo3_probe_prefill_order.restype = _i
         L.olmo3_probe_decode_reads.argtypes = [_i, _i, _i, _i, _i, _i, _i, _i64, _i64, _p, _p]
         L.olmo3_probe_decode_reads.restype = _i
         if L.olmo3_abi_version() != ABI_VERSION:
@@ -461,6 +464,18 @@ def olmo3_probe_prefill_visits(T: int, window: int, layer_type: int, pos_offset:
                                           _ptr(visit, "visit"), _stream(None, visit.device))
     _check(st, "olmo3_probe_prefill_visits")
     return visit
+
+
+def olmo3_probe_prefill_order(B: int, T: int, H: int, G: int, window: int, layer_type: int,
+                              pos_offset: int = 0, kv_splits: int = 1) -> torch.Tensor:
+    """[n, 4] int32 CPU tensor: the (sequence, head, query block, key split)
+    each workgroup of the d = 128 prefill kernel takes, in workgroup order."""
+    n = -(-T // 128) * H * B * kv_splits
+    work = torch.zeros((n, 4), dtype=torch.int32)
+    st = lib().olmo3_probe_prefill_order(B, T, H, G, window, layer_type, pos_offset, kv_splits,
+                                         work.data_ptr(), work.numel())
+    _check(st, "olmo3_probe_prefill_order")
+    return work
 
 
 def olmo3_probe_decode_reads(B: int, H: int, G: int, d: int, window: int, layer_type: int,

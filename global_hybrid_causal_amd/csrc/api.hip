@@ -887,6 +887,32 @@ int olmo3_probe_prefill_visits(int T, int64_t pos_offset, int window, int layer_
                                          kv_splits, visit, (hipStream_t)stream));
 }
 
+int olmo3_probe_prefill_order(int B, int T, int H, int G, int window, int layer_type,
+                              int64_t pos_offset, int kv_splits, int32_t* work, int64_t work_len) {
+  if (B < 1 || T < 1 || G < 1 || H < G || H % G || window < 1 || pos_offset < 0 || !work)
+    return OLMO3_ERR_INVALID_ARG;
+  if (kv_splits != 1 && kv_splits != pf::kKvSplits) return OLMO3_ERR_INVALID_ARG;
+  if (layer_type != OLMO3_LAYER_SLIDING && layer_type != OLMO3_LAYER_FULL) return OLMO3_ERR_INVALID_ARG;
+  if (pos_offset + T > kMaxPrefillPositions) return OLMO3_ERR_UNSUPPORTED;
+  const int64_t n_qblk = (T + pf::kBQ - 1) / pf::kBQ;
+  const int64_t n = n_qblk * H * B * kv_splits;
+  if (n > ((int64_t)1 << 24)) return OLMO3_ERR_UNSUPPORTED;
+  if (work_len < 4 * n) return OLMO3_ERR_INVALID_ARG;
+  const int n_even = pf::even_blocks((int)n_qblk, H, G, layer_type == OLMO3_LAYER_SLIDING,
+                                     window, (int)pos_offset);
+  for (int bid = 0; bid < (int)n; ++bid) {
+    int split = 0;
+    const pf::Work w = kv_splits > 1
+                           ? pf::work_of_split(bid, (int)n, (int)n_qblk, H, n_even, split)
+                           : pf::work_of(bid, (int)n, (int)n_qblk, H, n_even);
+    work[4 * bid] = w.b;
+    work[4 * bid + 1] = w.h;
+    work[4 * bid + 2] = w.qb;
+    work[4 * bid + 3] = split;
+  }
+  return OLMO3_OK;
+}
+
 int olmo3_probe_decode_reads(int B, int H, int G, int d, int window, int layer_type, int dtype,
                              int64_t pos, int64_t cache_capacity, int32_t* count, void* stream) {
   if (B < 1 || G < 1 || H < G || H % G || d != 128 || window < 1 || pos < 0 || !count)

@@ -102,7 +102,7 @@ __device__ __forceinline__ float wave_sum(float x) {
 // Map the hardware workgroup id so that consecutive logical work items land
 // on the same XCD (workgroups are dealt round-robin over the 8 XCDs), which
 // keeps items that share K/V in one XCD's L2.  Identity when n % 8 != 0.
-__device__ __forceinline__ int xcd_remap(int bid, int n) {
+__host__ __device__ __forceinline__ int xcd_remap(int bid, int n) {
   constexpr int kXcd = 8;
   if (n % kXcd) return bid;
   return (bid % kXcd) * (n / kXcd) + bid / kXcd;

@@ -106,7 +106,7 @@ constexpr int kInterleaveMaxBlocks = 8192;
 // blocks of one pair keep their keys and values together where order does
 // not matter.  Otherwise (and with n_even = n_qblk) pair after pair, each
 // longest rows first.
-__device__ __forceinline__ Work work_at(int L, int n_qblk, int BH, int H, int n_even) {
+__host__ __device__ __forceinline__ Work work_at(int L, int n_qblk, int BH, int H, int n_even) {
   if (BH % 8 == 0 && n_qblk * BH <= kInterleaveMaxBlocks) {
     const int k = BH / 8;
     const int per = k * n_qblk;
@@ -133,8 +133,8 @@ __device__ __forceinline__ Work work_at(int L, int n_qblk, int BH, int H, int n_
 // windows are full (equal work, the last ones); everywhere else none.
 // Grouped query heads read the same keys and values, so they gain from
 // running side by side; full layers measured faster interleaved.
-__device__ __forceinline__ int even_blocks(int n_qblk, int H, int G, int sliding, int window,
-                                           int q_pos0) {
+__host__ __device__ __forceinline__ int even_blocks(int n_qblk, int H, int G, int sliding,
+                                                    int window, int q_pos0) {
   if (H != G || !sliding) return 0;
   // block qb starts at q_pos0 + qb kBQ; its window is full from q0 >= window - 1
   const int64_t d = (int64_t)window - 1 - q_pos0;
@@ -145,15 +145,15 @@ __device__ __forceinline__ int even_blocks(int n_qblk, int H, int G, int sliding
 
 // Workgroup -> (batch, head, query block): the query blocks of a (batch,
 // head) sit on one XCD (shared K/V in its L2).
-__device__ __forceinline__ Work work_of(int bid, int nblk, int n_qblk, int H, int n_even) {
+__host__ __device__ __forceinline__ Work work_of(int bid, int nblk, int n_qblk, int H, int n_even) {
   return work_at(xcd_remap(bid, nblk), n_qblk, nblk / n_qblk, H, n_even);
 }
 
 // With kKvSplits workgroups per query block: workgroup -> block and split
 // (the splits of a block are neighbours in the remapped order, so they share
 // an XCD).
-__device__ __forceinline__ Work work_of_split(int bid, int nblk, int n_qblk, int H, int n_even,
-                                              int& split) {
+__host__ __device__ __forceinline__ Work work_of_split(int bid, int nblk, int n_qblk, int H,
+                                                       int n_even, int& split) {
   const int L = xcd_remap(bid, nblk);
   split = L % kKvSplits;
   return work_at(L / kKvSplits, n_qblk, nblk / (kKvSplits * n_qblk), H, n_even);

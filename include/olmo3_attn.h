@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define OLMO3_ABI_VERSION 10
+#define OLMO3_ABI_VERSION 11
 
 typedef enum olmo3_status {
   OLMO3_OK = 0,
@@ -383,6 +383,18 @@ int olmo3_abi_version(void);
  * Errors: INVALID_ARG, UNSUPPORTED. */
 int olmo3_probe_prefill_visits(int T, int64_t pos_offset, int window, int layer_type,
                                int kv_splits, uint8_t* visit, void* stream);
+
+/* work [n][4] int32 (host memory; no device is touched): the (sequence,
+ * head, query block, key split) that each workgroup of the d = 128 prefill
+ * kernel over B uniform sequences of T queries at pos_offset takes, in
+ * workgroup order, as the kernel computes it (same functions): n =
+ * ceil(T / 128) * H * B workgroups with kv_splits 1, twice that with
+ * kv_splits 2 (the key-split instance; split 0 or 1, else 0).  work_len: the
+ * array's length in int32 (at least 4 n).  ABI version 11.
+ * Errors: INVALID_ARG (shapes, layer type, kv_splits other than 1 or 2, a
+ * null or short array), UNSUPPORTED (more than 2^24 workgroups). */
+int olmo3_probe_prefill_order(int B, int T, int H, int G, int window, int layer_type,
+                              int64_t pos_offset, int kv_splits, int32_t* work, int64_t work_len);
 
 /* count [cache_capacity] int32 (device): number of times the decode kernel
  * at position `pos` reads each cache slot of one (sequence, KV head) into

@@ -43,7 +43,7 @@ def test_header_binding_and_library_versions_agree():
 
 
 def test_abi_version():
-    assert A.olmo3_abi_version() == A.ABI_VERSION == 10
+    assert A.olmo3_abi_version() == A.ABI_VERSION == 11
 
 
 def test_layer_type_matches_oracle_bit_exact():
